@@ -1,0 +1,347 @@
+"""Float64 CPU oracle of the Hymba hybrid-head mixer (test infrastructure only).
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg
+use this module. Everything here is the plain definition, evaluated the slow
+and obvious way in NumPy float64 from the exact stored input values:
+
+* the Mamba branch: causal depthwise conv, the selective SSM recurrence run as
+  a sequential loop over time, the D skip and the silu(z) gate;
+* the attention branch: rotary embedding, grouped-query softmax attention over
+  a full score matrix with an explicit visibility mask (meta prefix, sliding
+  window or global causal);
+* the fusion: per-row RMS normalisation of each branch, per-channel beta, mean.
+
+Sources (web pages, cited by title and section):
+
+* [Hymba guide] "Hymba Guide: NVIDIA Hybrid-Head Mamba & Attention SLM":
+  "1. Parallel Hybrid-Head Layer Formulation", "2. Learnable Meta-Tokens",
+  "Systems Mechanics: Cross-Layer KV Cache Sharing".
+* [Jamba] "Jamba: Hybrid SSM-Transformer": "How It Actually Works",
+  "1. Layer Interleaving Ratio" (selective SSM update, scaled dot-product
+  attention), "2. KV Cache Memory Economics", "Worked Example", "Code".
+* [Lecture 04] "Lecture 04 - Beyond the Dense Transformer: Mamba, SSMs, and
+  the Hybrid Wave": section 1 (the KV cache loop), section 2 (SSM loop,
+  discretisation and the two limits of the step size), section 8 (sizes).
+* [Hymba-1.5B article] 51cto release article on Hymba-1.5B-Base: section 1
+  (meta tokens, cross-layer KV sharing, sliding-window attention), section 2
+  (model shapes: GQA, RoPE, 16 SSM states, 3 full-attention layers).
+
+Where the pages leave a step open, the plainest reading is taken; each such
+reading is named in the docstring of the function that applies it. The pages
+print no mixer output, so the numerics of the readings themselves (conv taps,
+RoPE pairing, value-head width, norm type) are fixed only by those readings;
+every function below is pinned by the CPU tests to closed forms, brute force,
+invariants or library routines.
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=F64)
+
+
+# ---------------------------------------------------------------------------
+# Mamba branch
+
+
+def causal_conv1d(x, w, history=None) -> np.ndarray:
+    """Causal depthwise conv along time, per channel.
+
+    u[b,t,c] = sum_j w[c,j] * x[b, t-(K-1)+j, c]; the last tap multiplies the
+    current row. Rows before the start come from ``history`` ([B, K-1, D],
+    oldest first) or are zero. No bias and no activation after the conv.
+    The pages do not describe this conv; this is the plain reading of a causal
+    depthwise conv1d placed before the selective scan.
+
+    x: [B, L, D]; w: [D, K] -> u: [B, L, D]
+    """
+    x = _f64(x)
+    w = _f64(w)
+    Bsz, L, D = x.shape
+    K = w.shape[1]
+    if history is None:
+        pad = np.zeros((Bsz, K - 1, D), F64)
+    else:
+        pad = _f64(history)
+    xp = np.concatenate([pad, x], axis=1)  # row t of x is row t+K-1 of xp
+    u = np.zeros((Bsz, L, D), F64)
+    for j in range(K):
+        u += w[None, None, :, j] * xp[:, j:j + L, :]
+    return u
+
+
+def selective_scan(u, dt, A, Bm, Cm, D, h0=None):
+    """Selective SSM recurrence, one time step after another.
+
+    Jamba, "1. Layer Interleaving Ratio": h_t = exp(dt_t A) h_{t-1} + (dt_t B_t) x_t,
+    y_t = C_t h_t. Lecture 04, section 2: A is discretised as exp(dt A) and B as
+    dt B; section 2's loop carries a fixed-size state through time. Here A is
+    per (channel, state) and diagonal, so the update is element-wise per
+    state; B_t and C_t are shared by all channels; D adds the skip D*u_t.
+
+    u, dt: [B, L, D]; A: [D, N]; Bm, Cm: [B, L, N]; D: [D]; h0: [B, D, N] or None.
+    Returns y [B, L, D] (before the gate) and the final state [B, D, N].
+    """
+    u, dt, A, Bm, Cm, D = map(_f64, (u, dt, A, Bm, Cm, D))
+    Bsz, L, Dch = u.shape
+    N = A.shape[1]
+    h = np.zeros((Bsz, Dch, N), F64) if h0 is None else _f64(h0).copy()
+    y = np.zeros((Bsz, L, Dch), F64)
+    for t in range(L):
+        dA = np.exp(dt[:, t, :, None] * A[None, :, :])                 # exp(dt A)
+        dBx = (dt[:, t, :, None] * Bm[:, t, None, :]) * u[:, t, :, None]  # (dt B) x
+        h = dA * h + dBx
+        y[:, t, :] = np.einsum("bdn,bn->bd", h, Cm[:, t, :]) + D[None, :] * u[:, t, :]
+    return y, h
+
+
+def silu_gate(y, z) -> np.ndarray:
+    """Output gate of the Mamba branch: y * silu(z), silu(z) = z / (1 + exp(-z)).
+    Not described on the pages; the plain reading of a silu(z) gate."""
+    y, z = _f64(y), _f64(z)
+    return y * (z / (1.0 + np.exp(-z)))
+
+
+# ---------------------------------------------------------------------------
+# Attention branch
+
+
+def rope_angles(positions, head_dim: int, base: float) -> np.ndarray:
+    """angle[p, i] = pos_p * base**(-2i/d) for i < d/2 (float64)."""
+    pos = _f64(positions)
+    i = np.arange(head_dim // 2, dtype=F64)
+    theta = base ** (-2.0 * i / head_dim)
+    return pos[:, None] * theta[None, :]
+
+
+def rope(x, positions, base: float) -> np.ndarray:
+    """Rotary position embedding (named in the Hymba-1.5B article, section 2).
+
+    Reading: rotate-half pairing, element i with element i + d/2, by the angle
+    pos * base**(-2i/d); absolute positions count the meta rows.
+    x: [..., P, H, d] with positions [P] -> same shape.
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    ang = rope_angles(positions, d, base)          # [P, d/2]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def visible(i, j, n_meta: int, window: int):
+    """May query row i attend to key row j?
+
+    Causal (j <= i). Meta rows (j < n_meta) are visible to every later row
+    under any window (Hymba guide, "2. Learnable Meta-Tokens"; Hymba-1.5B
+    article, section 2: meta tokens interact with all later tokens). Other
+    rows need i - j < window when the layer uses a sliding window (window > 0);
+    window <= 0 is a global (full causal) layer.
+    Works element-wise on integer arrays.
+    """
+    i = np.asarray(i)
+    j = np.asarray(j)
+    ok = j <= i
+    if window > 0:
+        ok = ok & ((j < n_meta) | (i - j < window))
+    return ok
+
+
+def mask_ranges(n_rows: int, n_meta: int, window: int) -> np.ndarray:
+    """Per query row: [meta_end, win_begin, win_end, count] (int32).
+
+    Found by enumerating ``visible`` over every key j: the visible meta keys
+    are [0, meta_end); the visible non-meta keys are [win_begin, win_end)
+    (both equal to n_meta when there are none); count is the number of
+    visible keys.
+    """
+    out = np.zeros((n_rows, 4), np.int32)
+    j = np.arange(n_rows)
+    for i in range(n_rows):
+        vis = visible(i, j, n_meta, window)
+        meta_vis = np.nonzero(vis & (j < n_meta))[0]
+        win_vis = np.nonzero(vis & (j >= n_meta))[0]
+        meta_end = int(meta_vis.max()) + 1 if meta_vis.size else 0
+        if win_vis.size:
+            wb, we = int(win_vis.min()), int(win_vis.max()) + 1
+        else:
+            wb = we = n_meta
+        out[i] = (meta_end, wb, we, int(vis.sum()))
+    return out
+
+
+def attention(q_rot, k_rot, v, n_meta: int, window: int, rows: Optional[np.ndarray] = None,
+              key_positions: Optional[np.ndarray] = None, query_positions: Optional[np.ndarray] = None,
+              block: int = 512) -> np.ndarray:
+    """Grouped-query scaled dot-product attention over a visibility mask.
+
+    Jamba, "1. Layer Interleaving Ratio": softmax(Q K^T / sqrt(d_k)) V. Each
+    group of Hq/Hkv consecutive query heads reads one key/value head
+    (GQA, Hymba-1.5B article, section 2). A full score block is formed per
+    (sequence, head), invisible entries are removed, and the softmax subtracts
+    the row maximum before exponentiating.
+
+    q_rot: [B, Lq, Hq, d]; k_rot: [B, Lk, Hkv, d]; v: [B, Lk, Hkv, dv]
+    rows: query rows to evaluate (default all); returns [B, len(rows), Hq, dv].
+    Positions default to the row indices (prefill).
+    """
+    q_rot, k_rot, v = _f64(q_rot), _f64(k_rot), _f64(v)
+    Bsz, Lq, Hq, d = q_rot.shape
+    Lk, Hkv, dv = k_rot.shape[1], k_rot.shape[2], v.shape[3]
+    group = Hq // Hkv
+    if rows is None:
+        rows = np.arange(Lq)
+    rows = np.asarray(rows)
+    qpos = np.arange(Lq) if query_positions is None else np.asarray(query_positions)
+    kpos = np.arange(Lk) if key_positions is None else np.asarray(key_positions)
+    scale = 1.0 / np.sqrt(d)
+    out = np.zeros((Bsz, len(rows), Hq, dv), F64)
+    for b in range(Bsz):
+        for h in range(Hq):
+            g = h // group
+            K = k_rot[b, :, g, :]
+            V = v[b, :, g, :]
+            for r0 in range(0, len(rows), block):
+                rr = rows[r0:r0 + block]
+                s = (q_rot[b, rr, h, :] @ K.T) * scale              # [nr, Lk]
+                m = visible(qpos[rr][:, None], kpos[None, :], n_meta, window)
+                s = np.where(m, s, -np.inf)
+                s = s - s.max(axis=1, keepdims=True)
+                p = np.exp(s)
+                p /= p.sum(axis=1, keepdims=True)
+                out[b, r0:r0 + len(rr), h, :] = p @ V
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Fusion of the two branches
+
+
+def rms_fuse(y_attn, y_ssm, beta_attn, beta_ssm, eps: float) -> np.ndarray:
+    """out = (beta_attn * n(y_attn) + beta_ssm * n(y_ssm)) / 2 per row, with
+    n(y) = y / sqrt(mean(y^2) + eps) over the row's channels.
+
+    The pages combine the two head families (Hymba guide, "1. Parallel
+    Hybrid-Head Layer Formulation", concatenation then an output projection
+    outside this mixer); the normalise-scale-average combination is the
+    reading used here: RMS norm without a separate gain, per-channel beta.
+    y_attn, y_ssm: [..., W]; beta_*: [W].
+    """
+    ya, ys = _f64(y_attn), _f64(y_ssm)
+    na = ya / np.sqrt(np.mean(ya * ya, axis=-1, keepdims=True) + eps)
+    ns = ys / np.sqrt(np.mean(ys * ys, axis=-1, keepdims=True) + eps)
+    return 0.5 * (_f64(beta_attn) * na + _f64(beta_ssm) * ns)
+
+
+# ---------------------------------------------------------------------------
+# Whole mixer
+
+
+def mixer_prefill(cfg, inp: Dict[str, np.ndarray], batches: Optional[Iterable[int]] = None,
+                  rows: Optional[np.ndarray] = None, with_attention: bool = True) -> Dict[str, np.ndarray]:
+    """Prefill of L = n_meta + n_tokens rows per sequence, meta rows first
+    (Hymba guide, "2. Learnable Meta-Tokens": meta tokens are prepended; they
+    pre-populate the SSM state and stay visible to attention).
+
+    Both branches read the same rows (Hymba guide, "1. Parallel Hybrid-Head
+    Layer Formulation"). The conv history and SSM state start at zero.
+
+    ``batches`` restricts to some sequences; ``rows`` restricts the attention
+    and fused outputs to some query rows (the scan always runs over all rows).
+    Returns float64 arrays: y_ssm [b, L, D], ssm_state [b, D, N],
+    conv_state [b, D, K-1] (last K-1 raw x rows, oldest first),
+    k_rot [b, L, Hkv, d], and for the selected rows y_attn [b, R, D] and
+    out [b, R, D].
+    """
+    bsel = np.arange(cfg.batch) if batches is None else np.asarray(list(batches))
+    L = cfg.seq_rows
+    rsel = np.arange(L) if rows is None else np.asarray(rows)
+    x = _f64(inp["x"])[bsel]
+    u = causal_conv1d(x, inp["conv_w"])
+    y, h = selective_scan(u, _f64(inp["dt"])[bsel], inp["A"], _f64(inp["B"])[bsel],
+                          _f64(inp["C"])[bsel], inp["D"])
+    y_ssm = silu_gate(y, _f64(inp["z"])[bsel])
+    K = cfg.d_conv
+    conv_state = np.zeros((len(bsel), cfg.d_inner, K - 1), F64)
+    for j in range(K - 1):                       # oldest first
+        t = L - (K - 1) + j
+        if t >= 0:
+            conv_state[:, :, j] = x[:, t, :]
+    res = {"y_ssm": y_ssm, "ssm_state": h, "conv_state": conv_state, "rows": rsel}
+    pos = np.arange(L)
+    k_rot = rope(_f64(inp["k"])[bsel], pos, cfg.rope_base)
+    res["k_rot"] = k_rot
+    if with_attention:
+        q_rot = rope(_f64(inp["q"])[bsel], pos, cfg.rope_base)
+        ya = attention(q_rot, k_rot, _f64(inp["v"])[bsel], cfg.n_meta, cfg.window, rows=rsel)
+        y_attn = ya.reshape(len(bsel), len(rsel), cfg.n_q_heads * cfg.head_dim_v)  # head-major concat
+        res["y_attn"] = y_attn
+        res["out"] = rms_fuse(y_attn, y_ssm[:, rsel, :], inp["beta_attn"], inp["beta_ssm"], cfg.norm_eps)
+    return res
+
+
+def mixer_decode(cfg, layer_inp: Dict[str, np.ndarray], k_cache, v_cache, k_new, v_new,
+                 cache_len) -> Dict[str, np.ndarray]:
+    """One new row per sequence at position p = cache_len[b].
+
+    Lecture 04, section 1: the new token attends over the cached keys and
+    values of earlier rows plus its own; section 2: the SSM carries a fixed
+    size state, updated once. The cache holds rotated keys and values for
+    rows < p and is only read (Hymba guide, "1. The KV Sharing Mechanism":
+    layers that share a cache read the same key/value tensors). Visibility is
+    the prefill rule at query row p. Conv state holds the last K-1 raw x rows,
+    oldest first, and both states are advanced by one row.
+
+    Returns out, y_attn, y_ssm [B, D] and the new ssm_state [B, D, N],
+    conv_state [B, D, K-1] (float64).
+    """
+    li = layer_inp
+    Bsz, D = li["x"].shape
+    K = cfg.d_conv
+    x = _f64(li["x"])[:, None, :]                                   # [B,1,D]
+    hist = np.transpose(_f64(li["conv_state"]), (0, 2, 1))          # [B,K-1,D]
+    u = causal_conv1d(x, li["conv_w"], history=hist)
+    y, h = selective_scan(u, _f64(li["dt"])[:, None, :], li["A"], _f64(li["B"])[:, None, :],
+                          _f64(li["C"])[:, None, :], li["D"], h0=li["ssm_state"])
+    y_ssm = silu_gate(y, _f64(li["z"])[:, None, :])[:, 0, :]
+    new_conv = np.concatenate([_f64(li["conv_state"])[:, :, 1:], _f64(li["x"])[:, :, None]], axis=2)
+
+    Hq, dv = cfg.n_q_heads, cfg.head_dim_v
+    y_attn = np.zeros((Bsz, Hq * dv), F64)
+    for b in range(Bsz):
+        p = int(cache_len[b])
+        pos = np.array([p])
+        q_rot = rope(_f64(li["q"])[b][None, None], pos, cfg.rope_base)          # [1,1,Hq,d]
+        kn = rope(_f64(k_new)[b][None, None], pos, cfg.rope_base)[0]             # [1,Hkv,d]
+        keys = np.concatenate([_f64(k_cache[b, :p]), kn], axis=0)[None]          # [1,p+1,Hkv,d]
+        vals = np.concatenate([_f64(v_cache[b, :p]), _f64(v_new)[b][None]], axis=0)[None]
+        ya = attention(q_rot, keys, vals, cfg.n_meta, cfg.window, rows=np.array([0]),
+                       key_positions=np.arange(p + 1), query_positions=pos)
+        y_attn[b] = ya.reshape(Hq * dv)
+    out = rms_fuse(y_attn, y_ssm, li["beta_attn"], li["beta_ssm"], cfg.norm_eps)
+    return {"out": out, "y_attn": y_attn, "y_ssm": y_ssm, "ssm_state": h, "conv_state": new_conv}
+
+
+# ---------------------------------------------------------------------------
+# Cache sizes
+
+
+def kv_cache_bytes(batch: int, seq_len: int, n_attn_layers: int, kv_heads: int, head_dim: int,
+                   dtype_bytes: int = 2) -> int:
+    """Jamba, "2. KV Cache Memory Economics": keys and values (factor 2), each
+    element dtype_bytes wide, for every token, attention layer, KV head and
+    head dimension. Lecture 04, section 1 states the same product."""
+    return 2 * dtype_bytes * batch * seq_len * n_attn_layers * kv_heads * head_dim
+
+
+def ssm_state_bytes(layers: int, heads: int, head_dim: int, d_state: int, batch: int,
+                    dtype_bytes: int = 2) -> int:
+    """Lecture 04, section 8: the fixed SSM state, independent of context."""
+    return layers * heads * head_dim * d_state * batch * dtype_bytes
