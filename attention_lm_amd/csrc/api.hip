@@ -1,0 +1,242 @@
+// C ABI of the Hymba mixer library: argument validation, workspace layout and
+// the order of kernel launches. Every check runs before anything is enqueued.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/hymba_mixer.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return HYMBA_OK;
+  g_last_hip_error = (int)e;
+  return HYMBA_EHIP;
+}
+
+#define HYMBA_TRY(expr)                         \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return hip_status(e_); \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t act_bytes(hymba_dtype t) { return t == HYMBA_BF16 ? 2 : 4; }
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Geometry checks shared by prefill and decode.
+int check_desc(const hymba_mixer_desc* d, bool decode) {
+  if (!d) return HYMBA_EINVAL;
+  if (d->act != HYMBA_F32 && d->act != HYMBA_BF16) return HYMBA_EINVAL;
+  if (d->batch < 1 || d->n_meta < 0 || d->d_inner < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 ||
+      d->head_dim < 1 || d->head_dim_v < 1 || d->d_state < 1 || d->d_conv < 1)
+    return HYMBA_EINVAL;
+  if (!decode && (d->n_tokens < 0 || (int64_t)d->n_meta + d->n_tokens < 1)) return HYMBA_EINVAL;
+  if ((int64_t)d->n_meta + d->n_tokens > INT32_MAX / 2) return HYMBA_EINVAL;
+  if (d->n_q_heads % d->n_kv_heads != 0) return HYMBA_EINVAL;
+  if ((int64_t)d->n_q_heads * d->head_dim_v != d->d_inner) return HYMBA_EINVAL;
+  if (!(d->rope_base > 0.f) || !(d->norm_eps >= 0.f)) return HYMBA_EINVAL;
+  if (d->cache_capacity < 0) return HYMBA_EINVAL;
+  if (decode && d->cache_capacity < 1) return HYMBA_EINVAL;
+  // what this build has kernels for
+  if (d->d_state != 16 || d->d_conv != 4 || d->head_dim != 64) return HYMBA_EUNSUPPORTED;
+  if (d->head_dim_v != 32 && d->head_dim_v != 64 && d->head_dim_v != 128) return HYMBA_EUNSUPPORTED;
+  if (d->n_q_heads / d->n_kv_heads > 10) return HYMBA_EUNSUPPORTED;
+  if (d->d_inner % 8 != 0) return HYMBA_EUNSUPPORTED;
+  return HYMBA_OK;
+}
+
+int check_params(const hymba_mixer_params* p) {
+  if (!p || !p->A || !p->D || !p->conv_w || !p->beta_attn || !p->beta_ssm) return HYMBA_EINVAL;
+  if (p->conv_b) return HYMBA_EUNSUPPORTED;
+  if (!aligned16(p->A) || !aligned16(p->D) || !aligned16(p->conv_w) || !aligned16(p->beta_attn) ||
+      !aligned16(p->beta_ssm))
+    return HYMBA_EALIGN;
+  return HYMBA_OK;
+}
+
+struct PrefillWs {
+  size_t q_rot, k_rot, y_attn, y_ssm, total;
+};
+PrefillWs prefill_ws(const hymba_mixer_desc* d) {
+  const size_t es = act_bytes(d->act);
+  const size_t rows = (size_t)d->batch * ((size_t)d->n_meta + d->n_tokens);
+  PrefillWs w;
+  w.q_rot = 0;
+  w.k_rot = w.q_rot + round256(rows * d->n_q_heads * d->head_dim * es);
+  w.y_attn = w.k_rot + round256(rows * d->n_kv_heads * d->head_dim * es);
+  w.y_ssm = w.y_attn + round256(rows * d->d_inner * es);
+  w.total = w.y_ssm + round256(rows * d->d_inner * es);
+  return w;
+}
+
+struct DecodeWs {
+  size_t partial, y_ssm, total;
+  int n_split, keys_per_split;
+};
+DecodeWs decode_ws(const hymba_mixer_desc* d) {
+  DecodeWs w;
+  hymba::decode_split_plan(d->n_meta, d->window, d->cache_capacity, &w.n_split, &w.keys_per_split);
+  w.partial = 0;
+  w.y_ssm = round256((size_t)d->batch * d->n_q_heads * w.n_split * (d->head_dim_v + 2) * sizeof(float));
+  w.total = w.y_ssm + round256((size_t)d->batch * d->d_inner * act_bytes(d->act));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hymba_mixer_prefill_workspace_bytes(const hymba_mixer_desc* desc) {
+  if (check_desc(desc, false) != HYMBA_OK) return 0;
+  return prefill_ws(desc).total;
+}
+
+size_t hymba_mixer_decode_workspace_bytes(const hymba_mixer_desc* desc) {
+  if (check_desc(desc, true) != HYMBA_OK) return 0;
+  return decode_ws(desc).total;
+}
+
+int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* params, const void* x,
+                        const void* z, const void* dt, const void* B, const void* C, const void* q, const void* k,
+                        const void* v, void* out, float* ssm_state_out, void* conv_state_out, void* k_cache,
+                        void* v_cache, void* y_attn_out, void* y_ssm_out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  int st = check_desc(desc, false);
+  if (st != HYMBA_OK) return st;
+  st = check_params(params);
+  if (st != HYMBA_OK) return st;
+  const void* req[] = {x, z, dt, B, C, q, k, v, out};
+  for (const void* p : req)
+    if (!p) return HYMBA_EINVAL;
+  for (const void* p : req)
+    if (!aligned16(p)) return HYMBA_EALIGN;
+  const void* opt[] = {ssm_state_out, conv_state_out, k_cache, v_cache, y_attn_out, y_ssm_out};
+  for (const void* p : opt)
+    if (p && !aligned16(p)) return HYMBA_EALIGN;
+  if ((k_cache == nullptr) != (v_cache == nullptr)) return HYMBA_EINVAL;
+  const int L = desc->n_meta + desc->n_tokens;
+  if (k_cache && desc->cache_capacity < L) return HYMBA_EINVAL;
+  const PrefillWs ws = prefill_ws(desc);
+  if (!workspace || workspace_bytes < ws.total) return HYMBA_EWORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HYMBA_EALIGN;
+
+  char* wsb = (char*)workspace;
+  void* q_rot = wsb + ws.q_rot;
+  void* k_rot = k_cache ? k_cache : (void*)(wsb + ws.k_rot);
+  const int64_t k_rows = k_cache ? desc->cache_capacity : L;
+  void* y_attn = y_attn_out ? y_attn_out : (void*)(wsb + ws.y_attn);
+  void* y_ssm = y_ssm_out ? y_ssm_out : (void*)(wsb + ws.y_ssm);
+
+  hymba::SsmPrefillArgs sa;
+  sa.x = x; sa.z = z; sa.dt = dt; sa.B = B; sa.C = C;
+  sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
+  sa.y = y_ssm; sa.state_out = ssm_state_out; sa.conv_state_out = conv_state_out;
+  sa.batch = desc->batch; sa.L = L; sa.d_inner = desc->d_inner; sa.act = desc->act;
+  HYMBA_TRY(hymba::launch_ssm_prefill(sa, stream));
+
+  hymba::RopeArgs ra;
+  ra.q = q; ra.k = k; ra.v = v; ra.q_rot = q_rot; ra.k_rot = k_rot; ra.v_copy = v_cache;
+  ra.k_rows = k_rows; ra.v_rows = desc->cache_capacity;
+  ra.batch = desc->batch; ra.L = L; ra.n_q_heads = desc->n_q_heads; ra.n_kv_heads = desc->n_kv_heads;
+  ra.head_dim = desc->head_dim; ra.head_dim_v = desc->head_dim_v; ra.rope_base = desc->rope_base;
+  ra.act = desc->act;
+  HYMBA_TRY(hymba::launch_rope_prefill(ra, stream));
+
+  hymba::AttnPrefillArgs aa;
+  aa.q_rot = q_rot; aa.k_rot = k_rot; aa.v = v; aa.k_rows = k_rows; aa.v_rows = L; aa.y = y_attn;
+  aa.batch = desc->batch; aa.L = L; aa.n_meta = desc->n_meta; aa.window = desc->window;
+  aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
+  aa.act = desc->act;
+  HYMBA_TRY(hymba::launch_attn_prefill(aa, stream));
+
+  HYMBA_TRY(hymba::launch_fuse(y_attn, y_ssm, params->beta_attn, params->beta_ssm, (int64_t)desc->batch * L,
+                               desc->d_inner, desc->norm_eps, desc->act, out, stream));
+  return HYMBA_OK;
+}
+
+int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* params, const void* x,
+                       const void* z, const void* dt, const void* B, const void* C, const void* q,
+                       const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
+                       const int32_t* cache_len, float* ssm_state, void* conv_state, void* out, void* y_attn_out,
+                       void* y_ssm_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_desc(desc, true);
+  if (st != HYMBA_OK) return st;
+  st = check_params(params);
+  if (st != HYMBA_OK) return st;
+  const void* req[] = {x, z, dt, B, C, q, k_new, v_new, k_cache, v_cache, cache_len, ssm_state, conv_state, out};
+  for (const void* p : req)
+    if (!p) return HYMBA_EINVAL;
+  for (const void* p : req)
+    if (!aligned16(p)) return HYMBA_EALIGN;
+  if ((y_attn_out && !aligned16(y_attn_out)) || (y_ssm_out && !aligned16(y_ssm_out))) return HYMBA_EALIGN;
+  const DecodeWs ws = decode_ws(desc);
+  if (!workspace || workspace_bytes < ws.total) return HYMBA_EWORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HYMBA_EALIGN;
+
+  char* wsb = (char*)workspace;
+  float* partial = (float*)(wsb + ws.partial);
+  void* y_ssm = y_ssm_out ? y_ssm_out : (void*)(wsb + ws.y_ssm);
+
+  hymba::SsmDecodeArgs sa;
+  sa.x = x; sa.z = z; sa.dt = dt; sa.B = B; sa.C = C;
+  sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
+  sa.state = ssm_state; sa.conv_state = conv_state; sa.y = y_ssm;
+  sa.batch = desc->batch; sa.d_inner = desc->d_inner; sa.act = desc->act;
+  HYMBA_TRY(hymba::launch_ssm_decode(sa, stream));
+
+  hymba::AttnDecodeArgs aa;
+  aa.q = q; aa.k_new = k_new; aa.v_new = v_new; aa.k_cache = k_cache; aa.v_cache = v_cache;
+  aa.cache_len = cache_len; aa.partial = partial; aa.n_split = ws.n_split; aa.keys_per_split = ws.keys_per_split;
+  aa.batch = desc->batch; aa.cap = desc->cache_capacity; aa.n_meta = desc->n_meta; aa.window = desc->window;
+  aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
+  aa.rope_base = desc->rope_base; aa.act = desc->act;
+  HYMBA_TRY(hymba::launch_attn_decode(aa, stream));
+
+  hymba::DecodeCombineArgs ca;
+  ca.partial = partial; ca.y_ssm = y_ssm; ca.beta_attn = params->beta_attn; ca.beta_ssm = params->beta_ssm;
+  ca.out = out; ca.y_attn_out = y_attn_out; ca.n_split = ws.n_split; ca.batch = desc->batch;
+  ca.n_q_heads = desc->n_q_heads; ca.head_dim_v = desc->head_dim_v; ca.eps = desc->norm_eps; ca.act = desc->act;
+  HYMBA_TRY(hymba::launch_decode_combine(ca, stream));
+  return HYMBA_OK;
+}
+
+int hymba_fuse_heads(const void* y_attn, const void* y_ssm, const float* beta_attn, const float* beta_ssm,
+                     int64_t n_rows, int32_t width, float eps, hymba_dtype act, void* out, hipStream_t stream) {
+  if (act != HYMBA_F32 && act != HYMBA_BF16) return HYMBA_EINVAL;
+  if (n_rows < 0 || width < 1 || !(eps >= 0.f)) return HYMBA_EINVAL;
+  if (n_rows == 0) return HYMBA_OK;  // nothing to do (empty tensors may carry null pointers)
+  if (!y_attn || !y_ssm || !beta_attn || !beta_ssm || !out) return HYMBA_EINVAL;
+  if (!aligned16(y_attn) || !aligned16(y_ssm) || !aligned16(beta_attn) || !aligned16(beta_ssm) || !aligned16(out))
+    return HYMBA_EALIGN;
+  return hip_status(hymba::launch_fuse(y_attn, y_ssm, beta_attn, beta_ssm, n_rows, width, eps, act, out, stream));
+}
+
+int hymba_debug_mask_ranges(const hymba_mixer_desc* desc, int32_t* ranges, hipStream_t stream) {
+  if (!desc || !ranges) return HYMBA_EINVAL;
+  if (desc->n_meta < 0 || desc->n_tokens < 0 || (int64_t)desc->n_meta + desc->n_tokens > INT32_MAX / 2)
+    return HYMBA_EINVAL;
+  if (!aligned16(ranges)) return HYMBA_EALIGN;
+  return hip_status(hymba::launch_mask_ranges(desc->n_meta + desc->n_tokens, desc->n_meta, desc->window, ranges,
+                                              stream));
+}
+
+const char* hymba_status_string(int status) {
+  switch (status) {
+    case HYMBA_OK: return "ok";
+    case HYMBA_EINVAL: return "invalid argument";
+    case HYMBA_EUNSUPPORTED: return "unsupported geometry";
+    case HYMBA_EALIGN: return "pointer not 16-byte aligned (workspace: 256-byte)";
+    case HYMBA_EHIP: return "HIP runtime error";
+    case HYMBA_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int hymba_last_hip_error(void) { return g_last_hip_error; }
+
+int hymba_abi_version(void) { return HYMBA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Shared device helpers for the Hymba mixer kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hymba {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bf16 storage type (bit pattern). Arithmetic always happens in fp32.
+struct bf16 {
+  uint16_t u;
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float((uint32_t)v.u << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float f) { return bf16{f32_to_bf16_bits(f)}; }
+
+// Elements of T per 16-byte vector.
+template <typename T> struct Vec16 { static constexpr int n = 16 / sizeof(T); };
+
+// Load 16 bytes (Vec16<T>::n elements) as fp32.
+__device__ __forceinline__ void load16(const float* p, float* o) {
+  float4 v = *reinterpret_cast<const float4*>(p);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void load16(const bf16* p, float* o) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+  o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+}
+__device__ __forceinline__ void store16(float* p, const float* o) {
+  *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+}
+__device__ __forceinline__ void store16(bf16* p, const float* o) {
+  uint4 v;
+  v.x = pack_bf16x2(o[0], o[1]); v.y = pack_bf16x2(o[2], o[3]);
+  v.z = pack_bf16x2(o[4], o[5]); v.w = pack_bf16x2(o[6], o[7]);
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+// Wave64 butterfly sum / max (deterministic order).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Visibility of key row j to query row i (the one rule all kernels use).
+//
+// Causal: j <= i. The meta-token rows j < n_meta are visible to every later
+// row under any window (Hymba guide, "2. Learnable Meta-Tokens"; the
+// Hymba-1.5B article, section 2). Other rows need i - j < window in a
+// sliding-window layer (window > 0); window <= 0 is a global causal layer.
+struct MaskRange {
+  int meta_end;   // visible meta keys: [0, meta_end)
+  int win_begin;  // visible non-meta keys: [win_begin, win_end); both n_meta if none
+  int win_end;
+};
+
+__host__ __device__ __forceinline__ MaskRange mask_range(int i, int n_meta, int window) {
+  MaskRange r;
+  r.meta_end = i + 1 < n_meta ? i + 1 : n_meta;
+  int wb = n_meta;
+  if (window > 0) {
+    int lo = i - window + 1;
+    wb = lo > n_meta ? lo : n_meta;
+  }
+  int we = i + 1;
+  if (we <= wb) { wb = n_meta; we = n_meta; }
+  r.win_begin = wb;
+  r.win_end = we;
+  return r;
+}
+
+__host__ __device__ __forceinline__ bool key_visible(int i, int j, int n_meta, int window) {
+  if (j > i) return false;
+  if (window <= 0 || j < n_meta) return true;
+  return i - j < window;
+}
+
+}  // namespace hymba

@@ -1,0 +1,106 @@
+// Fusion of the two branch outputs: per row, RMS-normalise each branch over its
+// channels, scale by the per-channel betas and average. HBM-bound: each row's
+// two inputs are read once from HBM (the second pass over the row hits cache)
+// and the output written once. One wave per row, four rows per workgroup.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace hymba {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void fuse_rows_kernel(
+    const T* __restrict__ ya, const T* __restrict__ ys, const float* __restrict__ ba,
+    const float* __restrict__ bs, int64_t n_rows, int width, float eps, T* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  const T* a = ya + row * (int64_t)width;
+  const T* s = ys + row * (int64_t)width;
+  T* o = out + row * (int64_t)width;
+  constexpr int V = VEC ? Vec16<T>::n : 1;
+
+  float sa = 0.f, ss = 0.f;
+  for (int c = lane * V; c < width; c += 64 * V) {
+    float va[V], vs[V];
+    if constexpr (VEC) {
+      load16(a + c, va);
+      load16(s + c, vs);
+    } else {
+      va[0] = to_f32(a[c]);
+      vs[0] = to_f32(s[c]);
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      sa = fmaf(va[e], va[e], sa);
+      ss = fmaf(vs[e], vs[e], ss);
+    }
+  }
+  sa = wave_sum(sa);
+  ss = wave_sum(ss);
+  const float inv_w = 1.0f / (float)width;
+  const float ra = 0.5f / sqrtf(sa * inv_w + eps);
+  const float rs = 0.5f / sqrtf(ss * inv_w + eps);
+
+  for (int c = lane * V; c < width; c += 64 * V) {
+    float va[V], vs[V], r[V];
+    if constexpr (VEC) {
+      load16(a + c, va);
+      load16(s + c, vs);
+    } else {
+      va[0] = to_f32(a[c]);
+      vs[0] = to_f32(s[c]);
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) r[e] = fmaf(ba[c + e] * ra, va[e], bs[c + e] * rs * vs[e]);
+    if constexpr (VEC) {
+      store16(o + c, r);
+    } else {
+      o[c] = from_f32<T>(r[0]);
+    }
+  }
+}
+
+__global__ void mask_ranges_kernel(int n_rows, int n_meta, int window, int32_t* __restrict__ ranges) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_rows) return;
+  MaskRange r = mask_range(i, n_meta, window);
+  int4 v = make_int4(r.meta_end, r.win_begin, r.win_end, r.meta_end + (r.win_end - r.win_begin));
+  *reinterpret_cast<int4*>(ranges + 4 * (int64_t)i) = v;
+}
+
+template <typename T>
+hipError_t fuse_t(const void* ya, const void* ys, const float* ba, const float* bs, int64_t n_rows,
+                  int width, float eps, void* out, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const bool vec = (width % Vec16<T>::n) == 0;
+  dim3 grid((unsigned)blocks), block(64 * kRowsPerBlock);
+  if (vec)
+    hipLaunchKernelGGL((fuse_rows_kernel<T, true>), grid, block, 0, stream, (const T*)ya, (const T*)ys, ba,
+                       bs, n_rows, width, eps, (T*)out);
+  else
+    hipLaunchKernelGGL((fuse_rows_kernel<T, false>), grid, block, 0, stream, (const T*)ya, (const T*)ys, ba,
+                       bs, n_rows, width, eps, (T*)out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fuse(const void* y_attn, const void* y_ssm, const float* beta_attn, const float* beta_ssm,
+                       int64_t n_rows, int width, float eps, hymba_dtype act, void* out, hipStream_t stream) {
+  if (act == HYMBA_BF16) return fuse_t<bf16>(y_attn, y_ssm, beta_attn, beta_ssm, n_rows, width, eps, out, stream);
+  return fuse_t<float>(y_attn, y_ssm, beta_attn, beta_ssm, n_rows, width, eps, out, stream);
+}
+
+hipError_t launch_mask_ranges(int n_rows, int n_meta, int window, int32_t* ranges, hipStream_t stream) {
+  if (n_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mask_ranges_kernel, dim3((n_rows + 255) / 256), dim3(256), 0, stream, n_rows, n_meta,
+                     window, ranges);
+  return hipGetLastError();
+}
+
+}  // namespace hymba

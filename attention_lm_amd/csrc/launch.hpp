@@ -1,0 +1,92 @@
+// Internal launchers shared by the C-ABI layer (api.hip) and the kernel files.
+// All arguments have been validated by the caller; launchers only enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/hymba_mixer.h"
+
+namespace hymba {
+
+// fuse.hip ------------------------------------------------------------------
+hipError_t launch_fuse(const void* y_attn, const void* y_ssm, const float* beta_attn,
+                       const float* beta_ssm, int64_t n_rows, int width, float eps,
+                       hymba_dtype act, void* out, hipStream_t stream);
+hipError_t launch_mask_ranges(int n_rows, int n_meta, int window, int32_t* ranges,
+                              hipStream_t stream);
+
+// ssm.hip -------------------------------------------------------------------
+struct SsmPrefillArgs {
+  const void *x, *z, *dt, *B, *C;
+  const float *A, *D, *conv_w;
+  void* y;                 // [batch, L, d_inner] act
+  float* state_out;        // optional [batch, d_inner, 16]
+  void* conv_state_out;    // optional [batch, d_inner, 3]
+  int batch, L, d_inner;
+  hymba_dtype act;
+};
+hipError_t launch_ssm_prefill(const SsmPrefillArgs& a, hipStream_t stream);
+
+struct SsmDecodeArgs {
+  const void *x, *z, *dt, *B, *C;
+  const float *A, *D, *conv_w;
+  float* state;            // in/out [batch, d_inner, 16]
+  void* conv_state;        // in/out [batch, d_inner, 3] act
+  void* y;                 // [batch, d_inner] act
+  int batch, d_inner;
+  hymba_dtype act;
+};
+hipError_t launch_ssm_decode(const SsmDecodeArgs& a, hipStream_t stream);
+
+// attn.hip ------------------------------------------------------------------
+struct RopeArgs {
+  const void *q, *k, *v;   // inputs [batch, L, H, d]
+  void* q_rot;             // [batch, L, Hq, hd] act
+  void* k_rot;             // rows with stride k_rows per sequence
+  void* v_copy;            // optional, rows with stride v_rows per sequence
+  int64_t k_rows, v_rows;  // rows per sequence of k_rot / v_copy (>= L)
+  int batch, L, n_q_heads, n_kv_heads, head_dim, head_dim_v;
+  float rope_base;
+  hymba_dtype act;
+};
+hipError_t launch_rope_prefill(const RopeArgs& a, hipStream_t stream);
+
+struct AttnPrefillArgs {
+  const void* q_rot;       // [batch, L, Hq, 64]
+  const void* k_rot;       // [batch, k_rows, Hkv, 64]
+  const void* v;           // [batch, v_rows, Hkv, dv]
+  int64_t k_rows, v_rows;
+  void* y;                 // [batch, L, Hq*dv] act
+  int batch, L, n_meta, window, n_q_heads, n_kv_heads, head_dim_v;
+  hymba_dtype act;
+};
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream);
+
+struct AttnDecodeArgs {
+  const void *q, *k_new, *v_new;       // [batch, H, d] not rotated
+  const void *k_cache, *v_cache;       // [batch, cap, Hkv, d]
+  const int32_t* cache_len;
+  float* partial;                      // [batch, Hq, n_split, dv + 2]
+  int n_split, keys_per_split;
+  int batch, cap, n_meta, window, n_q_heads, n_kv_heads, head_dim_v;
+  float rope_base;
+  hymba_dtype act;
+};
+hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream);
+void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_per_split);
+
+struct DecodeCombineArgs {
+  const float* partial;    // [batch, Hq, n_split, dv + 2]
+  const void* y_ssm;       // [batch, d_inner] act
+  const float *beta_attn, *beta_ssm;
+  void* out;               // [batch, d_inner]
+  void* y_attn_out;        // optional
+  int n_split, batch, n_q_heads, head_dim_v;
+  float eps;
+  hymba_dtype act;
+};
+hipError_t launch_decode_combine(const DecodeCombineArgs& a, hipStream_t stream);
+
+}  // namespace hymba

@@ -1,0 +1,204 @@
+/*
+ * hymba_mixer.h -- C ABI of the Hymba hybrid-head token mixer for MI355X (gfx950).
+ *
+ * The mixer of one Hymba layer, taking the already-projected tensors. The same
+ * rows feed two parallel branches ("Hymba Guide: NVIDIA Hybrid-Head Mamba &
+ * Attention SLM", section "1. Parallel Hybrid-Head Layer Formulation"):
+ *
+ *   Mamba branch     u = causal depthwise conv1d(x);
+ *                    h_t = exp(dt_t * A) (.) h_{t-1} + (dt_t * B_t) * u_t,
+ *                    y_t = C_t . h_t + D * u_t;  y_ssm = y * silu(z)
+ *                    ("Jamba: Hybrid SSM-Transformer", "1. Layer Interleaving
+ *                    Ratio"; "Lecture 04 - Beyond the Dense Transformer",
+ *                    section 2, discretisation exp(dt A), dt B).
+ *   Attention branch GQA softmax(q k^T / sqrt(64)) v with RoPE on q and k, over
+ *                    meta-token rows that every later row sees plus a sliding
+ *                    window (or all earlier rows in a global layer)
+ *                    (Hymba guide, "2. Learnable Meta-Tokens"; 51cto Hymba-1.5B
+ *                    article, sections 1-2: GQA, RoPE, sliding-window attention
+ *                    in most layers, three full-attention layers).
+ *   Fusion           out = (beta_attn * rmsnorm(y_attn) + beta_ssm * rmsnorm(y_ssm)) / 2
+ *                    per row (RMS norm over the row's d_inner channels, no gain).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers, caller-owned, contiguous row-major,
+ *    16-byte aligned. The library never allocates or frees device memory and
+ *    never synchronises the host; scratch space comes from the caller's
+ *    `workspace` argument (size from the *_workspace_bytes queries).
+ *  - All argument checks run on the host first; on any error nothing is
+ *    enqueued and a negative hymba_status is returned.
+ *  - Work is enqueued asynchronously on `stream` (NULL = the null stream).
+ *    Results are deterministic run to run: reductions use no atomics.
+ *  - Inputs are read-only. No output may alias an input or another output.
+ *  - Activation tensors (x, z, dt, B, C, q, k, v, out, y_*, conv state, KV
+ *    cache) share one dtype, `act`. Parameters and the SSM state are fp32.
+ *    Arithmetic is fp32 throughout; bf16 products on the matrix cores
+ *    accumulate in fp32; each output is rounded once to its storage type.
+ *  - Return value: HYMBA_OK, or a negative hymba_status. HYMBA_EHIP means a
+ *    HIP call failed; hymba_last_hip_error() gives its hipError_t (per thread).
+ */
+#ifndef HYMBA_MIXER_H_
+#define HYMBA_MIXER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYMBA_ABI_VERSION 1
+
+typedef enum { HYMBA_F32 = 0, HYMBA_BF16 = 1 } hymba_dtype;
+
+typedef enum {
+  HYMBA_OK = 0,
+  HYMBA_EINVAL = -1,        /* null pointer, bad size or inconsistent geometry */
+  HYMBA_EUNSUPPORTED = -2,  /* valid geometry this build has no kernel for     */
+  HYMBA_EALIGN = -3,        /* a tensor pointer is not 16-byte aligned          */
+  HYMBA_EHIP = -4,          /* a HIP runtime call or kernel launch failed       */
+  HYMBA_EWORKSPACE = -5     /* workspace missing or smaller than required       */
+} hymba_status;
+
+/* Geometry of one mixer call.
+ *  batch       sequences (prefill) or sequences with one new row each (decode)
+ *  n_meta      meta-token rows at the start of every sequence (Hymba guide,
+ *              "2. Learnable Meta-Tokens": prepended to the prompt)
+ *  n_tokens    prompt rows after the meta rows (prefill); L = n_meta + n_tokens
+ *              rows per sequence. Decode ignores it.
+ *  d_inner     Mamba channels; also the attention output width (n_q_heads * head_dim_v)
+ *  d_state     SSM state size per channel: 16 (Hymba-1.5B article, section 2)
+ *  d_conv      conv taps: 4
+ *  n_q_heads, n_kv_heads   GQA: query head h reads kv head h / (n_q_heads / n_kv_heads)
+ *  head_dim    query/key width: 64
+ *  head_dim_v  value width: d_inner / n_q_heads, one of 32, 64, 128
+ *  window      > 0: query row i sees non-meta key rows j with i - j < window;
+ *              <= 0: global causal layer. Meta rows are always visible.
+ *  cache_capacity  rows per sequence in k_cache / v_cache
+ *  rope_base   rotary base (10000); rotation pairs element i with i + head_dim/2
+ *  norm_eps    added to the mean square in the RMS norm (1e-6)
+ *  act         dtype of every activation tensor and of the KV cache
+ */
+typedef struct {
+  int32_t batch, n_meta, n_tokens;
+  int32_t d_inner, d_state, d_conv;
+  int32_t n_q_heads, n_kv_heads, head_dim, head_dim_v;
+  int32_t window;
+  int32_t cache_capacity;
+  float rope_base, norm_eps;
+  hymba_dtype act;
+} hymba_mixer_desc;
+
+/* Per-layer fp32 parameters, device pointers.
+ *  A          [d_inner, d_state], negative entries (continuous-time decay)
+ *  D          [d_inner] skip weight
+ *  conv_w     [d_inner, d_conv]; tap d_conv-1 multiplies the current row
+ *  conv_b     must be NULL (the conv has no bias)
+ *  beta_attn, beta_ssm   [d_inner] per-channel scales of the fusion        */
+typedef struct {
+  const float *A, *D, *conv_w, *conv_b;
+  const float *beta_attn, *beta_ssm;
+} hymba_mixer_params;
+
+/* Bytes of caller-provided device workspace the call needs for this geometry
+ * (0 if none). Returns 0 as well for an invalid descriptor; the call itself
+ * then reports the error. */
+size_t hymba_mixer_prefill_workspace_bytes(const hymba_mixer_desc* desc);
+size_t hymba_mixer_decode_workspace_bytes(const hymba_mixer_desc* desc);
+
+/* Prefill of L = n_meta + n_tokens rows per sequence, meta rows first; conv
+ * history and SSM state start at zero (the meta rows fill them: Hymba guide,
+ * "2. Learnable Meta-Tokens").
+ *  x, z, dt   [batch, L, d_inner]   dt already positive (no softplus inside)
+ *  B, C       [batch, L, d_state]   shared by all channels
+ *  q          [batch, L, n_q_heads, head_dim]    not rotated
+ *  k          [batch, L, n_kv_heads, head_dim]   not rotated
+ *  v          [batch, L, n_kv_heads, head_dim_v]
+ *  out        [batch, L, d_inner]   fused output
+ * Optional outputs (NULL = not written):
+ *  ssm_state_out   [batch, d_inner, d_state] fp32 state after row L-1
+ *  conv_state_out  [batch, d_inner, d_conv-1] raw x of rows L-3..L-1, oldest
+ *                  first (zeros where the row index is negative)
+ *  k_cache, v_cache  [batch, cache_capacity, n_kv_heads, head_dim(_v)]: rows
+ *                  0..L-1 receive the rotated keys and the values; needs
+ *                  cache_capacity >= L. Pass both or neither.
+ *  y_attn_out      [batch, L, d_inner] attention branch before the fusion,
+ *                  head-major (channel c = head c / head_dim_v, dim c % head_dim_v)
+ *  y_ssm_out       [batch, L, d_inner] Mamba branch before the fusion
+ *  workspace       device scratch of hymba_mixer_prefill_workspace_bytes(desc)
+ *                  bytes, 256-byte aligned; contents are not preserved.       */
+int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
+                        const void* x, const void* z, const void* dt, const void* B, const void* C,
+                        const void* q, const void* k, const void* v,
+                        void* out,
+                        float* ssm_state_out, void* conv_state_out,
+                        void* k_cache, void* v_cache,
+                        void* y_attn_out, void* y_ssm_out,
+                        void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* One decode step: one new row per sequence at position p_b = cache_len[b]
+ * ("Lecture 04 - Beyond the Dense Transformer", section 1: the new token
+ * attends over the cached rows and itself; section 2: the SSM state is updated
+ * once and does not grow).
+ *  x, z, dt   [batch, d_inner];  B, C [batch, d_state]
+ *  q          [batch, n_q_heads, head_dim]; k_new [batch, n_kv_heads, head_dim];
+ *  v_new      [batch, n_kv_heads, head_dim_v]   (q, k_new not rotated: both are
+ *             rotated to position p_b inside)
+ *  k_cache, v_cache  READ-ONLY [batch, cache_capacity, n_kv_heads, head_dim(_v)]
+ *             holding rotated keys and values of rows < p_b. Several layers may
+ *             pass the same buffers (Hymba guide, "Systems Mechanics: Cross-Layer
+ *             KV Cache Sharing"); the library never writes them. Appending the
+ *             new row is the caller's job.
+ *  cache_len  [batch] int32 on the device; n_meta <= p_b <= cache_capacity is the
+ *             caller's contract. Out-of-range values are clamped to
+ *             [0, cache_capacity] so that no access leaves the buffers.
+ *  ssm_state  IN/OUT [batch, d_inner, d_state] fp32, updated in place
+ *  conv_state IN/OUT [batch, d_inner, d_conv-1] raw x, oldest first, shifted in place
+ *  out        [batch, d_inner]; y_attn_out, y_ssm_out optional [batch, d_inner]
+ *  workspace  hymba_mixer_decode_workspace_bytes(desc) bytes, 256-byte aligned. */
+int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
+                       const void* x, const void* z, const void* dt, const void* B, const void* C,
+                       const void* q, const void* k_new, const void* v_new,
+                       const void* k_cache, const void* v_cache, const int32_t* cache_len,
+                       float* ssm_state, void* conv_state,
+                       void* out, void* y_attn_out, void* y_ssm_out,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* The fusion on its own: for each of n_rows rows of `width` channels,
+ *   out = (beta_attn * y_attn / sqrt(mean(y_attn^2) + eps)
+ *        + beta_ssm  * y_ssm  / sqrt(mean(y_ssm^2)  + eps)) / 2.
+ * y_attn, y_ssm, out: [n_rows, width] of dtype act; beta_*: [width] fp32.
+ * n_rows may be 0 (nothing enqueued). width >= 1.                            */
+int hymba_fuse_heads(const void* y_attn, const void* y_ssm,
+                     const float* beta_attn, const float* beta_ssm,
+                     int64_t n_rows, int32_t width, float eps, hymba_dtype act,
+                     void* out, hipStream_t stream);
+
+/* The visibility rule every attention kernel uses, exported for exact tests.
+ * For each query row i < L = n_meta + n_tokens writes 4 int32 to ranges[4*i]:
+ *   meta_end   visible meta keys are [0, meta_end)         = min(n_meta, i+1)
+ *   win_begin, win_end   visible non-meta keys are [win_begin, win_end); both
+ *              equal n_meta when there are none
+ *   count      number of visible keys
+ * ranges: device int32 [L, 4].                                               */
+int hymba_debug_mask_ranges(const hymba_mixer_desc* desc, int32_t* ranges, hipStream_t stream);
+
+/* Static text for a hymba_status value. */
+const char* hymba_status_string(int status);
+
+/* hipError_t of the last failed HIP call made by this library on the calling
+ * thread (hipSuccess if none). */
+int hymba_last_hip_error(void);
+
+/* HYMBA_ABI_VERSION of the built library. */
+int hymba_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYMBA_MIXER_H_ */

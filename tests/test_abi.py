@@ -1,0 +1,143 @@
+"""The C ABI library loads, exports every function the header declares, and
+rejects bad arguments on the host before enqueuing anything. No GPU needed:
+every call here returns from host-side validation (pointers are never
+dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_lm_amd as H
+from attention_lm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hymba_mixer.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\**\s*(hymba_\w+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import attention_lm_amd.build as b
+        b.build()
+    return H.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("hymba_mixer_prefill", "hymba_mixer_decode", "hymba_fuse_heads", "hymba_debug_mask_ranges"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names
+    for n in names:
+        assert hasattr(lib, n), n
+    # the binding wraps each one under the same name
+    for n in names:
+        assert hasattr(H, n) or n in ("hymba_abi_version",), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert H.hymba_abi_version() == 1
+    assert H.hymba_status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, -5):
+        assert H.hymba_status_string(s) != "unknown status"
+    assert H.hymba_last_hip_error() == 0
+
+
+def c1_desc(**kw):
+    d = dict(batch=1, n_meta=128, n_tokens=2048, d_inner=3200, n_q_heads=25, n_kv_heads=5, window=1024,
+             act="bf16", cache_capacity=8192)
+    d.update(kw)
+    return H.make_desc(**d)
+
+
+def test_workspace_sizes(lib):
+    d = c1_desc()
+    L = 2176
+    expect = (L * 25 * 64 + L * 5 * 64 + 2 * L * 3200) * 2
+    got = H.hymba_mixer_prefill_workspace_bytes(d)
+    assert expect <= got <= expect + 4 * 256
+    dd = c1_desc(batch=64)
+    n_split = (128 + 1024 + 63) // 64
+    assert H.hymba_mixer_decode_workspace_bytes(dd) >= 64 * 25 * n_split * 130 * 4 + 64 * 3200 * 2
+    assert H.hymba_mixer_prefill_workspace_bytes(c1_desc(n_q_heads=24)) == 0     # invalid -> 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=24), -1),          # Hq * dv != d_inner
+    (dict(n_kv_heads=4), -1),          # Hq % Hkv != 0
+    (dict(batch=0), -1),
+    (dict(n_meta=0, n_tokens=0), -1),
+    (dict(d_state=8), -2),
+    (dict(head_dim=128), -2),
+    (dict(act=7), -1),
+])
+def test_prefill_rejects_bad_geometry(lib, kw, status):
+    d = c1_desc(**kw)
+    fake = 0x100000  # aligned, never dereferenced: validation fails first
+    p = _lib.MixerParams(fake, fake, fake, None, fake, fake)
+    st = lib.hymba_mixer_prefill(ctypes.byref(d), ctypes.byref(p), *([fake] * 9), None, None, None, None, None,
+                                 None, fake, 1 << 40, None)
+    assert st == status
+
+
+def test_prefill_rejects_pointers_and_workspace(lib):
+    d = c1_desc()
+    fake = 0x100000
+    p = _lib.MixerParams(fake, fake, fake, None, fake, fake)
+    call = lambda args, ws=fake, wsb=1 << 40, params=p: lib.hymba_mixer_prefill(
+        ctypes.byref(d), ctypes.byref(params), *args, None, None, None, None, None, None, ws, wsb, None)
+    ok = [fake] * 9
+    assert call([None] + ok[1:]) == -1                       # null input
+    assert call(ok[:3] + [fake + 2] + ok[4:]) == -3          # misaligned input
+    assert call(ok, ws=None) == -5                           # no workspace
+    assert call(ok, wsb=16) == -5                            # workspace too small
+    assert call(ok, ws=fake + 16) == -3                      # workspace not 256-byte aligned
+    bad = _lib.MixerParams(fake, fake, fake, fake, fake, fake)
+    assert call(ok, params=bad) == -2                        # conv bias unsupported
+    nullp = _lib.MixerParams(None, fake, fake, None, fake, fake)
+    assert call(ok, params=nullp) == -1
+    # k_cache without v_cache, and a cache too short for L rows
+    st = lib.hymba_mixer_prefill(ctypes.byref(d), ctypes.byref(p), *ok, None, None, fake, None, None, None, fake,
+                                 1 << 40, None)
+    assert st == -1
+    d2 = c1_desc(cache_capacity=100)
+    st = lib.hymba_mixer_prefill(ctypes.byref(d2), ctypes.byref(p), *ok, None, None, fake, fake, None, None, fake,
+                                 1 << 40, None)
+    assert st == -1
+
+
+def test_decode_rejects_bad_arguments(lib):
+    d = c1_desc(batch=64)
+    fake = 0x100000
+    p = _lib.MixerParams(fake, fake, fake, None, fake, fake)
+    args = [fake] * 14
+    call = lambda a, desc=d: lib.hymba_mixer_decode(ctypes.byref(desc), ctypes.byref(p), *a[:13], a[13], None,
+                                                    None, fake, 1 << 40, None)
+    assert call(args[:10] + [None] + args[11:]) == -1        # null cache_len
+    assert call(args[:8] + [fake + 4] + args[9:]) == -3      # misaligned k_cache
+    assert call(args, desc=c1_desc(batch=64, cache_capacity=0)) == -1
+    st = lib.hymba_mixer_decode(ctypes.byref(d), ctypes.byref(p), *args, None, None, fake, 8, None)
+    assert st == -5
+
+
+def test_fuse_and_mask_validation(lib):
+    fake = 0x100000
+    assert lib.hymba_fuse_heads(fake, fake, fake, fake, 4, 0, 1e-6, 1, fake, None) == -1
+    assert lib.hymba_fuse_heads(fake, fake, fake, fake, -1, 8, 1e-6, 1, fake, None) == -1
+    assert lib.hymba_fuse_heads(fake, None, fake, fake, 4, 8, 1e-6, 1, fake, None) == -1
+    assert lib.hymba_fuse_heads(fake, fake, fake, fake, 4, 8, 1e-6, 9, fake, None) == -1
+    assert lib.hymba_fuse_heads(fake + 8, fake, fake, fake, 4, 8, 1e-6, 1, fake, None) == -3
+    d = c1_desc()
+    assert lib.hymba_debug_mask_ranges(ctypes.byref(d), None, None) == -1
+    assert lib.hymba_debug_mask_ranges(ctypes.byref(d), fake + 4, None) == -3

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 CPU
+oracle on seeded synthetic inputs. Relative L2 bounds: 1e-5 for fp32
+workloads, 5e-3 for bf16 (fp32 accumulation); bit-exact for the mask ranges.
+Each branch is checked before the fusion too, since the row RMS norm would hide
+a per-row scale error."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+
+H = pytest.importorskip("attention_lm_amd")
+from harness import TOL, Decode, Prefill, dev, host, rel_l2  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    H.load_library()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check(name, got, ref, tol):
+    e = rel_l2(got, ref)
+    say(f"  {name:14s} rel_l2={e:.3e} (tol {tol:.0e})")
+    assert np.all(np.isfinite(got)), name
+    assert e <= tol, (name, e)
+
+
+# ---------------------------------------------------------------------------
+# mask ranges: bit exact
+
+
+@pytest.mark.parametrize("L,M,W", [(72, 8, 32), (2176, 128, 1024), (8320, 128, 0), (100, 0, 1), (50, 60, 7),
+                                   (300, 5, 1000), (33, 3, 2)])
+def test_mask_ranges_bit_exact(L, M, W):
+    desc = H.make_desc(batch=1, n_meta=M, n_tokens=L - M if L >= M else 0, d_inner=64, n_q_heads=1,
+                       n_kv_heads=1, window=W, act="f32")
+    Lr = desc.n_meta + desc.n_tokens
+    r = torch.empty((Lr, 4), dtype=torch.int32, device="cuda")
+    H.hymba_debug_mask_ranges(desc, r)
+    torch.cuda.synchronize()
+    ref = O.mask_ranges(Lr, M, W)
+    np.testing.assert_array_equal(r.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------------------
+# fusion alone
+
+
+@pytest.mark.parametrize("act,rows,width", [("f32", 37, 128), ("bf16", 100, 3200), ("bf16", 5, 77), ("f32", 3, 13),
+                                            ("bf16", 0, 64)])
+def test_fuse_heads(act, rows, width):
+    g = np.random.default_rng(rows * 1000 + width)
+    ya = g.standard_normal((rows, width)).astype(np.float32) * 3
+    ys = g.standard_normal((rows, width)).astype(np.float32) * 0.1
+    ba = g.standard_normal(width).astype(np.float32)
+    bs = g.standard_normal(width).astype(np.float32)
+    if act == "bf16":
+        ya, ys = synth.round_bf16(ya), synth.round_bf16(ys)
+    tya, tys = dev(ya, act), dev(ys, act)
+    out = torch.empty((rows, width), dtype=tya.dtype, device="cuda")
+    H.hymba_fuse_heads(tya, tys, dev(ba), dev(bs), rows, width, 1e-6, act, out)
+    torch.cuda.synchronize()
+    if rows == 0:
+        return
+    ref = O.rms_fuse(ya, ys, ba, bs, 1e-6)
+    check("fuse", host(out), ref, TOL[act])
+
+
+# ---------------------------------------------------------------------------
+# prefill
+
+
+def run_prefill_parity(cfg, rows=None, batches=None, state_tol=None):
+    say(f"prefill {cfg.name}: B={cfg.batch} L={cfg.seq_rows} D={cfg.d_inner} Hq={cfg.n_q_heads} "
+        f"Hkv={cfg.n_kv_heads} W={cfg.window} act={cfg.act}")
+    inp = synth.make_prefill_inputs(cfg)
+    run = Prefill(cfg, inp)
+    run()
+    torch.cuda.synchronize()
+    got = run.results()
+    bsel = np.arange(cfg.batch) if batches is None else np.asarray(batches)
+    ref = O.mixer_prefill(cfg, inp, batches=bsel, rows=rows)
+    rsel = ref["rows"]
+    tol = TOL[cfg.act]
+    check("y_ssm", got["y_ssm_out"][bsel], ref["y_ssm"], tol)
+    check("y_attn", got["y_attn_out"][bsel][:, rsel], ref["y_attn"], tol)
+    check("out", got["out"][bsel][:, rsel], ref["out"], tol)
+    check("ssm_state", got["ssm_state_out"][bsel], ref["ssm_state"], state_tol or tol)
+    check("conv_state", got["conv_state_out"][bsel], ref["conv_state"], 0.0)
+    L = cfg.seq_rows
+    check("k_cache", got["k_cache"][bsel][:, :L], ref["k_rot"], tol)
+    np.testing.assert_array_equal(got["v_cache"][bsel][:, :L], inp["v"][bsel])
+    return run, inp, got
+
+
+def test_prefill_tiny_f32():
+    run_prefill_parity(synth.config("tiny_f32"))
+
+
+SMALL = [
+    # several tiles and ragged tails: L not a multiple of 32/64, windows crossing tiles
+    dict(batch=2, n_meta=5, n_tokens=150, d_inner=320, n_q_heads=5, n_kv_heads=1, window=40, act="bf16", seed=11),
+    dict(batch=1, n_meta=0, n_tokens=97, d_inner=128, n_q_heads=4, n_kv_heads=2, window=0, act="bf16", seed=12),
+    dict(batch=3, n_meta=33, n_tokens=70, d_inner=256, n_q_heads=2, n_kv_heads=2, window=17, act="f32", seed=13),
+    dict(batch=1, n_meta=128, n_tokens=300, d_inner=640, n_q_heads=5, n_kv_heads=1, window=64, act="bf16", seed=14),
+    dict(batch=2, n_meta=8, n_tokens=1, d_inner=64, n_q_heads=1, n_kv_heads=1, window=1, act="f32", seed=15),
+    dict(batch=1, n_meta=70, n_tokens=0, d_inner=160, n_q_heads=5, n_kv_heads=5, window=4, act="bf16", seed=16),
+]
+
+
+@pytest.mark.parametrize("kw", SMALL, ids=[f"small{i}" for i in range(len(SMALL))])
+def test_prefill_small_shapes(kw):
+    cfg = synth.config("tiny_f32").with_(**kw, name="small")
+    run_prefill_parity(cfg)
+
+
+def test_prefill_swa_layer_full():
+    run_prefill_parity(synth.config("swa_layer"))
+
+
+@pytest.mark.slow
+def test_prefill_global_layer_sampled_rows():
+    cfg = synth.config("global_layer")
+    L = cfg.seq_rows
+    rows = np.unique(np.concatenate([np.arange(0, 130), np.linspace(0, L - 1, 48).astype(int), np.arange(L - 40, L)]))
+    run_prefill_parity(cfg, rows=rows)
+
+
+@pytest.mark.slow
+def test_prefill_batched_sampled():
+    cfg = synth.config("batched_prefill")
+    L = cfg.seq_rows
+    rows = np.unique(np.concatenate([np.arange(0, 70), np.linspace(0, L - 1, 40).astype(int), np.arange(L - 30, L)]))
+    run_prefill_parity(cfg, rows=rows, batches=[0, 9, 15])
+
+
+def test_prefill_deterministic_and_branch_isolation():
+    cfg = synth.config("tiny_f32").with_(**SMALL[0], name="det")
+    inp = synth.make_prefill_inputs(cfg)
+    run = Prefill(cfg, inp)
+    run()
+    a = run.results()
+    run()
+    b = run.results()
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+    # beta = (1, 0): out is half the normalised attention branch
+    inp2 = dict(inp, beta_ssm=np.zeros_like(inp["beta_ssm"]))
+    run2 = Prefill(cfg, inp2)
+    run2()
+    got = run2.results()
+    ya = got["y_attn_out"]
+    ref = O.rms_fuse(ya, np.ones_like(ya), np.ones(cfg.d_inner), np.zeros(cfg.d_inner), cfg.norm_eps)
+    check("beta=(1,0)", got["out"], ref, TOL[cfg.act])
+
+
+# ---------------------------------------------------------------------------
+# decode
+
+
+def run_decode_parity(cfg, cache_len=None):
+    say(f"decode {cfg.name}: B={cfg.batch} cap={cfg.cache_capacity} D={cfg.d_inner} W={cfg.window} act={cfg.act}")
+    inp = synth.make_decode_inputs(cfg, cache_len=cache_len)
+    run = Decode(cfg, inp)
+    kc0 = run.k_cache.clone()
+    vc0 = run.v_cache.clone()
+    for l in range(cfg.n_layers):
+        run.call(l)
+    torch.cuda.synchronize()
+    tol = TOL[cfg.act]
+    assert torch.equal(run.k_cache, kc0) and torch.equal(run.v_cache, vc0)   # read-only, shared by both layers
+    for l in range(cfg.n_layers):
+        ref = O.mixer_decode(cfg, inp["layers"][l], inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"],
+                             inp["cache_len"])
+        L = run.layers[l]
+        say(f" layer {l}")
+        check("y_ssm", host(L["y_ssm_out"]), ref["y_ssm"], tol)
+        check("y_attn", host(L["y_attn_out"]), ref["y_attn"], tol)
+        check("out", host(L["out"]), ref["out"], tol)
+        check("ssm_state", host(L["ssm_state"]), ref["ssm_state"], tol)
+        check("conv_state", host(L["conv_state"]), ref["conv_state"], 0.0)
+    return run
+
+
+def test_decode_small_ragged_cache_lengths():
+    cfg = synth.config("decode").with_(batch=5, d_inner=320, n_q_heads=5, n_kv_heads=1, n_meta=8, window=50,
+                                       cache_capacity=300, cache_len=0, name="dsmall")
+    run_decode_parity(cfg, cache_len=np.array([300, 8, 9, 57, 120], np.int32))
+
+
+def test_decode_small_global_f32():
+    cfg = synth.config("decode").with_(batch=3, d_inner=128, n_q_heads=2, n_kv_heads=1, n_meta=4, window=0,
+                                       cache_capacity=200, act="f32", name="dglob")
+    run_decode_parity(cfg, cache_len=np.array([199, 4, 130], np.int32))
+
+
+def test_decode_full_config():
+    run_decode_parity(synth.config("decode"))
+
+
+def test_decode_continues_prefill():
+    """decode(prefill of L-1 rows) on the GPU equals the oracle's prefill of L rows, last row."""
+    cfg = synth.config("tiny_f32").with_(batch=2, n_meta=6, n_tokens=90, d_inner=320, n_q_heads=5, n_kv_heads=1,
+                                         window=33, act="bf16", seed=31, name="cont")
+    full = synth.make_prefill_inputs(cfg)
+    L = cfg.seq_rows
+    short_cfg = cfg.with_(n_tokens=cfg.n_tokens - 1)
+    short = {k: (v[:, :L - 1] if k in ("x", "z", "dt", "B", "C", "q", "k", "v") else v) for k, v in full.items()}
+    pre = Prefill(short_cfg, short, cache_capacity=L + 3)
+    pre()
+    torch.cuda.synchronize()
+    dcfg = cfg.with_(decode=True, cache_capacity=L + 3, n_layers=1)
+    layer = {"x": full["x"][:, L - 1], "z": full["z"][:, L - 1], "dt": full["dt"][:, L - 1],
+             "B": full["B"][:, L - 1], "C": full["C"][:, L - 1], "q": full["q"][:, L - 1],
+             "ssm_state": np.zeros((2, 320, 16), np.float32), "conv_state": np.zeros((2, 320, 3), np.float32),
+             **{k: full[k] for k in ("A", "D", "conv_w", "beta_attn", "beta_ssm")}}
+    inp = {"k_cache": np.zeros((2, L + 3, 1, 64), np.float32), "v_cache": np.zeros((2, L + 3, 1, 64), np.float32),
+           "k_new": full["k"][:, L - 1], "v_new": full["v"][:, L - 1],
+           "cache_len": np.full(2, L - 1, np.int32), "layers": [layer]}
+    run = Decode(dcfg, inp)
+    run.k_cache.copy_(pre.o["k_cache"])
+    run.v_cache.copy_(pre.o["v_cache"])
+    run.layers[0]["ssm_state"].copy_(pre.o["ssm_state_out"])
+    run.layers[0]["conv_state"].copy_(pre.o["conv_state_out"])
+    run.call(0)
+    torch.cuda.synchronize()
+    ref = O.mixer_prefill(cfg, full, rows=np.array([L - 1]))
+    check("y_ssm", host(run.layers[0]["y_ssm_out"]), ref["y_ssm"][:, L - 1], 5e-3)
+    check("y_attn", host(run.layers[0]["y_attn_out"]), ref["y_attn"][:, 0], 5e-3)
+    check("out", host(run.layers[0]["out"]), ref["out"][:, 0], 5e-3)
