@@ -69,9 +69,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hymba_mixer_prefill_workspace_bytes.restype = sz
     lib.hymba_mixer_decode_workspace_bytes.argtypes = [pdesc]
     lib.hymba_mixer_decode_workspace_bytes.restype = sz
-    lib.hymba_mixer_prefill.argtypes = [pdesc, pparams] + [vp] * 8 + [vp] + [vp] * 6 + [vp, sz, vp]
+    lib.hymba_mixer_prefill.argtypes = [pdesc, pparams] + [vp] * 8 + [vp] + [vp] * 6 + [vp, sz, vp, vp]
     lib.hymba_mixer_prefill.restype = ctypes.c_int
-    lib.hymba_mixer_decode.argtypes = [pdesc, pparams] + [vp] * 8 + [vp, vp, vp] + [vp, vp] + [vp, vp, vp] + [vp, sz, vp]
+    lib.hymba_mixer_decode.argtypes = [pdesc, pparams] + [vp] * 8 + [vp, vp, vp] + [vp, vp] + [vp, vp, vp] + [vp, sz, vp, vp]
     lib.hymba_mixer_decode.restype = ctypes.c_int
     lib.hymba_fuse_heads.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, ctypes.c_int, vp, vp]
     lib.hymba_fuse_heads.restype = ctypes.c_int
@@ -85,6 +85,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hymba_abi_version.restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+PREFILL_STAGES = ("ssm_prefill", "rope_prefill", "attn_prefill", "fuse")
+DECODE_STAGES = ("ssm_decode", "attn_decode", "decode_combine_fuse")
 
 
 def make_desc(batch, n_meta, n_tokens, d_inner, n_q_heads, n_kv_heads, window, act, head_dim=64,
@@ -142,7 +146,7 @@ def hymba_mixer_decode_workspace_bytes(desc: MixerDesc) -> int:
 
 def hymba_mixer_prefill(desc: MixerDesc, params: MixerParams, x, z, dt, B, C, q, k, v, out,
                         ssm_state_out=None, conv_state_out=None, k_cache=None, v_cache=None,
-                        y_attn_out=None, y_ssm_out=None, workspace=None, stream=None):
+                        y_attn_out=None, y_ssm_out=None, workspace=None, stage_events=None, stream=None):
     lib = load_library()
     if workspace is None:
         workspace = _workspace(hymba_mixer_prefill_workspace_bytes(desc), out.device)
@@ -150,13 +154,13 @@ def hymba_mixer_prefill(desc: MixerDesc, params: MixerParams, x, z, dt, B, C, q,
         ctypes.byref(desc), ctypes.byref(params), _ptr(x), _ptr(z), _ptr(dt), _ptr(B), _ptr(C), _ptr(q),
         _ptr(k), _ptr(v), _ptr(out), _ptr(ssm_state_out), _ptr(conv_state_out), _ptr(k_cache), _ptr(v_cache),
         _ptr(y_attn_out), _ptr(y_ssm_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream))
+        stage_events, _stream(stream))
     _check("hymba_mixer_prefill", st)
 
 
 def hymba_mixer_decode(desc: MixerDesc, params: MixerParams, x, z, dt, B, C, q, k_new, v_new, k_cache,
                        v_cache, cache_len, ssm_state, conv_state, out, y_attn_out=None, y_ssm_out=None,
-                       workspace=None, stream=None):
+                       workspace=None, stage_events=None, stream=None):
     lib = load_library()
     if workspace is None:
         workspace = _workspace(hymba_mixer_decode_workspace_bytes(desc), out.device)
@@ -164,7 +168,7 @@ def hymba_mixer_decode(desc: MixerDesc, params: MixerParams, x, z, dt, B, C, q, 
         ctypes.byref(desc), ctypes.byref(params), _ptr(x), _ptr(z), _ptr(dt), _ptr(B), _ptr(C), _ptr(q),
         _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(ssm_state),
         _ptr(conv_state), _ptr(out), _ptr(y_attn_out), _ptr(y_ssm_out), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream))
+        workspace.numel() * workspace.element_size(), stage_events, _stream(stream))
     _check("hymba_mixer_decode", st)
 
 

@@ -103,7 +103,7 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
                         const void* z, const void* dt, const void* B, const void* C, const void* q, const void* k,
                         const void* v, void* out, float* ssm_state_out, void* conv_state_out, void* k_cache,
                         void* v_cache, void* y_attn_out, void* y_ssm_out, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+                        size_t workspace_bytes, hipEvent_t* stage_events, hipStream_t stream) {
   int st = check_desc(desc, false);
   if (st != HYMBA_OK) return st;
   st = check_params(params);
@@ -130,12 +130,17 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   void* y_attn = y_attn_out ? y_attn_out : (void*)(wsb + ws.y_attn);
   void* y_ssm = y_ssm_out ? y_ssm_out : (void*)(wsb + ws.y_ssm);
 
+  auto mark = [&](int i) -> hipError_t {
+    return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+  };
+  HYMBA_TRY(mark(0));
   hymba::SsmPrefillArgs sa;
   sa.x = x; sa.z = z; sa.dt = dt; sa.B = B; sa.C = C;
   sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
   sa.y = y_ssm; sa.state_out = ssm_state_out; sa.conv_state_out = conv_state_out;
   sa.batch = desc->batch; sa.L = L; sa.d_inner = desc->d_inner; sa.act = desc->act;
   HYMBA_TRY(hymba::launch_ssm_prefill(sa, stream));
+  HYMBA_TRY(mark(1));
 
   hymba::RopeArgs ra;
   ra.q = q; ra.k = k; ra.v = v; ra.q_rot = q_rot; ra.k_rot = k_rot; ra.v_copy = v_cache;
@@ -144,6 +149,7 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   ra.head_dim = desc->head_dim; ra.head_dim_v = desc->head_dim_v; ra.rope_base = desc->rope_base;
   ra.act = desc->act;
   HYMBA_TRY(hymba::launch_rope_prefill(ra, stream));
+  HYMBA_TRY(mark(2));
 
   hymba::AttnPrefillArgs aa;
   aa.q_rot = q_rot; aa.k_rot = k_rot; aa.v = v; aa.k_rows = k_rows; aa.v_rows = L; aa.y = y_attn;
@@ -151,9 +157,11 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
   aa.act = desc->act;
   HYMBA_TRY(hymba::launch_attn_prefill(aa, stream));
+  HYMBA_TRY(mark(3));
 
   HYMBA_TRY(hymba::launch_fuse(y_attn, y_ssm, params->beta_attn, params->beta_ssm, (int64_t)desc->batch * L,
                                desc->d_inner, desc->norm_eps, desc->act, out, stream));
+  HYMBA_TRY(mark(4));
   return HYMBA_OK;
 }
 
@@ -161,7 +169,8 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
                        const void* z, const void* dt, const void* B, const void* C, const void* q,
                        const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
                        const int32_t* cache_len, float* ssm_state, void* conv_state, void* out, void* y_attn_out,
-                       void* y_ssm_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                       void* y_ssm_out, void* workspace, size_t workspace_bytes, hipEvent_t* stage_events,
+                       hipStream_t stream) {
   int st = check_desc(desc, true);
   if (st != HYMBA_OK) return st;
   st = check_params(params);
@@ -180,12 +189,17 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
   float* partial = (float*)(wsb + ws.partial);
   void* y_ssm = y_ssm_out ? y_ssm_out : (void*)(wsb + ws.y_ssm);
 
+  auto mark = [&](int i) -> hipError_t {
+    return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+  };
+  HYMBA_TRY(mark(0));
   hymba::SsmDecodeArgs sa;
   sa.x = x; sa.z = z; sa.dt = dt; sa.B = B; sa.C = C;
   sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
   sa.state = ssm_state; sa.conv_state = conv_state; sa.y = y_ssm;
   sa.batch = desc->batch; sa.d_inner = desc->d_inner; sa.act = desc->act;
   HYMBA_TRY(hymba::launch_ssm_decode(sa, stream));
+  HYMBA_TRY(mark(1));
 
   hymba::AttnDecodeArgs aa;
   aa.q = q; aa.k_new = k_new; aa.v_new = v_new; aa.k_cache = k_cache; aa.v_cache = v_cache;
@@ -194,12 +208,14 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
   aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
   aa.rope_base = desc->rope_base; aa.act = desc->act;
   HYMBA_TRY(hymba::launch_attn_decode(aa, stream));
+  HYMBA_TRY(mark(2));
 
   hymba::DecodeCombineArgs ca;
   ca.partial = partial; ca.y_ssm = y_ssm; ca.beta_attn = params->beta_attn; ca.beta_ssm = params->beta_ssm;
   ca.out = out; ca.y_attn_out = y_attn_out; ca.n_split = ws.n_split; ca.batch = desc->batch;
   ca.n_q_heads = desc->n_q_heads; ca.head_dim_v = desc->head_dim_v; ca.eps = desc->norm_eps; ca.act = desc->act;
   HYMBA_TRY(hymba::launch_decode_combine(ca, stream));
+  HYMBA_TRY(mark(3));
   return HYMBA_OK;
 }
 

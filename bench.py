@@ -1,0 +1,366 @@
+#!/usr/bin/env python3
+"""Benchmark of the Hymba hybrid-head mixer on one MI355X.
+
+One step = one prefill of the Hymba-1.5B-shaped sliding-window layer
+(B=1, 2048 prompt rows + 128 meta rows, 25q/5kv x 64, window 1024, d_inner 3200,
+d_state 16, bf16) through the library's C ABI: conv + selective scan, RoPE,
+MFMA flash attention, fusion, plus the KV-cache and state hand-off outputs.
+Inputs are seeded synthetic tensors already resident in HBM. Several input sets
+are rotated so that back-to-back steps do not simply re-read the last step's
+inputs from the 256 MB last-level cache.
+
+Also reported, in the same JSON line: the decode step of 64 sequences over an
+8192-row cache shared read-only by two layers (two mixer calls), per-kernel
+durations from HIP events recorded between the library's launches, the
+roofline of the dominant kernel, and the CPU oracle timed on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+METRIC = "hybrid-head mixer prefill tokens/s + decode µs/step; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+# VALU issue: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz lane-slots/s; a transcendental
+# (v_exp_f32) takes two slots on gfx950.
+ALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+SCAN_SLOTS_PER_ELEM = 6          # mul(dt*A) + exp(2) + mul(dt*u*B) + fma(h) + fma(C.h)
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+KERNEL_SOURCES = ["common.hpp", "ssm.hip", "attn.hip", "fuse.hip", "api.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# HIP events through the runtime's C API (plumbing for per-kernel timing)
+
+
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.all = []
+
+    def array(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            arr[i] = ev.value
+            self.all.append(ev.value)
+        return arr
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(out.value)
+
+    def close(self):
+        for e in self.all:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.all = []
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of each kernel (each input read once, each output written once)
+
+
+def visible_pairs(L, n_meta, window):
+    total = 0
+    for i in range(L):
+        total += min(i + 1, n_meta + window) if window > 0 else i + 1
+    return total
+
+
+def prefill_work(cfg):
+    es = 2 if cfg.act == "bf16" else 4
+    B, L, D, N = cfg.batch, cfg.seq_rows, cfg.d_inner, cfg.d_state
+    Hq, Hkv, hd, dv = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.head_dim_v
+    rows = B * L
+    scan_bytes = rows * (4 * D * es + 2 * N * es) + B * D * N * 4 + B * D * 3 * es + D * (N + 1 + 4) * 4
+    elems = rows * D * N
+    rope_bytes = rows * ((Hq + Hkv) * hd * es * 2 + Hkv * dv * es * 2)
+    pairs = B * visible_pairs(L, cfg.n_meta, cfg.window)
+    attn_flops = pairs * Hq * (2 * hd + 2 * dv)
+    attn_bytes = rows * ((Hq + Hkv) * hd * es + Hkv * dv * es + D * es)
+    fuse_bytes = rows * 3 * D * es + 2 * D * 4
+    return {
+        "ssm_prefill": {"bytes": scan_bytes, "alu_slots": elems * SCAN_SLOTS_PER_ELEM, "elems": elems},
+        "rope_prefill": {"bytes": rope_bytes},
+        "attn_prefill": {"bytes": attn_bytes, "flops": attn_flops, "pairs": pairs},
+        "fuse": {"bytes": fuse_bytes},
+    }
+
+
+def decode_work(cfg):
+    es = 2 if cfg.act == "bf16" else 4
+    B, D, N = cfg.batch, cfg.d_inner, cfg.d_state
+    Hq, Hkv, hd, dv = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.head_dim_v
+    n_vis = min(cfg.cache_len + 1, cfg.n_meta + cfg.window) if cfg.window > 0 else cfg.cache_len + 1
+    ssm_bytes = B * D * N * 4 * 2 + B * D * 3 * es * 2 + B * (3 * D + 2 * N) * es + B * D * es + D * (N + 5) * 4
+    attn_bytes = B * Hkv * (n_vis - 1) * (hd + dv) * es + B * (Hq * hd + Hkv * (hd + dv)) * es
+    comb_bytes = B * D * es * 2 + 2 * D * 4
+    return {"ssm_decode": {"bytes": ssm_bytes}, "attn_decode": {"bytes": attn_bytes, "n_vis": n_vis},
+            "decode_combine_fuse": {"bytes": comb_bytes},
+            "total_bytes": ssm_bytes + attn_bytes + comb_bytes}
+
+
+def kernel_report(name, avg_ms, work, act):
+    t = avg_ms * 1e-3
+    r = {"avg_us": round(avg_ms * 1e3, 2)}
+    fr = {}
+    if "bytes" in work:
+        gbs = work["bytes"] / t / 1e9
+        r["hbm_GBs"] = round(gbs, 1)
+        fr["hbm"] = gbs / HBM_PEAK_GBS
+    if "flops" in work:
+        tf = work["flops"] / t / 1e12
+        r["mfma_TFLOPs"] = round(tf, 1)
+        fr["mfma"] = tf / MFMA_PEAK_TFLOPS[act]
+    if "alu_slots" in work:
+        ts = work["alu_slots"] / t / 1e12
+        r["alu_Tslots"] = round(ts, 2)
+        fr["alu"] = ts / ALU_PEAK_TSLOTS
+    r["frac"] = {k: round(v, 4) for k, v in fr.items()}
+    r["bound"] = max(fr, key=fr.get)
+    return r
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "attention_lm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+
+
+def bench_prefill(cfg, steps, warmup, n_sets, ev):
+    import torch
+    import synth
+    from harness import Prefill
+    import attention_lm_amd as H
+
+    log(f"[bench] prefill {cfg.name}: generating inputs")
+    inp = synth.make_prefill_inputs(cfg)
+    runs = [Prefill(cfg, inp, with_outputs=False, with_cache=True) for _ in range(n_sets)]
+    for r in runs:   # hand-off outputs a real prefill writes: final SSM/conv state (KV cache is on)
+        r.o["ssm_state_out"] = torch.empty((cfg.batch, cfg.d_inner, cfg.d_state), dtype=torch.float32, device="cuda")
+        r.o["conv_state_out"] = torch.empty((cfg.batch, cfg.d_inner, cfg.d_conv - 1), dtype=r.out.dtype, device="cuda")
+    nst = len(H._lib.PREFILL_STAGES)
+    evs = [ev.array(nst + 1) for _ in range(steps)]
+    log(f"[bench] prefill warmup {warmup}")
+    for i in range(warmup):
+        runs[i % n_sets]()
+    torch.cuda.synchronize()
+    log(f"[bench] prefill timed {steps} steps")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        r = runs[i % n_sets]
+        t = r.t
+        H.hymba_mixer_prefill(r.desc, r.params, t["x"], t["z"], t["dt"], t["B"], t["C"], t["q"], t["k"], t["v"],
+                              r.out, workspace=r.ws, stage_events=evs[i], **r.o)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {name: sum(ev.ms(e[j], e[j + 1]) for e in evs) / steps for j, name in enumerate(H._lib.PREFILL_STAGES)}
+    return wall / steps * 1e3, stage_ms
+
+
+def bench_decode(cfg, steps, warmup, n_sets, ev):
+    import torch
+    import synth
+    from harness import Decode
+    import attention_lm_amd as H
+
+    log(f"[bench] decode {cfg.name}: generating inputs")
+    inp = synth.make_decode_inputs(cfg)
+    runs = []
+    for s in range(n_sets):
+        runs.append(Decode(cfg, inp))
+        log(f"[bench] decode set {s} on device")
+    nst = len(H._lib.DECODE_STAGES)
+    evs = [[ev.array(nst + 1) for _ in range(cfg.n_layers)] for _ in range(steps)]
+    for i in range(warmup):
+        for l in range(cfg.n_layers):
+            runs[i % n_sets].call(l, with_branches=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        r = runs[i % n_sets]
+        for l in range(cfg.n_layers):
+            L = r.layers[l]
+            H.hymba_mixer_decode(r.desc, L["params"], L["x"], L["z"], L["dt"], L["B"], L["C"], L["q"], r.k_new,
+                                 r.v_new, r.k_cache, r.v_cache, r.cache_len, L["ssm_state"], L["conv_state"],
+                                 L["out"], workspace=r.ws, stage_events=evs[i][l])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_layer_ms = [sum(ev.ms(evs[i][l][0], evs[i][l][nst]) for i in range(steps)) / steps for l in range(cfg.n_layers)]
+    stage_ms = {}
+    for j, name in enumerate(H._lib.DECODE_STAGES):
+        stage_ms[name] = [sum(ev.ms(evs[i][l][j], evs[i][l][j + 1]) for i in range(steps)) / steps
+                          for l in range(cfg.n_layers)]
+    return wall / steps * 1e3, per_layer_ms, stage_ms
+
+
+def cpu_baseline(cfg, min_seconds=10.0):
+    import numpy as np
+    import synth
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    inp = synth.make_prefill_inputs(cfg)
+    reps = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        while True:
+            O.mixer_prefill(cfg, inp)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                break
+    return {
+        "value": round(cfg.batch * cfg.n_tokens * reps / el, 1),
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{reps} full float64 oracle prefill(s) of the same workload ({cfg.batch}x{cfg.seq_rows} rows, "
+                   f"all rows, attention and scan) in {el:.1f} s; BLAS threads={cores}, element-wise NumPy and the "
+                   f"scan's time loop single-threaded; cpu={_cpu_model()}"),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=4, help="input sets rotated through the timed steps")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import attention_lm_amd as H
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(1)
+    H.load_library()
+    ev = HipEvents()
+    cfg = synth.config("swa_layer")
+    ms, stage_ms = bench_prefill(cfg, args.steps, args.warmup, args.sets, ev)
+    work = prefill_work(cfg)
+    kernels = {k: kernel_report(k, stage_ms[k], work[k], cfg.act) for k in stage_ms}
+    dom = max(stage_ms, key=stage_ms.get)
+    kd = kernels[dom]
+    bound = kd["bound"]
+    if bound == "hbm":
+        ach, peak, unit = kd["hbm_GBs"], HBM_PEAK_GBS, "GB/s"
+    elif bound == "mfma":
+        ach, peak, unit = kd["mfma_TFLOPs"], MFMA_PEAK_TFLOPS[cfg.act], "TFLOP/s"
+    else:
+        ach, peak, unit = kd["alu_Tslots"], round(ALU_PEAK_TSLOTS, 2), "Tslot/s"
+    traffic = traffic_for(dom)
+    roofline = {"kernel": dom, "bound": bound, "achieved": ach, "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": traffic,
+                "hbm_frac": kd["frac"].get("hbm")}
+
+    res = {
+        "metric": METRIC,
+        "value": round(cfg.batch * cfg.n_tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.act,
+        "data": "synthetic",
+        "config": {"workload": cfg.workload, "batch": cfg.batch, "n_tokens": cfg.n_tokens, "n_meta": cfg.n_meta,
+                   "d_inner": cfg.d_inner, "d_state": cfg.d_state, "n_q_heads": cfg.n_q_heads,
+                   "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "head_dim_v": cfg.head_dim_v,
+                   "window": cfg.window, "input_sets": args.sets},
+        "rows_per_s_incl_meta": round(cfg.batch * cfg.seq_rows / (ms * 1e-3), 1),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_decode:
+        dcfg = synth.config("decode")
+        dms, per_layer, dstage = bench_decode(dcfg, args.steps, args.warmup, 3, ev)
+        dw = decode_work(dcfg)
+        dk = {k: kernel_report(k, sum(v) / len(v), dw[k], dcfg.act) for k, v in dstage.items()}
+        call_us = sum(per_layer) / len(per_layer) * 1e3
+        res["decode"] = {
+            "workload": dcfg.workload,
+            "us_per_step": round(dms * 1e3, 2),
+            "layers_per_step": dcfg.n_layers,
+            "us_per_call": [round(x * 1e3, 2) for x in per_layer],
+            "hbm_GBs_per_call": round(dw["total_bytes"] / (call_us * 1e-6) / 1e9, 1),
+            "hbm_frac_per_call": round(dw["total_bytes"] / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_call": dw["total_bytes"],
+            "kernels": dk,
+        }
+    ev.close()
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

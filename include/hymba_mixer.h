@@ -50,6 +50,8 @@ extern "C" {
 #endif
 
 #define HYMBA_ABI_VERSION 1
+#define HYMBA_PREFILL_STAGES 4
+#define HYMBA_DECODE_STAGES 3
 
 typedef enum { HYMBA_F32 = 0, HYMBA_BF16 = 1 } hymba_dtype;
 
@@ -128,7 +130,11 @@ size_t hymba_mixer_decode_workspace_bytes(const hymba_mixer_desc* desc);
  *                  head-major (channel c = head c / head_dim_v, dim c % head_dim_v)
  *  y_ssm_out       [batch, L, d_inner] Mamba branch before the fusion
  *  workspace       device scratch of hymba_mixer_prefill_workspace_bytes(desc)
- *                  bytes, 256-byte aligned; contents are not preserved.       */
+ *                  bytes, 256-byte aligned; contents are not preserved.
+ *  stage_events    NULL, or HYMBA_PREFILL_STAGES + 1 caller-created events:
+ *                  event i is recorded on `stream` before stage i, the last one
+ *                  after the final stage (stages: conv+scan, rotary, attention,
+ *                  fusion). For per-kernel timing; the caller owns the events. */
 int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
                         const void* x, const void* z, const void* dt, const void* B, const void* C,
                         const void* q, const void* k, const void* v,
@@ -137,7 +143,7 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
                         void* k_cache, void* v_cache,
                         void* y_attn_out, void* y_ssm_out,
                         void* workspace, size_t workspace_bytes,
-                        hipStream_t stream);
+                        hipEvent_t* stage_events, hipStream_t stream);
 
 /* One decode step: one new row per sequence at position p_b = cache_len[b]
  * ("Lecture 04 - Beyond the Dense Transformer", section 1: the new token
@@ -158,7 +164,10 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
  *  ssm_state  IN/OUT [batch, d_inner, d_state] fp32, updated in place
  *  conv_state IN/OUT [batch, d_inner, d_conv-1] raw x, oldest first, shifted in place
  *  out        [batch, d_inner]; y_attn_out, y_ssm_out optional [batch, d_inner]
- *  workspace  hymba_mixer_decode_workspace_bytes(desc) bytes, 256-byte aligned. */
+ *  workspace  hymba_mixer_decode_workspace_bytes(desc) bytes, 256-byte aligned.
+ *  stage_events NULL, or HYMBA_DECODE_STAGES + 1 caller-created events, recorded
+ *             as for prefill (stages: SSM step, attention partials,
+ *             merge + fusion). */
 int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
                        const void* x, const void* z, const void* dt, const void* B, const void* C,
                        const void* q, const void* k_new, const void* v_new,
@@ -166,7 +175,7 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
                        float* ssm_state, void* conv_state,
                        void* out, void* y_attn_out, void* y_ssm_out,
                        void* workspace, size_t workspace_bytes,
-                       hipStream_t stream);
+                       hipEvent_t* stage_events, hipStream_t stream);
 
 /* The fusion on its own: for each of n_rows rows of `width` channels,
  *   out = (beta_attn * y_attn / sqrt(mean(y_attn^2) + eps)

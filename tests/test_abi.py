@@ -87,7 +87,7 @@ def test_prefill_rejects_bad_geometry(lib, kw, status):
     fake = 0x100000  # aligned, never dereferenced: validation fails first
     p = _lib.MixerParams(fake, fake, fake, None, fake, fake)
     st = lib.hymba_mixer_prefill(ctypes.byref(d), ctypes.byref(p), *([fake] * 9), None, None, None, None, None,
-                                 None, fake, 1 << 40, None)
+                                 None, fake, 1 << 40, None, None)
     assert st == status
 
 
@@ -96,7 +96,7 @@ def test_prefill_rejects_pointers_and_workspace(lib):
     fake = 0x100000
     p = _lib.MixerParams(fake, fake, fake, None, fake, fake)
     call = lambda args, ws=fake, wsb=1 << 40, params=p: lib.hymba_mixer_prefill(
-        ctypes.byref(d), ctypes.byref(params), *args, None, None, None, None, None, None, ws, wsb, None)
+        ctypes.byref(d), ctypes.byref(params), *args, None, None, None, None, None, None, ws, wsb, None, None)
     ok = [fake] * 9
     assert call([None] + ok[1:]) == -1                       # null input
     assert call(ok[:3] + [fake + 2] + ok[4:]) == -3          # misaligned input
@@ -109,11 +109,11 @@ def test_prefill_rejects_pointers_and_workspace(lib):
     assert call(ok, params=nullp) == -1
     # k_cache without v_cache, and a cache too short for L rows
     st = lib.hymba_mixer_prefill(ctypes.byref(d), ctypes.byref(p), *ok, None, None, fake, None, None, None, fake,
-                                 1 << 40, None)
+                                 1 << 40, None, None)
     assert st == -1
     d2 = c1_desc(cache_capacity=100)
     st = lib.hymba_mixer_prefill(ctypes.byref(d2), ctypes.byref(p), *ok, None, None, fake, fake, None, None, fake,
-                                 1 << 40, None)
+                                 1 << 40, None, None)
     assert st == -1
 
 
@@ -123,11 +123,11 @@ def test_decode_rejects_bad_arguments(lib):
     p = _lib.MixerParams(fake, fake, fake, None, fake, fake)
     args = [fake] * 14
     call = lambda a, desc=d: lib.hymba_mixer_decode(ctypes.byref(desc), ctypes.byref(p), *a[:13], a[13], None,
-                                                    None, fake, 1 << 40, None)
+                                                    None, fake, 1 << 40, None, None)
     assert call(args[:10] + [None] + args[11:]) == -1        # null cache_len
     assert call(args[:8] + [fake + 4] + args[9:]) == -3      # misaligned k_cache
     assert call(args, desc=c1_desc(batch=64, cache_capacity=0)) == -1
-    st = lib.hymba_mixer_decode(ctypes.byref(d), ctypes.byref(p), *args, None, None, fake, 8, None)
+    st = lib.hymba_mixer_decode(ctypes.byref(d), ctypes.byref(p), *args, None, None, fake, 8, None, None)
     assert st == -5
 
 
