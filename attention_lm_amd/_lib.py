@@ -88,7 +88,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 
 PREFILL_STAGES = ("ssm_prefill", "rope_prefill", "attn_prefill", "fuse")
-DECODE_STAGES = ("ssm_decode", "attn_decode", "decode_combine_fuse")
+DECODE_STAGES = ("ssm_decode", "attn_decode", "decode_merge_fuse")
 
 
 def make_desc(batch, n_meta, n_tokens, d_inner, n_q_heads, n_kv_heads, window, act, head_dim=64,

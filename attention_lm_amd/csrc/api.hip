@@ -43,7 +43,7 @@ int check_desc(const hymba_mixer_desc* d, bool decode) {
   // what this build has kernels for
   if (d->d_state != 16 || d->d_conv != 4 || d->head_dim != 64) return HYMBA_EUNSUPPORTED;
   if (d->head_dim_v != 32 && d->head_dim_v != 64 && d->head_dim_v != 128) return HYMBA_EUNSUPPORTED;
-  if (d->n_q_heads / d->n_kv_heads > 10) return HYMBA_EUNSUPPORTED;
+  if (d->n_q_heads / d->n_kv_heads > 8) return HYMBA_EUNSUPPORTED;
   if (d->d_inner % 8 != 0) return HYMBA_EUNSUPPORTED;
   return HYMBA_OK;
 }
@@ -58,7 +58,8 @@ int check_params(const hymba_mixer_params* p) {
 }
 
 struct PrefillWs {
-  size_t q_rot, k_rot, y_attn, y_ssm, total;
+  size_t q_rot, k_rot, y_attn, y_ssm, agg, sdt, carry, total;
+  int chunk_rows;
 };
 PrefillWs prefill_ws(const hymba_mixer_desc* d) {
   const size_t es = act_bytes(d->act);
@@ -68,20 +69,31 @@ PrefillWs prefill_ws(const hymba_mixer_desc* d) {
   w.k_rot = w.q_rot + round256(rows * d->n_q_heads * d->head_dim * es);
   w.y_attn = w.k_rot + round256(rows * d->n_kv_heads * d->head_dim * es);
   w.y_ssm = w.y_attn + round256(rows * d->d_inner * es);
-  w.total = w.y_ssm + round256(rows * d->d_inner * es);
+  w.agg = w.y_ssm + round256(rows * d->d_inner * es);
+  const int L = d->n_meta + d->n_tokens;
+  w.chunk_rows = hymba::ssm_prefill_chunk_rows(d->batch, L, d->d_inner);
+  const size_t nchunk = (size_t)((L + w.chunk_rows - 1) / w.chunk_rows);
+  const size_t chans = (size_t)d->batch * d->d_inner;
+  w.sdt = w.agg + round256(nchunk * chans * 16 * sizeof(float));
+  w.carry = w.sdt + round256(nchunk * chans * sizeof(float));
+  w.total = w.carry + round256(nchunk * chans * 16 * sizeof(float));
   return w;
 }
 
 struct DecodeWs {
-  size_t partial, y_ssm, total;
+  size_t partial, y_ssm, y_attn, q_rot, k_rot, total;
   int n_split, keys_per_split;
 };
 DecodeWs decode_ws(const hymba_mixer_desc* d) {
   DecodeWs w;
   hymba::decode_split_plan(d->n_meta, d->window, d->cache_capacity, &w.n_split, &w.keys_per_split);
+  const size_t B = (size_t)d->batch;
   w.partial = 0;
-  w.y_ssm = round256((size_t)d->batch * d->n_q_heads * w.n_split * (d->head_dim_v + 2) * sizeof(float));
-  w.total = w.y_ssm + round256((size_t)d->batch * d->d_inner * act_bytes(d->act));
+  w.y_ssm = round256(B * d->n_q_heads * w.n_split * (d->head_dim_v + 2) * sizeof(float));
+  w.y_attn = w.y_ssm + round256(B * d->d_inner * act_bytes(d->act));
+  w.q_rot = w.y_attn + round256(B * d->d_inner * act_bytes(d->act));
+  w.k_rot = w.q_rot + round256(B * d->n_q_heads * d->head_dim * sizeof(float));
+  w.total = w.k_rot + round256(B * d->n_kv_heads * d->head_dim * sizeof(float));
   return w;
 }
 
@@ -138,6 +150,8 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   sa.x = x; sa.z = z; sa.dt = dt; sa.B = B; sa.C = C;
   sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
   sa.y = y_ssm; sa.state_out = ssm_state_out; sa.conv_state_out = conv_state_out;
+  sa.agg = (float*)(wsb + ws.agg); sa.sdt = (float*)(wsb + ws.sdt); sa.carry = (float*)(wsb + ws.carry);
+  sa.chunk_rows = ws.chunk_rows;
   sa.batch = desc->batch; sa.L = L; sa.d_inner = desc->d_inner; sa.act = desc->act;
   HYMBA_TRY(hymba::launch_ssm_prefill(sa, stream));
   HYMBA_TRY(mark(1));
@@ -188,6 +202,7 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
   char* wsb = (char*)workspace;
   float* partial = (float*)(wsb + ws.partial);
   void* y_ssm = y_ssm_out ? y_ssm_out : (void*)(wsb + ws.y_ssm);
+  void* y_attn = y_attn_out ? y_attn_out : (void*)(wsb + ws.y_attn);
 
   auto mark = [&](int i) -> hipError_t {
     return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
@@ -203,18 +218,20 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
 
   hymba::AttnDecodeArgs aa;
   aa.q = q; aa.k_new = k_new; aa.v_new = v_new; aa.k_cache = k_cache; aa.v_cache = v_cache;
-  aa.cache_len = cache_len; aa.partial = partial; aa.n_split = ws.n_split; aa.keys_per_split = ws.keys_per_split;
+  aa.cache_len = cache_len; aa.partial = partial;
+  aa.q_rot = (float*)(wsb + ws.q_rot); aa.k_rot = (float*)(wsb + ws.k_rot); aa.n_split = ws.n_split; aa.keys_per_split = ws.keys_per_split;
   aa.batch = desc->batch; aa.cap = desc->cache_capacity; aa.n_meta = desc->n_meta; aa.window = desc->window;
   aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
   aa.rope_base = desc->rope_base; aa.act = desc->act;
   HYMBA_TRY(hymba::launch_attn_decode(aa, stream));
   HYMBA_TRY(mark(2));
 
-  hymba::DecodeCombineArgs ca;
-  ca.partial = partial; ca.y_ssm = y_ssm; ca.beta_attn = params->beta_attn; ca.beta_ssm = params->beta_ssm;
-  ca.out = out; ca.y_attn_out = y_attn_out; ca.n_split = ws.n_split; ca.batch = desc->batch;
-  ca.n_q_heads = desc->n_q_heads; ca.head_dim_v = desc->head_dim_v; ca.eps = desc->norm_eps; ca.act = desc->act;
-  HYMBA_TRY(hymba::launch_decode_combine(ca, stream));
+  hymba::DecodeMergeArgs ma;
+  ma.partial = partial; ma.y_attn = y_attn; ma.n_split = ws.n_split; ma.batch = desc->batch;
+  ma.n_q_heads = desc->n_q_heads; ma.head_dim_v = desc->head_dim_v; ma.act = desc->act;
+  HYMBA_TRY(hymba::launch_decode_merge(ma, stream));
+  HYMBA_TRY(hymba::launch_fuse(y_attn, y_ssm, params->beta_attn, params->beta_ssm, desc->batch, desc->d_inner,
+                               desc->norm_eps, desc->act, out, stream));
   HYMBA_TRY(mark(3));
   return HYMBA_OK;
 }

@@ -106,9 +106,11 @@ __global__ __launch_bounds__(256) void rope_prefill_kernel(
 // ---------------------------------------------------------------------------
 // Prefill attention on the matrix cores.
 //
-// Workgroup = one (sequence, kv head, block of 32*PB query rows); one wave per
-// (query head of the group, 32-row block). All its waves read the same key and
-// value tiles, staged in LDS once per workgroup (GQA reuse).
+// Workgroup = 4 waves = 128 query columns of one (sequence, kv head): P
+// consecutive positions times the G query heads of the GQA group (column c is
+// position p0 + c / G, head c % G; P = floor(128 / G)). All columns read the
+// same key/value tiles, staged in LDS once per workgroup, so a K/V byte is
+// fetched once for every query head that uses it.
 //
 // Per 32-key sub-tile each wave computes S^T = K Q^T with 32x32x16 bf16 MFMA
 // (fp32 inputs: 32x32x2). In that layout each lane owns one query column and
@@ -116,9 +118,14 @@ __global__ __launch_bounds__(256) void rope_prefill_kernel(
 // l+32) and the exp'd scores, converted in registers, are directly the B
 // operand of O^T = V^T P^T: no LDS round trip for P. V is stored transposed in
 // LDS with keys permuted inside each 16-key chunk to match that operand.
-// Online softmax keeps running max m and per-lane partial sums l.
+// The online softmax keeps a reference max per column and rescales the
+// accumulators only when a new score exceeds it by more than 2^8 (exact: the
+// numerator and denominator use the same reference).
 
 constexpr int BK = 64;                     // keys per LDS stage (two 32-key sub-tiles)
+constexpr int kAttnWaves = 4;
+constexpr int kAttnCols = 32 * kAttnWaves;
+constexpr float kRescaleSlack = 8.0f;
 template <typename T> struct AttnTile {
   static constexpr int kpad = kHd + 16 / (int)sizeof(T);   // padded K row (elements)
   static constexpr int vpad = BK + 16 / (int)sizeof(T);    // padded V^T row (elements)
@@ -170,33 +177,173 @@ struct Mma<float> {
   }
 };
 
+// Global -> registers -> LDS staging of one 64-key tile.
+//  K: 16-byte chunks copied as is into padded rows.
+//  V (bf16): item = (group of 4 V^T slots, 8-wide dv chunk dc); the thread
+//    reads the 4 keys of the slot group at dv 8dc..8dc+7 and writes eight
+//    8-byte V^T row pieces (one per dv), transposed with byte permutes. Slot
+//    groups are the fastest index, so the 16 lanes of an 8-byte LDS write phase
+//    cover all 32 banks of one row.
+//  V (fp32): item = (4-key quad, dv chunk), quads fastest.
+template <typename T, int DV, int NT>
+struct TileStage;
+
+template <int DV, int NT>
+struct TileStage<bf16, DV, NT> {
+  static constexpr int KCH = kHd / 8;                        // 16-byte chunks per K row
+  static constexpr int KMAX = (BK * KCH + NT - 1) / NT;
+  static constexpr int VITEMS = (BK / 4) * (DV / 8);         // (4-key group, 8-wide dv chunk)
+  static constexpr int VMAX = (VITEMS + NT - 1) / NT;
+  uint4 kreg[KMAX];
+  uint4 vreg[VMAX][4];
+  // item it: slot group sg = it & 15 (4 slots 4sg..4sg+3 of the 64-key stage),
+  // dv chunk dc = it >> 4. Slots are kperm-ordered inside each 16-key chunk, so
+  // the 4 keys of a slot group are consecutive keys.
+  static __device__ __forceinline__ int first_key(int sg) { return (sg & ~3) * 4 + kperm((sg & 3) * 4); }
+  __device__ __forceinline__ void fetch(const bf16* kbase, const bf16* vbase, int64_t kstride, int64_t vstride,
+                                        int j0, int L, int tid) {
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      const int it = tid + r * NT;
+      kreg[r] = make_uint4(0, 0, 0, 0);
+      if (it < BK * KCH) {
+        const int j = j0 + it / KCH;
+        if (j < L) kreg[r] = *reinterpret_cast<const uint4*>(kbase + (int64_t)j * kstride + (it % KCH) * 8);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < VMAX; ++r) {
+      const int it = tid + r * NT;
+      if (it < VITEMS) {
+        const int sg = it & 15, dc = it >> 4;
+        const int k0 = j0 + first_key(sg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vreg[r][e] = make_uint4(0, 0, 0, 0);
+          if (k0 + e < L) vreg[r][e] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(k0 + e) * vstride + 8 * dc);
+        }
+      }
+    }
+  }
+  template <int KP, int VP>
+  __device__ __forceinline__ void stash(bf16 (*Ks)[KP], bf16 (*Vt)[VP], int tid) {
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      const int it = tid + r * NT;
+      if (it < BK * KCH) *reinterpret_cast<uint4*>(&Ks[it / KCH][(it % KCH) * 8]) = kreg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VMAX; ++r) {
+      const int it = tid + r * NT;
+      if (it < VITEMS) {
+        const int sg = it & 15, dc = it >> 4;
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(vreg[r]);   // w[4e + q]: key e, dv 2q, 2q+1
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          // dv 8dc + t of keys e = 0..3: low half (t even) or high half (t odd) of word t/2
+          const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+          uint2 o;
+          o.x = __builtin_amdgcn_perm(w[4 * 1 + t / 2], w[4 * 0 + t / 2], sel);
+          o.y = __builtin_amdgcn_perm(w[4 * 3 + t / 2], w[4 * 2 + t / 2], sel);
+          *reinterpret_cast<uint2*>(&Vt[8 * dc + t][4 * sg]) = o;
+        }
+      }
+    }
+  }
+};
+
+template <int DV, int NT>
+struct TileStage<float, DV, NT> {
+  static constexpr int KCH = kHd / 4;
+  static constexpr int KMAX = (BK * KCH + NT - 1) / NT;
+  static constexpr int NQ = BK / 4, NC = DV / 8;
+  static constexpr int VMAX = (NQ * NC + NT - 1) / NT;
+  float4 kreg[KMAX];
+  float vreg[VMAX][4][8];
+  __device__ __forceinline__ void fetch(const float* kbase, const float* vbase, int64_t kstride, int64_t vstride,
+                                        int j0, int L, int tid) {
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      const int it = tid + r * NT;
+      kreg[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (it < BK * KCH) {
+        const int j = j0 + it / KCH;
+        if (j < L) kreg[r] = *reinterpret_cast<const float4*>(kbase + (int64_t)j * kstride + (it % KCH) * 4);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < VMAX; ++r) {
+      const int it = tid + r * NT;
+      if (it < NQ * NC) {
+        const int kq = it % NQ, dc = it / NQ;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = j0 + 4 * kq + e;
+          if (key < L) {
+            load8(vbase + (int64_t)key * vstride + 8 * dc, vreg[r][e]);
+          } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) vreg[r][e][t] = 0.f;
+          }
+        }
+      }
+    }
+  }
+  template <int KP, int VP>
+  __device__ __forceinline__ void stash(float (*Ks)[KP], float (*Vt)[VP], int tid) {
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      const int it = tid + r * NT;
+      if (it < BK * KCH) *reinterpret_cast<float4*>(&Ks[it / KCH][(it % KCH) * 4]) = kreg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VMAX; ++r) {
+      const int it = tid + r * NT;
+      if (it < NQ * NC) {
+        const int kq = it % NQ, dc = it / NQ;
+        const int kk0 = 4 * kq;
+        const int col = (kk0 & ~15) + kperm(kk0 & 15);  // 4 contiguous slots
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          *reinterpret_cast<float4*>(&Vt[8 * dc + t][col]) =
+              make_float4(vreg[r][0][t], vreg[r][1][t], vreg[r][2][t], vreg[r][3][t]);
+      }
+    }
+  }
+};
+
 template <typename T, int DV>
-__global__ __launch_bounds__(640) void attn_prefill_kernel(
+__global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
     const T* __restrict__ q_rot, const T* __restrict__ k_rot, const T* __restrict__ v, T* __restrict__ y,
-    int64_t k_rows, int64_t v_rows, int L, int n_meta, int window, int Hq, int Hkv, int pb) {
+    int64_t k_rows, int64_t v_rows, int L, int n_meta, int window, int Hq, int Hkv) {
   typedef Mma<T> M;
   typedef typename M::Frag Frag;
   constexpr int KP = AttnTile<T>::kpad;
   constexpr int VP = AttnTile<T>::vpad;
   constexpr int NDB = DV / 32;
+  constexpr int NT = 64 * kAttnWaves;
   __shared__ __attribute__((aligned(16))) T Ks[2][BK][KP];
   __shared__ __attribute__((aligned(16))) T Vt[2][DV][VP];
 
-  const int group = Hq / Hkv;
-  const int nthreads = blockDim.x;
+  const int G = Hq / Hkv;                 // query heads per kv head
+  const int P = kAttnCols / G;            // positions per workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int lq = lane & 31;   // query column / operand row of this lane
+  const int lq = lane & 31;   // query column (within the wave) / operand row of this lane
   const int hh = lane >> 5;   // lane half
   const int g = blockIdx.y;
   const int64_t b = blockIdx.z;
-  const int p0 = blockIdx.x * 32 * pb;
-  const int p1 = min(p0 + 32 * pb, L);
-  const int h = g * group + (wave % group);
-  const int q0 = p0 + 32 * (wave / group);
-  const int qa = q0, qb = min(q0 + 32, L);
-  const int my_q = q0 + lq;
+  const int p0 = blockIdx.x * P;
+  const int p1 = min(p0 + P, L);
+  const int col = 32 * wave + lq;
+  const bool col_ok = col < P * G;
+  const int my_q = col_ok ? p0 + col / G : L;          // position of this lane's column (L = none)
+  const int h = g * G + (col_ok ? col % G : 0);
+  // positions spanned by this wave's valid columns
+  const int c_lo = 32 * wave, c_hi = min(32 * wave + 31, P * G - 1);
+  const int qa = p0 + c_lo / G;
+  const int qb = c_lo <= c_hi ? min(p0 + c_hi / G + 1, L) : qa;
 
   // Q^T operand: lane holds Q[my_q][16 kc + 8 hh .. +7]
   Frag qf[4];
@@ -219,8 +366,8 @@ __global__ __launch_bounds__(640) void attn_prefill_kernel(
   for (int d = 0; d < NDB; ++d)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
-  float m_run = -INFINITY;  // running max of scaled scores (log2 units)
-  float l_run = 0.f;        // this lane's partial sum
+  float m_run = -INFINITY;  // reference max of scaled scores (log2 units)
+  float l_run = 0.f;        // this lane's partial sum of 2^(s - m_run)
 
   // key tiles: meta part then window part
   const int meta_end = min(n_meta, p1);
@@ -233,71 +380,26 @@ __global__ __launch_bounds__(640) void attn_prefill_kernel(
 
   const T* kbase = k_rot + (b * k_rows) * Hkv * kHd + g * kHd;
   const T* vbase = v + (b * v_rows) * Hkv * DV + g * DV;
-  constexpr int KCH = kHd * (int)sizeof(T) / 16;  // 16-byte chunks per K row
-  constexpr int E16 = 16 / (int)sizeof(T);
+  const int64_t kstride = (int64_t)Hkv * kHd, vstride = (int64_t)Hkv * DV;
+  TileStage<T, DV, NT> stage;
+  auto tile_j0 = [&](int idx) { return (idx < n1 ? idx : k2s + (idx - n1)) * BK; };
 
-  auto load_tile = [&](int idx, int buf) {
-    const int kt = idx < n1 ? idx : k2s + (idx - n1);
-    const int j0 = kt * BK;
-    for (int it = tid; it < BK * KCH; it += nthreads) {
-      const int kk = it / KCH, ch = it % KCH;
-      const int j = j0 + kk;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (j < L) val = *reinterpret_cast<const uint4*>(kbase + (int64_t)j * Hkv * kHd + ch * E16);
-      *reinterpret_cast<uint4*>(&Ks[buf][kk][ch * E16]) = val;
-    }
-    // V: item = (4-key quad, 8-wide dv chunk); written transposed, keys permuted
-    constexpr int NQ = BK / 4, NC = DV / 8;
-    for (int it = tid; it < NQ * NC; it += nthreads) {
-      const int kq = it / NC, dc = it % NC;
-      float vv[4][8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + 4 * kq + e;
-        if (j < L) {
-          load8(vbase + (int64_t)j * Hkv * DV + 8 * dc, vv[e]);
-        } else {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) vv[e][t] = 0.f;
-        }
-      }
-      const int kk0 = 4 * kq;                       // first key of the quad within the stage
-      const int col = (kk0 & ~15) + kperm(kk0 & 15);  // 4 contiguous slots
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        T* dst = &Vt[buf][8 * dc + t][col];
-        if constexpr (sizeof(T) == 2) {
-          uint2 w2;
-          w2.x = pack_bf16x2(vv[0][t], vv[1][t]);
-          w2.y = pack_bf16x2(vv[2][t], vv[3][t]);
-          *reinterpret_cast<uint2*>(dst) = w2;
-        } else {
-          *reinterpret_cast<float4*>(dst) = make_float4(vv[0][t], vv[1][t], vv[2][t], vv[3][t]);
-        }
-      }
-    }
-  };
-
-  if (ntiles > 0) load_tile(0, 0);
+  if (ntiles > 0) {
+    stage.fetch(kbase, vbase, kstride, vstride, tile_j0(0), L, tid);
+    stage.template stash<KP, VP>(Ks[0], Vt[0], tid);
+  }
   __syncthreads();
 
   for (int idx = 0; idx < ntiles; ++idx) {
     const int buf = idx & 1;
-    if (idx + 1 < ntiles) load_tile(idx + 1, buf ^ 1);
-    const int kt = idx < n1 ? idx : k2s + (idx - n1);
-
+    if (idx + 1 < ntiles) stage.fetch(kbase, vbase, kstride, vstride, tile_j0(idx + 1), L, tid);
+    const int jt = tile_j0(idx);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      const int j0 = kt * BK + sub * 32;
-      const int j1 = j0 + 32;
-      // classify this 32x32 block for this wave
-      if (qa >= qb) continue;
-      const bool none = (j0 > qb - 1) ||
-                        (window > 0 && j0 >= n_meta && qa - (j1 - 1) >= window);
+      const int j0 = jt + sub * 32, j1 = j0 + 32;
+      const bool none = qa >= qb || (j0 > qb - 1) || (window > 0 && j0 >= n_meta && qa - (j1 - 1) >= window);
       if (none) continue;
-      const bool full = (j1 - 1 <= qa) &&
-                        (window <= 0 || j1 <= n_meta || (qb - 1) - max(j0, n_meta) < window);
-
+      const bool full = (j1 - 1 <= qa) && (window <= 0 || j1 <= n_meta || (qb - 1) - max(j0, n_meta) < window);
       f32x16_t s;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -306,37 +408,37 @@ __global__ __launch_bounds__(640) void attn_prefill_kernel(
         const Frag a = M::lds_frag(&Ks[buf][sub * 32 + lq][16 * kc + 8 * hh]);
         s = M::mma(a, qf[kc], s);
       }
-      // scores of keys j0 + 8(r/4) + 4hh + (r%4), query my_q
-      float mt = -INFINITY;
-      if (full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
-      } else {
+      // lane holds scores of keys j0 + 8(r/4) + 4hh + (r%4) for position my_q
+      if (!full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
           const bool vis = my_q < L && key_visible(my_q, j, n_meta, window);
           s[r] = vis ? s[r] : -INFINITY;
-          mt = fmaxf(mt, s[r]);
         }
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt * kScaleLog2e);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
+      float mt = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * kScaleLog2e;
+      const bool need = mt > m_run + kRescaleSlack;
+      if (__any(need)) {
+        const float m_new = need ? mt : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;   // 0 when m_run = -inf
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float p[16];
-      float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         p[r] = fast_exp2(fmaf(s[r], kScaleLog2e, -m_use));
-        psum += p[r];
+        l_run += p[r];
       }
-      l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-      for (int d = 0; d < NDB; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
       const Frag pf0 = M::from_f32(&p[0]);
       const Frag pf1 = M::from_f32(&p[8]);
 #pragma unroll
@@ -347,10 +449,11 @@ __global__ __launch_bounds__(640) void attn_prefill_kernel(
         acc[d] = M::mma(va1, pf1, acc[d]);
       }
     }
+    if (idx + 1 < ntiles) stage.template stash<KP, VP>(Ks[buf ^ 1], Vt[buf ^ 1], tid);
     __syncthreads();
   }
 
-  // normalise and store: lane holds O[my_q][32 d + 8 jj + 4 hh + (0..3)]
+  // normalise and store: lane holds O[column][32 d + 8 jj + 4 hh + (0..3)]
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (my_q < L) {
     const float inv = 1.0f / l_tot;
@@ -359,16 +462,16 @@ __global__ __launch_bounds__(640) void attn_prefill_kernel(
     for (int d = 0; d < NDB; ++d) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int col = 32 * d + 8 * jj + 4 * hh;
+        const int c = 32 * d + 8 * jj + 4 * hh;
         const float o0 = acc[d][4 * jj + 0] * inv, o1 = acc[d][4 * jj + 1] * inv;
         const float o2 = acc[d][4 * jj + 2] * inv, o3 = acc[d][4 * jj + 3] * inv;
         if constexpr (sizeof(T) == 2) {
           uint2 w2;
           w2.x = pack_bf16x2(o0, o1);
           w2.y = pack_bf16x2(o2, o3);
-          *reinterpret_cast<uint2*>(yrow + col) = w2;
+          *reinterpret_cast<uint2*>(yrow + c) = w2;
         } else {
-          *reinterpret_cast<float4*>(yrow + col) = make_float4(o0, o1, o2, o3);
+          *reinterpret_cast<float4*>(yrow + c) = make_float4(o0, o1, o2, o3);
         }
       }
     }
@@ -376,39 +479,67 @@ __global__ __launch_bounds__(640) void attn_prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode attention: one workgroup per (split of the visible keys, kv head,
-// sequence). The visible keys of position p are the meta rows and the window
-// rows of the cache plus the new row p itself; they are numbered meta first,
-// then window, and split into chunks of kKeysPerSplit. Each workgroup writes
-// (o, m, l) per query head of the group; the combine kernel merges them.
+// Decode attention.
+//
+// decode_rope: rotates each sequence's queries and its new key to position
+// p = cache_len[b] once (fp32, into the workspace).
+// attn_decode: one workgroup per (chunk of the visible keys, kv head,
+// sequence). The visible keys of row p are the meta rows, the window rows of
+// the cache and the new row p itself, numbered meta first, then window. Each
+// workgroup reads its chunk's K rows straight into registers (one key per
+// thread), stages the V rows in LDS, and writes per query head of the group
+// the partial (o, m, l) of an online softmax.
+// decode_merge: one workgroup per (query head, sequence) merges the chunks'
+// partials into the attention output of that head.
 
-constexpr int kKeysPerSplit = 64;
-constexpr int kMaxGroup = 16;
+constexpr int kKeysPerSplit = 128;
+constexpr int kMaxGroup = 10;
+
+__device__ __forceinline__ int clamp_pos(int p, int cap) { return p < 0 ? 0 : (p > cap ? cap : p); }
+
+template <typename T>
+__global__ __launch_bounds__(256) void decode_rope_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
+                                                          const int32_t* __restrict__ cache_len,
+                                                          float* __restrict__ q_rot, float* __restrict__ k_rot,
+                                                          int batch, int Hq, int Hkv, int cap, float base) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, head, i)
+  const int H = Hq + Hkv;
+  if (idx >= (int64_t)batch * H * (kHd / 2)) return;
+  const int i = (int)(idx % (kHd / 2));
+  const int hd = (int)((idx / (kHd / 2)) % H);
+  const int64_t b = idx / ((kHd / 2) * H);
+  const int p = clamp_pos(cache_len[b], cap);
+  float c, sn;
+  rope_cs(p, i, base, &c, &sn);
+  const T* src = hd < Hq ? q + (b * Hq + hd) * kHd : k_new + (b * Hkv + (hd - Hq)) * kHd;
+  float* dst = hd < Hq ? q_rot + (b * Hq + hd) * kHd : k_rot + (b * Hkv + (hd - Hq)) * kHd;
+  const float lo = to_f32(src[i]), hi = to_f32(src[i + 32]);
+  dst[i] = lo * c - hi * sn;
+  dst[i + 32] = hi * c + lo * sn;
+}
 
 template <typename T, int DV>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
-    const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
+    const float* __restrict__ q_rot, const float* __restrict__ k_rot, const T* __restrict__ v_new,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
-    float* __restrict__ partial, int n_split, int cap, int n_meta, int window, int Hq, int Hkv, float base) {
+    float* __restrict__ partial, int n_split, int cap, int n_meta, int window, int Hq, int Hkv) {
   constexpr int KS = kKeysPerSplit;
+  constexpr int E = Vec16<T>::n;            // elements per 16-byte load
   __shared__ float qs[kMaxGroup][kHd];
-  __shared__ float kn[kHd];
-  __shared__ float Ks[KS][kHd + 1];
-  __shared__ float Vs[KS][DV];
   __shared__ float ps[kMaxGroup][KS];
+  __shared__ __attribute__((aligned(16))) T Vs[KS][DV];
 
   const int s = blockIdx.x, g = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int group = Hq / Hkv;
   const int tid = threadIdx.x;
-  int p = cache_len[b];
-  p = p < 0 ? 0 : (p > cap ? cap : p);
+  const int p = clamp_pos(cache_len[b], cap);
   const MaskRange mr = mask_range(p, n_meta, window);
   const int n_vis = mr.meta_end + (mr.win_end - mr.win_begin);
   const int i0 = s * KS;
   const int nk = max(0, min(KS, n_vis - i0));
   float* outp = partial + (((b * Hq) + g * group) * n_split + s) * (DV + 2);
-  const int64_t pstride = (int64_t)n_split * (DV + 2);  // between heads
+  const int64_t pstride = (int64_t)n_split * (DV + 2);  // between query heads
 
   if (nk == 0) {
     for (int t = tid; t < group * (DV + 2); t += blockDim.x) {
@@ -417,135 +548,100 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     }
     return;
   }
+  auto key_row = [&](int vi) { return vi < mr.meta_end ? vi : mr.win_begin + (vi - mr.meta_end); };
 
-  // rotate the group's queries and the new key to position p
-  for (int t = tid; t < (group + 1) * (kHd / 2); t += blockDim.x) {
-    const int hq = t / (kHd / 2), i = t % (kHd / 2);
-    float c, sn;
-    rope_cs(p, i, base, &c, &sn);
-    const T* src = hq < group ? q + (b * Hq + g * group + hq) * kHd : k_new + (b * Hkv + g) * kHd;
-    const float lo = to_f32(src[i]), hi = to_f32(src[i + 32]);
-    float* dst = hq < group ? qs[hq] : kn;
-    dst[i] = lo * c - hi * sn;
-    dst[i + 32] = hi * c + lo * sn;
+  // V rows of the chunk -> LDS (raw copy)
+  constexpr int VCH = DV / E;
+  for (int it = tid; it < nk * VCH; it += blockDim.x) {
+    const int kk = it / VCH, ch = it % VCH;
+    const int j = key_row(i0 + kk);
+    const T* src = j == p ? v_new + (b * Hkv + g) * DV : v_cache + ((b * cap + j) * Hkv + g) * DV;
+    *reinterpret_cast<uint4*>(&Vs[kk][ch * E]) = *reinterpret_cast<const uint4*>(src + ch * E);
   }
-  __syncthreads();
-
-  // stage K and V rows of the chunk (new row from k_new / v_new)
-  constexpr int E = Vec16<T>::n;
-  for (int it = tid; it < nk * (kHd / E); it += blockDim.x) {
-    const int kk = it / (kHd / E), ch = it % (kHd / E);
-    const int vi = i0 + kk;
-    const int j = vi < mr.meta_end ? vi : mr.win_begin + (vi - mr.meta_end);
-    float tmp[E];
+  for (int t = tid; t < group * kHd; t += blockDim.x) qs[t / kHd][t % kHd] = q_rot[(b * Hq + g * group) * kHd + t];
+  // this thread's key row -> registers
+  float kr[kHd];
+  const bool has_key = tid < nk;
+  if (has_key) {
+    const int j = key_row(i0 + tid);
     if (j == p) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) tmp[e] = kn[ch * E + e];
+      for (int d = 0; d < kHd; ++d) kr[d] = k_rot[(b * Hkv + g) * kHd + d];
     } else {
-      load16(k_cache + ((b * cap + j) * Hkv + g) * kHd + ch * E, tmp);
+      const T* src = k_cache + ((b * cap + j) * Hkv + g) * kHd;
+#pragma unroll
+      for (int ch = 0; ch < kHd / E; ++ch) load16(src + ch * E, kr + ch * E);
     }
-#pragma unroll
-    for (int e = 0; e < E; ++e) Ks[kk][ch * E + e] = tmp[e];
-  }
-  for (int it = tid; it < nk * (DV / E); it += blockDim.x) {
-    const int kk = it / (DV / E), ch = it % (DV / E);
-    const int vi = i0 + kk;
-    const int j = vi < mr.meta_end ? vi : mr.win_begin + (vi - mr.meta_end);
-    const T* src = j == p ? v_new + (b * Hkv + g) * DV + ch * E : v_cache + ((b * cap + j) * Hkv + g) * DV + ch * E;
-    float tmp[E];
-    load16(src, tmp);
-#pragma unroll
-    for (int e = 0; e < E; ++e) Vs[kk][ch * E + e] = tmp[e];
   }
   __syncthreads();
-
-  // scores (log2 units)
-  for (int t = tid; t < group * KS; t += blockDim.x) {
-    const int hq = t / KS, kk = t % KS;
-    float sc = -INFINITY;
-    if (kk < nk) {
+  if (tid < KS) {
+    for (int hq = 0; hq < group; ++hq) {
       float a = 0.f;
-#pragma unroll 16
-      for (int d = 0; d < kHd; ++d) a = fmaf(qs[hq][d], Ks[kk][d], a);
-      sc = a * kScaleLog2e;
+#pragma unroll
+      for (int d = 0; d < kHd; ++d) a = fmaf(qs[hq][d], kr[d], a);
+      ps[hq][tid] = has_key ? a * kScaleLog2e : -INFINITY;
     }
-    ps[hq][kk] = sc;
   }
   __syncthreads();
-  // softmax pieces per head: one wave per head (KS == 64 == wave size)
+  // softmax pieces: one wave per query head, two keys per lane
   const int lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   for (int hq = wave; hq < group; hq += nw) {
-    const float sc = ps[hq][lane];
-    float m = sc;
+    const float s0 = ps[hq][lane], s1 = ps[hq][lane + 64];
+    float m = fmaxf(s0, s1);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const float pv = lane < nk ? fast_exp2(sc - m) : 0.f;
-    const float l = wave_sum(pv);
-    ps[hq][lane] = pv;
+    const float p0 = fast_exp2(s0 - m), p1 = fast_exp2(s1 - m);   // exp2(-inf) = 0 for absent keys
+    const float l = wave_sum(p0 + p1);
+    ps[hq][lane] = p0;
+    ps[hq][lane + 64] = p1;
     if (lane == 0) {
       outp[hq * pstride + DV] = m;
       outp[hq * pstride + DV + 1] = l;
     }
   }
   __syncthreads();
-  // o = sum_k p_k v_k
-  for (int t = tid; t < group * DV; t += blockDim.x) {
-    const int hq = t / DV, d = t % DV;
-    float a = 0.f;
-    for (int kk = 0; kk < nk; ++kk) a = fmaf(ps[hq][kk], Vs[kk][d], a);
-    outp[hq * pstride + d] = a;
+  // o[h][d..d+3] = sum_k p[h][k] v[k][d..d+3]
+  constexpr int NQ = DV / 4;
+  for (int t = tid; t < group * NQ; t += blockDim.x) {
+    const int hq = t / NQ, dq = t % NQ;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int kk = 0; kk < nk; ++kk) {
+      const float pk = ps[hq][kk];
+      float v4[4];
+      if constexpr (sizeof(T) == 2) {
+        const uint2 w2 = *reinterpret_cast<const uint2*>(&Vs[kk][4 * dq]);
+        v4[0] = bf16_lo(w2.x); v4[1] = bf16_hi(w2.x); v4[2] = bf16_lo(w2.y); v4[3] = bf16_hi(w2.y);
+      } else {
+        const float4 w4 = *reinterpret_cast<const float4*>(&Vs[kk][4 * dq]);
+        v4[0] = w4.x; v4[1] = w4.y; v4[2] = w4.z; v4[3] = w4.w;
+      }
+      a0 = fmaf(pk, v4[0], a0); a1 = fmaf(pk, v4[1], a1);
+      a2 = fmaf(pk, v4[2], a2); a3 = fmaf(pk, v4[3], a3);
+    }
+    *reinterpret_cast<float4*>(outp + hq * pstride + 4 * dq) = make_float4(a0, a1, a2, a3);
   }
 }
 
-// Merge the split partials of every head, then fuse with the Mamba branch:
-// one workgroup per sequence.
+// Merge the chunk partials of one (query head, sequence): y = sum_s o_s 2^(m_s-m) / sum_s l_s 2^(m_s-m).
 template <typename T, int DV>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
-    const float* __restrict__ partial, const T* __restrict__ y_ssm, const float* __restrict__ ba,
-    const float* __restrict__ bs, T* __restrict__ out, T* __restrict__ y_attn_out, int n_split, int Hq,
-    float eps) {
-  extern __shared__ float ya[];   // [Hq * DV]
-  __shared__ float red[2][4];
-  const int64_t b = blockIdx.x;
-  const int W = Hq * DV;
-  const int tid = threadIdx.x;
-  const float* pb = partial + b * Hq * (int64_t)n_split * (DV + 2);
-  float sa = 0.f, ss = 0.f;
-  for (int t = tid; t < W; t += blockDim.x) {
-    const int h = t / DV, d = t % DV;
-    const float* ph = pb + (int64_t)h * n_split * (DV + 2);
-    float m = -INFINITY;
-    for (int s = 0; s < n_split; ++s) m = fmaxf(m, ph[s * (DV + 2) + DV]);
-    float l = 0.f, o = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float ms = ph[s * (DV + 2) + DV];
-      if (ms == -INFINITY) continue;
-      const float f = fast_exp2(ms - m);
-      l = fmaf(ph[s * (DV + 2) + DV + 1], f, l);
-      o = fmaf(ph[s * (DV + 2) + d], f, o);
-    }
-    const float v = o / l;
-    ya[t] = v;
-    sa = fmaf(v, v, sa);
-    const float vs = to_f32(y_ssm[b * W + t]);
-    ss = fmaf(vs, vs, ss);
+__global__ __launch_bounds__(DV) void decode_merge_kernel(const float* __restrict__ partial, T* __restrict__ y,
+                                                          int n_split, int Hq) {
+  const int h = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const int d = threadIdx.x;
+  const float* ph = partial + ((b * Hq) + h) * (int64_t)n_split * (DV + 2);
+  float m = -INFINITY;
+#pragma unroll 8
+  for (int s = 0; s < n_split; ++s) m = fmaxf(m, ph[s * (DV + 2) + DV]);
+  float l = 0.f, o = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < n_split; ++s) {
+    const float ms = ph[s * (DV + 2) + DV];
+    const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - m);   // empty chunks weigh nothing
+    l = fmaf(ph[s * (DV + 2) + DV + 1], f, l);
+    o = fmaf(ph[s * (DV + 2) + d], f, o);
   }
-  sa = wave_sum(sa);
-  ss = wave_sum(ss);
-  const int lane = tid & 63, wave = tid >> 6;
-  if (lane == 0) { red[0][wave] = sa; red[1][wave] = ss; }
-  __syncthreads();
-  sa = 0.f; ss = 0.f;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) { sa += red[0][w]; ss += red[1][w]; }
-  const float inv_w = 1.0f / (float)W;
-  const float ra = 0.5f / sqrtf(sa * inv_w + eps);
-  const float rs = 0.5f / sqrtf(ss * inv_w + eps);
-  for (int t = tid; t < W; t += blockDim.x) {
-    const float v = ya[t];
-    const float vs = to_f32(y_ssm[b * W + t]);
-    out[b * W + t] = from_f32<T>(fmaf(ba[t] * ra, v, bs[t] * rs * vs));
-    if (y_attn_out) y_attn_out[b * W + t] = from_f32<T>(v);
-  }
+  y[(b * Hq + h) * DV + d] = from_f32<T>(o / l);
 }
 
 template <typename T>
@@ -559,34 +655,33 @@ hipError_t rope_t(const RopeArgs& a, hipStream_t stream) {
 
 template <typename T, int DV>
 hipError_t attn_prefill_t(const AttnPrefillArgs& a, hipStream_t stream) {
-  // 32-row query blocks per workgroup: two (more K/V reuse per LDS stage) when
-  // that still leaves several workgroups per compute unit; at most 10 waves.
-  const int group = a.n_q_heads / a.n_kv_heads;
-  const int64_t blocks1 = (int64_t)((a.L + 31) / 32) * a.n_kv_heads * a.batch;
-  const int pb = (group <= 5 && blocks1 >= 1024) ? 2 : 1;
-  dim3 grid((a.L + 32 * pb - 1) / (32 * pb), a.n_kv_heads, a.batch);
-  dim3 block(64 * group * pb);
-  hipLaunchKernelGGL((attn_prefill_kernel<T, DV>), grid, block, 0, stream, (const T*)a.q_rot, (const T*)a.k_rot,
-                     (const T*)a.v, (T*)a.y, a.k_rows, a.v_rows, a.L, a.n_meta, a.window, a.n_q_heads, a.n_kv_heads,
-                     pb);
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int P = kAttnCols / G;   // positions per workgroup
+  dim3 grid((a.L + P - 1) / P, a.n_kv_heads, a.batch);
+  hipLaunchKernelGGL((attn_prefill_kernel<T, DV>), grid, dim3(64 * kAttnWaves), 0, stream, (const T*)a.q_rot,
+                     (const T*)a.k_rot, (const T*)a.v, (T*)a.y, a.k_rows, a.v_rows, a.L, a.n_meta, a.window,
+                     a.n_q_heads, a.n_kv_heads);
   return hipGetLastError();
 }
 
 template <typename T, int DV>
 hipError_t attn_decode_t(const AttnDecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.n_split, a.n_kv_heads, a.batch);
-  hipLaunchKernelGGL((attn_decode_kernel<T, DV>), grid, dim3(256), 0, stream, (const T*)a.q, (const T*)a.k_new,
-                     (const T*)a.v_new, (const T*)a.k_cache, (const T*)a.v_cache, a.cache_len, a.partial,
-                     a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads, a.n_kv_heads, a.rope_base);
+  const int64_t n = (int64_t)a.batch * (a.n_q_heads + a.n_kv_heads) * (kHd / 2);
+  hipLaunchKernelGGL(decode_rope_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, (const T*)a.q,
+                     (const T*)a.k_new, a.cache_len, a.q_rot, a.k_rot, a.batch, a.n_q_heads, a.n_kv_heads, a.cap,
+                     a.rope_base);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_decode_kernel<T, DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream,
+                     a.q_rot, a.k_rot, (const T*)a.v_new, (const T*)a.k_cache, (const T*)a.v_cache, a.cache_len,
+                     a.partial, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads, a.n_kv_heads);
   return hipGetLastError();
 }
 
 template <typename T, int DV>
-hipError_t combine_t(const DecodeCombineArgs& a, hipStream_t stream) {
-  const size_t shm = (size_t)a.n_q_heads * DV * sizeof(float);
-  hipLaunchKernelGGL((decode_combine_kernel<T, DV>), dim3(a.batch), dim3(256), shm, stream, a.partial,
-                     (const T*)a.y_ssm, a.beta_attn, a.beta_ssm, (T*)a.out, (T*)a.y_attn_out, a.n_split,
-                     a.n_q_heads, a.eps);
+hipError_t merge_t(const DecodeMergeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_merge_kernel<T, DV>), dim3(a.n_q_heads, a.batch), dim3(DV), 0, stream, a.partial,
+                     (T*)a.y_attn, a.n_split, a.n_q_heads);
   return hipGetLastError();
 }
 
@@ -623,9 +718,9 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream) {
   HYMBA_DISPATCH_DV(a.head_dim_v, attn_decode_t, float, a, stream)
 }
 
-hipError_t launch_decode_combine(const DecodeCombineArgs& a, hipStream_t stream) {
-  if (a.act == HYMBA_BF16) { HYMBA_DISPATCH_DV(a.head_dim_v, combine_t, bf16, a, stream) }
-  HYMBA_DISPATCH_DV(a.head_dim_v, combine_t, float, a, stream)
+hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream) {
+  if (a.act == HYMBA_BF16) { HYMBA_DISPATCH_DV(a.head_dim_v, merge_t, bf16, a, stream) }
+  HYMBA_DISPATCH_DV(a.head_dim_v, merge_t, float, a, stream)
 }
 
 }  // namespace hymba

@@ -11,7 +11,10 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;
 
-template <typename T, bool VEC>
+// VEC: 16-byte vectors; MAXV > 0: the row fits in MAXV vectors per lane and is
+// kept in registers (all loads issued up front); MAXV == 0: two passes over
+// the row (the second one hits cache).
+template <typename T, bool VEC, int MAXV>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void fuse_rows_kernel(
     const T* __restrict__ ya, const T* __restrict__ ys, const float* __restrict__ ba,
     const float* __restrict__ bs, int64_t n_rows, int width, float eps, T* __restrict__ out) {
@@ -22,44 +25,85 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void fuse_rows_kernel(
   const T* s = ys + row * (int64_t)width;
   T* o = out + row * (int64_t)width;
   constexpr int V = VEC ? Vec16<T>::n : 1;
-
-  float sa = 0.f, ss = 0.f;
-  for (int c = lane * V; c < width; c += 64 * V) {
-    float va[V], vs[V];
-    if constexpr (VEC) {
-      load16(a + c, va);
-      load16(s + c, vs);
-    } else {
-      va[0] = to_f32(a[c]);
-      vs[0] = to_f32(s[c]);
-    }
-#pragma unroll
-    for (int e = 0; e < V; ++e) {
-      sa = fmaf(va[e], va[e], sa);
-      ss = fmaf(vs[e], vs[e], ss);
-    }
-  }
-  sa = wave_sum(sa);
-  ss = wave_sum(ss);
   const float inv_w = 1.0f / (float)width;
-  const float ra = 0.5f / sqrtf(sa * inv_w + eps);
-  const float rs = 0.5f / sqrtf(ss * inv_w + eps);
 
-  for (int c = lane * V; c < width; c += 64 * V) {
-    float va[V], vs[V], r[V];
-    if constexpr (VEC) {
-      load16(a + c, va);
-      load16(s + c, vs);
-    } else {
-      va[0] = to_f32(a[c]);
-      vs[0] = to_f32(s[c]);
+  if constexpr (MAXV > 0) {
+    float va[MAXV][V], vs[MAXV][V];
+    float sa = 0.f, ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int c = (lane + 64 * i) * V;
+      if (c < width) {
+        load16(a + c, va[i]);
+        load16(s + c, vs[i]);
+      }
     }
 #pragma unroll
-    for (int e = 0; e < V; ++e) r[e] = fmaf(ba[c + e] * ra, va[e], bs[c + e] * rs * vs[e]);
-    if constexpr (VEC) {
-      store16(o + c, r);
-    } else {
-      o[c] = from_f32<T>(r[0]);
+    for (int i = 0; i < MAXV; ++i) {
+      const int c = (lane + 64 * i) * V;
+      if (c < width) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          sa = fmaf(va[i][e], va[i][e], sa);
+          ss = fmaf(vs[i][e], vs[i][e], ss);
+        }
+      }
+    }
+    sa = wave_sum(sa);
+    ss = wave_sum(ss);
+    const float ra = 0.5f / sqrtf(sa * inv_w + eps);
+    const float rs = 0.5f / sqrtf(ss * inv_w + eps);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int c = (lane + 64 * i) * V;
+      if (c < width) {
+        float bav[V], bsv[V], r[V];
+        load16(ba + c, bav);
+        if constexpr (V == 8) load16(ba + c + 4, bav + 4);
+        load16(bs + c, bsv);
+        if constexpr (V == 8) load16(bs + c + 4, bsv + 4);
+#pragma unroll
+        for (int e = 0; e < V; ++e) r[e] = fmaf(bav[e] * ra, va[i][e], bsv[e] * rs * vs[i][e]);
+        store16(o + c, r);
+      }
+    }
+  } else {
+    float sa = 0.f, ss = 0.f;
+    for (int c = lane * V; c < width; c += 64 * V) {
+      float va[V], vs[V];
+      if constexpr (VEC) {
+        load16(a + c, va);
+        load16(s + c, vs);
+      } else {
+        va[0] = to_f32(a[c]);
+        vs[0] = to_f32(s[c]);
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        sa = fmaf(va[e], va[e], sa);
+        ss = fmaf(vs[e], vs[e], ss);
+      }
+    }
+    sa = wave_sum(sa);
+    ss = wave_sum(ss);
+    const float ra = 0.5f / sqrtf(sa * inv_w + eps);
+    const float rs = 0.5f / sqrtf(ss * inv_w + eps);
+    for (int c = lane * V; c < width; c += 64 * V) {
+      float va[V], vs[V], r[V];
+      if constexpr (VEC) {
+        load16(a + c, va);
+        load16(s + c, vs);
+      } else {
+        va[0] = to_f32(a[c]);
+        vs[0] = to_f32(s[c]);
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) r[e] = fmaf(ba[c + e] * ra, va[e], bs[c + e] * rs * vs[e]);
+      if constexpr (VEC) {
+        store16(o + c, r);
+      } else {
+        o[c] = from_f32<T>(r[0]);
+      }
     }
   }
 }
@@ -77,13 +121,17 @@ hipError_t fuse_t(const void* ya, const void* ys, const float* ba, const float* 
                   int width, float eps, void* out, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
   const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  const bool vec = (width % Vec16<T>::n) == 0;
+  constexpr int V = Vec16<T>::n;
+  const bool vec = (width % V) == 0;
   dim3 grid((unsigned)blocks), block(64 * kRowsPerBlock);
-  if (vec)
-    hipLaunchKernelGGL((fuse_rows_kernel<T, true>), grid, block, 0, stream, (const T*)ya, (const T*)ys, ba,
+  if (vec && width <= 64 * V * 8)
+    hipLaunchKernelGGL((fuse_rows_kernel<T, true, 8>), grid, block, 0, stream, (const T*)ya, (const T*)ys, ba,
+                       bs, n_rows, width, eps, (T*)out);
+  else if (vec)
+    hipLaunchKernelGGL((fuse_rows_kernel<T, true, 0>), grid, block, 0, stream, (const T*)ya, (const T*)ys, ba,
                        bs, n_rows, width, eps, (T*)out);
   else
-    hipLaunchKernelGGL((fuse_rows_kernel<T, false>), grid, block, 0, stream, (const T*)ya, (const T*)ys, ba,
+    hipLaunchKernelGGL((fuse_rows_kernel<T, false, 0>), grid, block, 0, stream, (const T*)ya, (const T*)ys, ba,
                        bs, n_rows, width, eps, (T*)out);
   return hipGetLastError();
 }

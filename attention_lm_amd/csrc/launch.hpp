@@ -24,9 +24,14 @@ struct SsmPrefillArgs {
   void* y;                 // [batch, L, d_inner] act
   float* state_out;        // optional [batch, d_inner, 16]
   void* conv_state_out;    // optional [batch, d_inner, 3]
+  float* agg;              // workspace [n_chunks, batch, d_inner, 16]
+  float* sdt;              // workspace [n_chunks, batch, d_inner]
+  float* carry;            // workspace [n_chunks, batch, d_inner, 16]
+  int chunk_rows;          // from ssm_prefill_chunk_rows()
   int batch, L, d_inner;
   hymba_dtype act;
 };
+int ssm_prefill_chunk_rows(int batch, int L, int d_inner);
 hipError_t launch_ssm_prefill(const SsmPrefillArgs& a, hipStream_t stream);
 
 struct SsmDecodeArgs {
@@ -68,6 +73,8 @@ struct AttnDecodeArgs {
   const void *q, *k_new, *v_new;       // [batch, H, d] not rotated
   const void *k_cache, *v_cache;       // [batch, cap, Hkv, d]
   const int32_t* cache_len;
+  float* q_rot;                        // workspace [batch, Hq, 64]
+  float* k_rot;                        // workspace [batch, Hkv, 64]
   float* partial;                      // [batch, Hq, n_split, dv + 2]
   int n_split, keys_per_split;
   int batch, cap, n_meta, window, n_q_heads, n_kv_heads, head_dim_v;
@@ -77,16 +84,12 @@ struct AttnDecodeArgs {
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream);
 void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_per_split);
 
-struct DecodeCombineArgs {
+struct DecodeMergeArgs {
   const float* partial;    // [batch, Hq, n_split, dv + 2]
-  const void* y_ssm;       // [batch, d_inner] act
-  const float *beta_attn, *beta_ssm;
-  void* out;               // [batch, d_inner]
-  void* y_attn_out;        // optional
+  void* y_attn;            // [batch, Hq * dv] act
   int n_split, batch, n_q_heads, head_dim_v;
-  float eps;
   hymba_dtype act;
 };
-hipError_t launch_decode_combine(const DecodeCombineArgs& a, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream);
 
 }  // namespace hymba

@@ -5,20 +5,19 @@
 // "Lecture 04 - Beyond the Dense Transformer", section 2):
 //   h_t = exp(dt_t A) (.) h_{t-1} + (dt_t B_t) u_t,   y_t = C_t . h_t + D u_t.
 //
-// Prefill design. A workgroup owns CPB channels of one sequence and walks the
-// sequence in blocks of NW*TC rows; wave w takes rows [w*TC, (w+1)*TC) of each
-// block. Lane (channel c, slice s) holds SPL of the 16 states of c in
-// registers. Per block:
-//   pass 1  each wave scans its TC rows from a zero state, keeping every
-//           exp(dt A) factor in registers, and leaves its end state and the
-//           sum of its dt in LDS;
-//   combine one thread per (channel, state) chains the NW wave results with
-//           the block's carried state: the decay over a wave's rows is
-//           exp(A * sum(dt)), so a wave's carry-in is a short linear chain;
-//   pass 2  each wave re-runs its rows from its true carry-in using the cached
-//           factors (no further exp), forms y_t, gates it and stores it.
-// So every (row, channel, state) costs one exp. Rows past the end of the
-// sequence use dt = 0, which leaves the state unchanged.
+// Prefill design: the sequence is cut into chunks of CT rows and every
+// (sequence, 128-channel block, chunk) is a workgroup, one lane per channel
+// with its 16 states in registers, so even a single sequence fills the chip.
+//   1. chunk_end:   each chunk (except the last) is scanned from a zero state;
+//                   its end state a_k and the sum of its dt, S_k, go to the
+//                   workspace.
+//   2. chunk_carry: one thread per (sequence, channel, state) chains the chunks:
+//                   H_{k+1} = exp(A S_k) H_k + a_k (the decay over a chunk is
+//                   exp(A times its total dt)), giving every chunk's carry-in H_k.
+//   3. chunk_out:   each chunk is scanned again from its carry-in, forming
+//                   y_t = C_t . h_t + D u_t, gated by silu(z_t); the last chunk
+//                   also writes the final state and the conv history.
+// The conv history of a chunk is re-read from x (3 rows before it).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -66,152 +65,153 @@ __device__ __forceinline__ float silu(float z) {
 constexpr int kStates = 16;
 constexpr int kConv = 4;
 
-template <typename T, int SPL, int TC, int NW>
-__global__ __launch_bounds__(64 * NW) void ssm_prefill_kernel(
-    const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ dt,
-    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ A,
-    const float* __restrict__ Dp, const float* __restrict__ conv_w, T* __restrict__ y,
-    float* __restrict__ state_out, T* __restrict__ conv_state_out, int L, int Dch) {
-  constexpr int LPC = kStates / SPL;  // lanes per channel
-  constexpr int CPB = 64 / LPC;       // channels per workgroup
-  constexpr int NT = 64 * NW;
+constexpr int kChanPerBlock = 128;   // one lane per channel
 
-  __shared__ float aggH[NW][kStates][CPB];
-  __shared__ float aggS[NW][CPB];
-  __shared__ float carryH[kStates][CPB];
-  __shared__ float A2s[kStates][CPB];
+// 16 wave-uniform values of one row of B or C (shared by all channels)
+template <typename T>
+__device__ __forceinline__ void load_row16(const T* p, float* o) {
+  load_n<kStates>(p, o);
+}
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int cl = lane / LPC;
-  const int qs = lane % LPC;
-  const int c0 = blockIdx.x * CPB;
-  const int c = c0 + cl;
-  const bool cvalid = c < Dch;
-  const int n0 = qs * SPL;
-  const int64_t seq = (int64_t)blockIdx.y * L;
+template <typename T>
+__global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_end_kernel(
+    const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm, const float* __restrict__ A,
+    const float* __restrict__ conv_w, float* __restrict__ agg, float* __restrict__ sdt, int L, int Dch, int CT) {
+  const int c = blockIdx.x * kChanPerBlock + threadIdx.x;
+  const int k = blockIdx.y;
+  const int b = blockIdx.z;
+  const int batch = gridDim.z;
+  const bool cv = c < Dch;
+  const int cc = cv ? c : Dch - 1;   // clamped channel for loads; results of invalid lanes are dropped
+  const int64_t seq = (int64_t)b * L;
+  const int t0 = k * CT, t1 = min(t0 + CT, L);
 
-  for (int k = threadIdx.x; k < kStates * CPB; k += NT) {
-    const int n = k / CPB, cc = k % CPB;
-    const int cg = c0 + cc;
-    A2s[n][cc] = cg < Dch ? A[(int64_t)cg * kStates + n] * kLog2e : 0.f;
-    carryH[n][cc] = 0.f;
+  float A2[kStates], w[kConv], h[kStates];
+#pragma unroll
+  for (int n = 0; n < kStates; ++n) {
+    A2[n] = A[(int64_t)cc * kStates + n] * kLog2e;
+    h[n] = 0.f;
   }
-  float A2[SPL];
 #pragma unroll
-  for (int j = 0; j < SPL; ++j) A2[j] = cvalid ? A[(int64_t)c * kStates + n0 + j] * kLog2e : 0.f;
-  float w[kConv];
+  for (int j = 0; j < kConv; ++j) w[j] = conv_w[(int64_t)cc * kConv + j];
+  float xm3 = t0 >= 3 ? to_f32(x[(seq + t0 - 3) * Dch + cc]) : 0.f;
+  float xm2 = t0 >= 2 ? to_f32(x[(seq + t0 - 2) * Dch + cc]) : 0.f;
+  float xm1 = t0 >= 1 ? to_f32(x[(seq + t0 - 1) * Dch + cc]) : 0.f;
+  float S = 0.f;
+  // next row's x and dt are loaded one iteration ahead
+  T xn = x[(seq + t0) * Dch + cc], dn = dt[(seq + t0) * Dch + cc];
+#pragma unroll 2
+  for (int t = t0; t < t1; ++t) {
+    const float xt = to_f32(xn), d = to_f32(dn);
+    const int tn = min(t + 1, t1 - 1);
+    xn = x[(seq + tn) * Dch + cc];
+    dn = dt[(seq + tn) * Dch + cc];
+    const float u = fmaf(w[0], xm3, fmaf(w[1], xm2, fmaf(w[2], xm1, w[3] * xt)));
+    xm3 = xm2; xm2 = xm1; xm1 = xt;
+    const float du = d * u;
+    float Bv[kStates];
+    load_row16(Bm + (seq + t) * kStates, Bv);
 #pragma unroll
-  for (int j = 0; j < kConv; ++j) w[j] = cvalid ? conv_w[(int64_t)c * kConv + j] : 0.f;
-  const float Dc = cvalid ? Dp[c] : 0.f;
-  __syncthreads();
-
-  constexpr int ROWS = NW * TC;
-  const int nblk = (L + ROWS - 1) / ROWS;
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int r0 = blk * ROWS + wave * TC;
-    // conv over rows r0-3 .. r0+TC-1 (zero history before row 0)
-    float xv[TC + kConv - 1];
-#pragma unroll
-    for (int k = 0; k < TC + kConv - 1; ++k) {
-      const int t = r0 - (kConv - 1) + k;
-      xv[k] = (cvalid && t >= 0 && t < L) ? to_f32(x[(seq + t) * Dch + c]) : 0.f;
-    }
-    float u[TC], dtv[TC], dtu[TC], zv[TC];
-#pragma unroll
-    for (int i = 0; i < TC; ++i) {
-      const int t = r0 + i;
-      const bool ok = cvalid && t < L;
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < kConv; ++j) acc = fmaf(w[j], xv[i + j], acc);
-      u[i] = acc;
-      dtv[i] = ok ? to_f32(dt[(seq + t) * Dch + c]) : 0.f;
-      zv[i] = ok ? to_f32(z[(seq + t) * Dch + c]) : 0.f;
-      dtu[i] = dtv[i] * acc;
-    }
-
-    // pass 1: scan from zero, cache exp(dt A)
-    float dA[TC][SPL];
-    float h[SPL];
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) h[j] = 0.f;
-    float S = 0.f;
-#pragma unroll
-    for (int i = 0; i < TC; ++i) {
-      const int t = min(r0 + i, L - 1);
-      float Bv[SPL];
-      load_n<SPL>(Bm + (seq + t) * kStates + n0, Bv);
-#pragma unroll
-      for (int j = 0; j < SPL; ++j) {
-        const float a = fast_exp2(dtv[i] * A2[j]);
-        dA[i][j] = a;
-        h[j] = fmaf(a, h[j], dtu[i] * Bv[j]);
-      }
-      S += dtv[i];
-    }
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) aggH[wave][n0 + j][cl] = h[j];
-    if (qs == 0) aggS[wave][cl] = S;
-    __syncthreads();
-
-    // combine: carry-in of each wave, then the block's end state
-    for (int k = threadIdx.x; k < kStates * CPB; k += NT) {
-      const int n = k / CPB, cc = k % CPB;
-      float carry = carryH[n][cc];
-      const float a2 = A2s[n][cc];
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float hw = aggH[ww][n][cc];
-        const float P = fast_exp2(a2 * aggS[ww][cc]);
-        aggH[ww][n][cc] = carry;
-        carry = fmaf(P, carry, hw);
-      }
-      carryH[n][cc] = carry;
-    }
-    __syncthreads();
-
-    // pass 2: rerun from the true carry-in, output gated y
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) h[j] = aggH[wave][n0 + j][cl];
-#pragma unroll
-    for (int i = 0; i < TC; ++i) {
-      const int t = r0 + i;
-      const int tc = min(t, L - 1);
-      float Bv[SPL], Cv[SPL];
-      load_n<SPL>(Bm + (seq + tc) * kStates + n0, Bv);
-      load_n<SPL>(Cm + (seq + tc) * kStates + n0, Cv);
-      float part = 0.f;
-#pragma unroll
-      for (int j = 0; j < SPL; ++j) {
-        h[j] = fmaf(dA[i][j], h[j], dtu[i] * Bv[j]);
-        part = fmaf(Cv[j], h[j], part);
-      }
-#pragma unroll
-      for (int o = 1; o < LPC; o <<= 1) part += __shfl_xor(part, o, 64);
-      const float yv = fmaf(Dc, u[i], part) * silu(zv[i]);
-      if (qs == 0 && cvalid && t < L) y[(seq + t) * Dch + c] = from_f32<T>(yv);
-    }
-    // the next block's pass 1 writes aggH/aggS only after every wave passed the
-    // barrier above; its combine runs after the next barrier
+    for (int n = 0; n < kStates; ++n) h[n] = fmaf(fast_exp2(d * A2[n]), h[n], du * Bv[n]);
+    S += d;
   }
+  if (!cv) return;
+  const int64_t o = (((int64_t)k * batch + b) * Dch + c);
+  float4* ap = reinterpret_cast<float4*>(agg + o * kStates);
+#pragma unroll
+  for (int q = 0; q < kStates / 4; ++q) ap[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+  sdt[o] = S;
+}
 
-  const int b = blockIdx.y;
-  if (state_out) {
-    for (int k = threadIdx.x; k < kStates * CPB; k += NT) {
-      const int cc = k / kStates, n = k % kStates;
-      const int cg = c0 + cc;
-      if (cg < Dch) state_out[((int64_t)b * Dch + cg) * kStates + n] = carryH[n][cc];
-    }
+// carry[k] = state entering chunk k, from the chunk end states agg[k] (zero start)
+// and the chunk dt sums sdt[k].
+__global__ __launch_bounds__(256) void ssm_chunk_carry_kernel(const float* __restrict__ A,
+                                                              const float* __restrict__ agg,
+                                                              const float* __restrict__ sdt,
+                                                              float* __restrict__ carry, int nchunk, int batch,
+                                                              int Dch) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, c, n)
+  const int64_t per = (int64_t)batch * Dch * kStates;
+  if (idx >= per) return;
+  const int n = (int)(idx % kStates);
+  const int64_t bc = idx / kStates;
+  const int c = (int)(bc % Dch);
+  const float a2 = A[(int64_t)c * kStates + n] * kLog2e;
+  float H = 0.f;
+  carry[idx] = 0.f;
+#pragma unroll 4
+  for (int k = 0; k + 1 < nchunk; ++k) {
+    const float a = agg[k * per + idx];
+    const float s = sdt[k * (per / kStates) + bc];
+    H = fmaf(fast_exp2(a2 * s), H, a);
+    carry[(k + 1) * per + idx] = H;
   }
-  if (conv_state_out) {
-    for (int k = threadIdx.x; k < (kConv - 1) * CPB; k += NT) {
-      const int cc = k / (kConv - 1), j = k % (kConv - 1);
-      const int cg = c0 + cc;
-      const int t = L - (kConv - 1) + j;
-      if (cg < Dch)
-        conv_state_out[((int64_t)b * Dch + cg) * (kConv - 1) + j] =
-            t >= 0 ? x[(seq + t) * Dch + cg] : from_f32<T>(0.f);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_out_kernel(
+    const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ dt, const T* __restrict__ Bm,
+    const T* __restrict__ Cm, const float* __restrict__ A, const float* __restrict__ Dp,
+    const float* __restrict__ conv_w, const float* __restrict__ carry, T* __restrict__ y,
+    float* __restrict__ state_out, T* __restrict__ conv_state_out, int L, int Dch, int CT) {
+  const int c = blockIdx.x * kChanPerBlock + threadIdx.x;
+  const int k = blockIdx.y;
+  const int b = blockIdx.z;
+  const int batch = gridDim.z;
+  const int nchunk = gridDim.y;
+  const bool cv = c < Dch;
+  const int cc = cv ? c : Dch - 1;
+  const int64_t seq = (int64_t)b * L;
+  const int t0 = k * CT, t1 = min(t0 + CT, L);
+
+  float A2[kStates], w[kConv], h[kStates];
+  const float4* cp = reinterpret_cast<const float4*>(carry + (((int64_t)k * batch + b) * Dch + cc) * kStates);
+#pragma unroll
+  for (int q = 0; q < kStates / 4; ++q) {
+    const float4 v = cp[q];
+    h[4 * q] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
+  }
+#pragma unroll
+  for (int n = 0; n < kStates; ++n) A2[n] = A[(int64_t)cc * kStates + n] * kLog2e;
+#pragma unroll
+  for (int j = 0; j < kConv; ++j) w[j] = conv_w[(int64_t)cc * kConv + j];
+  const float Dc = Dp[cc];
+  float xm3 = t0 >= 3 ? to_f32(x[(seq + t0 - 3) * Dch + cc]) : 0.f;
+  float xm2 = t0 >= 2 ? to_f32(x[(seq + t0 - 2) * Dch + cc]) : 0.f;
+  float xm1 = t0 >= 1 ? to_f32(x[(seq + t0 - 1) * Dch + cc]) : 0.f;
+  T xn = x[(seq + t0) * Dch + cc], dn = dt[(seq + t0) * Dch + cc], zn = z[(seq + t0) * Dch + cc];
+#pragma unroll 2
+  for (int t = t0; t < t1; ++t) {
+    const float xt = to_f32(xn), d = to_f32(dn), zt = to_f32(zn);
+    const int tn = min(t + 1, t1 - 1);
+    xn = x[(seq + tn) * Dch + cc];
+    dn = dt[(seq + tn) * Dch + cc];
+    zn = z[(seq + tn) * Dch + cc];
+    const float u = fmaf(w[0], xm3, fmaf(w[1], xm2, fmaf(w[2], xm1, w[3] * xt)));
+    xm3 = xm2; xm2 = xm1; xm1 = xt;
+    const float du = d * u;
+    float Bv[kStates], Cv[kStates];
+    load_row16(Bm + (seq + t) * kStates, Bv);
+    load_row16(Cm + (seq + t) * kStates, Cv);
+    float acc = Dc * u;
+#pragma unroll
+    for (int n = 0; n < kStates; ++n) {
+      h[n] = fmaf(fast_exp2(d * A2[n]), h[n], du * Bv[n]);
+      acc = fmaf(Cv[n], h[n], acc);
+    }
+    if (cv) y[(seq + t) * Dch + c] = from_f32<T>(acc * silu(zt));
+  }
+  if (k == nchunk - 1 && cv) {
+    if (state_out) {
+      float4* sp = reinterpret_cast<float4*>(state_out + ((int64_t)b * Dch + c) * kStates);
+#pragma unroll
+      for (int q = 0; q < kStates / 4; ++q) sp[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+    }
+    if (conv_state_out) {   // raw x of rows L-3, L-2, L-1 (zero before row 0)
+      T* cs = conv_state_out + ((int64_t)b * Dch + c) * (kConv - 1);
+      cs[0] = from_f32<T>(xm3);
+      cs[1] = from_f32<T>(xm2);
+      cs[2] = from_f32<T>(xm1);
     }
   }
 }
@@ -266,31 +266,45 @@ __global__ __launch_bounds__(256) void ssm_decode_kernel(
   }
 }
 
-template <typename T, int SPL, int TC, int NW>
-hipError_t prefill_t(const SsmPrefillArgs& a, hipStream_t stream) {
-  constexpr int CPB = 64 / (kStates / SPL);
-  dim3 grid((a.d_inner + CPB - 1) / CPB, a.batch);
-  hipLaunchKernelGGL((ssm_prefill_kernel<T, SPL, TC, NW>), grid, dim3(64 * NW), 0, stream, (const T*)a.x,
-                     (const T*)a.z, (const T*)a.dt, (const T*)a.B, (const T*)a.C, a.A, a.D, a.conv_w, (T*)a.y,
-                     a.state_out, (T*)a.conv_state_out, a.L, a.d_inner);
-  return hipGetLastError();
-}
-
 template <typename T>
-hipError_t prefill_pick(const SsmPrefillArgs& a, hipStream_t stream) {
-  // Enough workgroups to cover the 256 compute units: fewer states per lane
-  // (more lanes per channel) when the batch has few channels.
-  const int64_t chans = (int64_t)a.batch * a.d_inner;
-  if (chans >= 64 * 256) return prefill_t<T, 16, 4, 8>(a, stream);
-  if (chans >= 32 * 256) return prefill_t<T, 8, 8, 8>(a, stream);
-  return prefill_t<T, 4, 8, 8>(a, stream);
+hipError_t prefill_t(const SsmPrefillArgs& a, hipStream_t stream) {
+  const int CT = a.chunk_rows;
+  const int nchunk = (a.L + CT - 1) / CT;
+  const dim3 block(kChanPerBlock);
+  const int cblocks = (a.d_inner + kChanPerBlock - 1) / kChanPerBlock;
+  if (nchunk > 1) {
+    hipLaunchKernelGGL(ssm_chunk_end_kernel<T>, dim3(cblocks, nchunk - 1, a.batch), block, 0, stream, (const T*)a.x,
+                       (const T*)a.dt, (const T*)a.B, a.A, a.conv_w, a.agg, a.sdt, a.L, a.d_inner, CT);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t per = (int64_t)a.batch * a.d_inner * kStates;
+  hipLaunchKernelGGL(ssm_chunk_carry_kernel, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, stream, a.A, a.agg,
+                     a.sdt, a.carry, nchunk, a.batch, a.d_inner);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ssm_chunk_out_kernel<T>, dim3(cblocks, nchunk, a.batch), block, 0, stream, (const T*)a.x,
+                     (const T*)a.z, (const T*)a.dt, (const T*)a.B, (const T*)a.C, a.A, a.D, a.conv_w, a.carry,
+                     (T*)a.y, a.state_out, (T*)a.conv_state_out, a.L, a.d_inner, CT);
+  return hipGetLastError();
 }
 
 }  // namespace
 
+int ssm_prefill_chunk_rows(int batch, int L, int d_inner) {
+  // enough (sequence, channel block, chunk) workgroups to fill the chip
+  // several times over, without making the carry chain long
+  const int64_t per_chunk = (int64_t)batch * ((d_inner + kChanPerBlock - 1) / kChanPerBlock);
+  const int64_t want = (2048 + per_chunk - 1) / per_chunk;   // chunks per sequence
+  int64_t ct = (L + want - 1) / want;
+  ct = (ct + 15) / 16 * 16;
+  if (ct < 16) ct = 16;
+  return (int)ct;
+}
+
 hipError_t launch_ssm_prefill(const SsmPrefillArgs& a, hipStream_t stream) {
-  if (a.act == HYMBA_BF16) return prefill_pick<bf16>(a, stream);
-  return prefill_pick<float>(a, stream);
+  if (a.act == HYMBA_BF16) return prefill_t<bf16>(a, stream);
+  return prefill_t<float>(a, stream);
 }
 
 hipError_t launch_ssm_decode(const SsmDecodeArgs& a, hipStream_t stream) {

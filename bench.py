@@ -119,9 +119,9 @@ def decode_work(cfg):
     n_vis = min(cfg.cache_len + 1, cfg.n_meta + cfg.window) if cfg.window > 0 else cfg.cache_len + 1
     ssm_bytes = B * D * N * 4 * 2 + B * D * 3 * es * 2 + B * (3 * D + 2 * N) * es + B * D * es + D * (N + 5) * 4
     attn_bytes = B * Hkv * (n_vis - 1) * (hd + dv) * es + B * (Hq * hd + Hkv * (hd + dv)) * es
-    comb_bytes = B * D * es * 2 + 2 * D * 4
+    comb_bytes = B * D * es * 3 + 2 * D * 4
     return {"ssm_decode": {"bytes": ssm_bytes}, "attn_decode": {"bytes": attn_bytes, "n_vis": n_vis},
-            "decode_combine_fuse": {"bytes": comb_bytes},
+            "decode_merge_fuse": {"bytes": comb_bytes},
             "total_bytes": ssm_bytes + attn_bytes + comb_bytes}
 
 
@@ -285,6 +285,8 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated through the timed steps")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="also run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -299,6 +301,15 @@ def main():
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
         sys.exit(1)
     H.load_library()
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes x3 for counter calibration")
+        del src, dst
     ev = HipEvents()
     cfg = synth.config("swa_layer")
     ms, stage_ms = bench_prefill(cfg, args.steps, args.warmup, args.sets, ev)

@@ -73,7 +73,8 @@ typedef enum {
  *  d_inner     Mamba channels; also the attention output width (n_q_heads * head_dim_v)
  *  d_state     SSM state size per channel: 16 (Hymba-1.5B article, section 2)
  *  d_conv      conv taps: 4
- *  n_q_heads, n_kv_heads   GQA: query head h reads kv head h / (n_q_heads / n_kv_heads)
+ *  n_q_heads, n_kv_heads   GQA: query head h reads kv head h / (n_q_heads / n_kv_heads);
+ *              this build supports groups of up to 8 query heads per kv head
  *  head_dim    query/key width: 64
  *  head_dim_v  value width: d_inner / n_q_heads, one of 32, 64, 128
  *  window      > 0: query row i sees non-meta key rows j with i - j < window;
