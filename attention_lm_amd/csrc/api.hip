@@ -3,12 +3,42 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <unordered_map>
+
 #include "../../include/hymba_mixer.h"
 #include "launch.hpp"
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Per calling thread and device: a second stream (default priority) and two
+// events, used to run the Mamba branch concurrently with the attention branch.
+// Per-thread so that calls from different host threads never share them.
+struct ForkCtx {
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  ~ForkCtx() {
+    if (fork) (void)hipEventDestroy(fork);
+    if (join) (void)hipEventDestroy(join);
+    if (aux) (void)hipStreamDestroy(aux);
+  }
+};
+thread_local std::unordered_map<int, ForkCtx> g_fork;
+
+hipError_t fork_ctx(ForkCtx** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  ForkCtx& c = g_fork[dev];
+  if (!c.aux) {
+    if ((e = hipStreamCreateWithFlags(&c.aux, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&c.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&c.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &c;
+  return hipSuccess;
+}
 
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return HYMBA_OK;
@@ -145,6 +175,16 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   auto mark = [&](int i) -> hipError_t {
     return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
   };
+  // The two branches are independent until the fusion: without stage events the
+  // Mamba branch runs on a second stream, concurrently with the attention branch.
+  ForkCtx* fc = nullptr;
+  if (!stage_events) HYMBA_TRY(fork_ctx(&fc));
+  hipStream_t ssm_stream = stream;
+  if (fc) {
+    HYMBA_TRY(hipEventRecord(fc->fork, stream));
+    HYMBA_TRY(hipStreamWaitEvent(fc->aux, fc->fork, 0));
+    ssm_stream = fc->aux;
+  }
   HYMBA_TRY(mark(0));
   hymba::SsmPrefillArgs sa;
   sa.x = x; sa.z = z; sa.dt = dt; sa.B = B; sa.C = C;
@@ -153,7 +193,8 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   sa.agg = (float*)(wsb + ws.agg); sa.sdt = (float*)(wsb + ws.sdt); sa.carry = (float*)(wsb + ws.carry);
   sa.chunk_rows = ws.chunk_rows;
   sa.batch = desc->batch; sa.L = L; sa.d_inner = desc->d_inner; sa.act = desc->act;
-  HYMBA_TRY(hymba::launch_ssm_prefill(sa, stream));
+  HYMBA_TRY(hymba::launch_ssm_prefill(sa, ssm_stream));
+  if (fc) HYMBA_TRY(hipEventRecord(fc->join, fc->aux));
   HYMBA_TRY(mark(1));
 
   hymba::RopeArgs ra;
@@ -172,6 +213,7 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   aa.act = desc->act;
   HYMBA_TRY(hymba::launch_attn_prefill(aa, stream));
   HYMBA_TRY(mark(3));
+  if (fc) HYMBA_TRY(hipStreamWaitEvent(stream, fc->join, 0));
 
   HYMBA_TRY(hymba::launch_fuse(y_attn, y_ssm, params->beta_attn, params->beta_ssm, (int64_t)desc->batch * L,
                                desc->d_inner, desc->norm_eps, desc->act, out, stream));

@@ -66,95 +66,36 @@ constexpr int kStates = 16;
 constexpr int kConv = 4;
 
 constexpr int kChanPerBlock = 128;   // one lane per channel
+constexpr int kRowBlock = 16;        // rows staged in LDS per step
 
-// 16 wave-uniform values of one row of B or C (shared by all channels)
-template <typename T>
-__device__ __forceinline__ void load_row16(const T* p, float* o) {
-  load_n<kStates>(p, o);
-}
-
-template <typename T>
-__global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_end_kernel(
-    const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm, const float* __restrict__ A,
-    const float* __restrict__ conv_w, float* __restrict__ agg, float* __restrict__ sdt, int L, int Dch, int CT) {
-  const int c = blockIdx.x * kChanPerBlock + threadIdx.x;
-  const int k = blockIdx.y;
-  const int b = blockIdx.z;
-  const int batch = gridDim.z;
-  const bool cv = c < Dch;
-  const int cc = cv ? c : Dch - 1;   // clamped channel for loads; results of invalid lanes are dropped
-  const int64_t seq = (int64_t)b * L;
-  const int t0 = k * CT, t1 = min(t0 + CT, L);
-
-  float A2[kStates], w[kConv], h[kStates];
-#pragma unroll
-  for (int n = 0; n < kStates; ++n) {
-    A2[n] = A[(int64_t)cc * kStates + n] * kLog2e;
-    h[n] = 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < kConv; ++j) w[j] = conv_w[(int64_t)cc * kConv + j];
-  float xm3 = t0 >= 3 ? to_f32(x[(seq + t0 - 3) * Dch + cc]) : 0.f;
-  float xm2 = t0 >= 2 ? to_f32(x[(seq + t0 - 2) * Dch + cc]) : 0.f;
-  float xm1 = t0 >= 1 ? to_f32(x[(seq + t0 - 1) * Dch + cc]) : 0.f;
-  float S = 0.f;
-  // next row's x and dt are loaded one iteration ahead
-  T xn = x[(seq + t0) * Dch + cc], dn = dt[(seq + t0) * Dch + cc];
-#pragma unroll 2
-  for (int t = t0; t < t1; ++t) {
-    const float xt = to_f32(xn), d = to_f32(dn);
-    const int tn = min(t + 1, t1 - 1);
-    xn = x[(seq + tn) * Dch + cc];
-    dn = dt[(seq + tn) * Dch + cc];
-    const float u = fmaf(w[0], xm3, fmaf(w[1], xm2, fmaf(w[2], xm1, w[3] * xt)));
-    xm3 = xm2; xm2 = xm1; xm1 = xt;
-    const float du = d * u;
-    float Bv[kStates];
-    load_row16(Bm + (seq + t) * kStates, Bv);
-#pragma unroll
-    for (int n = 0; n < kStates; ++n) h[n] = fmaf(fast_exp2(d * A2[n]), h[n], du * Bv[n]);
-    S += d;
-  }
-  if (!cv) return;
-  const int64_t o = (((int64_t)k * batch + b) * Dch + c);
-  float4* ap = reinterpret_cast<float4*>(agg + o * kStates);
-#pragma unroll
-  for (int q = 0; q < kStates / 4; ++q) ap[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
-  sdt[o] = S;
-}
-
-// carry[k] = state entering chunk k, from the chunk end states agg[k] (zero start)
-// and the chunk dt sums sdt[k].
-__global__ __launch_bounds__(256) void ssm_chunk_carry_kernel(const float* __restrict__ A,
-                                                              const float* __restrict__ agg,
-                                                              const float* __restrict__ sdt,
-                                                              float* __restrict__ carry, int nchunk, int batch,
-                                                              int Dch) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, c, n)
-  const int64_t per = (int64_t)batch * Dch * kStates;
-  if (idx >= per) return;
-  const int n = (int)(idx % kStates);
-  const int64_t bc = idx / kStates;
-  const int c = (int)(bc % Dch);
-  const float a2 = A[(int64_t)c * kStates + n] * kLog2e;
-  float H = 0.f;
-  carry[idx] = 0.f;
-#pragma unroll 4
-  for (int k = 0; k + 1 < nchunk; ++k) {
-    const float a = agg[k * per + idx];
-    const float s = sdt[k * (per / kStates) + bc];
-    H = fmaf(fast_exp2(a2 * s), H, a);
-    carry[(k + 1) * per + idx] = H;
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_out_kernel(
+// One pass of the chunked scan over rows [t0, t1) of 128 channels.
+//  OUT = false: start from zero, write the chunk's end state and dt sum.
+//  OUT = true:  start from the chunk's carry-in, write gated y (and, for the
+//               last chunk, the final SSM state and conv history).
+// Inputs are staged through LDS in blocks of kRowBlock rows, double-buffered:
+// the global loads of block i+1 are in flight while block i is scanned.
+template <typename T, bool OUT>
+__global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_kernel(
     const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ dt, const T* __restrict__ Bm,
     const T* __restrict__ Cm, const float* __restrict__ A, const float* __restrict__ Dp,
-    const float* __restrict__ conv_w, const float* __restrict__ carry, T* __restrict__ y,
-    float* __restrict__ state_out, T* __restrict__ conv_state_out, int L, int Dch, int CT) {
-  const int c = blockIdx.x * kChanPerBlock + threadIdx.x;
+    const float* __restrict__ conv_w, const float* __restrict__ carry, float* __restrict__ agg,
+    float* __restrict__ sdt, T* __restrict__ y, float* __restrict__ state_out, T* __restrict__ conv_state_out,
+    int L, int Dch, int CT) {
+  constexpr int E = Vec16<T>::n;                  // elements per 16-byte vector
+  constexpr int RV = kChanPerBlock / E;           // vectors per 128-channel row
+  constexpr int XR = kRowBlock + kConv - 1;       // x rows per block (with conv history)
+  constexpr int NX = (XR * RV + kChanPerBlock - 1) / kChanPerBlock;
+  constexpr int NR = (kRowBlock * RV + kChanPerBlock - 1) / kChanPerBlock;
+  constexpr int NBC = (kRowBlock * kStates / E + kChanPerBlock - 1) / kChanPerBlock;
+  __shared__ __attribute__((aligned(16))) T xs[2][XR][kChanPerBlock];
+  __shared__ __attribute__((aligned(16))) T ds[2][kRowBlock][kChanPerBlock];
+  __shared__ __attribute__((aligned(16))) T zs[OUT ? 2 : 1][OUT ? kRowBlock : 1][kChanPerBlock];
+  __shared__ __attribute__((aligned(16))) float bs[2][kRowBlock][kStates];
+  __shared__ __attribute__((aligned(16))) float cs[OUT ? 2 : 1][OUT ? kRowBlock : 1][kStates];
+
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * kChanPerBlock;
+  const int c = c0 + tid;
   const int k = blockIdx.y;
   const int b = blockIdx.z;
   const int batch = gridDim.z;
@@ -164,54 +105,197 @@ __global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_out_kernel(
   const int64_t seq = (int64_t)b * L;
   const int t0 = k * CT, t1 = min(t0 + CT, L);
 
-  float A2[kStates], w[kConv], h[kStates];
-  const float4* cp = reinterpret_cast<const float4*>(carry + (((int64_t)k * batch + b) * Dch + cc) * kStates);
+  // staging registers
+  uint4 rx[NX], rd[NR], rz[OUT ? NR : 1], rb[NBC], rc[OUT ? NBC : 1];
+  auto vec_ok = [&](int t, int v) { return t >= 0 && t < L && c0 + (v + 1) * E <= Dch; };
+  auto fetch = [&](int tb) {
 #pragma unroll
-  for (int q = 0; q < kStates / 4; ++q) {
-    const float4 v = cp[q];
-    h[4 * q] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
-  }
+    for (int r = 0; r < NX; ++r) {
+      const int it = tid + r * kChanPerBlock, row = it / RV, v = it % RV, t = tb - (kConv - 1) + row;
+      rx[r] = make_uint4(0, 0, 0, 0);
+      if (it < XR * RV && vec_ok(t, v)) rx[r] = *reinterpret_cast<const uint4*>(x + (seq + t) * Dch + c0 + v * E);
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int it = tid + r * kChanPerBlock, row = it / RV, v = it % RV, t = tb + row;
+      rd[r] = make_uint4(0, 0, 0, 0);
+      if (it < kRowBlock * RV && t < t1 && vec_ok(t, v))
+        rd[r] = *reinterpret_cast<const uint4*>(dt + (seq + t) * Dch + c0 + v * E);
+      if constexpr (OUT) {
+        rz[r] = make_uint4(0, 0, 0, 0);
+        if (it < kRowBlock * RV && t < t1 && vec_ok(t, v))
+          rz[r] = *reinterpret_cast<const uint4*>(z + (seq + t) * Dch + c0 + v * E);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NBC; ++r) {
+      const int it = tid + r * kChanPerBlock;          // 16-byte vector of the block's B (or C) rows
+      const int t = tb + (it * E) / kStates;
+      rb[r] = make_uint4(0, 0, 0, 0);
+      if (it * E < kRowBlock * kStates && t < t1) rb[r] = *reinterpret_cast<const uint4*>(Bm + seq * kStates + (int64_t)tb * kStates + it * E);
+      if constexpr (OUT) {
+        rc[r] = make_uint4(0, 0, 0, 0);
+        if (it * E < kRowBlock * kStates && t < t1) rc[r] = *reinterpret_cast<const uint4*>(Cm + seq * kStates + (int64_t)tb * kStates + it * E);
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < NX; ++r) {
+      const int it = tid + r * kChanPerBlock;
+      if (it < XR * RV) *reinterpret_cast<uint4*>(&xs[buf][it / RV][(it % RV) * E]) = rx[r];
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int it = tid + r * kChanPerBlock;
+      if (it < kRowBlock * RV) {
+        *reinterpret_cast<uint4*>(&ds[buf][it / RV][(it % RV) * E]) = rd[r];
+        if constexpr (OUT) *reinterpret_cast<uint4*>(&zs[buf][it / RV][(it % RV) * E]) = rz[r];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NBC; ++r) {
+      const int it = tid + r * kChanPerBlock;
+      if (it * E < kRowBlock * kStates) {
+        float f[E];
+        load16(reinterpret_cast<const T*>(&rb[r]), f);
+        float* dst = &bs[buf][0][0] + it * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[e] = f[e];
+        if constexpr (OUT) {
+          load16(reinterpret_cast<const T*>(&rc[r]), f);
+          float* dc = &cs[buf][0][0] + it * E;
+#pragma unroll
+          for (int e = 0; e < E; ++e) dc[e] = f[e];
+        }
+      }
+    }
+  };
+
+  float A2[kStates], w[kConv], h[kStates];
 #pragma unroll
   for (int n = 0; n < kStates; ++n) A2[n] = A[(int64_t)cc * kStates + n] * kLog2e;
 #pragma unroll
   for (int j = 0; j < kConv; ++j) w[j] = conv_w[(int64_t)cc * kConv + j];
-  const float Dc = Dp[cc];
-  float xm3 = t0 >= 3 ? to_f32(x[(seq + t0 - 3) * Dch + cc]) : 0.f;
-  float xm2 = t0 >= 2 ? to_f32(x[(seq + t0 - 2) * Dch + cc]) : 0.f;
-  float xm1 = t0 >= 1 ? to_f32(x[(seq + t0 - 1) * Dch + cc]) : 0.f;
-  T xn = x[(seq + t0) * Dch + cc], dn = dt[(seq + t0) * Dch + cc], zn = z[(seq + t0) * Dch + cc];
-#pragma unroll 2
-  for (int t = t0; t < t1; ++t) {
-    const float xt = to_f32(xn), d = to_f32(dn), zt = to_f32(zn);
-    const int tn = min(t + 1, t1 - 1);
-    xn = x[(seq + tn) * Dch + cc];
-    dn = dt[(seq + tn) * Dch + cc];
-    zn = z[(seq + tn) * Dch + cc];
-    const float u = fmaf(w[0], xm3, fmaf(w[1], xm2, fmaf(w[2], xm1, w[3] * xt)));
-    xm3 = xm2; xm2 = xm1; xm1 = xt;
-    const float du = d * u;
-    float Bv[kStates], Cv[kStates];
-    load_row16(Bm + (seq + t) * kStates, Bv);
-    load_row16(Cm + (seq + t) * kStates, Cv);
-    float acc = Dc * u;
+  float Dc = 0.f;
+  if constexpr (OUT) {
+    Dc = Dp[cc];
+    const float4* cp = reinterpret_cast<const float4*>(carry + (((int64_t)k * batch + b) * Dch + cc) * kStates);
 #pragma unroll
-    for (int n = 0; n < kStates; ++n) {
-      h[n] = fmaf(fast_exp2(d * A2[n]), h[n], du * Bv[n]);
-      acc = fmaf(Cv[n], h[n], acc);
+    for (int q = 0; q < kStates / 4; ++q) {
+      const float4 v4 = cp[q];
+      h[4 * q] = v4.x; h[4 * q + 1] = v4.y; h[4 * q + 2] = v4.z; h[4 * q + 3] = v4.w;
     }
-    if (cv) y[(seq + t) * Dch + c] = from_f32<T>(acc * silu(zt));
+  } else {
+#pragma unroll
+    for (int n = 0; n < kStates; ++n) h[n] = 0.f;
   }
-  if (k == nchunk - 1 && cv) {
+  float S = 0.f;
+  float xm3 = 0.f, xm2 = 0.f, xm1 = 0.f;
+
+  const int nblk = (t1 - t0 + kRowBlock - 1) / kRowBlock;
+  fetch(t0);
+  stash(0);
+  __syncthreads();
+  for (int ib = 0; ib < nblk; ++ib) {
+    const int buf = ib & 1;
+    const int tb = t0 + ib * kRowBlock;
+    if (ib + 1 < nblk) fetch(tb + kRowBlock);
+    xm3 = to_f32(xs[buf][0][tid]);
+    xm2 = to_f32(xs[buf][1][tid]);
+    xm1 = to_f32(xs[buf][2][tid]);
+    // staged rows at or past t1 hold dt = 0 (state unchanged) and are not stored
+#pragma unroll 4
+    for (int i = 0; i < kRowBlock; ++i) {
+      const float xt = to_f32(xs[buf][i + kConv - 1][tid]);
+      const float d = to_f32(ds[buf][i][tid]);
+      const float u = fmaf(w[0], xm3, fmaf(w[1], xm2, fmaf(w[2], xm1, w[3] * xt)));
+      if (tb + i < t1) { xm3 = xm2; xm2 = xm1; xm1 = xt; }
+      const float du = d * u;
+      float Bv[kStates];
+#pragma unroll
+      for (int q = 0; q < kStates / 4; ++q) {
+        const float4 v4 = *reinterpret_cast<const float4*>(&bs[buf][i][4 * q]);
+        Bv[4 * q] = v4.x; Bv[4 * q + 1] = v4.y; Bv[4 * q + 2] = v4.z; Bv[4 * q + 3] = v4.w;
+      }
+      if constexpr (OUT) {
+        float Cv[kStates];
+#pragma unroll
+        for (int q = 0; q < kStates / 4; ++q) {
+          const float4 v4 = *reinterpret_cast<const float4*>(&cs[buf][i][4 * q]);
+          Cv[4 * q] = v4.x; Cv[4 * q + 1] = v4.y; Cv[4 * q + 2] = v4.z; Cv[4 * q + 3] = v4.w;
+        }
+        float acc = Dc * u;
+#pragma unroll
+        for (int n = 0; n < kStates; ++n) {
+          h[n] = fmaf(fast_exp2(d * A2[n]), h[n], du * Bv[n]);
+          acc = fmaf(Cv[n], h[n], acc);
+        }
+        const float zt = to_f32(zs[buf][i][tid]);
+        if (cv && tb + i < t1) y[(seq + tb + i) * Dch + c] = from_f32<T>(acc * silu(zt));
+      } else {
+#pragma unroll
+        for (int n = 0; n < kStates; ++n) h[n] = fmaf(fast_exp2(d * A2[n]), h[n], du * Bv[n]);
+        S += d;
+      }
+    }
+    if (ib + 1 < nblk) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!cv) return;
+  if constexpr (!OUT) {
+    const int64_t o = (((int64_t)k * batch + b) * Dch + c);
+    float4* ap = reinterpret_cast<float4*>(agg + o * kStates);
+#pragma unroll
+    for (int q = 0; q < kStates / 4; ++q) ap[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+    sdt[o] = S;
+  } else if (k == nchunk - 1) {
     if (state_out) {
       float4* sp = reinterpret_cast<float4*>(state_out + ((int64_t)b * Dch + c) * kStates);
 #pragma unroll
       for (int q = 0; q < kStates / 4; ++q) sp[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
     }
     if (conv_state_out) {   // raw x of rows L-3, L-2, L-1 (zero before row 0)
-      T* cs = conv_state_out + ((int64_t)b * Dch + c) * (kConv - 1);
-      cs[0] = from_f32<T>(xm3);
-      cs[1] = from_f32<T>(xm2);
-      cs[2] = from_f32<T>(xm1);
+      T* csp = conv_state_out + ((int64_t)b * Dch + c) * (kConv - 1);
+      csp[0] = from_f32<T>(xm3);
+      csp[1] = from_f32<T>(xm2);
+      csp[2] = from_f32<T>(xm1);
+    }
+  }
+}
+
+// carry[k] = state entering chunk k, from the chunk end states agg[k] (zero start)
+// and the chunk dt sums sdt[k]; loads are issued in batches ahead of the chain.
+__global__ __launch_bounds__(256) void ssm_chunk_carry_kernel(const float* __restrict__ A,
+                                                              const float* __restrict__ agg,
+                                                              const float* __restrict__ sdt,
+                                                              float* __restrict__ carry, int nchunk, int batch,
+                                                              int Dch) {
+  constexpr int KB = 16;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, c, n)
+  const int64_t per = (int64_t)batch * Dch * kStates;
+  if (idx >= per) return;
+  const int n = (int)(idx % kStates);
+  const int64_t bc = idx / kStates;
+  const int c = (int)(bc % Dch);
+  const float a2 = A[(int64_t)c * kStates + n] * kLog2e;
+  float H = 0.f;
+  carry[idx] = 0.f;
+  for (int k0 = 0; k0 + 1 < nchunk; k0 += KB) {
+    float av[KB], sv[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int kk = min(k0 + i, nchunk - 2);
+      av[i] = agg[kk * per + idx];
+      sv[i] = sdt[kk * (per / kStates) + bc];
+    }
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      if (k0 + i + 1 < nchunk) {
+        H = fmaf(fast_exp2(a2 * sv[i]), H, av[i]);
+        carry[(k0 + i + 1) * per + idx] = H;
+      }
     }
   }
 }
@@ -273,8 +357,10 @@ hipError_t prefill_t(const SsmPrefillArgs& a, hipStream_t stream) {
   const dim3 block(kChanPerBlock);
   const int cblocks = (a.d_inner + kChanPerBlock - 1) / kChanPerBlock;
   if (nchunk > 1) {
-    hipLaunchKernelGGL(ssm_chunk_end_kernel<T>, dim3(cblocks, nchunk - 1, a.batch), block, 0, stream, (const T*)a.x,
-                       (const T*)a.dt, (const T*)a.B, a.A, a.conv_w, a.agg, a.sdt, a.L, a.d_inner, CT);
+    hipLaunchKernelGGL((ssm_chunk_kernel<T, false>), dim3(cblocks, nchunk - 1, a.batch), block, 0, stream,
+                       (const T*)a.x, (const T*)a.z, (const T*)a.dt, (const T*)a.B, (const T*)a.C, a.A, a.D,
+                       a.conv_w, (const float*)nullptr, a.agg, a.sdt, (T*)nullptr, (float*)nullptr, (T*)nullptr,
+                       a.L, a.d_inner, CT);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -283,9 +369,11 @@ hipError_t prefill_t(const SsmPrefillArgs& a, hipStream_t stream) {
                      a.sdt, a.carry, nchunk, a.batch, a.d_inner);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ssm_chunk_out_kernel<T>, dim3(cblocks, nchunk, a.batch), block, 0, stream, (const T*)a.x,
+  // the output pass covers every chunk (the grid's y extent is nchunk)
+  hipLaunchKernelGGL((ssm_chunk_kernel<T, true>), dim3(cblocks, nchunk, a.batch), block, 0, stream, (const T*)a.x,
                      (const T*)a.z, (const T*)a.dt, (const T*)a.B, (const T*)a.C, a.A, a.D, a.conv_w, a.carry,
-                     (T*)a.y, a.state_out, (T*)a.conv_state_out, a.L, a.d_inner, CT);
+                     (float*)nullptr, (float*)nullptr, (T*)a.y, a.state_out, (T*)a.conv_state_out, a.L, a.d_inner,
+                     CT);
   return hipGetLastError();
 }
 

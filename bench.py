@@ -184,22 +184,30 @@ def bench_prefill(cfg, steps, warmup, n_sets, ev):
         r.o["ssm_state_out"] = torch.empty((cfg.batch, cfg.d_inner, cfg.d_state), dtype=torch.float32, device="cuda")
         r.o["conv_state_out"] = torch.empty((cfg.batch, cfg.d_inner, cfg.d_conv - 1), dtype=r.out.dtype, device="cuda")
     nst = len(H._lib.PREFILL_STAGES)
-    evs = [ev.array(nst + 1) for _ in range(steps)]
+
+    def step(r, events=None):
+        t = r.t
+        H.hymba_mixer_prefill(r.desc, r.params, t["x"], t["z"], t["dt"], t["B"], t["C"], t["q"], t["k"], t["v"],
+                              r.out, workspace=r.ws, stage_events=events, **r.o)
+
     log(f"[bench] prefill warmup {warmup}")
     for i in range(warmup):
-        runs[i % n_sets]()
+        step(runs[i % n_sets])
     torch.cuda.synchronize()
     log(f"[bench] prefill timed {steps} steps")
     t0 = time.perf_counter()
     for i in range(steps):
-        r = runs[i % n_sets]
-        t = r.t
-        H.hymba_mixer_prefill(r.desc, r.params, t["x"], t["z"], t["dt"], t["B"], t["C"], t["q"], t["k"], t["v"],
-                              r.out, workspace=r.ws, stage_events=evs[i], **r.o)
+        step(runs[i % n_sets])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # per-kernel durations: the same steps with stage events (stages serialized)
+    evs = [ev.array(nst + 1) for _ in range(steps)]
+    for i in range(steps):
+        step(runs[i % n_sets], evs[i])
+    torch.cuda.synchronize()
     stage_ms = {name: sum(ev.ms(e[j], e[j + 1]) for e in evs) / steps for j, name in enumerate(H._lib.PREFILL_STAGES)}
-    return wall / steps * 1e3, stage_ms
+    serial_ms = sum(ev.ms(e[0], e[nst]) for e in evs) / steps
+    return wall / steps * 1e3, stage_ms, serial_ms
 
 
 def bench_decode(cfg, steps, warmup, n_sets, ev):
@@ -312,7 +320,7 @@ def main():
         del src, dst
     ev = HipEvents()
     cfg = synth.config("swa_layer")
-    ms, stage_ms = bench_prefill(cfg, args.steps, args.warmup, args.sets, ev)
+    ms, stage_ms, serial_ms = bench_prefill(cfg, args.steps, args.warmup, args.sets, ev)
     work = prefill_work(cfg)
     kernels = {k: kernel_report(k, stage_ms[k], work[k], cfg.act) for k in stage_ms}
     dom = max(stage_ms, key=stage_ms.get)
@@ -347,6 +355,7 @@ def main():
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "head_dim_v": cfg.head_dim_v,
                    "window": cfg.window, "input_sets": args.sets},
         "rows_per_s_incl_meta": round(cfg.batch * cfg.seq_rows / (ms * 1e-3), 1),
+        "serial_ms_per_step": round(serial_ms, 4),
         "roofline": roofline,
         "kernels": kernels,
     }

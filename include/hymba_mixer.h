@@ -135,7 +135,11 @@ size_t hymba_mixer_decode_workspace_bytes(const hymba_mixer_desc* desc);
  *  stage_events    NULL, or HYMBA_PREFILL_STAGES + 1 caller-created events:
  *                  event i is recorded on `stream` before stage i, the last one
  *                  after the final stage (stages: conv+scan, rotary, attention,
- *                  fusion). For per-kernel timing; the caller owns the events. */
+ *                  fusion). For per-kernel timing; the caller owns the events.
+ * Without stage events the Mamba branch (conv + scan) runs on a second stream
+ * of the calling thread, concurrently with the attention branch; both join on
+ * `stream` before the fusion, so ordering on `stream` is as if serial. With
+ * stage events every stage runs on `stream`, one after the other.            */
 int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
                         const void* x, const void* z, const void* dt, const void* B, const void* C,
                         const void* q, const void* k, const void* v,
