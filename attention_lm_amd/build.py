@@ -27,6 +27,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # never form packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the softmax rescale and the epilogue
+    # work on them with VALU instructions, which cannot read AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

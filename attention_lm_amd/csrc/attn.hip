@@ -196,48 +196,66 @@ struct TileStage<bf16, DV, NT> {
   static constexpr int VMAX = (VITEMS + NT - 1) / NT;
   uint4 kreg[KMAX];
   uint4 vreg[VMAX][4];
+  // per-thread constants: K item rows and global/LDS offsets, V item first keys and offsets
+  int krow[KMAX];
+  int64_t kgoff[KMAX];
+  int kloff[KMAX];
+  int vkey[VMAX];
+  int64_t vgoff[VMAX];
+  int vloff[VMAX];
+  int64_t kstride_, vstride_;
   // item it: slot group sg = it & 15 (4 slots 4sg..4sg+3 of the 64-key stage),
   // dv chunk dc = it >> 4. Slots are kperm-ordered inside each 16-key chunk, so
   // the 4 keys of a slot group are consecutive keys.
   static __device__ __forceinline__ int first_key(int sg) { return (sg & ~3) * 4 + kperm((sg & 3) * 4); }
-  __device__ __forceinline__ void fetch(const bf16* kbase, const bf16* vbase, int64_t kstride, int64_t vstride,
-                                        int j0, int L, int tid) {
+  template <int KP, int VP>
+  __device__ __forceinline__ void init(int tid, int64_t kstride, int64_t vstride) {
+    kstride_ = kstride;
+    vstride_ = vstride;
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
       const int it = tid + r * NT;
-      kreg[r] = make_uint4(0, 0, 0, 0);
-      if (it < BK * KCH) {
-        const int j = j0 + it / KCH;
-        if (j < L) kreg[r] = *reinterpret_cast<const uint4*>(kbase + (int64_t)j * kstride + (it % KCH) * 8);
-      }
+      krow[r] = it < BK * KCH ? it / KCH : BK;            // BK = no item
+      kgoff[r] = (int64_t)krow[r] * kstride + (it % KCH) * 8;
+      kloff[r] = krow[r] * KP + (it % KCH) * 8;
     }
 #pragma unroll
     for (int r = 0; r < VMAX; ++r) {
       const int it = tid + r * NT;
-      if (it < VITEMS) {
-        const int sg = it & 15, dc = it >> 4;
-        const int k0 = j0 + first_key(sg);
+      const int sg = it & 15, dc = it >> 4;
+      vkey[r] = it < VITEMS ? first_key(sg) : BK;
+      vgoff[r] = (int64_t)vkey[r] * vstride + 8 * dc;
+      vloff[r] = (8 * dc) * VP + 4 * sg;
+    }
+  }
+  __device__ __forceinline__ void fetch(const bf16* kbase, const bf16* vbase, int j0, int L) {
+    const int lim = L - j0;                            // rows < lim exist
+    const bf16* kb = kbase + (int64_t)j0 * kstride_;
+    const bf16* vb = vbase + (int64_t)j0 * vstride_;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vreg[r][e] = make_uint4(0, 0, 0, 0);
-          if (k0 + e < L) vreg[r][e] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(k0 + e) * vstride + 8 * dc);
-        }
+    for (int r = 0; r < KMAX; ++r) {
+      kreg[r] = make_uint4(0, 0, 0, 0);
+      if (krow[r] < lim) kreg[r] = *reinterpret_cast<const uint4*>(kb + kgoff[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < VMAX; ++r) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vreg[r][e] = make_uint4(0, 0, 0, 0);
+        if (vkey[r] + e < lim) vreg[r][e] = *reinterpret_cast<const uint4*>(vb + vgoff[r] + e * vstride_);
       }
     }
   }
   template <int KP, int VP>
-  __device__ __forceinline__ void stash(bf16 (*Ks)[KP], bf16 (*Vt)[VP], int tid) {
+  __device__ __forceinline__ void stash(bf16 (*Ks)[KP], bf16 (*Vt)[VP]) {
 #pragma unroll
-    for (int r = 0; r < KMAX; ++r) {
-      const int it = tid + r * NT;
-      if (it < BK * KCH) *reinterpret_cast<uint4*>(&Ks[it / KCH][(it % KCH) * 8]) = kreg[r];
-    }
+    for (int r = 0; r < KMAX; ++r)
+      if (krow[r] < BK) *reinterpret_cast<uint4*>(&Ks[0][0] + kloff[r]) = kreg[r];
 #pragma unroll
     for (int r = 0; r < VMAX; ++r) {
-      const int it = tid + r * NT;
-      if (it < VITEMS) {
-        const int sg = it & 15, dc = it >> 4;
+      if (vkey[r] < BK) {
         const uint32_t* w = reinterpret_cast<const uint32_t*>(vreg[r]);   // w[4e + q]: key e, dv 2q, 2q+1
+        bf16* dst = &Vt[0][0] + vloff[r];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           // dv 8dc + t of keys e = 0..3: low half (t even) or high half (t odd) of word t/2
@@ -245,7 +263,7 @@ struct TileStage<bf16, DV, NT> {
           uint2 o;
           o.x = __builtin_amdgcn_perm(w[4 * 1 + t / 2], w[4 * 0 + t / 2], sel);
           o.y = __builtin_amdgcn_perm(w[4 * 3 + t / 2], w[4 * 2 + t / 2], sel);
-          *reinterpret_cast<uint2*>(&Vt[8 * dc + t][4 * sg]) = o;
+          *reinterpret_cast<uint2*>(dst + t * VP) = o;
         }
       }
     }
@@ -260,27 +278,34 @@ struct TileStage<float, DV, NT> {
   static constexpr int VMAX = (NQ * NC + NT - 1) / NT;
   float4 kreg[KMAX];
   float vreg[VMAX][4][8];
-  __device__ __forceinline__ void fetch(const float* kbase, const float* vbase, int64_t kstride, int64_t vstride,
-                                        int j0, int L, int tid) {
+  int tid_;
+  int64_t kstride_, vstride_;
+  template <int KP, int VP>
+  __device__ __forceinline__ void init(int tid, int64_t kstride, int64_t vstride) {
+    tid_ = tid;
+    kstride_ = kstride;
+    vstride_ = vstride;
+  }
+  __device__ __forceinline__ void fetch(const float* kbase, const float* vbase, int j0, int L) {
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
-      const int it = tid + r * NT;
+      const int it = tid_ + r * NT;
       kreg[r] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (it < BK * KCH) {
         const int j = j0 + it / KCH;
-        if (j < L) kreg[r] = *reinterpret_cast<const float4*>(kbase + (int64_t)j * kstride + (it % KCH) * 4);
+        if (j < L) kreg[r] = *reinterpret_cast<const float4*>(kbase + (int64_t)j * kstride_ + (it % KCH) * 4);
       }
     }
 #pragma unroll
     for (int r = 0; r < VMAX; ++r) {
-      const int it = tid + r * NT;
+      const int it = tid_ + r * NT;
       if (it < NQ * NC) {
         const int kq = it % NQ, dc = it / NQ;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = j0 + 4 * kq + e;
           if (key < L) {
-            load8(vbase + (int64_t)key * vstride + 8 * dc, vreg[r][e]);
+            load8(vbase + (int64_t)key * vstride_ + 8 * dc, vreg[r][e]);
           } else {
 #pragma unroll
             for (int t = 0; t < 8; ++t) vreg[r][e][t] = 0.f;
@@ -290,15 +315,15 @@ struct TileStage<float, DV, NT> {
     }
   }
   template <int KP, int VP>
-  __device__ __forceinline__ void stash(float (*Ks)[KP], float (*Vt)[VP], int tid) {
+  __device__ __forceinline__ void stash(float (*Ks)[KP], float (*Vt)[VP]) {
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
-      const int it = tid + r * NT;
+      const int it = tid_ + r * NT;
       if (it < BK * KCH) *reinterpret_cast<float4*>(&Ks[it / KCH][(it % KCH) * 4]) = kreg[r];
     }
 #pragma unroll
     for (int r = 0; r < VMAX; ++r) {
-      const int it = tid + r * NT;
+      const int it = tid_ + r * NT;
       if (it < NQ * NC) {
         const int kq = it % NQ, dc = it / NQ;
         const int kk0 = 4 * kq;
@@ -382,17 +407,18 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   const T* vbase = v + (b * v_rows) * Hkv * DV + g * DV;
   const int64_t kstride = (int64_t)Hkv * kHd, vstride = (int64_t)Hkv * DV;
   TileStage<T, DV, NT> stage;
+  stage.template init<KP, VP>(tid, kstride, vstride);
   auto tile_j0 = [&](int idx) { return (idx < n1 ? idx : k2s + (idx - n1)) * BK; };
 
   if (ntiles > 0) {
-    stage.fetch(kbase, vbase, kstride, vstride, tile_j0(0), L, tid);
-    stage.template stash<KP, VP>(Ks[0], Vt[0], tid);
+    stage.fetch(kbase, vbase, tile_j0(0), L);
+    stage.template stash<KP, VP>(Ks[0], Vt[0]);
   }
   __syncthreads();
 
   for (int idx = 0; idx < ntiles; ++idx) {
     const int buf = idx & 1;
-    if (idx + 1 < ntiles) stage.fetch(kbase, vbase, kstride, vstride, tile_j0(idx + 1), L, tid);
+    if (idx + 1 < ntiles) stage.fetch(kbase, vbase, tile_j0(idx + 1), L);
     const int jt = tile_j0(idx);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -417,12 +443,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
           s[r] = vis ? s[r] : -INFINITY;
         }
       }
-      float mt = s[0];
+      // This lane's max; the column's reference m_run is shared by lanes l and
+      // l+32. Only when some lane exceeds it by more than the slack do the two
+      // halves exchange maxima and rescale (rare after the first tile).
+      float lm = s[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * kScaleLog2e;
-      const bool need = mt > m_run + kRescaleSlack;
-      if (__any(need)) {
+      for (int r = 1; r < 16; ++r) lm = fmaxf(lm, s[r]);
+      lm *= kScaleLog2e;
+      if (__any(lm > m_run + kRescaleSlack)) {
+        const float mt = fmaxf(lm, __shfl_xor(lm, 32, 64));
+        const bool need = mt > m_run + kRescaleSlack;        // same in both halves of a column
         const float m_new = need ? mt : m_run;
         const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;   // 0 when m_run = -inf
         m_run = m_new;
@@ -449,7 +479,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
         acc[d] = M::mma(va1, pf1, acc[d]);
       }
     }
-    if (idx + 1 < ntiles) stage.template stash<KP, VP>(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+    if (idx + 1 < ntiles) stage.template stash<KP, VP>(Ks[buf ^ 1], Vt[buf ^ 1]);
     __syncthreads();
   }
 
