@@ -75,6 +75,11 @@ int check_desc(const hymba_mixer_desc* d, bool decode) {
   if (d->head_dim_v != 32 && d->head_dim_v != 64 && d->head_dim_v != 128) return HYMBA_EUNSUPPORTED;
   if (d->n_q_heads / d->n_kv_heads > 8) return HYMBA_EUNSUPPORTED;
   if (d->d_inner % 8 != 0) return HYMBA_EUNSUPPORTED;
+  // prefill attention addresses one sequence's K and V rows of one kv head
+  // with 32-bit byte offsets
+  const int64_t row_bytes = (int64_t)d->n_kv_heads * (d->head_dim > d->head_dim_v ? d->head_dim : d->head_dim_v) *
+                            (int64_t)act_bytes(d->act);
+  if (!decode && ((int64_t)d->n_meta + d->n_tokens) * row_bytes > INT32_MAX) return HYMBA_EUNSUPPORTED;
   return HYMBA_OK;
 }
 

@@ -45,7 +45,9 @@ __device__ __forceinline__ void rope_cs(int pos, int i, float base, float* c, fl
 
 // ---------------------------------------------------------------------------
 // RoPE prologue (prefill): q -> q_rot, k -> k_rot (e.g. straight into the KV
-// cache), optionally v -> v_copy. Rotate-half pairs (i, i+32).
+// cache), optionally v -> v_copy. Rotate-half pairs (i, i+32). The rotated
+// queries are also scaled by log2(e)/sqrt(64), so that q.k comes out as the
+// softmax exponent in base 2.
 
 constexpr int kRopeRows = 8;
 
@@ -53,7 +55,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void rope_prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ q_rot,
     T* __restrict__ k_rot, T* __restrict__ v_copy, int64_t k_rows, int64_t v_rows, int L, int Hq, int Hkv,
-    int dv, float base) {
+    int dv, float base, float q_scale) {
   __shared__ float cs[kRopeRows][kHd / 2];
   __shared__ float sn[kRopeRows][kHd / 2];
   const int r0 = blockIdx.x * kRopeRows;
@@ -75,12 +77,15 @@ __global__ __launch_bounds__(256) void rope_prefill_kernel(
     const int row = r0 + r;
     const T* src;
     T* dst;
+    float sc;
     if (hd < Hq) {
       src = q + ((b * L + row) * Hq + hd) * kHd;
       dst = q_rot + ((b * L + row) * Hq + hd) * kHd;
+      sc = q_scale;
     } else {
       src = k + ((b * L + row) * Hkv + (hd - Hq)) * kHd;
       dst = k_rot + ((b * k_rows + row) * Hkv + (hd - Hq)) * kHd;
+      sc = 1.f;
     }
     float lo[8], hi[8], olo[8], ohi[8];
     load8(src + 8 * g8, lo);
@@ -88,8 +93,8 @@ __global__ __launch_bounds__(256) void rope_prefill_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float c = cs[r][8 * g8 + e], s = sn[r][8 * g8 + e];
-      olo[e] = lo[e] * c - hi[e] * s;
-      ohi[e] = hi[e] * c + lo[e] * s;
+      olo[e] = (lo[e] * c - hi[e] * s) * sc;
+      ohi[e] = (hi[e] * c + lo[e] * s) * sc;
     }
     store8(dst + 8 * g8, olo);
     store8(dst + 32 + 8 * g8, ohi);
@@ -118,9 +123,15 @@ __global__ __launch_bounds__(256) void rope_prefill_kernel(
 // l+32) and the exp'd scores, converted in registers, are directly the B
 // operand of O^T = V^T P^T: no LDS round trip for P. V is stored transposed in
 // LDS with keys permuted inside each 16-key chunk to match that operand.
-// The online softmax keeps a reference max per column and rescales the
-// accumulators only when a new score exceeds it by more than 2^8 (exact: the
-// numerator and denominator use the same reference).
+//
+// Scores come out of the MFMA already in log2 units and already shifted by the
+// column's reference max: Q is pre-scaled by log2(e)/sqrt(64) in the RoPE
+// prologue and the score accumulator starts at -m. Each score then costs one
+// exp2. The reference moves (and the running sums are rescaled) only when a
+// score exceeds it by more than 2^8; numerator and denominator always share
+// it, so the result is exact up to rounding. Both sub-tiles' score products are
+// issued before the first softmax so that the exp work of one overlaps the
+// matrix work of the other.
 
 constexpr int BK = 64;                     // keys per LDS stage (two 32-key sub-tiles)
 constexpr int kAttnWaves = 4;
@@ -134,16 +145,28 @@ template <typename T> struct AttnTile {
 // slot s of a 16-key chunk holds key kperm(s); an involution
 __device__ __forceinline__ int kperm(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
 
+// Raw buffer loads (gfx9 descriptor: 32-bit data format, no stride or swizzle).
+// A 16-byte load whose byte offset is at or past the descriptor's size reads
+// zeros and touches no memory.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
 template <typename T>
 struct Mma;
 template <>
 struct Mma<bf16> {
   typedef bf16x8_t Frag;   // 8 bf16 per lane
-  static __device__ __forceinline__ Frag lds_frag(const bf16* p) {
-    return __builtin_bit_cast(Frag, *reinterpret_cast<const uint4*>(p));
+  static __device__ __forceinline__ Frag frag_at(const bf16* p) {
+    return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4_t*>(p));
   }
+  static __device__ __forceinline__ Frag zero() { return __builtin_bit_cast(Frag, u32x4_t{0u, 0u, 0u, 0u}); }
   static __device__ __forceinline__ Frag from_f32(const float* v) {
-    uint4 u;
+    u32x4_t u;
     u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
     u.z = pack_bf16x2(v[4], v[5]); u.w = pack_bf16x2(v[6], v[7]);
     return __builtin_bit_cast(Frag, u);
@@ -156,12 +179,18 @@ struct F32x8 { float v[8]; };
 template <>
 struct Mma<float> {
   typedef F32x8 Frag;      // 8 fp32 per lane; slot t of lane half h is k = 8h + t
-  static __device__ __forceinline__ Frag lds_frag(const float* p) {
+  static __device__ __forceinline__ Frag frag_at(const float* p) {
     Frag f;
     float4 a = *reinterpret_cast<const float4*>(p);
     float4 b = *reinterpret_cast<const float4*>(p + 4);
     f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
     f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+  }
+  static __device__ __forceinline__ Frag zero() {
+    Frag f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f.v[t] = 0.f;
     return f;
   }
   static __device__ __forceinline__ Frag from_f32(const float* v) {
@@ -185,64 +214,62 @@ struct Mma<float> {
 //    groups are the fastest index, so the 16 lanes of an 8-byte LDS write phase
 //    cover all 32 banks of one row.
 //  V (fp32): item = (4-key quad, dv chunk), quads fastest.
+// Rows at or past L are staged as zeros; their keys are masked out of every
+// score.
 template <typename T, int DV, int NT>
 struct TileStage;
 
 template <int DV, int NT>
 struct TileStage<bf16, DV, NT> {
   static constexpr int KCH = kHd / 8;                        // 16-byte chunks per K row
-  static constexpr int KMAX = (BK * KCH + NT - 1) / NT;
+  static constexpr int KITEMS = BK * KCH;
+  static constexpr int KMAX = (KITEMS + NT - 1) / NT;
   static constexpr int VITEMS = (BK / 4) * (DV / 8);         // (4-key group, 8-wide dv chunk)
   static constexpr int VMAX = (VITEMS + NT - 1) / NT;
-  uint4 kreg[KMAX];
-  uint4 vreg[VMAX][4];
-  // per-thread constants: K item rows and global/LDS offsets, V item first keys and offsets
-  int krow[KMAX];
-  int64_t kgoff[KMAX];
-  int kloff[KMAX];
-  int vkey[VMAX];
-  int64_t vgoff[VMAX];
-  int vloff[VMAX];
-  int64_t kstride_, vstride_;
+  u32x4_t kreg[KMAX];
+  u32x4_t vreg[VMAX][4];
+  // per-thread constants: byte offset of the item in a tile that starts at
+  // row 0, and its LDS element offset (-1: no item)
+  uint32_t koff[KMAX], voff[VMAX];
+  int kloff[KMAX], vloff[VMAX];
+  uint32_t kstride_b, vstride_b;
+  __amdgpu_buffer_rsrc_t krs, vrs;
   // item it: slot group sg = it & 15 (4 slots 4sg..4sg+3 of the 64-key stage),
   // dv chunk dc = it >> 4. Slots are kperm-ordered inside each 16-key chunk, so
   // the 4 keys of a slot group are consecutive keys.
   static __device__ __forceinline__ int first_key(int sg) { return (sg & ~3) * 4 + kperm((sg & 3) * 4); }
   template <int KP, int VP>
-  __device__ __forceinline__ void init(int tid, int64_t kstride, int64_t vstride) {
-    kstride_ = kstride;
-    vstride_ = vstride;
+  __device__ __forceinline__ void init(int tid, const bf16* kbase, const bf16* vbase, int64_t kstride,
+                                       int64_t vstride, int L) {
+    kstride_b = (uint32_t)(kstride * 2);
+    vstride_b = (uint32_t)(vstride * 2);
+    krs = make_rsrc(kbase, (uint32_t)(((int64_t)(L - 1) * kstride + kHd) * 2));
+    vrs = make_rsrc(vbase, (uint32_t)(((int64_t)(L - 1) * vstride + DV) * 2));
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
       const int it = tid + r * NT;
-      krow[r] = it < BK * KCH ? it / KCH : BK;            // BK = no item
-      kgoff[r] = (int64_t)krow[r] * kstride + (it % KCH) * 8;
-      kloff[r] = krow[r] * KP + (it % KCH) * 8;
+      const int row = it / KCH, c = (it % KCH) * 8;
+      koff[r] = (uint32_t)row * kstride_b + 2u * c;
+      kloff[r] = it < KITEMS ? row * KP + c : -1;
     }
 #pragma unroll
     for (int r = 0; r < VMAX; ++r) {
       const int it = tid + r * NT;
       const int sg = it & 15, dc = it >> 4;
-      vkey[r] = it < VITEMS ? first_key(sg) : BK;
-      vgoff[r] = (int64_t)vkey[r] * vstride + 8 * dc;
-      vloff[r] = (8 * dc) * VP + 4 * sg;
+      voff[r] = (uint32_t)first_key(sg) * vstride_b + 16u * dc;
+      vloff[r] = it < VITEMS ? (8 * dc) * VP + 4 * sg : -1;
     }
   }
-  __device__ __forceinline__ void fetch(const bf16* kbase, const bf16* vbase, int j0, int L) {
-    const int lim = L - j0;                            // rows < lim exist
-    const bf16* kb = kbase + (int64_t)j0 * kstride_;
-    const bf16* vb = vbase + (int64_t)j0 * vstride_;
+  __device__ __forceinline__ void fetch(int j0) {
+    const uint32_t kt = (uint32_t)j0 * kstride_b, vt = (uint32_t)j0 * vstride_b;
 #pragma unroll
-    for (int r = 0; r < KMAX; ++r) {
-      kreg[r] = make_uint4(0, 0, 0, 0);
-      if (krow[r] < lim) kreg[r] = *reinterpret_cast<const uint4*>(kb + kgoff[r]);
-    }
+    for (int r = 0; r < KMAX; ++r)
+      if (KITEMS % NT == 0 || kloff[r] >= 0) kreg[r] = buf_load16(krs, koff[r] + kt);
 #pragma unroll
     for (int r = 0; r < VMAX; ++r) {
+      if (VITEMS % NT == 0 || vloff[r] >= 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vreg[r][e] = make_uint4(0, 0, 0, 0);
-        if (vkey[r] + e < lim) vreg[r][e] = *reinterpret_cast<const uint4*>(vb + vgoff[r] + e * vstride_);
+        for (int e = 0; e < 4; ++e) vreg[r][e] = buf_load16(vrs, voff[r] + vt + e * vstride_b);
       }
     }
   }
@@ -250,19 +277,19 @@ struct TileStage<bf16, DV, NT> {
   __device__ __forceinline__ void stash(bf16 (*Ks)[KP], bf16 (*Vt)[VP]) {
 #pragma unroll
     for (int r = 0; r < KMAX; ++r)
-      if (krow[r] < BK) *reinterpret_cast<uint4*>(&Ks[0][0] + kloff[r]) = kreg[r];
+      if (KITEMS % NT == 0 || kloff[r] >= 0) *reinterpret_cast<u32x4_t*>(&Ks[0][0] + kloff[r]) = kreg[r];
 #pragma unroll
     for (int r = 0; r < VMAX; ++r) {
-      if (vkey[r] < BK) {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(vreg[r]);   // w[4e + q]: key e, dv 2q, 2q+1
+      if (VITEMS % NT == 0 || vloff[r] >= 0) {
+        const u32x4_t* w = vreg[r];   // w[e][q]: key e, dv 2q, 2q+1
         bf16* dst = &Vt[0][0] + vloff[r];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           // dv 8dc + t of keys e = 0..3: low half (t even) or high half (t odd) of word t/2
           const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
           uint2 o;
-          o.x = __builtin_amdgcn_perm(w[4 * 1 + t / 2], w[4 * 0 + t / 2], sel);
-          o.y = __builtin_amdgcn_perm(w[4 * 3 + t / 2], w[4 * 2 + t / 2], sel);
+          o.x = __builtin_amdgcn_perm(w[1][t / 2], w[0][t / 2], sel);
+          o.y = __builtin_amdgcn_perm(w[3][t / 2], w[2][t / 2], sel);
           *reinterpret_cast<uint2*>(dst + t * VP) = o;
         }
       }
@@ -278,22 +305,27 @@ struct TileStage<float, DV, NT> {
   static constexpr int VMAX = (NQ * NC + NT - 1) / NT;
   float4 kreg[KMAX];
   float vreg[VMAX][4][8];
-  int tid_;
+  int tid_, L_;
+  const float *kbase_, *vbase_;
   int64_t kstride_, vstride_;
   template <int KP, int VP>
-  __device__ __forceinline__ void init(int tid, int64_t kstride, int64_t vstride) {
+  __device__ __forceinline__ void init(int tid, const float* kbase, const float* vbase, int64_t kstride,
+                                       int64_t vstride, int L) {
     tid_ = tid;
+    L_ = L;
+    kbase_ = kbase;
+    vbase_ = vbase;
     kstride_ = kstride;
     vstride_ = vstride;
   }
-  __device__ __forceinline__ void fetch(const float* kbase, const float* vbase, int j0, int L) {
+  __device__ __forceinline__ void fetch(int j0) {
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
       const int it = tid_ + r * NT;
       kreg[r] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (it < BK * KCH) {
         const int j = j0 + it / KCH;
-        if (j < L) kreg[r] = *reinterpret_cast<const float4*>(kbase + (int64_t)j * kstride_ + (it % KCH) * 4);
+        if (j < L_) kreg[r] = *reinterpret_cast<const float4*>(kbase_ + (int64_t)j * kstride_ + (it % KCH) * 4);
       }
     }
 #pragma unroll
@@ -304,8 +336,8 @@ struct TileStage<float, DV, NT> {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = j0 + 4 * kq + e;
-          if (key < L) {
-            load8(vbase + (int64_t)key * vstride_ + 8 * dc, vreg[r][e]);
+          if (key < L_) {
+            load8(vbase_ + (int64_t)key * vstride_ + 8 * dc, vreg[r][e]);
           } else {
 #pragma unroll
             for (int t = 0; t < 8; ++t) vreg[r][e][t] = 0.f;
@@ -337,6 +369,89 @@ struct TileStage<float, DV, NT> {
   }
 };
 
+// Per-lane state of the online softmax of one query column (shared by lanes l
+// and l+32, which hold 16 keys each of every 32-key sub-tile).
+template <int NDB>
+struct SoftmaxState {
+  f32x16_t acc[NDB];   // O^T block d: this lane's column, dv 32d + 8(r/4) + 4hh + r%4
+  f32x16_t negm;       // every entry -mref: the initial score accumulator
+  float mref;          // reference max (log2 units) subtracted from the scores
+  float thr;           // rescale when a shifted score exceeds this (-inf until a score was seen)
+  float l;             // this lane's part of the sum of 2^(s - mref)
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = 0.f;
+    mref = 0.f;
+    thr = -INFINITY;
+    l = 0.f;
+  }
+  // A shifted score of this column (t: this lane's max) passed the threshold:
+  // agree on the column max with the partner lane, move the reference to it and
+  // rescale the sums. s (and s_next, scored against the same reference) are
+  // re-shifted.
+  __device__ __forceinline__ void rescale(float t, f32x16_t& s, f32x16_t* s_next) {
+    const float mt = fmaxf(t, __shfl_xor(t, 32, 64));
+    const bool need = mt > thr;                 // the same in both lanes of the column
+    const float delta = need ? mt : 0.f;
+    // nothing has been accumulated before the first reference: scale by 0
+    const float alpha = need ? (thr == -INFINITY ? 0.f : fast_exp2(-delta)) : 1.f;
+    if (need) thr = kRescaleSlack;
+    mref += delta;
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      negm[r] -= delta;
+      s[r] -= delta;
+    }
+    if (s_next) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) (*s_next)[r] -= delta;
+    }
+  }
+};
+
+// Visible keys of this lane's query, as intervals: meta keys [0, meta_hi) and
+// window keys [win_lo, win_hi) (both empty for a column without a query).
+struct LaneKeys {
+  int meta_hi, win_lo, win_hi;
+};
+
+// s[r] (key j0 + 4hh + 8(r/4) + r%4) := -inf where the key is not visible.
+// A sub-tile entirely below n_meta or entirely at or above it needs one
+// interval test per score; one that straddles n_meta (n_meta not a multiple
+// of 32) tests both.
+__device__ __forceinline__ void mask_scores(f32x16_t& s, const LaneKeys& lk, int j0, int hh, int n_meta) {
+  const int base = j0 + 4 * hh;
+  if (j0 + 32 <= n_meta || j0 >= n_meta) {
+    const bool meta = j0 < n_meta;
+    const int lo = meta ? 0 : lk.win_lo, hi = meta ? lk.meta_hi : lk.win_hi;
+    const int rel = base - lo;
+    const uint32_t len = (uint32_t)max(hi - lo, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t u = (uint32_t)(rel + 8 * (r >> 2) + (r & 3));
+      s[r] = u < len ? s[r] : -INFINITY;
+    }
+  } else {
+    const uint32_t wlen = (uint32_t)max(lk.win_hi - lk.win_lo, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = base + 8 * (r >> 2) + (r & 3);
+      const bool vis = j < lk.meta_hi || (uint32_t)(j - lk.win_lo) < wlen;
+      s[r] = vis ? s[r] : -INFINITY;
+    }
+  }
+}
+
 template <typename T, int DV>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
     const T* __restrict__ q_rot, const T* __restrict__ k_rot, const T* __restrict__ v, T* __restrict__ y,
@@ -354,7 +469,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   const int P = kAttnCols / G;            // positions per workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile decisions are scalar
   const int lq = lane & 31;   // query column (within the wave) / operand row of this lane
   const int hh = lane >> 5;   // lane half
   const int g = blockIdx.y;
@@ -370,29 +485,19 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   const int qa = p0 + c_lo / G;
   const int qb = c_lo <= c_hi ? min(p0 + c_hi / G + 1, L) : qa;
 
-  // Q^T operand: lane holds Q[my_q][16 kc + 8 hh .. +7]
-  Frag qf[4];
-  {
-    float tmp[8];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      if (my_q < L) {
-        load8(q_rot + ((b * L + my_q) * Hq + h) * kHd + 16 * kc + 8 * hh, tmp);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) tmp[e] = 0.f;
-      }
-      qf[kc] = M::from_f32(tmp);
-    }
-  }
+  LaneKeys lk;
+  lk.meta_hi = my_q < L ? min(my_q + 1, n_meta) : 0;
+  lk.win_hi = my_q < L ? my_q + 1 : 0;
+  lk.win_lo = window > 0 ? max(my_q - window + 1, n_meta) : n_meta;
 
-  f32x16_t acc[NDB];
+  // Q^T operand: lane holds Q[my_q][16 kc + 8 hh .. +7] (pre-scaled)
+  Frag qf[4];
 #pragma unroll
-  for (int d = 0; d < NDB; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
-  float m_run = -INFINITY;  // reference max of scaled scores (log2 units)
-  float l_run = 0.f;        // this lane's partial sum of 2^(s - m_run)
+  for (int kc = 0; kc < 4; ++kc)
+    qf[kc] = my_q < L ? M::frag_at(q_rot + ((b * L + my_q) * Hq + h) * kHd + 16 * kc + 8 * hh) : M::zero();
+
+  SoftmaxState<NDB> st;
+  st.init();
 
   // key tiles: meta part then window part
   const int meta_end = min(n_meta, p1);
@@ -403,88 +508,73 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   if (k2s < n1) k2s = n1;
   const int ntiles = n1 + max(0, k2e - k2s);
 
-  const T* kbase = k_rot + (b * k_rows) * Hkv * kHd + g * kHd;
-  const T* vbase = v + (b * v_rows) * Hkv * DV + g * DV;
   const int64_t kstride = (int64_t)Hkv * kHd, vstride = (int64_t)Hkv * DV;
   TileStage<T, DV, NT> stage;
-  stage.template init<KP, VP>(tid, kstride, vstride);
+  stage.template init<KP, VP>(tid, k_rot + (b * k_rows) * kstride + g * kHd, v + (b * v_rows) * vstride + g * DV,
+                              kstride, vstride, L);
   auto tile_j0 = [&](int idx) { return (idx < n1 ? idx : k2s + (idx - n1)) * BK; };
 
-  if (ntiles > 0) {
-    stage.fetch(kbase, vbase, tile_j0(0), L);
-    stage.template stash<KP, VP>(Ks[0], Vt[0]);
-  }
+  // every workgroup has at least the tile of its own first position (ntiles >= 1)
+  stage.fetch(tile_j0(0));
+  stage.template stash<KP, VP>(Ks[0], Vt[0]);
   __syncthreads();
+
+  // sub-tile [j0, j0 + 32) against this wave's positions [qa, qb)
+  auto none_for = [&](int j0) {
+    const int j1 = j0 + 32;
+    return qa >= qb || (j0 > qb - 1) || (window > 0 && j0 >= n_meta && qa - (j1 - 1) >= window);
+  };
+  auto full_for = [&](int j0) {
+    const int j1 = j0 + 32;
+    return (j1 - 1 <= qa) && (window <= 0 || j1 <= n_meta || (qb - 1) - max(j0, n_meta) < window);
+  };
+  // scores of sub-tile sub of the staged tile, shifted by -mref
+  auto scores = [&](int buf, int sub) {
+    f32x16_t s = st.negm;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) s = M::mma(M::frag_at(&Ks[buf][sub * 32 + lq][16 * kc + 8 * hh]), qf[kc], s);
+    return s;
+  };
+  // softmax of one sub-tile and its P V product
+  auto consume = [&](int buf, int sub, int j0, bool full, f32x16_t& s, f32x16_t* s_next) {
+    if (!full) mask_scores(s, lk, j0, hh, n_meta);
+    float t = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) t = fmaxf(t, s[r]);
+    if (__any(t > st.thr)) st.rescale(t, s, s_next);
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(s[r]);
+    const Frag pf0 = M::from_f32(&p[0]);
+    const Frag pf1 = M::from_f32(&p[8]);
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ls += p[r];
+    st.l += ls;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      st.acc[d] = M::mma(M::frag_at(&Vt[buf][32 * d + lq][sub * 32 + 0 + 8 * hh]), pf0, st.acc[d]);
+      st.acc[d] = M::mma(M::frag_at(&Vt[buf][32 * d + lq][sub * 32 + 16 + 8 * hh]), pf1, st.acc[d]);
+    }
+  };
 
   for (int idx = 0; idx < ntiles; ++idx) {
     const int buf = idx & 1;
-    if (idx + 1 < ntiles) stage.fetch(kbase, vbase, tile_j0(idx + 1), L);
+    if (idx + 1 < ntiles) stage.fetch(tile_j0(idx + 1));
     const int jt = tile_j0(idx);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int j0 = jt + sub * 32, j1 = j0 + 32;
-      const bool none = qa >= qb || (j0 > qb - 1) || (window > 0 && j0 >= n_meta && qa - (j1 - 1) >= window);
-      if (none) continue;
-      const bool full = (j1 - 1 <= qa) && (window <= 0 || j1 <= n_meta || (qb - 1) - max(j0, n_meta) < window);
-      f32x16_t s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const Frag a = M::lds_frag(&Ks[buf][sub * 32 + lq][16 * kc + 8 * hh]);
-        s = M::mma(a, qf[kc], s);
-      }
-      // lane holds scores of keys j0 + 8(r/4) + 4hh + (r%4) for position my_q
-      if (!full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool vis = my_q < L && key_visible(my_q, j, n_meta, window);
-          s[r] = vis ? s[r] : -INFINITY;
-        }
-      }
-      // This lane's max; the column's reference m_run is shared by lanes l and
-      // l+32. Only when some lane exceeds it by more than the slack do the two
-      // halves exchange maxima and rescale (rare after the first tile).
-      float lm = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) lm = fmaxf(lm, s[r]);
-      lm *= kScaleLog2e;
-      if (__any(lm > m_run + kRescaleSlack)) {
-        const float mt = fmaxf(lm, __shfl_xor(lm, 32, 64));
-        const bool need = mt > m_run + kRescaleSlack;        // same in both halves of a column
-        const float m_new = need ? mt : m_run;
-        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;   // 0 when m_run = -inf
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(fmaf(s[r], kScaleLog2e, -m_use));
-        l_run += p[r];
-      }
-      const Frag pf0 = M::from_f32(&p[0]);
-      const Frag pf1 = M::from_f32(&p[8]);
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        const Frag va0 = M::lds_frag(&Vt[buf][32 * d + lq][sub * 32 + 0 + 8 * hh]);
-        acc[d] = M::mma(va0, pf0, acc[d]);
-        const Frag va1 = M::lds_frag(&Vt[buf][32 * d + lq][sub * 32 + 16 + 8 * hh]);
-        acc[d] = M::mma(va1, pf1, acc[d]);
-      }
-    }
+    const bool none0 = none_for(jt), none1 = none_for(jt + 32);
+    // both score products, also for a sub-tile this wave skips (rare: the
+    // edges of the key range), so that no accumulator copies are needed
+    f32x16_t s0 = scores(buf, 0);
+    f32x16_t s1 = scores(buf, 1);
+    if (!none0) consume(buf, 0, jt, full_for(jt), s0, &s1);
+    if (!none1) consume(buf, 1, jt + 32, full_for(jt + 32), s1, nullptr);
     if (idx + 1 < ntiles) stage.template stash<KP, VP>(Ks[buf ^ 1], Vt[buf ^ 1]);
     __syncthreads();
   }
 
   // normalise and store: lane holds O[column][32 d + 8 jj + 4 hh + (0..3)]
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = st.l + __shfl_xor(st.l, 32, 64);   // the column's sum over both lane halves
   if (my_q < L) {
     const float inv = 1.0f / l_tot;
     T* yrow = y + ((b * L + my_q) * Hq + h) * DV;
@@ -493,8 +583,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int c = 32 * d + 8 * jj + 4 * hh;
-        const float o0 = acc[d][4 * jj + 0] * inv, o1 = acc[d][4 * jj + 1] * inv;
-        const float o2 = acc[d][4 * jj + 2] * inv, o3 = acc[d][4 * jj + 3] * inv;
+        const float o0 = st.acc[d][4 * jj + 0] * inv, o1 = st.acc[d][4 * jj + 1] * inv;
+        const float o2 = st.acc[d][4 * jj + 2] * inv, o3 = st.acc[d][4 * jj + 3] * inv;
         if constexpr (sizeof(T) == 2) {
           uint2 w2;
           w2.x = pack_bf16x2(o0, o1);
@@ -679,7 +769,7 @@ hipError_t rope_t(const RopeArgs& a, hipStream_t stream) {
   dim3 grid((a.L + kRopeRows - 1) / kRopeRows, a.batch);
   hipLaunchKernelGGL(rope_prefill_kernel<T>, grid, dim3(256), 0, stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (T*)a.q_rot, (T*)a.k_rot, (T*)a.v_copy, a.k_rows, a.v_rows, a.L, a.n_q_heads,
-                     a.n_kv_heads, a.head_dim_v, a.rope_base);
+                     a.n_kv_heads, a.head_dim_v, a.rope_base, kScaleLog2e);
   return hipGetLastError();
 }
 
