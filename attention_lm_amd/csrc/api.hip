@@ -80,6 +80,9 @@ int check_desc(const hymba_mixer_desc* d, bool decode) {
   const int64_t row_bytes = (int64_t)d->n_kv_heads * (d->head_dim > d->head_dim_v ? d->head_dim : d->head_dim_v) *
                             (int64_t)act_bytes(d->act);
   if (!decode && ((int64_t)d->n_meta + d->n_tokens) * row_bytes > INT32_MAX) return HYMBA_EUNSUPPORTED;
+  // and the scan stores one sequence's y the same way
+  if (!decode && ((int64_t)d->n_meta + d->n_tokens) * d->d_inner * (int64_t)act_bytes(d->act) > INT32_MAX)
+    return HYMBA_EUNSUPPORTED;
   return HYMBA_OK;
 }
 
@@ -95,6 +98,7 @@ int check_params(const hymba_mixer_params* p) {
 struct PrefillWs {
   size_t q_rot, k_rot, y_attn, y_ssm, agg, sdt, carry, total;
   int chunk_rows;
+  bool carry_ok;
 };
 PrefillWs prefill_ws(const hymba_mixer_desc* d) {
   const size_t es = act_bytes(d->act);
@@ -112,6 +116,7 @@ PrefillWs prefill_ws(const hymba_mixer_desc* d) {
   w.sdt = w.agg + round256(nchunk * chans * 16 * sizeof(float));
   w.carry = w.sdt + round256(nchunk * chans * sizeof(float));
   w.total = w.carry + round256(nchunk * chans * 16 * sizeof(float));
+  w.carry_ok = nchunk * chans * 16 * sizeof(float) <= (size_t)INT32_MAX;   // 32-bit offsets in the carry chain
   return w;
 }
 
@@ -138,7 +143,8 @@ extern "C" {
 
 size_t hymba_mixer_prefill_workspace_bytes(const hymba_mixer_desc* desc) {
   if (check_desc(desc, false) != HYMBA_OK) return 0;
-  return prefill_ws(desc).total;
+  const PrefillWs ws = prefill_ws(desc);
+  return ws.carry_ok ? ws.total : 0;
 }
 
 size_t hymba_mixer_decode_workspace_bytes(const hymba_mixer_desc* desc) {
@@ -167,6 +173,7 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   const int L = desc->n_meta + desc->n_tokens;
   if (k_cache && desc->cache_capacity < L) return HYMBA_EINVAL;
   const PrefillWs ws = prefill_ws(desc);
+  if (!ws.carry_ok) return HYMBA_EUNSUPPORTED;
   if (!workspace || workspace_bytes < ws.total) return HYMBA_EWORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return HYMBA_EALIGN;
 

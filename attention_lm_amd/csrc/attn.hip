@@ -145,17 +145,6 @@ template <typename T> struct AttnTile {
 // slot s of a 16-key chunk holds key kperm(s); an involution
 __device__ __forceinline__ int kperm(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
 
-// Raw buffer loads (gfx9 descriptor: 32-bit data format, no stride or swizzle).
-// A 16-byte load whose byte offset is at or past the descriptor's size reads
-// zeros and touches no memory.
-constexpr int kBufferWord3 = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
-}
-__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-
 template <typename T>
 struct Mma;
 template <>

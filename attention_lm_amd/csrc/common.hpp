@@ -63,6 +63,31 @@ __device__ __forceinline__ void store16(bf16* p, const float* o) {
   *reinterpret_cast<uint4*>(p) = v;
 }
 
+// Raw buffer access (gfx9 descriptor word 3: 32-bit data format; no stride,
+// swizzle or index). A load whose byte offset is at or past the descriptor's
+// size reads zeros and a store there is dropped; neither touches memory.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16 v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v.u, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+// 16 bytes per lane straight into LDS: lane i of the wave writes bytes
+// [16 i, 16 i + 16) from lds_base (which must be the same for the whole wave);
+// an out-of-range lane writes zeros.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+}
+// an offset that every descriptor above treats as out of range
+constexpr uint32_t kBufferNowhere = 0x80000000u;
+
 // Wave64 butterfly sum / max (deterministic order).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

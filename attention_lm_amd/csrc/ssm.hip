@@ -68,12 +68,27 @@ constexpr int kConv = 4;
 constexpr int kChanPerBlock = 128;   // one lane per channel
 constexpr int kRowBlock = 16;        // rows staged in LDS per step
 
+// Row t of B or C (16 values, the same for every channel) as raw 32-bit words:
+// a uniform address, so the compiler reads it with scalar loads into SGPRs and
+// the VALU takes the values as scalar operands (no LDS broadcast traffic).
+template <typename T> struct RowWords { static constexpr int n = kStates * (int)sizeof(T) / 4; };
+template <typename T>
+__device__ __forceinline__ void load_words(const T* __restrict__ p, uint32_t* w) {
+#pragma unroll
+  for (int j = 0; j < RowWords<T>::n; ++j) w[j] = reinterpret_cast<const uint32_t*>(p)[j];
+}
+__device__ __forceinline__ float word_val(const uint32_t* w, int n, bf16*) {
+  return (n & 1) ? bf16_hi(w[n >> 1]) : bf16_lo(w[n >> 1]);
+}
+__device__ __forceinline__ float word_val(const uint32_t* w, int n, float*) { return __uint_as_float(w[n]); }
+
 // One pass of the chunked scan over rows [t0, t1) of 128 channels.
 //  OUT = false: start from zero, write the chunk's end state and dt sum.
 //  OUT = true:  start from the chunk's carry-in, write gated y (and, for the
 //               last chunk, the final SSM state and conv history).
-// Inputs are staged through LDS in blocks of kRowBlock rows, double-buffered:
-// the global loads of block i+1 are in flight while block i is scanned.
+// The per-channel inputs (x with its conv history, dt, z) are staged through
+// LDS in blocks of kRowBlock rows, double-buffered: the global loads of block
+// i+1 are in flight while block i is scanned.
 template <typename T, bool OUT>
 __global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_kernel(
     const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ dt, const T* __restrict__ Bm,
@@ -85,13 +100,13 @@ __global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_kernel(
   constexpr int RV = kChanPerBlock / E;           // vectors per 128-channel row
   constexpr int XR = kRowBlock + kConv - 1;       // x rows per block (with conv history)
   constexpr int NX = (XR * RV + kChanPerBlock - 1) / kChanPerBlock;
-  constexpr int NR = (kRowBlock * RV + kChanPerBlock - 1) / kChanPerBlock;
-  constexpr int NBC = (kRowBlock * kStates / E + kChanPerBlock - 1) / kChanPerBlock;
-  __shared__ __attribute__((aligned(16))) T xs[2][XR][kChanPerBlock];
-  __shared__ __attribute__((aligned(16))) T ds[2][kRowBlock][kChanPerBlock];
-  __shared__ __attribute__((aligned(16))) T zs[OUT ? 2 : 1][OUT ? kRowBlock : 1][kChanPerBlock];
-  __shared__ __attribute__((aligned(16))) float bs[2][kRowBlock][kStates];
-  __shared__ __attribute__((aligned(16))) float cs[OUT ? 2 : 1][OUT ? kRowBlock : 1][kStates];
+  constexpr int XRP = NX * kChanPerBlock / RV;    // x rows staged: XR, padded so every thread has NX items
+  constexpr int NR = kRowBlock * RV / kChanPerBlock;
+  static_assert(NX * kChanPerBlock % RV == 0 && kRowBlock * RV % kChanPerBlock == 0, "staging shape");
+  // one stage: a block is copied to registers before the next one is loaded
+  __shared__ __attribute__((aligned(16))) T xs[XRP][kChanPerBlock];
+  __shared__ __attribute__((aligned(16))) T ds[kRowBlock][kChanPerBlock];
+  __shared__ __attribute__((aligned(16))) T zs[OUT ? kRowBlock : 1][kChanPerBlock];
 
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * kChanPerBlock;
@@ -105,70 +120,30 @@ __global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_kernel(
   const int64_t seq = (int64_t)b * L;
   const int t0 = k * CT, t1 = min(t0 + CT, L);
 
-  // staging registers
-  uint4 rx[NX], rd[NR], rz[OUT ? NR : 1], rb[NBC], rc[OUT ? NBC : 1];
-  auto vec_ok = [&](int t, int v) { return t >= 0 && t < L && c0 + (v + 1) * E <= Dch; };
+  // Block staging: buffer loads that write LDS directly (16 bytes per lane,
+  // lanes contiguous), so no staging registers. x rows outside [0, L) and
+  // dt/z rows outside [0, t1) read as zeros (dt = 0 leaves the state as is).
+  // Item it = (row it / RV, 16-byte vector it % RV) lands at byte 16 it of the
+  // stage, which is exactly the [row][channel] layout.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t row_b = (uint32_t)(Dch * sizeof(T));
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + seq * Dch, (uint32_t)L * row_b);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(dt + seq * Dch, (uint32_t)t1 * row_b);
+  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(z + seq * Dch, (uint32_t)t1 * row_b);
   auto fetch = [&](int tb) {
 #pragma unroll
     for (int r = 0; r < NX; ++r) {
       const int it = tid + r * kChanPerBlock, row = it / RV, v = it % RV, t = tb - (kConv - 1) + row;
-      rx[r] = make_uint4(0, 0, 0, 0);
-      if (it < XR * RV && vec_ok(t, v)) rx[r] = *reinterpret_cast<const uint4*>(x + (seq + t) * Dch + c0 + v * E);
+      const int it0 = 64 * wave + r * kChanPerBlock;   // first item of this wave's load
+      buf_load16_lds(xrs, (uint32_t)t * row_b + (uint32_t)((c0 + v * E) * sizeof(T)), &xs[0][0] + it0 * E);
     }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const int it = tid + r * kChanPerBlock, row = it / RV, v = it % RV, t = tb + row;
-      rd[r] = make_uint4(0, 0, 0, 0);
-      if (it < kRowBlock * RV && t < t1 && vec_ok(t, v))
-        rd[r] = *reinterpret_cast<const uint4*>(dt + (seq + t) * Dch + c0 + v * E);
-      if constexpr (OUT) {
-        rz[r] = make_uint4(0, 0, 0, 0);
-        if (it < kRowBlock * RV && t < t1 && vec_ok(t, v))
-          rz[r] = *reinterpret_cast<const uint4*>(z + (seq + t) * Dch + c0 + v * E);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < NBC; ++r) {
-      const int it = tid + r * kChanPerBlock;          // 16-byte vector of the block's B (or C) rows
-      const int t = tb + (it * E) / kStates;
-      rb[r] = make_uint4(0, 0, 0, 0);
-      if (it * E < kRowBlock * kStates && t < t1) rb[r] = *reinterpret_cast<const uint4*>(Bm + seq * kStates + (int64_t)tb * kStates + it * E);
-      if constexpr (OUT) {
-        rc[r] = make_uint4(0, 0, 0, 0);
-        if (it * E < kRowBlock * kStates && t < t1) rc[r] = *reinterpret_cast<const uint4*>(Cm + seq * kStates + (int64_t)tb * kStates + it * E);
-      }
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < NX; ++r) {
-      const int it = tid + r * kChanPerBlock;
-      if (it < XR * RV) *reinterpret_cast<uint4*>(&xs[buf][it / RV][(it % RV) * E]) = rx[r];
-    }
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int it = tid + r * kChanPerBlock;
-      if (it < kRowBlock * RV) {
-        *reinterpret_cast<uint4*>(&ds[buf][it / RV][(it % RV) * E]) = rd[r];
-        if constexpr (OUT) *reinterpret_cast<uint4*>(&zs[buf][it / RV][(it % RV) * E]) = rz[r];
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < NBC; ++r) {
-      const int it = tid + r * kChanPerBlock;
-      if (it * E < kRowBlock * kStates) {
-        float f[E];
-        load16(reinterpret_cast<const T*>(&rb[r]), f);
-        float* dst = &bs[buf][0][0] + it * E;
-#pragma unroll
-        for (int e = 0; e < E; ++e) dst[e] = f[e];
-        if constexpr (OUT) {
-          load16(reinterpret_cast<const T*>(&rc[r]), f);
-          float* dc = &cs[buf][0][0] + it * E;
-#pragma unroll
-          for (int e = 0; e < E; ++e) dc[e] = f[e];
-        }
-      }
+      const int it0 = 64 * wave + r * kChanPerBlock;
+      const uint32_t off = (uint32_t)t * row_b + (uint32_t)((c0 + v * E) * sizeof(T));
+      buf_load16_lds(drs, off, &ds[0][0] + it0 * E);
+      if constexpr (OUT) buf_load16_lds(zrs, off, &zs[0][0] + it0 * E);
     }
   };
 
@@ -191,56 +166,75 @@ __global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_kernel(
     for (int n = 0; n < kStates; ++n) h[n] = 0.f;
   }
   float S = 0.f;
-  float xm3 = 0.f, xm2 = 0.f, xm1 = 0.f;
+  const T* Bseq = Bm + seq * kStates;
+  const T* Cseq = Cm + seq * kStates;
+  // y of this sequence through a buffer descriptor that ends at row t1: stores
+  // of rows past the chunk and of lanes without a channel are dropped, so the
+  // row loop has no branches
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + seq * Dch, (uint32_t)((int64_t)t1 * Dch * sizeof(T)));
+  const uint32_t ylane = cv ? (uint32_t)(c * sizeof(T)) : kBufferNowhere;
+  constexpr int RW = RowWords<T>::n;
 
   const int nblk = (t1 - t0 + kRowBlock - 1) / kRowBlock;
   fetch(t0);
-  stash(0);
   __syncthreads();
   for (int ib = 0; ib < nblk; ++ib) {
-    const int buf = ib & 1;
     const int tb = t0 + ib * kRowBlock;
-    if (ib + 1 < nblk) fetch(tb + kRowBlock);
-    xm3 = to_f32(xs[buf][0][tid]);
-    xm2 = to_f32(xs[buf][1][tid]);
-    xm1 = to_f32(xs[buf][2][tid]);
-    // staged rows at or past t1 hold dt = 0 (state unchanged) and are not stored
-#pragma unroll 4
+    // this block's per-channel inputs, LDS -> registers, before any scalar
+    // load is in flight (scalar loads return out of order, so a wait for an
+    // LDS read behind one would also wait for it)
+    float xr[XR], dr[kRowBlock], zr[OUT ? kRowBlock : 1];
+#pragma unroll
+    for (int i = 0; i < XR; ++i) xr[i] = to_f32(xs[i][tid]);
+#pragma unroll
     for (int i = 0; i < kRowBlock; ++i) {
-      const float xt = to_f32(xs[buf][i + kConv - 1][tid]);
-      const float d = to_f32(ds[buf][i][tid]);
-      const float u = fmaf(w[0], xm3, fmaf(w[1], xm2, fmaf(w[2], xm1, w[3] * xt)));
-      if (tb + i < t1) { xm3 = xm2; xm2 = xm1; xm1 = xt; }
-      const float du = d * u;
-      float Bv[kStates];
+      dr[i] = to_f32(ds[i][tid]);
+      if constexpr (OUT) zr[i] = to_f32(zs[i][tid]);
+    }
+    __syncthreads();   // every wave has its copy: the stage is free
+    // the next block (past the chunk on the last one: then all dt are zero and
+    // it is never used), loading while this one is scanned; no branches
+    fetch(tb + kRowBlock);
+    // B/C rows one ahead of their use; staged rows at or past t1 hold dt = 0
+    // (state unchanged, y not stored) and read the B/C row t1 - 1
+    uint32_t bw[RW], cw[OUT ? RW : 1];
+    load_words(Bseq + (int64_t)min(tb, t1 - 1) * kStates, bw);
+    if constexpr (OUT) load_words(Cseq + (int64_t)min(tb, t1 - 1) * kStates, cw);
 #pragma unroll
-      for (int q = 0; q < kStates / 4; ++q) {
-        const float4 v4 = *reinterpret_cast<const float4*>(&bs[buf][i][4 * q]);
-        Bv[4 * q] = v4.x; Bv[4 * q + 1] = v4.y; Bv[4 * q + 2] = v4.z; Bv[4 * q + 3] = v4.w;
+    for (int i = 0; i < kRowBlock; ++i) {
+      // keep the scalar prefetch exactly one row ahead (SGPR pressure)
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t bn[RW], cn[OUT ? RW : 1];
+      if (i + 1 < kRowBlock) {
+        const int tn = min(tb + i + 1, t1 - 1);
+        load_words(Bseq + (int64_t)tn * kStates, bn);
+        if constexpr (OUT) load_words(Cseq + (int64_t)tn * kStates, cn);
       }
+      const float u = fmaf(w[0], xr[i], fmaf(w[1], xr[i + 1], fmaf(w[2], xr[i + 2], w[3] * xr[i + 3])));
+      const float d = dr[i];
+      const float du = d * u;
       if constexpr (OUT) {
-        float Cv[kStates];
-#pragma unroll
-        for (int q = 0; q < kStates / 4; ++q) {
-          const float4 v4 = *reinterpret_cast<const float4*>(&cs[buf][i][4 * q]);
-          Cv[4 * q] = v4.x; Cv[4 * q + 1] = v4.y; Cv[4 * q + 2] = v4.z; Cv[4 * q + 3] = v4.w;
-        }
         float acc = Dc * u;
 #pragma unroll
         for (int n = 0; n < kStates; ++n) {
-          h[n] = fmaf(fast_exp2(d * A2[n]), h[n], du * Bv[n]);
-          acc = fmaf(Cv[n], h[n], acc);
+          h[n] = fmaf(fast_exp2(d * A2[n]), h[n], du * word_val(bw, n, (T*)nullptr));
+          acc = fmaf(word_val(cw, n, (T*)nullptr), h[n], acc);
         }
-        const float zt = to_f32(zs[buf][i][tid]);
-        if (cv && tb + i < t1) y[(seq + tb + i) * Dch + c] = from_f32<T>(acc * silu(zt));
+        buf_store(yrs, (uint32_t)((tb + i) * Dch * (int)sizeof(T)) + ylane, from_f32<T>(acc * silu(zr[i])));
       } else {
 #pragma unroll
-        for (int n = 0; n < kStates; ++n) h[n] = fmaf(fast_exp2(d * A2[n]), h[n], du * Bv[n]);
+        for (int n = 0; n < kStates; ++n) h[n] = fmaf(fast_exp2(d * A2[n]), h[n], du * word_val(bw, n, (T*)nullptr));
         S += d;
       }
+      if (i + 1 < kRowBlock) {
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+          bw[j] = bn[j];
+          if constexpr (OUT) cw[j] = cn[j];
+        }
+      }
     }
-    if (ib + 1 < nblk) stash(buf ^ 1);
-    __syncthreads();
+    __syncthreads();   // (waits for the stage loads first)
   }
 
   if (!cv) return;
@@ -258,21 +252,27 @@ __global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_kernel(
     }
     if (conv_state_out) {   // raw x of rows L-3, L-2, L-1 (zero before row 0)
       T* csp = conv_state_out + ((int64_t)b * Dch + c) * (kConv - 1);
-      csp[0] = from_f32<T>(xm3);
-      csp[1] = from_f32<T>(xm2);
-      csp[2] = from_f32<T>(xm1);
+#pragma unroll
+      for (int j = 0; j < kConv - 1; ++j) {
+        const int t = L - (kConv - 1) + j;
+        csp[j] = t >= 0 ? x[(seq + t) * Dch + c] : from_f32<T>(0.f);
+      }
     }
   }
 }
 
-// carry[k] = state entering chunk k, from the chunk end states agg[k] (zero start)
-// and the chunk dt sums sdt[k]; loads are issued in batches ahead of the chain.
+// carry[k] = state entering chunk k, from the chunk end states agg[k] (zero
+// start) and the chunk dt sums sdt[k]. The chain is a few dozen dependent
+// fma steps per (sequence, channel, state); what costs is memory latency, so
+// the loads of the next batch of chunks are issued before the current batch
+// is chained.
+constexpr int kCarryBatch = 48;
 __global__ __launch_bounds__(256) void ssm_chunk_carry_kernel(const float* __restrict__ A,
                                                               const float* __restrict__ agg,
                                                               const float* __restrict__ sdt,
                                                               float* __restrict__ carry, int nchunk, int batch,
                                                               int Dch) {
-  constexpr int KB = 16;
+  constexpr int KB = kCarryBatch;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, c, n)
   const int64_t per = (int64_t)batch * Dch * kStates;
   if (idx >= per) return;
@@ -280,22 +280,33 @@ __global__ __launch_bounds__(256) void ssm_chunk_carry_kernel(const float* __res
   const int64_t bc = idx / kStates;
   const int c = (int)(bc % Dch);
   const float a2 = A[(int64_t)c * kStates + n] * kLog2e;
-  float H = 0.f;
+  const int last = nchunk - 2;   // chunks 0 .. nchunk-2 feed a later chunk
   carry[idx] = 0.f;
-  for (int k0 = 0; k0 + 1 < nchunk; k0 += KB) {
-    float av[KB], sv[KB];
+  if (last < 0) return;
+  float av[KB], sv[KB], an[KB], sn[KB];
+  auto load = [&](int k0, float* a, float* s) {
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      const int kk = min(k0 + i, nchunk - 2);
-      av[i] = agg[kk * per + idx];
-      sv[i] = sdt[kk * (per / kStates) + bc];
+      const int kk = min(k0 + i, last);
+      a[i] = agg[kk * per + idx];
+      s[i] = sdt[kk * (per / kStates) + bc];
+    }
+  };
+  // carry-ins past the last chunk are stored out of range (dropped)
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(carry, (uint32_t)((int64_t)nchunk * per * sizeof(float)));
+  load(0, av, sv);
+  float H = 0.f;
+  for (int k0 = 0; k0 <= last; k0 += KB) {
+    load(k0 + KB, an, sn);   // (clamped: past the end it re-reads the last chunk)
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      H = fmaf(fast_exp2(a2 * sv[i]), H, av[i]);
+      buf_store(crs, (uint32_t)(((int64_t)(k0 + i + 1) * per + idx) * sizeof(float)), H);
     }
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      if (k0 + i + 1 < nchunk) {
-        H = fmaf(fast_exp2(a2 * sv[i]), H, av[i]);
-        carry[(k0 + i + 1) * per + idx] = H;
-      }
+      av[i] = an[i];
+      sv[i] = sn[i];
     }
   }
 }
