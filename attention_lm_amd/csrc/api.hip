@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <unordered_map>
 
 #include "../../include/hymba_mixer.h"
@@ -37,6 +38,28 @@ hipError_t fork_ctx(ForkCtx** out) {
     if ((e = hipEventCreateWithFlags(&c.join, hipEventDisableTiming)) != hipSuccess) return e;
   }
   *out = &c;
+  return hipSuccess;
+}
+
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int* n_cu) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *n_cu = c;
+      return hipSuccess;
+    }
+  }
+  int v = 0;
+  e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (v < 1) v = 1;
+  if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  *n_cu = v;
   return hipSuccess;
 }
 
@@ -223,6 +246,7 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   aa.batch = desc->batch; aa.L = L; aa.n_meta = desc->n_meta; aa.window = desc->window;
   aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
   aa.act = desc->act;
+  HYMBA_TRY(device_cus(&aa.n_cu));
   HYMBA_TRY(hymba::launch_attn_prefill(aa, stream));
   HYMBA_TRY(mark(3));
   if (fc) HYMBA_TRY(hipStreamWaitEvent(stream, fc->join, 0));

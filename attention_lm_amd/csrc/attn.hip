@@ -19,6 +19,13 @@ constexpr int kHd = 64;                 // query/key head width
 constexpr float kScaleLog2e = 0.125f * kLog2e;  // 1/sqrt(64) folded with log2(e)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// max of three scores without the NaN-quieting copies the compiler puts in front
+// of fmaxf on values it cannot prove canonical (scores are never NaN)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // 8 consecutive elements <-> fp32
 __device__ __forceinline__ void load8(const bf16* p, float* o) { load16(p, o); }
@@ -444,7 +451,7 @@ __device__ __forceinline__ void mask_scores(f32x16_t& s, const LaneKeys& lk, int
 template <typename T, int DV>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
     const T* __restrict__ q_rot, const T* __restrict__ k_rot, const T* __restrict__ v, T* __restrict__ y,
-    int64_t k_rows, int64_t v_rows, int L, int n_meta, int window, int Hq, int Hkv) {
+    int64_t k_rows, int64_t v_rows, int L, int n_meta, int window, int Hq, int Hkv, int batch, int n_cu) {
   typedef Mma<T> M;
   typedef typename M::Frag Frag;
   constexpr int KP = AttnTile<T>::kpad;
@@ -461,9 +468,22 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile decisions are scalar
   const int lq = lane & 31;   // query column (within the wave) / operand row of this lane
   const int hh = lane >> 5;   // lane half
-  const int g = blockIdx.y;
-  const int64_t b = blockIdx.z;
-  const int p0 = blockIdx.x * P;
+  // Work order: a workgroup's cost grows with its position block (more keys
+  // in the causal window, up to the full window); two workgroups fit on a CU.
+  // Items are handed out heaviest first (largest-first scheduling). When all
+  // of them fit at once (at most two per CU), the first n_cu workgroups (one
+  // per CU) take the heaviest items and the rest the lightest, in ascending
+  // order, so that heavy items share a CU with light ones.
+  const int nxb = (L + P - 1) / P;
+  const int hb_n = Hkv * batch;
+  const int n_items = nxb * hb_n;
+  const int wg = (int)blockIdx.x;
+  int rank = wg;
+  if (n_items <= 2 * n_cu && wg >= n_cu) rank = n_items - 1 - (wg - n_cu);
+  const int pb = nxb - 1 - rank / hb_n;
+  const int g = (rank % hb_n) % Hkv;
+  const int64_t b = (rank % hb_n) / Hkv;
+  const int p0 = pb * P;
   const int p1 = min(p0 + P, L);
   const int col = 32 * wave + lq;
   const bool col_ok = col < P * G;
@@ -508,57 +528,90 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   stage.template stash<KP, VP>(Ks[0], Vt[0]);
   __syncthreads();
 
-  // sub-tile [j0, j0 + 32) against this wave's positions [qa, qb)
+  // sub-tile [j0, j0 + 32) against this wave's positions [qa, qb): no key
+  // visible to any column, or every key visible to every column
   auto none_for = [&](int j0) {
     const int j1 = j0 + 32;
     return qa >= qb || (j0 > qb - 1) || (window > 0 && j0 >= n_meta && qa - (j1 - 1) >= window);
   };
   auto full_for = [&](int j0) {
     const int j1 = j0 + 32;
-    return (j1 - 1 <= qa) && (window <= 0 || j1 <= n_meta || (qb - 1) - max(j0, n_meta) < window);
+    return qa < qb && (j1 - 1 <= qa) && (window <= 0 || j1 <= n_meta || (qb - 1) - max(j0, n_meta) < window);
   };
-  // scores of sub-tile sub of the staged tile, shifted by -mref
-  auto scores = [&](int buf, int sub) {
-    f32x16_t s = st.negm;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) s = M::mma(M::frag_at(&Ks[buf][sub * 32 + lq][16 * kc + 8 * hh]), qf[kc], s);
-    return s;
-  };
-  // softmax of one sub-tile and its P V product
-  auto consume = [&](int buf, int sub, int j0, bool full, f32x16_t& s, f32x16_t* s_next) {
-    if (!full) mask_scores(s, lk, j0, hh, n_meta);
-    float t = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int r = 2; r < 16; ++r) t = fmaxf(t, s[r]);
-    if (__any(t > st.thr)) st.rescale(t, s, s_next);
+  // 2^s of 16 shifted scores -> two B operands; l += their sum
+  auto probs = [&](const f32x16_t& s, Frag& pa, Frag& pb) {
     float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] = fast_exp2(s[r]);
-    const Frag pf0 = M::from_f32(&p[0]);
-    const Frag pf1 = M::from_f32(&p[8]);
-    float ls = 0.f;
+    pa = M::from_f32(&p[0]);
+    pb = M::from_f32(&p[8]);
+    float a[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ls += p[r];
-    st.l += ls;
+    for (int r = 0; r < 8; ++r) a[r] = p[r] + p[r + 8];
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      st.acc[d] = M::mma(M::frag_at(&Vt[buf][32 * d + lq][sub * 32 + 0 + 8 * hh]), pf0, st.acc[d]);
-      st.acc[d] = M::mma(M::frag_at(&Vt[buf][32 * d + lq][sub * 32 + 16 + 8 * hh]), pf1, st.acc[d]);
-    }
+    for (int r = 0; r < 4; ++r) a[r] += a[r + 4];
+    st.l += (a[0] + a[1]) + (a[2] + a[3]);
   };
 
   for (int idx = 0; idx < ntiles; ++idx) {
     const int buf = idx & 1;
-    if (idx + 1 < ntiles) stage.fetch(tile_j0(idx + 1));
     const int jt = tile_j0(idx);
-    const bool none0 = none_for(jt), none1 = none_for(jt + 32);
-    // both score products, also for a sub-tile this wave skips (rare: the
-    // edges of the key range), so that no accumulator copies are needed
-    f32x16_t s0 = scores(buf, 0);
-    f32x16_t s1 = scores(buf, 1);
-    if (!none0) consume(buf, 0, jt, full_for(jt), s0, &s1);
-    if (!none1) consume(buf, 1, jt + 32, full_for(jt + 32), s1, nullptr);
-    if (idx + 1 < ntiles) stage.template stash<KP, VP>(Ks[buf ^ 1], Vt[buf ^ 1]);
+    // the next tile into registers (after the last tile: rows that are staged
+    // but never read), so that the loop body has no data-dependent branches
+    stage.fetch(tile_j0(idx + 1));
+    if (!(none_for(jt) && none_for(jt + 32))) {
+      // K operands of both sub-tiles, then both score products
+      Frag kf[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) kf[c] = M::frag_at(&Ks[buf][(c >> 2) * 32 + lq][16 * (c & 3) + 8 * hh]);
+      f32x16_t s0 = st.negm, s1 = st.negm;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) s0 = M::mma(kf[kc], qf[kc], s0);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) s1 = M::mma(kf[4 + kc], qf[kc], s1);
+      // a sub-tile that some column sees only in part is masked (one that no
+      // column of the wave sees ends up all -inf and adds nothing)
+      if (!full_for(jt)) mask_scores(s0, lk, jt, hh, n_meta);
+      if (!full_for(jt + 32)) mask_scores(s1, lk, jt + 32, hh, n_meta);
+      // this lane's max of both sub-tiles: four independent max3 chains
+      float tm[4] = {s0[0], s0[1], s0[2], s0[3]};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tm[r] = max3f(tm[r], s1[r], s0[4 + r]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tm[r] = max3f(tm[r], s1[4 + r], s0[8 + r]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tm[r] = max3f(tm[r], s1[8 + r], s0[12 + r]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tm[r] = max3f(tm[r], s1[12 + r], s1[12 + r]);
+      const float t = max3f(tm[0], tm[1], max3f(tm[2], tm[3], tm[3]));
+      if (__any(t > st.thr)) st.rescale(t, s0, &s1);
+      // P of the first sub-tile and its V product, which runs while the second
+      // sub-tile's P is formed
+      Frag va[NDB][2], pa, pb;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        va[d][0] = M::frag_at(&Vt[buf][32 * d + lq][0 + 8 * hh]);
+        va[d][1] = M::frag_at(&Vt[buf][32 * d + lq][16 + 8 * hh]);
+      }
+      probs(s0, pa, pb);
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        st.acc[d] = M::mma(va[d][0], pa, st.acc[d]);
+        st.acc[d] = M::mma(va[d][1], pb, st.acc[d]);
+      }
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        va[d][0] = M::frag_at(&Vt[buf][32 * d + lq][32 + 8 * hh]);
+        va[d][1] = M::frag_at(&Vt[buf][32 * d + lq][48 + 8 * hh]);
+      }
+      probs(s1, pa, pb);
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        st.acc[d] = M::mma(va[d][0], pa, st.acc[d]);
+        st.acc[d] = M::mma(va[d][1], pb, st.acc[d]);
+      }
+    }
+    stage.template stash<KP, VP>(Ks[buf ^ 1], Vt[buf ^ 1]);
     __syncthreads();
   }
 
@@ -766,10 +819,10 @@ template <typename T, int DV>
 hipError_t attn_prefill_t(const AttnPrefillArgs& a, hipStream_t stream) {
   const int G = a.n_q_heads / a.n_kv_heads;
   const int P = kAttnCols / G;   // positions per workgroup
-  dim3 grid((a.L + P - 1) / P, a.n_kv_heads, a.batch);
-  hipLaunchKernelGGL((attn_prefill_kernel<T, DV>), grid, dim3(64 * kAttnWaves), 0, stream, (const T*)a.q_rot,
-                     (const T*)a.k_rot, (const T*)a.v, (T*)a.y, a.k_rows, a.v_rows, a.L, a.n_meta, a.window,
-                     a.n_q_heads, a.n_kv_heads);
+  const int64_t n_items = (int64_t)((a.L + P - 1) / P) * a.n_kv_heads * a.batch;
+  hipLaunchKernelGGL((attn_prefill_kernel<T, DV>), dim3((unsigned)n_items), dim3(64 * kAttnWaves), 0, stream,
+                     (const T*)a.q_rot, (const T*)a.k_rot, (const T*)a.v, (T*)a.y, a.k_rows, a.v_rows, a.L, a.n_meta,
+                     a.window, a.n_q_heads, a.n_kv_heads, a.batch, a.n_cu);
   return hipGetLastError();
 }
 

@@ -65,6 +65,7 @@ struct AttnPrefillArgs {
   int64_t k_rows, v_rows;
   void* y;                 // [batch, L, Hq*dv] act
   int batch, L, n_meta, window, n_q_heads, n_kv_heads, head_dim_v;
+  int n_cu;                // compute units of the device (work ordering)
   hymba_dtype act;
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream);
