@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     pdesc, pparams = ctypes.POINTER(MixerDesc), ctypes.POINTER(MixerParams)
     lib.hymba_mixer_prefill_workspace_bytes.argtypes = [pdesc]
     lib.hymba_mixer_prefill_workspace_bytes.restype = sz
+    lib.hymba_mixer_prefill_chunk_rows.argtypes = [pdesc]
+    lib.hymba_mixer_prefill_chunk_rows.restype = ctypes.c_int
     lib.hymba_mixer_decode_workspace_bytes.argtypes = [pdesc]
     lib.hymba_mixer_decode_workspace_bytes.restype = sz
     lib.hymba_mixer_prefill.argtypes = [pdesc, pparams] + [vp] * 8 + [vp] + [vp] * 6 + [vp, sz, vp, vp]
@@ -87,7 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
-PREFILL_STAGES = ("ssm_prefill", "rope_prefill", "attn_prefill", "fuse")
+PREFILL_STAGES = ("ssm_chunk_end", "ssm_chunk_carry", "ssm_chunk_out", "rope_prefill", "attn_prefill", "fuse")
 DECODE_STAGES = ("ssm_decode", "attn_decode", "decode_merge_fuse")
 
 
@@ -138,6 +140,10 @@ def _workspace(nbytes: int, device):
 
 def hymba_mixer_prefill_workspace_bytes(desc: MixerDesc) -> int:
     return int(load_library().hymba_mixer_prefill_workspace_bytes(ctypes.byref(desc)))
+
+
+def hymba_mixer_prefill_chunk_rows(desc: MixerDesc) -> int:
+    return int(load_library().hymba_mixer_prefill_chunk_rows(ctypes.byref(desc)))
 
 
 def hymba_mixer_decode_workspace_bytes(desc: MixerDesc) -> int:

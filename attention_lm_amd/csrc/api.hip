@@ -170,6 +170,11 @@ size_t hymba_mixer_prefill_workspace_bytes(const hymba_mixer_desc* desc) {
   return ws.carry_ok ? ws.total : 0;
 }
 
+int hymba_mixer_prefill_chunk_rows(const hymba_mixer_desc* desc) {
+  if (check_desc(desc, false) != HYMBA_OK) return 0;
+  return prefill_ws(desc).chunk_rows;
+}
+
 size_t hymba_mixer_decode_workspace_bytes(const hymba_mixer_desc* desc) {
   if (check_desc(desc, true) != HYMBA_OK) return 0;
   return decode_ws(desc).total;
@@ -207,8 +212,14 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   void* y_attn = y_attn_out ? y_attn_out : (void*)(wsb + ws.y_attn);
   void* y_ssm = y_ssm_out ? y_ssm_out : (void*)(wsb + ws.y_ssm);
 
-  auto mark = [&](int i) -> hipError_t {
-    return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+  // stage i's kernel records stage_events[2i] when it starts and [2i+1] when it ends
+  auto tm = [&](int i) -> hymba::Timing {
+    hymba::Timing t;
+    if (stage_events) {
+      t.start = stage_events[2 * i];
+      t.stop = stage_events[2 * i + 1];
+    }
+    return t;
   };
   // The two branches are independent until the fusion: without stage events the
   // Mamba branch runs on a second stream, concurrently with the attention branch.
@@ -220,7 +231,6 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
     HYMBA_TRY(hipStreamWaitEvent(fc->aux, fc->fork, 0));
     ssm_stream = fc->aux;
   }
-  HYMBA_TRY(mark(0));
   hymba::SsmPrefillArgs sa;
   sa.x = x; sa.z = z; sa.dt = dt; sa.B = B; sa.C = C;
   sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
@@ -228,9 +238,10 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   sa.agg = (float*)(wsb + ws.agg); sa.sdt = (float*)(wsb + ws.sdt); sa.carry = (float*)(wsb + ws.carry);
   sa.chunk_rows = ws.chunk_rows;
   sa.batch = desc->batch; sa.L = L; sa.d_inner = desc->d_inner; sa.act = desc->act;
-  HYMBA_TRY(hymba::launch_ssm_prefill(sa, ssm_stream));
+  HYMBA_TRY(hymba::launch_ssm_chunk_end(sa, ssm_stream, tm(0)));
+  HYMBA_TRY(hymba::launch_ssm_chunk_carry(sa, ssm_stream, tm(1)));
+  HYMBA_TRY(hymba::launch_ssm_chunk_out(sa, ssm_stream, tm(2)));
   if (fc) HYMBA_TRY(hipEventRecord(fc->join, fc->aux));
-  HYMBA_TRY(mark(1));
 
   hymba::RopeArgs ra;
   ra.q = q; ra.k = k; ra.v = v; ra.q_rot = q_rot; ra.k_rot = k_rot; ra.v_copy = v_cache;
@@ -238,8 +249,7 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   ra.batch = desc->batch; ra.L = L; ra.n_q_heads = desc->n_q_heads; ra.n_kv_heads = desc->n_kv_heads;
   ra.head_dim = desc->head_dim; ra.head_dim_v = desc->head_dim_v; ra.rope_base = desc->rope_base;
   ra.act = desc->act;
-  HYMBA_TRY(hymba::launch_rope_prefill(ra, stream));
-  HYMBA_TRY(mark(2));
+  HYMBA_TRY(hymba::launch_rope_prefill(ra, stream, tm(3)));
 
   hymba::AttnPrefillArgs aa;
   aa.q_rot = q_rot; aa.k_rot = k_rot; aa.v = v; aa.k_rows = k_rows; aa.v_rows = L; aa.y = y_attn;
@@ -247,13 +257,11 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
   aa.act = desc->act;
   HYMBA_TRY(device_cus(&aa.n_cu));
-  HYMBA_TRY(hymba::launch_attn_prefill(aa, stream));
-  HYMBA_TRY(mark(3));
+  HYMBA_TRY(hymba::launch_attn_prefill(aa, stream, tm(4)));
   if (fc) HYMBA_TRY(hipStreamWaitEvent(stream, fc->join, 0));
 
   HYMBA_TRY(hymba::launch_fuse(y_attn, y_ssm, params->beta_attn, params->beta_ssm, (int64_t)desc->batch * L,
-                               desc->d_inner, desc->norm_eps, desc->act, out, stream));
-  HYMBA_TRY(mark(4));
+                               desc->d_inner, desc->norm_eps, desc->act, out, stream, tm(5)));
   return HYMBA_OK;
 }
 
@@ -282,17 +290,20 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
   void* y_ssm = y_ssm_out ? y_ssm_out : (void*)(wsb + ws.y_ssm);
   void* y_attn = y_attn_out ? y_attn_out : (void*)(wsb + ws.y_attn);
 
-  auto mark = [&](int i) -> hipError_t {
-    return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+  auto tm = [&](int i) -> hymba::Timing {
+    hymba::Timing t;
+    if (stage_events) {
+      t.start = stage_events[2 * i];
+      t.stop = stage_events[2 * i + 1];
+    }
+    return t;
   };
-  HYMBA_TRY(mark(0));
   hymba::SsmDecodeArgs sa;
   sa.x = x; sa.z = z; sa.dt = dt; sa.B = B; sa.C = C;
   sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
   sa.state = ssm_state; sa.conv_state = conv_state; sa.y = y_ssm;
   sa.batch = desc->batch; sa.d_inner = desc->d_inner; sa.act = desc->act;
-  HYMBA_TRY(hymba::launch_ssm_decode(sa, stream));
-  HYMBA_TRY(mark(1));
+  HYMBA_TRY(hymba::launch_ssm_decode(sa, stream, tm(0)));
 
   hymba::AttnDecodeArgs aa;
   aa.q = q; aa.k_new = k_new; aa.v_new = v_new; aa.k_cache = k_cache; aa.v_cache = v_cache;
@@ -301,16 +312,15 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
   aa.batch = desc->batch; aa.cap = desc->cache_capacity; aa.n_meta = desc->n_meta; aa.window = desc->window;
   aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
   aa.rope_base = desc->rope_base; aa.act = desc->act;
-  HYMBA_TRY(hymba::launch_attn_decode(aa, stream));
-  HYMBA_TRY(mark(2));
+  HYMBA_TRY(hymba::launch_attn_decode(aa, stream, tm(1)));
 
   hymba::DecodeMergeArgs ma;
   ma.partial = partial; ma.y_attn = y_attn; ma.n_split = ws.n_split; ma.batch = desc->batch;
   ma.n_q_heads = desc->n_q_heads; ma.head_dim_v = desc->head_dim_v; ma.act = desc->act;
-  HYMBA_TRY(hymba::launch_decode_merge(ma, stream));
+  const hymba::Timing t2 = tm(2);
+  HYMBA_TRY(hymba::launch_decode_merge(ma, stream, hymba::Timing{t2.start, nullptr}));
   HYMBA_TRY(hymba::launch_fuse(y_attn, y_ssm, params->beta_attn, params->beta_ssm, desc->batch, desc->d_inner,
-                               desc->norm_eps, desc->act, out, stream));
-  HYMBA_TRY(mark(3));
+                               desc->norm_eps, desc->act, out, stream, hymba::Timing{nullptr, t2.stop}));
   return HYMBA_OK;
 }
 

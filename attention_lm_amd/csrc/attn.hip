@@ -807,42 +807,45 @@ __global__ __launch_bounds__(DV) void decode_merge_kernel(const float* __restric
 }
 
 template <typename T>
-hipError_t rope_t(const RopeArgs& a, hipStream_t stream) {
+hipError_t rope_t(const RopeArgs& a, hipStream_t stream, Timing tm) {
   dim3 grid((a.L + kRopeRows - 1) / kRopeRows, a.batch);
-  hipLaunchKernelGGL(rope_prefill_kernel<T>, grid, dim3(256), 0, stream, (const T*)a.q, (const T*)a.k,
+  HYMBA_LAUNCH(rope_prefill_kernel<T>, grid, dim3(256), 0, stream, tm, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (T*)a.q_rot, (T*)a.k_rot, (T*)a.v_copy, a.k_rows, a.v_rows, a.L, a.n_q_heads,
                      a.n_kv_heads, a.head_dim_v, a.rope_base, kScaleLog2e);
   return hipGetLastError();
 }
 
 template <typename T, int DV>
-hipError_t attn_prefill_t(const AttnPrefillArgs& a, hipStream_t stream) {
+hipError_t attn_prefill_t(const AttnPrefillArgs& a, hipStream_t stream, Timing tm) {
   const int G = a.n_q_heads / a.n_kv_heads;
   const int P = kAttnCols / G;   // positions per workgroup
   const int64_t n_items = (int64_t)((a.L + P - 1) / P) * a.n_kv_heads * a.batch;
-  hipLaunchKernelGGL((attn_prefill_kernel<T, DV>), dim3((unsigned)n_items), dim3(64 * kAttnWaves), 0, stream,
+  HYMBA_LAUNCH((attn_prefill_kernel<T, DV>), dim3((unsigned)n_items), dim3(64 * kAttnWaves), 0, stream, tm,
                      (const T*)a.q_rot, (const T*)a.k_rot, (const T*)a.v, (T*)a.y, a.k_rows, a.v_rows, a.L, a.n_meta,
                      a.window, a.n_q_heads, a.n_kv_heads, a.batch, a.n_cu);
   return hipGetLastError();
 }
 
 template <typename T, int DV>
-hipError_t attn_decode_t(const AttnDecodeArgs& a, hipStream_t stream) {
+hipError_t attn_decode_t(const AttnDecodeArgs& a, hipStream_t stream, Timing tm) {
+  Timing t_first, t_last;   // the stage's start on its first kernel, its end on its last
+  t_first.start = tm.start;
+  t_last.stop = tm.stop;
   const int64_t n = (int64_t)a.batch * (a.n_q_heads + a.n_kv_heads) * (kHd / 2);
-  hipLaunchKernelGGL(decode_rope_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, (const T*)a.q,
+  HYMBA_LAUNCH(decode_rope_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, t_first, (const T*)a.q,
                      (const T*)a.k_new, a.cache_len, a.q_rot, a.k_rot, a.batch, a.n_q_heads, a.n_kv_heads, a.cap,
                      a.rope_base);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_decode_kernel<T, DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream,
+  HYMBA_LAUNCH((attn_decode_kernel<T, DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream, t_last,
                      a.q_rot, a.k_rot, (const T*)a.v_new, (const T*)a.k_cache, (const T*)a.v_cache, a.cache_len,
                      a.partial, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads, a.n_kv_heads);
   return hipGetLastError();
 }
 
 template <typename T, int DV>
-hipError_t merge_t(const DecodeMergeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_merge_kernel<T, DV>), dim3(a.n_q_heads, a.batch), dim3(DV), 0, stream, a.partial,
+hipError_t merge_t(const DecodeMergeArgs& a, hipStream_t stream, Timing tm) {
+  HYMBA_LAUNCH((decode_merge_kernel<T, DV>), dim3(a.n_q_heads, a.batch), dim3(DV), 0, stream, tm, a.partial,
                      (T*)a.y_attn, a.n_split, a.n_q_heads);
   return hipGetLastError();
 }
@@ -857,14 +860,14 @@ hipError_t merge_t(const DecodeMergeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_rope_prefill(const RopeArgs& a, hipStream_t stream) {
-  if (a.act == HYMBA_BF16) return rope_t<bf16>(a, stream);
-  return rope_t<float>(a, stream);
+hipError_t launch_rope_prefill(const RopeArgs& a, hipStream_t stream, Timing tm) {
+  if (a.act == HYMBA_BF16) return rope_t<bf16>(a, stream, tm);
+  return rope_t<float>(a, stream, tm);
 }
 
-hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream) {
-  if (a.act == HYMBA_BF16) { HYMBA_DISPATCH_DV(a.head_dim_v, attn_prefill_t, bf16, a, stream) }
-  HYMBA_DISPATCH_DV(a.head_dim_v, attn_prefill_t, float, a, stream)
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream, Timing tm) {
+  if (a.act == HYMBA_BF16) { HYMBA_DISPATCH_DV(a.head_dim_v, attn_prefill_t, bf16, a, stream, tm) }
+  HYMBA_DISPATCH_DV(a.head_dim_v, attn_prefill_t, float, a, stream, tm)
 }
 
 void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_per_split) {
@@ -875,14 +878,14 @@ void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_
   *n_split = (int)((max_vis + kKeysPerSplit - 1) / kKeysPerSplit);
 }
 
-hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream) {
-  if (a.act == HYMBA_BF16) { HYMBA_DISPATCH_DV(a.head_dim_v, attn_decode_t, bf16, a, stream) }
-  HYMBA_DISPATCH_DV(a.head_dim_v, attn_decode_t, float, a, stream)
+hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream, Timing tm) {
+  if (a.act == HYMBA_BF16) { HYMBA_DISPATCH_DV(a.head_dim_v, attn_decode_t, bf16, a, stream, tm) }
+  HYMBA_DISPATCH_DV(a.head_dim_v, attn_decode_t, float, a, stream, tm)
 }
 
-hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream) {
-  if (a.act == HYMBA_BF16) { HYMBA_DISPATCH_DV(a.head_dim_v, merge_t, bf16, a, stream) }
-  HYMBA_DISPATCH_DV(a.head_dim_v, merge_t, float, a, stream)
+hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream, Timing tm) {
+  if (a.act == HYMBA_BF16) { HYMBA_DISPATCH_DV(a.head_dim_v, merge_t, bf16, a, stream, tm) }
+  HYMBA_DISPATCH_DV(a.head_dim_v, merge_t, float, a, stream, tm)
 }
 
 }  // namespace hymba

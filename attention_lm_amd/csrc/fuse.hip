@@ -118,20 +118,20 @@ __global__ void mask_ranges_kernel(int n_rows, int n_meta, int window, int32_t* 
 
 template <typename T>
 hipError_t fuse_t(const void* ya, const void* ys, const float* ba, const float* bs, int64_t n_rows,
-                  int width, float eps, void* out, hipStream_t stream) {
-  if (n_rows == 0) return hipSuccess;
+                  int width, float eps, void* out, hipStream_t stream, Timing tm) {
+  if (n_rows == 0) return no_kernel(stream, tm);
   const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
   constexpr int V = Vec16<T>::n;
   const bool vec = (width % V) == 0;
   dim3 grid((unsigned)blocks), block(64 * kRowsPerBlock);
   if (vec && width <= 64 * V * 8)
-    hipLaunchKernelGGL((fuse_rows_kernel<T, true, 8>), grid, block, 0, stream, (const T*)ya, (const T*)ys, ba,
+    HYMBA_LAUNCH((fuse_rows_kernel<T, true, 8>), grid, block, 0, stream, tm, (const T*)ya, (const T*)ys, ba,
                        bs, n_rows, width, eps, (T*)out);
   else if (vec)
-    hipLaunchKernelGGL((fuse_rows_kernel<T, true, 0>), grid, block, 0, stream, (const T*)ya, (const T*)ys, ba,
+    HYMBA_LAUNCH((fuse_rows_kernel<T, true, 0>), grid, block, 0, stream, tm, (const T*)ya, (const T*)ys, ba,
                        bs, n_rows, width, eps, (T*)out);
   else
-    hipLaunchKernelGGL((fuse_rows_kernel<T, false, 0>), grid, block, 0, stream, (const T*)ya, (const T*)ys, ba,
+    HYMBA_LAUNCH((fuse_rows_kernel<T, false, 0>), grid, block, 0, stream, tm, (const T*)ya, (const T*)ys, ba,
                        bs, n_rows, width, eps, (T*)out);
   return hipGetLastError();
 }
@@ -139,9 +139,10 @@ hipError_t fuse_t(const void* ya, const void* ys, const float* ba, const float* 
 }  // namespace
 
 hipError_t launch_fuse(const void* y_attn, const void* y_ssm, const float* beta_attn, const float* beta_ssm,
-                       int64_t n_rows, int width, float eps, hymba_dtype act, void* out, hipStream_t stream) {
-  if (act == HYMBA_BF16) return fuse_t<bf16>(y_attn, y_ssm, beta_attn, beta_ssm, n_rows, width, eps, out, stream);
-  return fuse_t<float>(y_attn, y_ssm, beta_attn, beta_ssm, n_rows, width, eps, out, stream);
+                       int64_t n_rows, int width, float eps, hymba_dtype act, void* out, hipStream_t stream,
+                       Timing tm) {
+  if (act == HYMBA_BF16) return fuse_t<bf16>(y_attn, y_ssm, beta_attn, beta_ssm, n_rows, width, eps, out, stream, tm);
+  return fuse_t<float>(y_attn, y_ssm, beta_attn, beta_ssm, n_rows, width, eps, out, stream, tm);
 }
 
 hipError_t launch_mask_ranges(int n_rows, int n_meta, int window, int32_t* ranges, hipStream_t stream) {

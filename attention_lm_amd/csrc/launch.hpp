@@ -2,6 +2,7 @@
 // All arguments have been validated by the caller; launchers only enqueue.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,10 +11,26 @@
 
 namespace hymba {
 
+// Optional timing events of one launch, recorded by the dispatch itself
+// (start when the kernel begins, stop when it ends).
+struct Timing {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+#define HYMBA_LAUNCH(kernel, grid, block, shmem, stream, tm, ...) \
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, (tm).start, (tm).stop, 0, __VA_ARGS__)
+// a stage that has nothing to launch still records its events (zero length)
+inline hipError_t no_kernel(hipStream_t stream, Timing tm) {
+  if (tm.start) {
+    hipError_t e = hipEventRecord(tm.start, stream);
+    if (e != hipSuccess) return e;
+  }
+  return tm.stop ? hipEventRecord(tm.stop, stream) : hipSuccess;
+}
+
 // fuse.hip ------------------------------------------------------------------
 hipError_t launch_fuse(const void* y_attn, const void* y_ssm, const float* beta_attn,
                        const float* beta_ssm, int64_t n_rows, int width, float eps,
-                       hymba_dtype act, void* out, hipStream_t stream);
+                       hymba_dtype act, void* out, hipStream_t stream, Timing tm = {});
 hipError_t launch_mask_ranges(int n_rows, int n_meta, int window, int32_t* ranges,
                               hipStream_t stream);
 
@@ -32,7 +49,11 @@ struct SsmPrefillArgs {
   hymba_dtype act;
 };
 int ssm_prefill_chunk_rows(int batch, int L, int d_inner);
-hipError_t launch_ssm_prefill(const SsmPrefillArgs& a, hipStream_t stream);
+// The three kernels of the chunked prefill scan, in this order: chunk end
+// states (nothing to do for a single chunk), carries between chunks, output.
+hipError_t launch_ssm_chunk_end(const SsmPrefillArgs& a, hipStream_t stream, Timing tm = {});
+hipError_t launch_ssm_chunk_carry(const SsmPrefillArgs& a, hipStream_t stream, Timing tm = {});
+hipError_t launch_ssm_chunk_out(const SsmPrefillArgs& a, hipStream_t stream, Timing tm = {});
 
 struct SsmDecodeArgs {
   const void *x, *z, *dt, *B, *C;
@@ -43,7 +64,7 @@ struct SsmDecodeArgs {
   int batch, d_inner;
   hymba_dtype act;
 };
-hipError_t launch_ssm_decode(const SsmDecodeArgs& a, hipStream_t stream);
+hipError_t launch_ssm_decode(const SsmDecodeArgs& a, hipStream_t stream, Timing tm = {});
 
 // attn.hip ------------------------------------------------------------------
 struct RopeArgs {
@@ -56,7 +77,7 @@ struct RopeArgs {
   float rope_base;
   hymba_dtype act;
 };
-hipError_t launch_rope_prefill(const RopeArgs& a, hipStream_t stream);
+hipError_t launch_rope_prefill(const RopeArgs& a, hipStream_t stream, Timing tm = {});
 
 struct AttnPrefillArgs {
   const void* q_rot;       // [batch, L, Hq, 64]
@@ -68,7 +89,7 @@ struct AttnPrefillArgs {
   int n_cu;                // compute units of the device (work ordering)
   hymba_dtype act;
 };
-hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream);
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream, Timing tm = {});
 
 struct AttnDecodeArgs {
   const void *q, *k_new, *v_new;       // [batch, H, d] not rotated
@@ -82,7 +103,7 @@ struct AttnDecodeArgs {
   float rope_base;
   hymba_dtype act;
 };
-hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream);
+hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream, Timing tm = {});
 void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_per_split);
 
 struct DecodeMergeArgs {
@@ -91,6 +112,6 @@ struct DecodeMergeArgs {
   int n_split, batch, n_q_heads, head_dim_v;
   hymba_dtype act;
 };
-hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream, Timing tm = {});
 
 }  // namespace hymba

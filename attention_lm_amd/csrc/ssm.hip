@@ -362,29 +362,28 @@ __global__ __launch_bounds__(256) void ssm_decode_kernel(
 }
 
 template <typename T>
-hipError_t prefill_t(const SsmPrefillArgs& a, hipStream_t stream) {
+hipError_t chunk_end_t(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
   const int CT = a.chunk_rows;
   const int nchunk = (a.L + CT - 1) / CT;
-  const dim3 block(kChanPerBlock);
+  if (nchunk < 2) return no_kernel(stream, tm);
   const int cblocks = (a.d_inner + kChanPerBlock - 1) / kChanPerBlock;
-  if (nchunk > 1) {
-    hipLaunchKernelGGL((ssm_chunk_kernel<T, false>), dim3(cblocks, nchunk - 1, a.batch), block, 0, stream,
-                       (const T*)a.x, (const T*)a.z, (const T*)a.dt, (const T*)a.B, (const T*)a.C, a.A, a.D,
-                       a.conv_w, (const float*)nullptr, a.agg, a.sdt, (T*)nullptr, (float*)nullptr, (T*)nullptr,
-                       a.L, a.d_inner, CT);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int64_t per = (int64_t)a.batch * a.d_inner * kStates;
-  hipLaunchKernelGGL(ssm_chunk_carry_kernel, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, stream, a.A, a.agg,
-                     a.sdt, a.carry, nchunk, a.batch, a.d_inner);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // the output pass covers every chunk (the grid's y extent is nchunk)
-  hipLaunchKernelGGL((ssm_chunk_kernel<T, true>), dim3(cblocks, nchunk, a.batch), block, 0, stream, (const T*)a.x,
-                     (const T*)a.z, (const T*)a.dt, (const T*)a.B, (const T*)a.C, a.A, a.D, a.conv_w, a.carry,
-                     (float*)nullptr, (float*)nullptr, (T*)a.y, a.state_out, (T*)a.conv_state_out, a.L, a.d_inner,
+  HYMBA_LAUNCH((ssm_chunk_kernel<T, false>), dim3(cblocks, nchunk - 1, a.batch), dim3(kChanPerBlock), 0, stream, tm,
+                     (const T*)a.x, (const T*)a.z, (const T*)a.dt, (const T*)a.B, (const T*)a.C, a.A, a.D, a.conv_w,
+                     (const float*)nullptr, a.agg, a.sdt, (T*)nullptr, (float*)nullptr, (T*)nullptr, a.L, a.d_inner,
                      CT);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t chunk_out_t(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
+  const int CT = a.chunk_rows;
+  const int nchunk = (a.L + CT - 1) / CT;
+  const int cblocks = (a.d_inner + kChanPerBlock - 1) / kChanPerBlock;
+  // the output pass covers every chunk (the grid's y extent is nchunk)
+  HYMBA_LAUNCH((ssm_chunk_kernel<T, true>), dim3(cblocks, nchunk, a.batch), dim3(kChanPerBlock), 0, stream, tm,
+                     (const T*)a.x, (const T*)a.z, (const T*)a.dt, (const T*)a.B, (const T*)a.C, a.A, a.D, a.conv_w,
+                     a.carry, (float*)nullptr, (float*)nullptr, (T*)a.y, a.state_out, (T*)a.conv_state_out, a.L,
+                     a.d_inner, CT);
   return hipGetLastError();
 }
 
@@ -401,21 +400,34 @@ int ssm_prefill_chunk_rows(int batch, int L, int d_inner) {
   return (int)ct;
 }
 
-hipError_t launch_ssm_prefill(const SsmPrefillArgs& a, hipStream_t stream) {
-  if (a.act == HYMBA_BF16) return prefill_t<bf16>(a, stream);
-  return prefill_t<float>(a, stream);
+hipError_t launch_ssm_chunk_end(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
+  if (a.act == HYMBA_BF16) return chunk_end_t<bf16>(a, stream, tm);
+  return chunk_end_t<float>(a, stream, tm);
 }
 
-hipError_t launch_ssm_decode(const SsmDecodeArgs& a, hipStream_t stream) {
+hipError_t launch_ssm_chunk_carry(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
+  const int nchunk = (a.L + a.chunk_rows - 1) / a.chunk_rows;
+  const int64_t per = (int64_t)a.batch * a.d_inner * kStates;
+  HYMBA_LAUNCH(ssm_chunk_carry_kernel, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, stream, tm, a.A, a.agg,
+                     a.sdt, a.carry, nchunk, a.batch, a.d_inner);
+  return hipGetLastError();
+}
+
+hipError_t launch_ssm_chunk_out(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
+  if (a.act == HYMBA_BF16) return chunk_out_t<bf16>(a, stream, tm);
+  return chunk_out_t<float>(a, stream, tm);
+}
+
+hipError_t launch_ssm_decode(const SsmDecodeArgs& a, hipStream_t stream, Timing tm) {
   const int64_t threads = (int64_t)a.batch * a.d_inner * 4;
   if (threads == 0) return hipSuccess;
   dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   if (a.act == HYMBA_BF16)
-    hipLaunchKernelGGL(ssm_decode_kernel<bf16>, grid, block, 0, stream, (const bf16*)a.x, (const bf16*)a.z,
+    HYMBA_LAUNCH(ssm_decode_kernel<bf16>, grid, block, 0, stream, tm, (const bf16*)a.x, (const bf16*)a.z,
                        (const bf16*)a.dt, (const bf16*)a.B, (const bf16*)a.C, a.A, a.D, a.conv_w, a.state,
                        (bf16*)a.conv_state, (bf16*)a.y, a.batch, a.d_inner);
   else
-    hipLaunchKernelGGL(ssm_decode_kernel<float>, grid, block, 0, stream, (const float*)a.x, (const float*)a.z,
+    HYMBA_LAUNCH(ssm_decode_kernel<float>, grid, block, 0, stream, tm, (const float*)a.x, (const float*)a.z,
                        (const float*)a.dt, (const float*)a.B, (const float*)a.C, a.A, a.D, a.conv_w, a.state,
                        (float*)a.conv_state, (float*)a.y, a.batch, a.d_inner);
   return hipGetLastError();

@@ -34,9 +34,11 @@ METRIC = "hybrid-head mixer prefill tokens/s + decode µs/step; % HBM/MFMA roofl
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # VALU issue: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz lane-slots/s; a transcendental
-# (v_exp_f32) takes two slots on gfx950.
+# (v_exp_f32) issues at a quarter of the rate of an fma: four slots.
 ALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
-SCAN_SLOTS_PER_ELEM = 6          # mul(dt*A) + exp(2) + mul(dt*u*B) + fma(h) + fma(C.h)
+EXP_SLOTS = 4
+SCAN_END_SLOTS_PER_ELEM = 3 + EXP_SLOTS   # mul(dt*A) + exp + mul(dt*u*B) + fma(h)
+SCAN_OUT_SLOTS_PER_ELEM = 4 + EXP_SLOTS   # ... + fma(C.h)
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 KERNEL_SOURCES = ["common.hpp", "ssm.hip", "attn.hip", "fuse.hip", "api.hip"]
 
@@ -92,20 +94,32 @@ def visible_pairs(L, n_meta, window):
     return total
 
 
-def prefill_work(cfg):
+def prefill_work(cfg, chunk_rows):
+    """Algorithmic work of each prefill kernel: every input read once, every
+    output written once; ALU slots of the scan recurrence only."""
     es = 2 if cfg.act == "bf16" else 4
     B, L, D, N = cfg.batch, cfg.seq_rows, cfg.d_inner, cfg.d_state
     Hq, Hkv, hd, dv = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.head_dim_v
     rows = B * L
-    scan_bytes = rows * (4 * D * es + 2 * N * es) + B * D * N * 4 + B * D * 3 * es + D * (N + 1 + 4) * 4
-    elems = rows * D * N
+    nchunk = -(-L // chunk_rows)
+    end_rows = B * (nchunk - 1) * chunk_rows           # every chunk but the last
+    state = B * D * N * 4                                # one fp32 state set
+    params = D * (N + 1 + 4) * 4                         # A, D, conv taps
+    # end pass: x (with 3 rows of history per chunk), dt, B of its rows; end states + dt sums
+    end_bytes = end_rows * (2 * D * es + N * es) + (nchunk - 1) * (state + B * D * 4) + params
+    # carry chain: end states and dt sums in, carried-in states out
+    carry_bytes = (nchunk - 1) * (state + B * D * 4) + nchunk * state + D * N * 4
+    # output pass: x, dt, z, B, C, carried-in states; y, final state and conv history
+    out_bytes = rows * (4 * D * es + 2 * N * es) + nchunk * state + state + B * D * 3 * es + params
     rope_bytes = rows * ((Hq + Hkv) * hd * es * 2 + Hkv * dv * es * 2)
     pairs = B * visible_pairs(L, cfg.n_meta, cfg.window)
     attn_flops = pairs * Hq * (2 * hd + 2 * dv)
     attn_bytes = rows * ((Hq + Hkv) * hd * es + Hkv * dv * es + D * es)
     fuse_bytes = rows * 3 * D * es + 2 * D * 4
     return {
-        "ssm_prefill": {"bytes": scan_bytes, "alu_slots": elems * SCAN_SLOTS_PER_ELEM, "elems": elems},
+        "ssm_chunk_end": {"bytes": end_bytes, "alu_slots": end_rows * D * N * SCAN_END_SLOTS_PER_ELEM},
+        "ssm_chunk_carry": {"bytes": carry_bytes},
+        "ssm_chunk_out": {"bytes": out_bytes, "alu_slots": rows * D * N * SCAN_OUT_SLOTS_PER_ELEM},
         "rope_prefill": {"bytes": rope_bytes},
         "attn_prefill": {"bytes": attn_bytes, "flops": attn_flops, "pairs": pairs},
         "fuse": {"bytes": fuse_bytes},
@@ -168,10 +182,60 @@ def traffic_for(kernel):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+# rocprofv3 kernel names -> the stage keys above (bf16 instances: the benchmark's dtype)
+COUNTER_KERNELS = {
+    "ssm_chunk_end": ("ssm_chunk_kernel<hymba::bf16, false>",),
+    "ssm_chunk_carry": ("ssm_chunk_carry_kernel",),
+    "ssm_chunk_out": ("ssm_chunk_kernel<hymba::bf16, true>",),
+    "rope_prefill": ("rope_prefill_kernel<hymba::bf16>",),
+    "attn_prefill": ("attn_prefill_kernel<hymba::bf16",),
+    "fuse": ("fuse_rows_kernel<hymba::bf16",),
+}
+
+
+def summarize_counters(fetch_csv, write_csv, calib_mib, command):
+    """HBM bytes per launch of each prefill kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each divided by what the
+    same counter reads per KiB for the plain device copy of calib_mib MiB that
+    the same command ran (the largest copy dispatch)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals, copies = {}, []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if "copyBuffer" in name or "direct_copy" in name:
+                copies.append(v)
+            for key, pats in COUNTER_KERNELS.items():
+                if any(p in name for p in pats):
+                    vals.setdefault(key, []).append(v)
+        return vals, copies
+
+    fetch, fcopies = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, wcopies = per_kernel(write_csv, "WRITE_SIZE")
+    true_kib = calib_mib * 1024.0
+    ffac = max(fcopies) / true_kib
+    wfac = max(wcopies) / true_kib
+    kernels = {}
+    for key in COUNTER_KERNELS:
+        if key not in fetch or key not in write:
+            continue
+        f = sum(fetch[key]) / len(fetch[key])
+        w = sum(write[key]) / len(write[key])
+        kernels[key] = {"fetch_KiB": round(f, 1), "write_KiB": round(w, 1), "dispatches": len(fetch[key]),
+                        "hbm_bytes_per_launch": int(round((f / ffac + w / wfac) * 1024))}
+    return {"source_hash": source_hash(), "command": command,
+            "calibration": {"copy_MiB": calib_mib, "fetch_KiB_per_true_KiB": round(ffac, 4),
+                            "write_KiB_per_true_KiB": round(wfac, 4)},
+            "kernels": kernels}
+
+
 # ---------------------------------------------------------------------------
 
 
-def bench_prefill(cfg, steps, warmup, n_sets, ev):
+def bench_prefill(cfg, steps, warmup, n_sets, ev, serial=False):
     import torch
     import synth
     from harness import Prefill
@@ -191,22 +255,26 @@ def bench_prefill(cfg, steps, warmup, n_sets, ev):
                               r.out, workspace=r.ws, stage_events=events, **r.o)
 
     log(f"[bench] prefill warmup {warmup}")
+    wev = ev.array(2 * nst) if serial else None
     for i in range(warmup):
-        step(runs[i % n_sets])
+        step(runs[i % n_sets], wev)
     torch.cuda.synchronize()
     log(f"[bench] prefill timed {steps} steps")
+    tev = [ev.array(2 * nst) for _ in range(steps)] if serial else [None] * steps
     t0 = time.perf_counter()
     for i in range(steps):
-        step(runs[i % n_sets])
+        step(runs[i % n_sets], tev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # per-kernel durations: the same steps with stage events (stages serialized)
-    evs = [ev.array(nst + 1) for _ in range(steps)]
+    # per-kernel durations: the same steps with stage events (stages serialized;
+    # each kernel's dispatch records its own start and end)
+    evs = [ev.array(2 * nst) for _ in range(steps)]
     for i in range(steps):
         step(runs[i % n_sets], evs[i])
     torch.cuda.synchronize()
-    stage_ms = {name: sum(ev.ms(e[j], e[j + 1]) for e in evs) / steps for j, name in enumerate(H._lib.PREFILL_STAGES)}
-    serial_ms = sum(ev.ms(e[0], e[nst]) for e in evs) / steps
+    stage_ms = {name: sum(ev.ms(e[2 * j], e[2 * j + 1]) for e in evs) / steps
+                for j, name in enumerate(H._lib.PREFILL_STAGES)}
+    serial_ms = sum(ev.ms(e[0], e[2 * nst - 1]) for e in evs) / steps
     return wall / steps * 1e3, stage_ms, serial_ms
 
 
@@ -223,7 +291,7 @@ def bench_decode(cfg, steps, warmup, n_sets, ev):
         runs.append(Decode(cfg, inp))
         log(f"[bench] decode set {s} on device")
     nst = len(H._lib.DECODE_STAGES)
-    evs = [[ev.array(nst + 1) for _ in range(cfg.n_layers)] for _ in range(steps)]
+    evs = [[ev.array(2 * nst) for _ in range(cfg.n_layers)] for _ in range(steps)]
     for i in range(warmup):
         for l in range(cfg.n_layers):
             runs[i % n_sets].call(l, with_branches=False)
@@ -238,10 +306,11 @@ def bench_decode(cfg, steps, warmup, n_sets, ev):
                                  L["out"], workspace=r.ws, stage_events=evs[i][l])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_layer_ms = [sum(ev.ms(evs[i][l][0], evs[i][l][nst]) for i in range(steps)) / steps for l in range(cfg.n_layers)]
+    per_layer_ms = [sum(ev.ms(evs[i][l][0], evs[i][l][2 * nst - 1]) for i in range(steps)) / steps
+                    for l in range(cfg.n_layers)]
     stage_ms = {}
     for j, name in enumerate(H._lib.DECODE_STAGES):
-        stage_ms[name] = [sum(ev.ms(evs[i][l][j], evs[i][l][j + 1]) for i in range(steps)) / steps
+        stage_ms[name] = [sum(ev.ms(evs[i][l][2 * j], evs[i][l][2 * j + 1]) for i in range(steps)) / steps
                           for l in range(cfg.n_layers)]
     return wall / steps * 1e3, per_layer_ms, stage_ms
 
@@ -293,9 +362,22 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated through the timed steps")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--serial", action="store_true",
+                    help="time the prefill steps with the branches serialized (per-kernel events in every "
+                         "step, as in the per-kernel pass): for profiles whose kernel averages must match")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="also run a plain device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print per-kernel HBM bytes from two rocprofv3 --pmc counter CSVs (FETCH_SIZE, "
+                         "WRITE_SIZE) of a run with --copy-calibration, and exit")
+    ap.add_argument("--counter-command", default="", help="the command that produced the counter CSVs (recorded)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        if not args.copy_calibration:
+            ap.error("--summarize-counters needs the --copy-calibration size the counted run used")
+        print(json.dumps(summarize_counters(*args.summarize_counters, args.copy_calibration, args.counter_command),
+                         indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -320,8 +402,11 @@ def main():
         del src, dst
     ev = HipEvents()
     cfg = synth.config("swa_layer")
-    ms, stage_ms, serial_ms = bench_prefill(cfg, args.steps, args.warmup, args.sets, ev)
-    work = prefill_work(cfg)
+    ms, stage_ms, serial_ms = bench_prefill(cfg, args.steps, args.warmup, args.sets, ev, serial=args.serial)
+    chunk_rows = H.hymba_mixer_prefill_chunk_rows(H.make_desc(
+        batch=cfg.batch, n_meta=cfg.n_meta, n_tokens=cfg.n_tokens, d_inner=cfg.d_inner, n_q_heads=cfg.n_q_heads,
+        n_kv_heads=cfg.n_kv_heads, window=cfg.window, act=cfg.act))
+    work = prefill_work(cfg, chunk_rows)
     kernels = {k: kernel_report(k, stage_ms[k], work[k], cfg.act) for k in stage_ms}
     dom = max(stage_ms, key=stage_ms.get)
     kd = kernels[dom]
@@ -355,6 +440,7 @@ def main():
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "head_dim_v": cfg.head_dim_v,
                    "window": cfg.window, "input_sets": args.sets},
         "rows_per_s_incl_meta": round(cfg.batch * cfg.seq_rows / (ms * 1e-3), 1),
+        "prefill_branches": "serialized" if args.serial else "concurrent",
         "serial_ms_per_step": round(serial_ms, 4),
         "roofline": roofline,
         "kernels": kernels,

@@ -50,7 +50,7 @@ extern "C" {
 #endif
 
 #define HYMBA_ABI_VERSION 1
-#define HYMBA_PREFILL_STAGES 4
+#define HYMBA_PREFILL_STAGES 6
 #define HYMBA_DECODE_STAGES 3
 
 typedef enum { HYMBA_F32 = 0, HYMBA_BF16 = 1 } hymba_dtype;
@@ -111,6 +111,13 @@ typedef struct {
 size_t hymba_mixer_prefill_workspace_bytes(const hymba_mixer_desc* desc);
 size_t hymba_mixer_decode_workspace_bytes(const hymba_mixer_desc* desc);
 
+/* Rows per chunk of the prefill selective scan: the sequence is cut into
+ * chunks of this many rows that are scanned in parallel (the first pass
+ * computes the end state of every chunk but the last, a carry pass chains
+ * them, the output pass rescans every chunk from its carried-in state).
+ * Host-side query for sizing and work accounting; 0 if desc is invalid. */
+int hymba_mixer_prefill_chunk_rows(const hymba_mixer_desc* desc);
+
 /* Prefill of L = n_meta + n_tokens rows per sequence, meta rows first; conv
  * history and SSM state start at zero (the meta rows fill them: Hymba guide,
  * "2. Learnable Meta-Tokens").
@@ -132,10 +139,12 @@ size_t hymba_mixer_decode_workspace_bytes(const hymba_mixer_desc* desc);
  *  y_ssm_out       [batch, L, d_inner] Mamba branch before the fusion
  *  workspace       device scratch of hymba_mixer_prefill_workspace_bytes(desc)
  *                  bytes, 256-byte aligned; contents are not preserved.
- *  stage_events    NULL, or HYMBA_PREFILL_STAGES + 1 caller-created events:
- *                  event i is recorded on `stream` before stage i, the last one
- *                  after the final stage (stages: conv+scan, rotary, attention,
- *                  fusion). For per-kernel timing; the caller owns the events.
+ *  stage_events    NULL, or 2 * HYMBA_PREFILL_STAGES caller-created events:
+ *                  events 2i and 2i+1 are recorded when stage i's kernel starts
+ *                  and when it ends (stages: scan chunk end states, chunk
+ *                  carries, scan output, rotary, attention, fusion; one kernel
+ *                  each; a stage with nothing to do records both back to back).
+ *                  For per-kernel timing; the caller owns the events.
  * Without stage events the Mamba branch (conv + scan) runs on a second stream
  * of the calling thread, concurrently with the attention branch; both join on
  * `stream` before the fusion, so ordering on `stream` is as if serial. With
@@ -170,9 +179,10 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
  *  conv_state IN/OUT [batch, d_inner, d_conv-1] raw x, oldest first, shifted in place
  *  out        [batch, d_inner]; y_attn_out, y_ssm_out optional [batch, d_inner]
  *  workspace  hymba_mixer_decode_workspace_bytes(desc) bytes, 256-byte aligned.
- *  stage_events NULL, or HYMBA_DECODE_STAGES + 1 caller-created events, recorded
- *             as for prefill (stages: SSM step, attention partials,
- *             merge + fusion). */
+ *  stage_events NULL, or 2 * HYMBA_DECODE_STAGES caller-created events: start
+ *             and end of each stage as for prefill (stages: SSM step, query/key
+ *             rotation + attention partials, merge + fusion; the start event
+ *             is taken by the stage's first kernel, the end by its last). */
 int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
                        const void* x, const void* z, const void* dt, const void* B, const void* C,
                        const void* q, const void* k_new, const void* v_new,

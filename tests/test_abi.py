@@ -78,6 +78,8 @@ def test_workspace_sizes(lib):
     got = H.hymba_mixer_decode_workspace_bytes(dd)
     assert expect <= got <= expect + 5 * 256
     assert H.hymba_mixer_prefill_workspace_bytes(c1_desc(n_q_heads=24)) == 0     # invalid -> 0
+    assert H.hymba_mixer_prefill_chunk_rows(d) == 32
+    assert H.hymba_mixer_prefill_chunk_rows(c1_desc(n_q_heads=24)) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
