@@ -56,10 +56,14 @@ __device__ __forceinline__ void rope_cs(int pos, int i, float base, float* c, fl
 // queries are also scaled by log2(e)/sqrt(64), so that q.k comes out as the
 // softmax exponent in base 2.
 
-constexpr int kRopeRows = 8;
+// Two rows per workgroup: for the usual head counts a thread then has one
+// rotation item and at most one value-copy item, and both loads are issued
+// before either store (the kernel moves bytes; what limits it is latency).
+constexpr int kRopeRows = 2;
+constexpr int kRopeThreads = 256;
 
 template <typename T>
-__global__ __launch_bounds__(256) void rope_prefill_kernel(
+__global__ __launch_bounds__(kRopeThreads) void rope_prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ q_rot,
     T* __restrict__ k_rot, T* __restrict__ v_copy, int64_t k_rows, int64_t v_rows, int L, int Hq, int Hkv,
     int dv, float base, float q_scale) {
@@ -67,51 +71,57 @@ __global__ __launch_bounds__(256) void rope_prefill_kernel(
   __shared__ float sn[kRopeRows][kHd / 2];
   const int r0 = blockIdx.x * kRopeRows;
   const int64_t b = blockIdx.y;
-  for (int t = threadIdx.x; t < kRopeRows * (kHd / 2); t += blockDim.x) {
+  const int tid = threadIdx.x;
+  for (int t = tid; t < kRopeRows * (kHd / 2); t += blockDim.x) {
     const int r = t / (kHd / 2), i = t % (kHd / 2);
     rope_cs(r0 + r, i, base, &cs[r][i], &sn[r][i]);
   }
   __syncthreads();
   const int nrows = min(kRopeRows, L - r0);
-  // rotation work items: (row, head, group of 8 pairs); heads 0..Hq-1 are q, then k
   const int H = Hq + Hkv;
-  const int items = nrows * H * 4;
-  for (int it = threadIdx.x; it < items; it += blockDim.x) {
-    const int g8 = it & 3;
-    const int hr = it >> 2;
-    const int hd = hr % H;
-    const int r = hr / H;
-    const int row = r0 + r;
-    const T* src;
-    T* dst;
-    float sc;
-    if (hd < Hq) {
-      src = q + ((b * L + row) * Hq + hd) * kHd;
-      dst = q_rot + ((b * L + row) * Hq + hd) * kHd;
-      sc = q_scale;
-    } else {
-      src = k + ((b * L + row) * Hkv + (hd - Hq)) * kHd;
-      dst = k_rot + ((b * k_rows + row) * Hkv + (hd - Hq)) * kHd;
-      sc = 1.f;
-    }
-    float lo[8], hi[8], olo[8], ohi[8];
-    load8(src + 8 * g8, lo);
-    load8(src + 32 + 8 * g8, hi);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float c = cs[r][8 * g8 + e], s = sn[r][8 * g8 + e];
-      olo[e] = (lo[e] * c - hi[e] * s) * sc;
-      ohi[e] = (hi[e] * c + lo[e] * s) * sc;
-    }
-    store8(dst + 8 * g8, olo);
-    store8(dst + 32 + 8 * g8, ohi);
-  }
-  if (v_copy) {
-    const int per_row = Hkv * dv / 8;
-    for (int it = threadIdx.x; it < nrows * per_row; it += blockDim.x) {
+  const int rot_items = nrows * H * 4;                      // (row, head, group of 8 pairs)
+  const int per_row = Hkv * dv / 8;
+  const int v_items = v_copy ? nrows * per_row : 0;         // (row, 8-element chunk)
+  for (int it = tid; it < max(rot_items, v_items); it += blockDim.x) {
+    // loads of both items first
+    const bool has_v = it < v_items;
+    float vf[8];
+    int64_t v_dst = 0;
+    if (has_v) {
       const int r = it / per_row, e = it % per_row;
-      copy8(v + (b * L + r0 + r) * (int64_t)(Hkv * dv) + 8 * e, v_copy + (b * v_rows + r0 + r) * (int64_t)(Hkv * dv) + 8 * e);
+      load8(v + (b * L + r0 + r) * (int64_t)(Hkv * dv) + 8 * e, vf);
+      v_dst = (b * v_rows + r0 + r) * (int64_t)(Hkv * dv) + 8 * e;
     }
+    const bool has_r = it < rot_items;
+    const int g8 = it & 3, hr = it >> 2, hd = hr % H, rr = hr / H;
+    T* dst = nullptr;
+    float sc = 1.f, lo[8], hi[8];
+    if (has_r) {
+      const int row = r0 + rr;
+      const T* src;
+      if (hd < Hq) {
+        src = q + ((b * L + row) * Hq + hd) * kHd;
+        dst = q_rot + ((b * L + row) * Hq + hd) * kHd;
+        sc = q_scale;
+      } else {
+        src = k + ((b * L + row) * Hkv + (hd - Hq)) * kHd;
+        dst = k_rot + ((b * k_rows + row) * Hkv + (hd - Hq)) * kHd;
+      }
+      load8(src + 8 * g8, lo);
+      load8(src + 32 + 8 * g8, hi);
+    }
+    if (has_r) {
+      float olo[8], ohi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float c = cs[rr][8 * g8 + e], s = sn[rr][8 * g8 + e];
+        olo[e] = (lo[e] * c - hi[e] * s) * sc;
+        ohi[e] = (hi[e] * c + lo[e] * s) * sc;
+      }
+      store8(dst + 8 * g8, olo);
+      store8(dst + 32 + 8 * g8, ohi);
+    }
+    if (has_v) store8(v_copy + v_dst, vf);
   }
 }
 
@@ -809,7 +819,7 @@ __global__ __launch_bounds__(DV) void decode_merge_kernel(const float* __restric
 template <typename T>
 hipError_t rope_t(const RopeArgs& a, hipStream_t stream, Timing tm) {
   dim3 grid((a.L + kRopeRows - 1) / kRopeRows, a.batch);
-  HYMBA_LAUNCH(rope_prefill_kernel<T>, grid, dim3(256), 0, stream, tm, (const T*)a.q, (const T*)a.k,
+  HYMBA_LAUNCH(rope_prefill_kernel<T>, grid, dim3(kRopeThreads), 0, stream, tm, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (T*)a.q_rot, (T*)a.k_rot, (T*)a.v_copy, a.k_rows, a.v_rows, a.L, a.n_q_heads,
                      a.n_kv_heads, a.head_dim_v, a.rope_base, kScaleLog2e);
   return hipGetLastError();
