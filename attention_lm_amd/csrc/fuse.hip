@@ -19,8 +19,12 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void fuse_rows_kernel(
     const T* __restrict__ ya, const T* __restrict__ ys, const float* __restrict__ ba,
     const float* __restrict__ bs, int64_t n_rows, int width, float eps, T* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= n_rows) return;
+  int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const bool live = row < n_rows;
+  if (!live) {
+    if constexpr (MAXV == 0) return;
+    row = n_rows - 1;   // a past-the-end wave only helps stage the betas; it stores nothing
+  }
   const T* a = ya + row * (int64_t)width;
   const T* s = ys + row * (int64_t)width;
   T* o = out + row * (int64_t)width;
@@ -28,6 +32,9 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void fuse_rows_kernel(
   const float inv_w = 1.0f / (float)width;
 
   if constexpr (MAXV > 0) {
+    // the workgroup's copy of the betas (dynamic LDS: 2 x width floats), read
+    // from L2 once per workgroup while the rows are loading
+    extern __shared__ float sbeta[];
     float va[MAXV][V], vs[MAXV][V];
     float sa = 0.f, ss = 0.f;
 #pragma unroll
@@ -38,6 +45,11 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void fuse_rows_kernel(
         load16(s + c, vs[i]);
       }
     }
+    for (int c4 = threadIdx.x * 4; c4 < width; c4 += blockDim.x * 4) {
+      *reinterpret_cast<float4*>(sbeta + c4) = *reinterpret_cast<const float4*>(ba + c4);
+      *reinterpret_cast<float4*>(sbeta + width + c4) = *reinterpret_cast<const float4*>(bs + c4);
+    }
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
       const int c = (lane + 64 * i) * V;
@@ -53,15 +65,16 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void fuse_rows_kernel(
     ss = wave_sum(ss);
     const float ra = 0.5f / sqrtf(sa * inv_w + eps);
     const float rs = 0.5f / sqrtf(ss * inv_w + eps);
+    if (!live) return;
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
       const int c = (lane + 64 * i) * V;
       if (c < width) {
         float bav[V], bsv[V], r[V];
-        load16(ba + c, bav);
-        if constexpr (V == 8) load16(ba + c + 4, bav + 4);
-        load16(bs + c, bsv);
-        if constexpr (V == 8) load16(bs + c + 4, bsv + 4);
+        load16(sbeta + c, bav);
+        if constexpr (V == 8) load16(sbeta + c + 4, bav + 4);
+        load16(sbeta + width + c, bsv);
+        if constexpr (V == 8) load16(sbeta + width + c + 4, bsv + 4);
 #pragma unroll
         for (int e = 0; e < V; ++e) r[e] = fmaf(bav[e] * ra, va[i][e], bsv[e] * rs * vs[i][e]);
         store16(o + c, r);
@@ -125,7 +138,7 @@ hipError_t fuse_t(const void* ya, const void* ys, const float* ba, const float* 
   const bool vec = (width % V) == 0;
   dim3 grid((unsigned)blocks), block(64 * kRowsPerBlock);
   if (vec && width <= 64 * V * 8)
-    HYMBA_LAUNCH((fuse_rows_kernel<T, true, 8>), grid, block, 0, stream, tm, (const T*)ya, (const T*)ys, ba,
+    HYMBA_LAUNCH((fuse_rows_kernel<T, true, 8>), grid, block, 2 * width * sizeof(float), stream, tm, (const T*)ya, (const T*)ys, ba,
                        bs, n_rows, width, eps, (T*)out);
   else if (vec)
     HYMBA_LAUNCH((fuse_rows_kernel<T, true, 0>), grid, block, 0, stream, tm, (const T*)ya, (const T*)ys, ba,
