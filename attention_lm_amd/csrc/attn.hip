@@ -154,10 +154,9 @@ constexpr int BK = 64;                     // keys per LDS stage (two 32-key sub
 constexpr int kAttnWaves = 4;
 constexpr int kAttnCols = 32 * kAttnWaves;
 constexpr float kRescaleSlack = 8.0f;
-template <typename T> struct AttnTile {
-  static constexpr int kpad = kHd + 16 / (int)sizeof(T);   // padded K row (elements)
-  static constexpr int vpad = BK + 16 / (int)sizeof(T);    // padded V^T row (elements)
-};
+// wait for this wave's outstanding global loads, including those that write LDS
+// (gfx9 s_waitcnt: vmcnt 0; expcnt and lgkmcnt left at their maximum)
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // slot s of a 16-key chunk holds key kperm(s); an involution
 __device__ __forceinline__ int kperm(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
@@ -212,119 +211,149 @@ struct Mma<float> {
   }
 };
 
-// Global -> registers -> LDS staging of one 64-key tile.
-//  K: 16-byte chunks copied as is into padded rows.
-//  V (bf16): item = (group of 4 V^T slots, 8-wide dv chunk dc); the thread
-//    reads the 4 keys of the slot group at dv 8dc..8dc+7 and writes eight
-//    8-byte V^T row pieces (one per dv), transposed with byte permutes. Slot
-//    groups are the fastest index, so the 16 lanes of an 8-byte LDS write phase
-//    cover all 32 banks of one row.
-//  V (fp32): item = (4-key quad, dv chunk), quads fastest.
-// Rows at or past L are staged as zeros; their keys are masked out of every
-// score.
+// Staging of one 64-key K/V tile in LDS (two stages, double-buffered).
+//
+// bf16: buffer loads write LDS directly (16 bytes per lane, lanes contiguous),
+// so no staging registers and no stash. K rows (128 B) and V rows (2 dv B)
+// keep their natural layout; the 16-byte chunks of a row are XOR-swizzled by
+// the row index so that the operand reads below are bank-conflict free (the
+// swizzle is applied on the global side: each lane loads the chunk that
+// belongs at its LDS position). K operands are plain 16-byte reads (8
+// consecutive dims of one key). V operands need 8 keys of one dv: two
+// transposing reads (ds_read_b64_tr_b16), each giving a 16-lane group 4 keys x
+// 16 dvs, so V is never transposed in memory.
+// fp32: registers -> padded LDS, with V stored transposed (tests use fp32).
+// Rows at or past L read as zeros; their keys are masked out of every score.
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
 template <typename T, int DV, int NT>
 struct TileStage;
 
 template <int DV, int NT>
 struct TileStage<bf16, DV, NT> {
-  static constexpr int KCH = kHd / 8;                        // 16-byte chunks per K row
-  static constexpr int KITEMS = BK * KCH;
-  static constexpr int KMAX = (KITEMS + NT - 1) / NT;
-  static constexpr int VITEMS = (BK / 4) * (DV / 8);         // (4-key group, 8-wide dv chunk)
-  static constexpr int VMAX = (VITEMS + NT - 1) / NT;
-  u32x4_t kreg[KMAX];
-  u32x4_t vreg[VMAX][4];
-  // per-thread constants: byte offset of the item in a tile that starts at
-  // row 0, and its LDS element offset (-1: no item)
-  uint32_t koff[KMAX], voff[VMAX];
-  int kloff[KMAX], vloff[VMAX];
-  uint32_t kstride_b, vstride_b;
+  typedef bf16x8_t Frag;
+  static constexpr int KROWB = kHd * 2, VROWB = DV * 2;          // bytes per K / V row
+  static constexpr int KCH = KROWB / 16, VCH = VROWB / 16;       // 16-byte chunks per row
+  static constexpr int KSTAGE = BK * KROWB, VSTAGE = BK * VROWB;
+  static constexpr int kStageBytes = KSTAGE + VSTAGE;
+  static constexpr int KN = BK * KCH / NT, VN = BK * VCH / NT;   // loads per thread per tile
+  static_assert(BK * KCH % NT == 0 && BK * VCH % NT == 0, "tile shape");
+  // K: 16 consecutive rows at one chunk hit 16 distinct 16-byte bank slots.
+  static __device__ __forceinline__ int ksw(int row) { return (row >> 1) & (KCH - 1); }
+  // V: the 4 rows x 2 halves of 32 bytes that one 32-lane half of a
+  // transposing read touches land in 8 distinct 32-byte bank slots.
+  static constexpr int VRPB = VROWB >= 256 ? 1 : 256 / VROWB;   // V rows per 256-byte bank sweep
+  static __device__ __forceinline__ int vsw(int row) { return (4 * ((row & 3) / VRPB)) & (VCH - 1); }
   __amdgpu_buffer_rsrc_t krs, vrs;
-  // item it: slot group sg = it & 15 (4 slots 4sg..4sg+3 of the 64-key stage),
-  // dv chunk dc = it >> 4. Slots are kperm-ordered inside each 16-key chunk, so
-  // the 4 keys of a slot group are consecutive keys.
-  static __device__ __forceinline__ int first_key(int sg) { return (sg & ~3) * 4 + kperm((sg & 3) * 4); }
-  template <int KP, int VP>
+  uint32_t kstride_b, vstride_b;
+  uint32_t koff[KN], voff[VN];   // per-lane global byte offsets of a tile starting at row 0
+  int kro[4], vro[DV / 32];      // per-lane LDS byte offsets of the operand reads (see kfrag, vfrag)
+  int wave, lane;
   __device__ __forceinline__ void init(int tid, const bf16* kbase, const bf16* vbase, int64_t kstride,
                                        int64_t vstride, int L) {
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    lane = tid & 63;
     kstride_b = (uint32_t)(kstride * 2);
     vstride_b = (uint32_t)(vstride * 2);
     krs = make_rsrc(kbase, (uint32_t)(((int64_t)(L - 1) * kstride + kHd) * 2));
     vrs = make_rsrc(vbase, (uint32_t)(((int64_t)(L - 1) * vstride + DV) * 2));
 #pragma unroll
-    for (int r = 0; r < KMAX; ++r) {
-      const int it = tid + r * NT;
-      const int row = it / KCH, c = (it % KCH) * 8;
-      koff[r] = (uint32_t)row * kstride_b + 2u * c;
-      kloff[r] = it < KITEMS ? row * KP + c : -1;
+    for (int r = 0; r < KN; ++r) {
+      const int pos = r * NT + 64 * wave + lane, row = pos / KCH, cp = pos % KCH;
+      koff[r] = (uint32_t)row * kstride_b + 16u * (uint32_t)(cp ^ ksw(row));
     }
 #pragma unroll
-    for (int r = 0; r < VMAX; ++r) {
-      const int it = tid + r * NT;
-      const int sg = it & 15, dc = it >> 4;
-      voff[r] = (uint32_t)first_key(sg) * vstride_b + 16u * dc;
-      vloff[r] = it < VITEMS ? (8 * dc) * VP + 4 * sg : -1;
+    for (int r = 0; r < VN; ++r) {
+      const int pos = r * NT + 64 * wave + lane, row = pos / VCH, cp = pos % VCH;
+      voff[r] = (uint32_t)row * vstride_b + 16u * (uint32_t)(cp ^ vsw(row));
+    }
+    // The swizzles of the rows read below depend on the lane only (rows
+    // 32 i + lq for K; 4 (g / 2) + j / 4 plus a multiple of 4 for V), so each
+    // read is a per-lane offset plus a constant.
+    const int lq = lane & 31, hh = lane >> 5, g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) kro[cc] = lq * KROWB + 16 * ((2 * cc + hh) ^ ksw(lq));
+    const int vrow = 4 * (g >> 1) + (j >> 2);
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d) {
+      const int dv = 32 * d + 16 * (g & 1) + 4 * (j & 3);
+      vro[d] = KSTAGE + vrow * VROWB + 16 * ((dv >> 3) ^ vsw(vrow)) + 8 * ((dv >> 2) & 1);
     }
   }
-  __device__ __forceinline__ void fetch(int j0) {
+  // tile rows [j0, j0 + BK) into the stage at dst
+  __device__ __forceinline__ void fetch(int j0, lds_char* dst) {
     const uint32_t kt = (uint32_t)j0 * kstride_b, vt = (uint32_t)j0 * vstride_b;
+    lds_char* kd = dst;
+    lds_char* vd = dst + KSTAGE;
 #pragma unroll
-    for (int r = 0; r < KMAX; ++r)
-      if (KITEMS % NT == 0 || kloff[r] >= 0) kreg[r] = buf_load16(krs, koff[r] + kt);
+    for (int r = 0; r < KN; ++r) buf_load16_lds(krs, koff[r] + kt, kd + (r * NT + 64 * wave) * 16);
 #pragma unroll
-    for (int r = 0; r < VMAX; ++r) {
-      if (VITEMS % NT == 0 || vloff[r] >= 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vreg[r][e] = buf_load16(vrs, voff[r] + vt + e * vstride_b);
-      }
-    }
+    for (int r = 0; r < VN; ++r) buf_load16_lds(vrs, voff[r] + vt, vd + (r * NT + 64 * wave) * 16);
   }
-  template <int KP, int VP>
-  __device__ __forceinline__ void stash(bf16 (*Ks)[KP], bf16 (*Vt)[VP]) {
-#pragma unroll
-    for (int r = 0; r < KMAX; ++r)
-      if (KITEMS % NT == 0 || kloff[r] >= 0) *reinterpret_cast<u32x4_t*>(&Ks[0][0] + kloff[r]) = kreg[r];
-#pragma unroll
-    for (int r = 0; r < VMAX; ++r) {
-      if (VITEMS % NT == 0 || vloff[r] >= 0) {
-        const u32x4_t* w = vreg[r];   // w[e][q]: key e, dv 2q, 2q+1
-        bf16* dst = &Vt[0][0] + vloff[r];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          // dv 8dc + t of keys e = 0..3: low half (t even) or high half (t odd) of word t/2
-          const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-          uint2 o;
-          o.x = __builtin_amdgcn_perm(w[1][t / 2], w[0][t / 2], sel);
-          o.y = __builtin_amdgcn_perm(w[3][t / 2], w[2][t / 2], sel);
-          *reinterpret_cast<uint2*>(dst + t * VP) = o;
-        }
-      }
-    }
+  __device__ __forceinline__ void stash(lds_char*) {}
+  // The B operand of S^T = K Q^T for the 16 dims of chunk c % 4 and the 32
+  // keys of half c / 4: lane l holds K[32 (c / 4) + l % 32][16 (c % 4) + 8 (l / 32) + t].
+  // Addresses are formed as the stage base plus one offset, so that the
+  // compiler sees which stage every read is in.
+  __device__ __forceinline__ Frag kfrag(const lds_char* src, int c) const {
+    const lds_char* p = src + kro[c & 3] + (c >> 2) * 32 * KROWB;
+    return __builtin_bit_cast(Frag, *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(p));
+  }
+  // The A operand of O^T = V^T P^T for dv block d and the 16 keys from key0:
+  // lane l holds V[key0 + 8(t/4) + 4(l/32) + t%4][32 d + l%32] in slot t.
+  // (key0 a multiple of 16.) In a 16-lane group g, lane j = 4 k + m points at
+  // V[key0 + 4 (g / 2) + k][32 d + 16 (g % 2) + 4 m .. + 3]; the transposing
+  // read hands lane j the 4 keys of dv 32 d + 16 (g % 2) + j.
+  __device__ __forceinline__ Frag vfrag(const lds_char* src, int d, int key0) const {
+    typedef __attribute__((address_space(3))) v4i16_t lds_v4;
+    const lds_char* p = src + vro[d] + key0 * VROWB;
+    const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)p);
+    const v4i16_t c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p + 8 * VROWB));
+    typedef short v8i16_t __attribute__((ext_vector_type(8)));
+    const v8i16_t v = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    return __builtin_bit_cast(Frag, v);
   }
 };
 
 template <int DV, int NT>
 struct TileStage<float, DV, NT> {
+  typedef F32x8 Frag;
+  static constexpr int KP = kHd + 4;     // padded K row (floats)
+  static constexpr int VP = BK + 4;      // padded V^T row (floats)
+  static constexpr int KSTAGE = BK * KP * 4, VSTAGE = DV * VP * 4;
+  static constexpr int kStageBytes = KSTAGE + VSTAGE;
   static constexpr int KCH = kHd / 4;
   static constexpr int KMAX = (BK * KCH + NT - 1) / NT;
   static constexpr int NQ = BK / 4, NC = DV / 8;
   static constexpr int VMAX = (NQ * NC + NT - 1) / NT;
   float4 kreg[KMAX];
   float vreg[VMAX][4][8];
-  int tid_, L_;
+  int tid_, L_, lane;
   const float *kbase_, *vbase_;
   int64_t kstride_, vstride_;
-  template <int KP, int VP>
+  typedef __attribute__((address_space(3))) float lds_float;
+  static __device__ __forceinline__ lds_float* Ks(lds_char* p) { return (lds_float*)p; }
+  static __device__ __forceinline__ lds_float* Vt(lds_char* p) { return (lds_float*)(p + KSTAGE); }
+  static __device__ __forceinline__ const lds_float* Ks(const lds_char* p) { return (const lds_float*)p; }
+  static __device__ __forceinline__ const lds_float* Vt(const lds_char* p) { return (const lds_float*)(p + KSTAGE); }
+  static __device__ __forceinline__ Frag frag_at(const lds_float* p) {
+    Frag f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f.v[t] = p[t];
+    return f;
+  }
   __device__ __forceinline__ void init(int tid, const float* kbase, const float* vbase, int64_t kstride,
                                        int64_t vstride, int L) {
     tid_ = tid;
+    lane = tid & 63;
     L_ = L;
     kbase_ = kbase;
     vbase_ = vbase;
     kstride_ = kstride;
     vstride_ = vstride;
   }
-  __device__ __forceinline__ void fetch(int j0) {
+  __device__ __forceinline__ void fetch(int j0, lds_char*) {
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
       const int it = tid_ + r * NT;
@@ -352,12 +381,17 @@ struct TileStage<float, DV, NT> {
       }
     }
   }
-  template <int KP, int VP>
-  __device__ __forceinline__ void stash(float (*Ks)[KP], float (*Vt)[VP]) {
+  // V stored transposed, keys permuted inside each 16-key chunk (slot s holds key kperm(s))
+  __device__ __forceinline__ void stash(lds_char* dst) {
+    lds_float* ks = Ks(dst);
+    lds_float* vt = Vt(dst);
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
       const int it = tid_ + r * NT;
-      if (it < BK * KCH) *reinterpret_cast<float4*>(&Ks[it / KCH][(it % KCH) * 4]) = kreg[r];
+      if (it < BK * KCH) {
+        lds_float* d = &ks[(it / KCH) * KP + (it % KCH) * 4];
+        d[0] = kreg[r].x; d[1] = kreg[r].y; d[2] = kreg[r].z; d[3] = kreg[r].w;
+      }
     }
 #pragma unroll
     for (int r = 0; r < VMAX; ++r) {
@@ -367,11 +401,18 @@ struct TileStage<float, DV, NT> {
         const int kk0 = 4 * kq;
         const int col = (kk0 & ~15) + kperm(kk0 & 15);  // 4 contiguous slots
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-          *reinterpret_cast<float4*>(&Vt[8 * dc + t][col]) =
-              make_float4(vreg[r][0][t], vreg[r][1][t], vreg[r][2][t], vreg[r][3][t]);
+        for (int t = 0; t < 8; ++t) {
+          lds_float* d = &vt[(8 * dc + t) * VP + col];
+          d[0] = vreg[r][0][t]; d[1] = vreg[r][1][t]; d[2] = vreg[r][2][t]; d[3] = vreg[r][3][t];
+        }
       }
     }
+  }
+  __device__ __forceinline__ Frag kfrag(const lds_char* src, int c) const {
+    return frag_at(Ks(src) + ((c >> 2) * 32 + (lane & 31)) * KP + 8 * (2 * (c & 3) + (lane >> 5)));
+  }
+  __device__ __forceinline__ Frag vfrag(const lds_char* src, int d, int key0) const {
+    return frag_at(Vt(src) + (32 * d + (lane & 31)) * VP + key0 + 8 * (lane >> 5));
   }
 };
 
@@ -464,12 +505,15 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
     int64_t k_rows, int64_t v_rows, int L, int n_meta, int window, int Hq, int Hkv, int batch, int n_cu) {
   typedef Mma<T> M;
   typedef typename M::Frag Frag;
-  constexpr int KP = AttnTile<T>::kpad;
-  constexpr int VP = AttnTile<T>::vpad;
   constexpr int NDB = DV / 32;
   constexpr int NT = 64 * kAttnWaves;
-  __shared__ __attribute__((aligned(16))) T Ks[2][BK][KP];
-  __shared__ __attribute__((aligned(16))) T Vt[2][DV][VP];
+  typedef TileStage<T, DV, NT> Stage;
+  // the two stages are separate objects, so that the compiler can tell reads
+  // of one from the loads into the other and need not wait for those
+  __shared__ __attribute__((aligned(16))) char lds_stage0[Stage::kStageBytes];
+  __shared__ __attribute__((aligned(16))) char lds_stage1[Stage::kStageBytes];
+  lds_char* const stage0 = (lds_char*)lds_stage0;
+  lds_char* const stage1 = (lds_char*)lds_stage1;
 
   const int G = Hq / Hkv;                 // query heads per kv head
   const int P = kAttnCols / G;            // positions per workgroup
@@ -528,14 +572,15 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   const int ntiles = n1 + max(0, k2e - k2s);
 
   const int64_t kstride = (int64_t)Hkv * kHd, vstride = (int64_t)Hkv * DV;
-  TileStage<T, DV, NT> stage;
-  stage.template init<KP, VP>(tid, k_rot + (b * k_rows) * kstride + g * kHd, v + (b * v_rows) * vstride + g * DV,
-                              kstride, vstride, L);
+  Stage stage;
+  stage.init(tid, k_rot + (b * k_rows) * kstride + g * kHd, v + (b * v_rows) * vstride + g * DV, kstride, vstride,
+             L);
   auto tile_j0 = [&](int idx) { return (idx < n1 ? idx : k2s + (idx - n1)) * BK; };
 
   // every workgroup has at least the tile of its own first position (ntiles >= 1)
-  stage.fetch(tile_j0(0));
-  stage.template stash<KP, VP>(Ks[0], Vt[0]);
+  stage.fetch(tile_j0(0), stage0);
+  stage.stash(stage0);
+  wait_loads();
   __syncthreads();
 
   // sub-tile [j0, j0 + 32) against this wave's positions [qa, qb): no key
@@ -563,17 +608,17 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
     st.l += (a[0] + a[1]) + (a[2] + a[3]);
   };
 
-  for (int idx = 0; idx < ntiles; ++idx) {
-    const int buf = idx & 1;
+  // one tile: scores from stage cur while the next tile loads into nxt
+  auto tile = [&](int idx, lds_char* cur, lds_char* nxt) __attribute__((always_inline)) {
     const int jt = tile_j0(idx);
-    // the next tile into registers (after the last tile: rows that are staged
-    // but never read), so that the loop body has no data-dependent branches
-    stage.fetch(tile_j0(idx + 1));
+    // the next tile (after the last tile: rows that are staged but never
+    // read), so that the loop body has no data-dependent branches
+    stage.fetch(tile_j0(idx + 1), nxt);
     if (!(none_for(jt) && none_for(jt + 32))) {
       // K operands of both sub-tiles, then both score products
       Frag kf[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) kf[c] = M::frag_at(&Ks[buf][(c >> 2) * 32 + lq][16 * (c & 3) + 8 * hh]);
+      for (int c = 0; c < 8; ++c) kf[c] = stage.kfrag(cur, c);
       f32x16_t s0 = st.negm, s1 = st.negm;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) s0 = M::mma(kf[kc], qf[kc], s0);
@@ -600,8 +645,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
       Frag va[NDB][2], pa, pb;
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
-        va[d][0] = M::frag_at(&Vt[buf][32 * d + lq][0 + 8 * hh]);
-        va[d][1] = M::frag_at(&Vt[buf][32 * d + lq][16 + 8 * hh]);
+        va[d][0] = stage.vfrag(cur, d, 0);
+        va[d][1] = stage.vfrag(cur, d, 16);
       }
       probs(s0, pa, pb);
 #pragma unroll
@@ -611,8 +656,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
       }
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
-        va[d][0] = M::frag_at(&Vt[buf][32 * d + lq][32 + 8 * hh]);
-        va[d][1] = M::frag_at(&Vt[buf][32 * d + lq][48 + 8 * hh]);
+        va[d][0] = stage.vfrag(cur, d, 32);
+        va[d][1] = stage.vfrag(cur, d, 48);
       }
       probs(s1, pa, pb);
 #pragma unroll
@@ -621,8 +666,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
         st.acc[d] = M::mma(va[d][1], pb, st.acc[d]);
       }
     }
-    stage.template stash<KP, VP>(Ks[buf ^ 1], Vt[buf ^ 1]);
+    stage.stash(nxt);
+    wait_loads();
     __syncthreads();
+  };
+  // two tiles per trip, so that each stage is a fixed object in each half
+  for (int idx = 0;;) {
+    tile(idx, stage0, stage1);
+    if (++idx >= ntiles) break;
+    tile(idx, stage1, stage0);
+    if (++idx >= ntiles) break;
   }
 
   // normalise and store: lane holds O[column][32 d + 8 jj + 4 hh + (0..3)]

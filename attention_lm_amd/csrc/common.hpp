@@ -82,8 +82,12 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off
 // 16 bytes per lane straight into LDS: lane i of the wave writes bytes
 // [16 i, 16 i + 16) from lds_base (which must be the same for the whole wave);
 // an out-of-range lane writes zeros.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               __attribute__((address_space(3))) void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, off, 0, 0, 0);
+}
 __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+  buf_load16_lds(r, off, (__attribute__((address_space(3))) void*)lds_base);
 }
 // an offset that every descriptor above treats as out of range
 constexpr uint32_t kBufferNowhere = 0x80000000u;
