@@ -262,51 +262,91 @@ __global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_kernel(
 }
 
 // carry[k] = state entering chunk k, from the chunk end states agg[k] (zero
-// start) and the chunk dt sums sdt[k]. The chain is a few dozen dependent
-// fma steps per (sequence, channel, state); what costs is memory latency, so
-// the loads of the next batch of chunks are issued before the current batch
-// is chained.
-constexpr int kCarryBatch = 48;
-__global__ __launch_bounds__(256) void ssm_chunk_carry_kernel(const float* __restrict__ A,
-                                                              const float* __restrict__ agg,
-                                                              const float* __restrict__ sdt,
-                                                              float* __restrict__ carry, int nchunk, int batch,
-                                                              int Dch) {
+// start) and the chunk dt sums sdt[k]: carry[0] = 0 and
+// carry[k+1] = exp(A sdt[k]) carry[k] + agg[k]. These affine steps compose
+// associatively, so each (sequence, channel, state) chain is cut into
+// kCarrySegs segments, one per wave of a workgroup of 64 chains. Each wave
+// composes its segment from a zero start (end state and summed dt), the waves
+// swap those through LDS, and each wave walks its segment again from its true
+// start, storing every carry. That is four times the waves of one walk per
+// chain (the chain is latency-bound: few dependent steps, all memory); the
+// second walk reuses the loaded values when a segment fits in one batch.
+constexpr int kCarrySegs = 4;
+constexpr int kCarryBatch = 24;
+__global__ __launch_bounds__(64 * kCarrySegs) void ssm_chunk_carry_kernel(const float* __restrict__ A,
+                                                                         const float* __restrict__ agg,
+                                                                         const float* __restrict__ sdt,
+                                                                         float* __restrict__ carry, int nchunk,
+                                                                         int batch, int Dch) {
   constexpr int KB = kCarryBatch;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, c, n)
+  __shared__ float seg_h[kCarrySegs][64], seg_s[kCarrySegs][64];
+  const int lane = threadIdx.x & 63;
+  const int seg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t per = (int64_t)batch * Dch * kStates;
-  if (idx >= per) return;
-  const int n = (int)(idx % kStates);
-  const int64_t bc = idx / kStates;
+  const int64_t idx = (int64_t)blockIdx.x * 64 + lane;   // chain (b, c, n)
+  const bool valid = idx < per;
+  const int64_t ci = valid ? idx : per - 1;
+  const int n = (int)(ci % kStates);
+  const int64_t bc = ci / kStates;
   const int c = (int)(bc % Dch);
   const float a2 = A[(int64_t)c * kStates + n] * kLog2e;
-  const int last = nchunk - 2;   // chunks 0 .. nchunk-2 feed a later chunk
-  carry[idx] = 0.f;
-  if (last < 0) return;
-  float av[KB], sv[KB], an[KB], sn[KB];
-  auto load = [&](int k0, float* a, float* s) {
+  const int steps = nchunk - 1;   // chunks 0 .. nchunk-2 feed a later chunk
+  const int seg_len = (steps + kCarrySegs - 1) / kCarrySegs;
+  const int k0 = min(steps, seg * seg_len), k1 = min(steps, k0 + seg_len);
+  const int nb = (k1 - k0 + KB - 1) / KB;
+  // Views of this segment's chunks (agg, sdt from chunk k0, carry from k0 + 1)
+  // sized to end with the segment: a step past it reads (agg 0, sdt 0), the
+  // identity step, and stores nothing.
+  const int64_t nseg = k1 - k0;
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(agg + k0 * per, (uint32_t)(nseg * per * sizeof(float)));
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc(sdt + k0 * (per / kStates), (uint32_t)(nseg * (per / kStates) * sizeof(float)));
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(carry + (k0 + 1) * per, (uint32_t)(nseg * per * sizeof(float)));
+  if (seg == 0 && valid) carry[idx] = 0.f;
+  auto load = [&](int kb, float* av, float* sv) {   // steps kb .. kb + KB - 1 of the segment
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      const int kk = min(k0 + i, last);
-      a[i] = agg[kk * per + idx];
-      s[i] = sdt[kk * (per / kStates) + bc];
+      const int64_t k = kb + i;
+      av[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ars, (uint32_t)((k * per + ci) * 4), 0, 0));
+      sv[i] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)((k * (per / kStates) + bc) * 4), 0, 0));
     }
   };
-  // carry-ins past the last chunk are stored out of range (dropped)
-  const __amdgpu_buffer_rsrc_t crs = make_rsrc(carry, (uint32_t)((int64_t)nchunk * per * sizeof(float)));
+  float av[KB], sv[KB], an[KB], sn[KB];
+  // first walk: the segment's own end state H and dt sum S
+  float H = 0.f, S = 0.f;
   load(0, av, sv);
-  float H = 0.f;
-  for (int k0 = 0; k0 <= last; k0 += KB) {
-    load(k0 + KB, an, sn);   // (clamped: past the end it re-reads the last chunk)
+  for (int j = 0; j < nb; ++j) {
+    if (j + 1 < nb) load((j + 1) * KB, an, sn);
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       H = fmaf(fast_exp2(a2 * sv[i]), H, av[i]);
-      buf_store(crs, (uint32_t)(((int64_t)(k0 + i + 1) * per + idx) * sizeof(float)), H);
+      S += sv[i];
     }
+    if (j + 1 < nb) {
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        av[i] = an[i];
+        sv[i] = sn[i];
+      }
+    }
+  }
+  seg_h[seg][lane] = H;
+  seg_s[seg][lane] = S;
+  __syncthreads();
+  // the state entering this segment: the earlier segments, in order
+  float H0 = 0.f;
+  for (int s = 0; s < seg; ++s) H0 = fmaf(fast_exp2(a2 * seg_s[s][lane]), H0, seg_h[s][lane]);
+  // second walk from the true start, storing carry[k + 1]
+  H = H0;
+  for (int j = 0; j < nb; ++j) {
+    const int kb = j * KB;
+    if (nb > 1) load(kb, av, sv);   // one batch: still in registers
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      av[i] = an[i];
-      sv[i] = sn[i];
+      H = fmaf(fast_exp2(a2 * sv[i]), H, av[i]);
+      const int64_t k = kb + i;
+      buf_store(crs, valid ? (uint32_t)((k * per + idx) * sizeof(float)) : kBufferNowhere, H);
     }
   }
 }
@@ -408,8 +448,8 @@ hipError_t launch_ssm_chunk_end(const SsmPrefillArgs& a, hipStream_t stream, Tim
 hipError_t launch_ssm_chunk_carry(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
   const int nchunk = (a.L + a.chunk_rows - 1) / a.chunk_rows;
   const int64_t per = (int64_t)a.batch * a.d_inner * kStates;
-  HYMBA_LAUNCH(ssm_chunk_carry_kernel, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, stream, tm, a.A, a.agg,
-                     a.sdt, a.carry, nchunk, a.batch, a.d_inner);
+  HYMBA_LAUNCH(ssm_chunk_carry_kernel, dim3((unsigned)((per + 63) / 64)), dim3(64 * kCarrySegs), 0, stream, tm,
+               a.A, a.agg, a.sdt, a.carry, nchunk, a.batch, a.d_inner);
   return hipGetLastError();
 }
 
