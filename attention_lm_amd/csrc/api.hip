@@ -103,6 +103,8 @@ int check_desc(const hymba_mixer_desc* d, bool decode) {
   const int64_t row_bytes = (int64_t)d->n_kv_heads * (d->head_dim > d->head_dim_v ? d->head_dim : d->head_dim_v) *
                             (int64_t)act_bytes(d->act);
   if (!decode && ((int64_t)d->n_meta + d->n_tokens) * row_bytes > INT32_MAX) return HYMBA_EUNSUPPORTED;
+  // decode attention likewise addresses one sequence's cache rows
+  if (decode && (int64_t)d->cache_capacity * row_bytes > INT32_MAX) return HYMBA_EUNSUPPORTED;
   // and the scan stores one sequence's y the same way
   if (!decode && ((int64_t)d->n_meta + d->n_tokens) * d->d_inner * (int64_t)act_bytes(d->act) > INT32_MAX)
     return HYMBA_EUNSUPPORTED;
@@ -312,10 +314,12 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
   aa.batch = desc->batch; aa.cap = desc->cache_capacity; aa.n_meta = desc->n_meta; aa.window = desc->window;
   aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
   aa.rope_base = desc->rope_base; aa.act = desc->act;
+  HYMBA_TRY(device_cus(&aa.n_cu));
+  aa.n_split = hymba::decode_active_splits(aa);   // <= ws.n_split partial slots
   HYMBA_TRY(hymba::launch_attn_decode(aa, stream, tm(1)));
 
   hymba::DecodeMergeArgs ma;
-  ma.partial = partial; ma.y_attn = y_attn; ma.n_split = ws.n_split; ma.batch = desc->batch;
+  ma.partial = partial; ma.y_attn = y_attn; ma.n_split = aa.n_split; ma.batch = desc->batch;
   ma.n_q_heads = desc->n_q_heads; ma.head_dim_v = desc->head_dim_v; ma.act = desc->act;
   const hymba::Timing t2 = tm(2);
   HYMBA_TRY(hymba::launch_decode_merge(ma, stream, hymba::Timing{t2.start, nullptr}));

@@ -8,6 +8,8 @@
 // global layer, every earlier row.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -157,6 +159,16 @@ constexpr float kRescaleSlack = 8.0f;
 // wait for this wave's outstanding global loads, including those that write LDS
 // (gfx9 s_waitcnt: vmcnt 0; expcnt and lgkmcnt left at their maximum)
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Workgroup barrier after LDS writes, without waiting for global loads in
+// flight (a __syncthreads() would wait for them, loads into LDS included):
+// lgkmcnt 0 (vmcnt and expcnt at their maximum), then s_barrier; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // slot s of a 16-key chunk holds key kperm(s); an involution
 __device__ __forceinline__ int kperm(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
@@ -847,6 +859,250 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
 }
 
+// bf16 decode attention on the matrix cores, flash-decoding style: one
+// workgroup of 4 waves per (split, kv head, sequence), where a split is a run
+// of 64-key tiles of the row's visible keys (meta keys first, then window
+// keys), and few splits per row: enough workgroups for about three per
+// compute unit, each streaming many tiles. Tiles go from the cache straight
+// into LDS (buffer loads with the LDS destination, 16-byte chunks of each row
+// XOR-swizzled by the row as in the prefill tiles), double-buffered, so that
+// the next tile loads while this one is used; the new row p, not in the
+// cache, is written into its tile from the rotated k and v_new. Every wave
+// scores the tile against the group's query heads (S^T = K Q^T, the heads as
+// MFMA columns padded to 32) and keeps an online softmax; wave w accumulates
+// the 32-wide dv blocks w, w + 4, ... of O^T = V^T P^T, V's operand coming
+// from transposing LDS reads. Writes the same partials (o, m, l) as
+// attn_decode_kernel, one per split.
+constexpr int kDecodeTile = 64;
+
+template <int DV>
+__global__ __launch_bounds__(256) void attn_decode_flash_kernel(
+    const float* __restrict__ q_rot, const float* __restrict__ k_rot, const bf16* __restrict__ v_new,
+    const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
+    float* __restrict__ partial, int n_split, int cap, int n_meta, int window, int Hq, int Hkv) {
+  constexpr int BT = kDecodeTile;
+  constexpr int NT = 256;
+  constexpr int KROWB = kHd * 2, VROWB = DV * 2;        // bytes per K / V row
+  constexpr int KCH = KROWB / 16, VCH = VROWB / 16;     // 16-byte chunks per row
+  constexpr int KN = BT * KCH / NT, VN = BT * VCH / NT; // loads per thread per tile
+  constexpr int KSTAGE = BT * KROWB, STAGE = KSTAGE + BT * VROWB;
+  constexpr int NDB = DV / 32;                          // 32-wide dv blocks
+  constexpr int VRPB = VROWB >= 256 ? 1 : 256 / VROWB;  // V rows per 256-byte bank sweep
+  static_assert(BT * KCH % NT == 0 && BT * VCH % NT == 0 && BT == 64, "tile shape");
+  // the stages are separate objects, so that the compiler can tell reads of
+  // one from the loads into the other
+  __shared__ __attribute__((aligned(16))) char lds_stage0[STAGE];
+  __shared__ __attribute__((aligned(16))) char lds_stage1[STAGE];
+  lds_char* const stage0 = (lds_char*)lds_stage0;
+  lds_char* const stage1 = (lds_char*)lds_stage1;
+  auto ksw = [](int row) { return (row >> 1) & (KCH - 1); };
+  auto vsw = [](int row) { return (4 * ((row & 3) / VRPB)) & (VCH - 1); };
+
+  const int s = blockIdx.x, g = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int group = Hq / Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hh = lane >> 5;
+  const int p = clamp_pos(cache_len[b], cap);
+  const MaskRange mr = mask_range(p, n_meta, window);
+  const int n_vis = mr.meta_end + (mr.win_end - mr.win_begin);
+  const int n_tiles = (n_vis + BT - 1) / BT;
+  const int per = (n_tiles + n_split - 1) / n_split;
+  const int t0 = min(n_tiles, s * per), t1 = min(n_tiles, t0 + per);
+  float* outp = partial + (((b * Hq) + g * group) * n_split + s) * (DV + 2);
+  const int64_t pstride = (int64_t)n_split * (DV + 2);  // between query heads
+  if (t0 >= t1) {   // (whole workgroup, before any barrier)
+    for (int t = tid; t < group * (DV + 2); t += blockDim.x) {
+      const int hq = t / (DV + 2), e = t % (DV + 2);
+      outp[hq * pstride + e] = e == DV ? -INFINITY : 0.f;
+    }
+    return;
+  }
+  auto key_row = [&](int vi) { return vi < mr.meta_end ? vi : mr.win_begin + (vi - mr.meta_end); };
+  const int vi_new = n_vis - 1;   // the new row p is the last visible key
+
+  // Tile t: row r is visible key 64 t + r. Rows past the visible keys and the
+  // new row read as zeros here (offset out of range).
+  const uint32_t kv_row = (uint32_t)Hkv * KROWB, vv_row = (uint32_t)Hkv * VROWB;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k_cache + b * cap * Hkv * kHd, (uint32_t)cap * kv_row);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v_cache + b * cap * Hkv * DV, (uint32_t)cap * vv_row);
+  auto fetch = [&](int t, lds_char* dst) {
+#pragma unroll
+    for (int r = 0; r < KN; ++r) {
+      const int it = r * NT + tid, row = it / KCH, cp = it % KCH, vi = BT * t + row;
+      const bool in = vi < vi_new;
+      const uint32_t off =
+          in ? (uint32_t)key_row(vi) * kv_row + (uint32_t)(g * KROWB + 16 * (cp ^ ksw(row))) : kBufferNowhere;
+      buf_load16_lds(krs, off, dst + (r * NT + 64 * wave) * 16);
+    }
+#pragma unroll
+    for (int r = 0; r < VN; ++r) {
+      const int it = r * NT + tid, row = it / VCH, cp = it % VCH, vi = BT * t + row;
+      const bool in = vi < vi_new;
+      const uint32_t off =
+          in ? (uint32_t)key_row(vi) * vv_row + (uint32_t)(g * VROWB + 16 * (cp ^ vsw(row))) : kBufferNowhere;
+      buf_load16_lds(vrs, off, dst + KSTAGE + (r * NT + 64 * wave) * 16);
+    }
+  };
+
+  // Q^T operand: lane (column lq = query head of the group, half hh) holds
+  // Q[16 kc + 8 hh .. +7] scaled by log2(e)/sqrt(64); columns past the group are zero
+  typedef Mma<bf16> M;
+  fetch(t0, stage0);
+  M::Frag qf[4];
+  {
+    const bool qv = lq < group;
+    const float sc = qv ? kScaleLog2e : 0.f;   // (a column past the group reads head 0 and zeroes it)
+    const float* qrow = q_rot + (b * Hq + g * group + (qv ? lq : 0)) * kHd;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      float v8[8];
+      load16(qrow + 16 * kc + 8 * hh, v8);
+      load16(qrow + 16 * kc + 8 * hh + 4, v8 + 4);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v8[t] *= sc;
+      qf[kc] = M::from_f32(v8);
+    }
+  }
+  // per-lane LDS offsets of the operand reads (the swizzles depend on the lane only)
+  const int kro = lq * KROWB + 16 * (hh ^ ksw(lq));
+  const int gi = lane >> 4, jj = lane & 15;
+  const int vrow = 4 * (gi >> 1) + (jj >> 2);
+  const int vdv = 16 * (gi & 1) + 4 * (jj & 3);
+  const int vro = KSTAGE + vrow * VROWB + 16 * ((vdv >> 3) ^ vsw(vrow)) + 8 * ((vdv >> 2) & 1);
+  typedef __attribute__((address_space(3))) v4i16_t lds_v4;
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  typedef short v8i16_t __attribute__((ext_vector_type(8)));
+
+  constexpr int NDW = (NDB + 3) / 4;   // dv blocks per wave (some waves have none when NDB < 4)
+  f32x16_t acc[NDW];
+#pragma unroll
+  for (int i = 0; i < NDW; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  // the new row's K (rotated, fp32 -> bf16) and V chunks, loaded now so that
+  // writing them into their tile later waits for nothing else
+  const bool has_new = vi_new / BT < t1;   // (then it is in this split's last tile)
+  M::Frag new_k = M::zero();
+  u32x4_t new_v = {0u, 0u, 0u, 0u};
+  if (has_new) {
+    if (tid < KCH) {
+      float v8[8];
+      load16(k_rot + (b * Hkv + g) * kHd + 8 * tid, v8);
+      load16(k_rot + (b * Hkv + g) * kHd + 8 * tid + 4, v8 + 4);
+      new_k = M::from_f32(v8);
+    } else if (tid < KCH + VCH) {
+      new_v = *reinterpret_cast<const u32x4_t*>(v_new + (b * Hkv + g) * DV + 8 * (tid - KCH));
+    }
+  }
+  wait_loads();
+  __syncthreads();
+
+  auto tile = [&](int t, lds_char* cur, lds_char* nxt) __attribute__((always_inline)) {
+    fetch(t + 1, nxt);   // (past the split: rows that are loaded and never used)
+    const int vbase = BT * t;
+    if (has_new && vi_new - vbase < BT) {   // the new row's K and V into this tile
+      const int rn = vi_new - vbase;
+      if (tid < KCH)
+        *(__attribute__((address_space(3))) M::Frag*)(cur + rn * KROWB + 16 * (tid ^ ksw(rn))) = new_k;
+      else if (tid < KCH + VCH)
+        *(lds_u32x4*)(cur + KSTAGE + rn * VROWB + 16 * ((tid - KCH) ^ vsw(rn))) = new_v;
+      lds_barrier();
+    }
+    // scores: lane holds keys 32 h2 + 8 (r / 4) + 4 hh + r % 4 of column lq
+    f32x16_t sc[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[h2][r] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const M::Frag kf =
+            __builtin_bit_cast(M::Frag, *(const lds_u32x4*)(cur + ((kro ^ (kc << 5)) + h2 * 32 * KROWB)));
+        sc[h2] = M::mma(kf, qf[kc], sc[h2]);
+      }
+    }
+    // keys past the visible ones (last tile only); online softmax of the column
+    float tmx = -INFINITY;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = vbase + 32 * h2 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        sc[h2][r] = key < n_vis ? sc[h2][r] : -INFINITY;
+        tmx = fmaxf(tmx, sc[h2][r]);
+      }
+    tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));   // a tile has a visible key: finite
+    const float mn = fmaxf(m, tmx);
+    const float alpha = fast_exp2(m - mn);       // 0 on the first tile
+    m = mn;
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < NDW; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+    M::Frag pf[4];   // P^T operands, 16 keys each
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      float pv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pv[r] = fast_exp2(sc[h2][r] - m);
+        l += pv[r];
+      }
+      pf[2 * h2] = M::from_f32(&pv[0]);
+      pf[2 * h2 + 1] = M::from_f32(&pv[8]);
+    }
+    // O^T blocks of this wave; in each 16-lane group gi, lane j = 4 k + q reads
+    // V[key0 + 4 (gi / 2) + k][32 d + 16 (gi % 2) + 4 q .. + 3] (transposed to lane j)
+#pragma unroll
+    for (int i = 0; i < NDW; ++i) {
+      const int d = wave + 4 * i;
+      if (d < NDB) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const lds_char* vp = cur + ((vro ^ (d << 6)) + 16 * kk * VROWB);
+          const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)vp);
+          const v4i16_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp + 8 * VROWB));
+          const v8i16_t v8 = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+          acc[i] = M::mma(__builtin_bit_cast(M::Frag, v8), pf[kk], acc[i]);
+        }
+      }
+    }
+    wait_loads();
+    __syncthreads();
+  };
+  // two tiles per trip, so that each stage is a fixed object in each half
+  for (int t = t0;;) {
+    tile(t, stage0, stage1);
+    if (++t >= t1) break;
+    tile(t, stage1, stage0);
+    if (++t >= t1) break;
+  }
+
+  l += __shfl_xor(l, 32, 64);
+  if (lq < group) {
+#pragma unroll
+    for (int i = 0; i < NDW; ++i) {
+      const int d = wave + 4 * i;
+      if (d < NDB) {
+        float* o = outp + lq * pstride + 32 * d + 4 * hh;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(o + 8 * q4) =
+              make_float4(acc[i][4 * q4], acc[i][4 * q4 + 1], acc[i][4 * q4 + 2], acc[i][4 * q4 + 3]);
+      }
+    }
+    if (wave == 0 && hh == 0) {
+      outp[lq * pstride + DV] = m;
+      outp[lq * pstride + DV + 1] = l;
+    }
+  }
+}
+
 // Merge the chunk partials of one (query head, sequence): y = sum_s o_s 2^(m_s-m) / sum_s l_s 2^(m_s-m).
 template <typename T, int DV>
 __global__ __launch_bounds__(DV) void decode_merge_kernel(const float* __restrict__ partial, T* __restrict__ y,
@@ -900,9 +1156,14 @@ hipError_t attn_decode_t(const AttnDecodeArgs& a, hipStream_t stream, Timing tm)
                      a.rope_base);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  HYMBA_LAUNCH((attn_decode_kernel<T, DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream, t_last,
-                     a.q_rot, a.k_rot, (const T*)a.v_new, (const T*)a.k_cache, (const T*)a.v_cache, a.cache_len,
-                     a.partial, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads, a.n_kv_heads);
+  if constexpr (sizeof(T) == 2)
+    HYMBA_LAUNCH((attn_decode_flash_kernel<DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream, t_last,
+                 a.q_rot, a.k_rot, (const bf16*)a.v_new, (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.cache_len,
+                 a.partial, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads, a.n_kv_heads);
+  else
+    HYMBA_LAUNCH((attn_decode_kernel<T, DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream, t_last,
+                 a.q_rot, a.k_rot, (const T*)a.v_new, (const T*)a.k_cache, (const T*)a.v_cache, a.cache_len,
+                 a.partial, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads, a.n_kv_heads);
   return hipGetLastError();
 }
 
@@ -933,12 +1194,29 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream, Tim
   HYMBA_DISPATCH_DV(a.head_dim_v, attn_prefill_t, float, a, stream, tm)
 }
 
-void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_per_split) {
-  // most keys a decode row can see: meta + window (SWA), or the whole cache + itself
+// most keys a decode row can see: meta + window (SWA), or the whole cache + itself
+static int64_t decode_max_visible(int n_meta, int window, int cap) {
   int64_t max_vis = (int64_t)cap + 1;
   if (window > 0 && (int64_t)n_meta + window < max_vis) max_vis = (int64_t)n_meta + window;
-  *keys_per_split = kKeysPerSplit;
-  *n_split = (int)((max_vis + kKeysPerSplit - 1) / kKeysPerSplit);
+  return max_vis;
+}
+
+void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_per_split) {
+  // room for one partial per 64-key tile: the most splits any launch uses
+  const int64_t max_vis = decode_max_visible(n_meta, window, cap);
+  *keys_per_split = kDecodeTile;
+  *n_split = (int)((max_vis + kDecodeTile - 1) / kDecodeTile);
+}
+
+int decode_active_splits(const AttnDecodeArgs& a) {
+  const int64_t max_vis = decode_max_visible(a.n_meta, a.window, a.cap);
+  if (a.act != HYMBA_BF16)   // one split per kKeysPerSplit keys
+    return (int)((max_vis + kKeysPerSplit - 1) / kKeysPerSplit);
+  // about three workgroups per compute unit, each streaming whole tiles
+  const int64_t tiles = (max_vis + kDecodeTile - 1) / kDecodeTile;
+  const int64_t rows = (int64_t)a.batch * a.n_kv_heads;
+  const int64_t want = std::max<int64_t>(1, (3 * (int64_t)a.n_cu) / std::max<int64_t>(1, rows));
+  return (int)std::min(tiles, want);
 }
 
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream, Timing tm) {

@@ -98,13 +98,17 @@ struct AttnDecodeArgs {
   float* q_rot;                        // workspace [batch, Hq, 64]
   float* k_rot;                        // workspace [batch, Hkv, 64]
   float* partial;                      // [batch, Hq, n_split, dv + 2]
-  int n_split, keys_per_split;
+  int n_split, keys_per_split;         // n_split: splits of this launch (decode_active_splits)
+  int n_cu;                            // compute units of the device (split count)
   int batch, cap, n_meta, window, n_q_heads, n_kv_heads, head_dim_v;
   float rope_base;
   hymba_dtype act;
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream, Timing tm = {});
+// partial slots per (sequence, query head) the workspace holds: enough for any launch
 void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_per_split);
+// splits (partials per head) one launch uses, at most the plan's slot count
+int decode_active_splits(const AttnDecodeArgs& a);
 
 struct DecodeMergeArgs {
   const float* partial;    // [batch, Hq, n_split, dv + 2]
