@@ -103,6 +103,8 @@ int check_desc(const hymba_mixer_desc* d, bool decode) {
   const int64_t row_bytes = (int64_t)d->n_kv_heads * (d->head_dim > d->head_dim_v ? d->head_dim : d->head_dim_v) *
                             (int64_t)act_bytes(d->act);
   if (!decode && ((int64_t)d->n_meta + d->n_tokens) * row_bytes > INT32_MAX) return HYMBA_EUNSUPPORTED;
+  // the decode epilogue keeps one sequence's row in the registers of one workgroup
+  if (decode && d->d_inner > 16384) return HYMBA_EUNSUPPORTED;
   // decode attention likewise addresses one sequence's cache rows
   if (decode && (int64_t)d->cache_capacity * row_bytes > INT32_MAX) return HYMBA_EUNSUPPORTED;
   // and the scan stores one sequence's y the same way
@@ -300,6 +302,8 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
     }
     return t;
   };
+  // (one stream: the step's kernels are a few µs each, and a fork/join across
+  // two streams measured ~10 µs slower per call than running them in order)
   hymba::SsmDecodeArgs sa;
   sa.x = x; sa.z = z; sa.dt = dt; sa.B = B; sa.C = C;
   sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
@@ -318,13 +322,12 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
   aa.n_split = hymba::decode_active_splits(aa);   // <= ws.n_split partial slots
   HYMBA_TRY(hymba::launch_attn_decode(aa, stream, tm(1)));
 
-  hymba::DecodeMergeArgs ma;
-  ma.partial = partial; ma.y_attn = y_attn; ma.n_split = aa.n_split; ma.batch = desc->batch;
-  ma.n_q_heads = desc->n_q_heads; ma.head_dim_v = desc->head_dim_v; ma.act = desc->act;
-  const hymba::Timing t2 = tm(2);
-  HYMBA_TRY(hymba::launch_decode_merge(ma, stream, hymba::Timing{t2.start, nullptr}));
-  HYMBA_TRY(hymba::launch_fuse(y_attn, y_ssm, params->beta_attn, params->beta_ssm, desc->batch, desc->d_inner,
-                               desc->norm_eps, desc->act, out, stream, hymba::Timing{nullptr, t2.stop}));
+  hymba::DecodeCombineArgs ca;
+  ca.partial = partial; ca.y_ssm = y_ssm; ca.beta_attn = params->beta_attn; ca.beta_ssm = params->beta_ssm;
+  ca.eps = desc->norm_eps; ca.y_attn = y_attn; ca.out = out;
+  ca.n_split = aa.n_split; ca.batch = desc->batch; ca.n_q_heads = desc->n_q_heads;
+  ca.head_dim_v = desc->head_dim_v; ca.act = desc->act;
+  HYMBA_TRY(hymba::launch_decode_combine(ca, stream, tm(2)));
   return HYMBA_OK;
 }
 

@@ -1103,26 +1103,115 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
   }
 }
 
-// Merge the chunk partials of one (query head, sequence): y = sum_s o_s 2^(m_s-m) / sum_s l_s 2^(m_s-m).
+// Decode epilogue, one workgroup per sequence: merge the split partials of
+// every query head, y = sum_s o_s 2^(m_s - m) / sum_s l_s 2^(m_s - m), write
+// the attention output and fuse it with the Mamba output as the prefill fusion
+// does (RMS-normalise each branch over the row, scale by the betas, average),
+// from the merged values in registers.
+constexpr int kCombineMaxThreads = 1024;
+constexpr int kCombineItems = 4;   // (head, 4 dv) items per thread: up to 16384 channels
+
 template <typename T, int DV>
-__global__ __launch_bounds__(DV) void decode_merge_kernel(const float* __restrict__ partial, T* __restrict__ y,
-                                                          int n_split, int Hq) {
-  const int h = blockIdx.x;
-  const int64_t b = blockIdx.y;
-  const int d = threadIdx.x;
-  const float* ph = partial + ((b * Hq) + h) * (int64_t)n_split * (DV + 2);
-  float m = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < n_split; ++s) m = fmaxf(m, ph[s * (DV + 2) + DV]);
-  float l = 0.f, o = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < n_split; ++s) {
-    const float ms = ph[s * (DV + 2) + DV];
-    const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - m);   // empty chunks weigh nothing
-    l = fmaf(ph[s * (DV + 2) + DV + 1], f, l);
-    o = fmaf(ph[s * (DV + 2) + d], f, o);
+__global__ __launch_bounds__(kCombineMaxThreads) void decode_combine_kernel(
+    const float* __restrict__ partial, const T* __restrict__ ys, const float* __restrict__ ba,
+    const float* __restrict__ bs, float eps, int n_split, int Hq, T* __restrict__ y_attn, T* __restrict__ out) {
+  constexpr int NQ = DV / 4;
+  __shared__ float red[2][kCombineMaxThreads / 64];
+  const int64_t b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;   // whole waves
+  const int width = Hq * DV;
+  const int n_items = Hq * NQ;
+  float ya[kCombineItems][4], yv[kCombineItems][4], bav[kCombineItems][4], bsv[kCombineItems][4];
+  float sa = 0.f, ss = 0.f;
+  // the Mamba output and the betas first: their loads overlap the merge's
+#pragma unroll
+  for (int k = 0; k < kCombineItems; ++k) {
+    const int it = tid + k * nt;
+    if (it < n_items) {
+      const int c = (it / NQ) * DV + 4 * (it % NQ);
+      if constexpr (sizeof(T) == 2) {
+        const uint2 w2 = *reinterpret_cast<const uint2*>(ys + b * width + c);
+        yv[k][0] = bf16_lo(w2.x); yv[k][1] = bf16_hi(w2.x); yv[k][2] = bf16_lo(w2.y); yv[k][3] = bf16_hi(w2.y);
+      } else {
+        load16(ys + b * width + c, yv[k]);
+      }
+      load16(ba + c, bav[k]);
+      load16(bs + c, bsv[k]);
+    }
   }
-  y[(b * Hq + h) * DV + d] = from_f32<T>(o / l);
+#pragma unroll
+  for (int k = 0; k < kCombineItems; ++k) {
+    const int it = tid + k * nt;
+    if (it < n_items) {
+      const int h = it / NQ, dq = it % NQ;
+      const float* ph = partial + ((b * Hq) + h) * (int64_t)n_split * (DV + 2);
+      float m = -INFINITY;
+#pragma unroll 4
+      for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, ph[sp * (DV + 2) + DV]);
+      float l = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+#pragma unroll 4
+      for (int sp = 0; sp < n_split; ++sp) {
+        const float* q = ph + sp * (DV + 2);
+        const float ms = q[DV];
+        const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - m);   // empty splits weigh nothing
+        const float4 o4 = *reinterpret_cast<const float4*>(q + 4 * dq);
+        l = fmaf(q[DV + 1], f, l);
+        o0 = fmaf(o4.x, f, o0); o1 = fmaf(o4.y, f, o1); o2 = fmaf(o4.z, f, o2); o3 = fmaf(o4.w, f, o3);
+      }
+      const float il = 1.0f / l;
+      ya[k][0] = o0 * il; ya[k][1] = o1 * il; ya[k][2] = o2 * il; ya[k][3] = o3 * il;
+      const int c = h * DV + 4 * dq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sa = fmaf(ya[k][e], ya[k][e], sa);
+        ss = fmaf(yv[k][e], yv[k][e], ss);
+      }
+      float w4[8] = {ya[k][0], ya[k][1], ya[k][2], ya[k][3], 0.f, 0.f, 0.f, 0.f};
+      if constexpr (sizeof(T) == 2) {
+        uint2 w2;
+        w2.x = pack_bf16x2(w4[0], w4[1]);
+        w2.y = pack_bf16x2(w4[2], w4[3]);
+        *reinterpret_cast<uint2*>(y_attn + b * width + c) = w2;
+      } else {
+        store16(y_attn + b * width + c, w4);
+      }
+    }
+  }
+  sa = wave_sum(sa);
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = sa;
+    red[1][tid >> 6] = ss;
+  }
+  __syncthreads();
+  sa = 0.f;
+  ss = 0.f;
+  for (int w = 0; w < nt / 64; ++w) {
+    sa += red[0][w];
+    ss += red[1][w];
+  }
+  const float inv_w = 1.0f / (float)width;
+  const float ra = 0.5f / sqrtf(sa * inv_w + eps);
+  const float rs = 0.5f / sqrtf(ss * inv_w + eps);
+#pragma unroll
+  for (int k = 0; k < kCombineItems; ++k) {
+    const int it = tid + k * nt;
+    if (it < n_items) {
+      const int c = (it / NQ) * DV + 4 * (it % NQ);
+      float r[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = fmaf(bav[k][e] * ra, ya[k][e], bsv[k][e] * rs * yv[k][e]);
+      if constexpr (sizeof(T) == 2) {
+        uint2 w2;
+        w2.x = pack_bf16x2(r[0], r[1]);
+        w2.y = pack_bf16x2(r[2], r[3]);
+        *reinterpret_cast<uint2*>(out + b * width + c) = w2;
+      } else {
+        store16(out + b * width + c, r);
+      }
+    }
+  }
 }
 
 template <typename T>
@@ -1168,9 +1257,13 @@ hipError_t attn_decode_t(const AttnDecodeArgs& a, hipStream_t stream, Timing tm)
 }
 
 template <typename T, int DV>
-hipError_t merge_t(const DecodeMergeArgs& a, hipStream_t stream, Timing tm) {
-  HYMBA_LAUNCH((decode_merge_kernel<T, DV>), dim3(a.n_q_heads, a.batch), dim3(DV), 0, stream, tm, a.partial,
-                     (T*)a.y_attn, a.n_split, a.n_q_heads);
+hipError_t combine_t(const DecodeCombineArgs& a, hipStream_t stream, Timing tm) {
+  // whole waves, kCombineItems (head, 4 dv) items per thread
+  const int n_items = a.n_q_heads * (DV / 4);
+  const int threads = std::max(64, (n_items + 64 * kCombineItems - 1) / (64 * kCombineItems) * 64);
+  if (threads > kCombineMaxThreads) return hipErrorInvalidValue;
+  HYMBA_LAUNCH((decode_combine_kernel<T, DV>), dim3(a.batch), dim3(threads), 0, stream, tm, a.partial,
+               (const T*)a.y_ssm, a.beta_attn, a.beta_ssm, a.eps, a.n_split, a.n_q_heads, (T*)a.y_attn, (T*)a.out);
   return hipGetLastError();
 }
 
@@ -1224,9 +1317,9 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream, Timin
   HYMBA_DISPATCH_DV(a.head_dim_v, attn_decode_t, float, a, stream, tm)
 }
 
-hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream, Timing tm) {
-  if (a.act == HYMBA_BF16) { HYMBA_DISPATCH_DV(a.head_dim_v, merge_t, bf16, a, stream, tm) }
-  HYMBA_DISPATCH_DV(a.head_dim_v, merge_t, float, a, stream, tm)
+hipError_t launch_decode_combine(const DecodeCombineArgs& a, hipStream_t stream, Timing tm) {
+  if (a.act == HYMBA_BF16) { HYMBA_DISPATCH_DV(a.head_dim_v, combine_t, bf16, a, stream, tm) }
+  HYMBA_DISPATCH_DV(a.head_dim_v, combine_t, float, a, stream, tm)
 }
 
 }  // namespace hymba

@@ -110,12 +110,17 @@ void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_
 // splits (partials per head) one launch uses, at most the plan's slot count
 int decode_active_splits(const AttnDecodeArgs& a);
 
-struct DecodeMergeArgs {
+// decode epilogue: merge of the split partials + fusion with the Mamba output
+struct DecodeCombineArgs {
   const float* partial;    // [batch, Hq, n_split, dv + 2]
-  void* y_attn;            // [batch, Hq * dv] act
+  const void* y_ssm;       // [batch, Hq * dv] act
+  const float *beta_attn, *beta_ssm;
+  float eps;
+  void* y_attn;            // out [batch, Hq * dv] act
+  void* out;               // out [batch, Hq * dv] act
   int n_split, batch, n_q_heads, head_dim_v;
   hymba_dtype act;
 };
-hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream, Timing tm = {});
+hipError_t launch_decode_combine(const DecodeCombineArgs& a, hipStream_t stream, Timing tm = {});
 
 }  // namespace hymba
