@@ -34,13 +34,6 @@ __device__ __forceinline__ void load8(const bf16* p, float* o) { load16(p, o); }
 __device__ __forceinline__ void load8(const float* p, float* o) { load16(p, o); load16(p + 4, o + 4); }
 __device__ __forceinline__ void store8(bf16* p, const float* o) { store16(p, o); }
 __device__ __forceinline__ void store8(float* p, const float* o) { store16(p, o); store16(p + 4, o + 4); }
-__device__ __forceinline__ void copy8(const bf16* s, bf16* d) {
-  *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
-}
-__device__ __forceinline__ void copy8(const float* s, float* d) {
-  *reinterpret_cast<float4*>(d) = *reinterpret_cast<const float4*>(s);
-  *reinterpret_cast<float4*>(d + 4) = *reinterpret_cast<const float4*>(s + 4);
-}
 
 // cos/sin of pos * base^(-2i/64), angle formed and reduced in fp64.
 __device__ __forceinline__ void rope_cs(int pos, int i, float base, float* c, float* s) {
@@ -872,14 +865,16 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 // MFMA columns padded to 32) and keeps an online softmax; wave w accumulates
 // the 32-wide dv blocks w, w + 4, ... of O^T = V^T P^T, V's operand coming
 // from transposing LDS reads. Writes the same partials (o, m, l) as
-// attn_decode_kernel, one per split.
+// attn_decode_kernel, one per split. The rotation of q and of the new key to
+// position p is done here, from cos/sin formed once per workgroup while the
+// first tile loads.
 constexpr int kDecodeTile = 64;
 
 template <int DV>
 __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
-    const float* __restrict__ q_rot, const float* __restrict__ k_rot, const bf16* __restrict__ v_new,
+    const bf16* __restrict__ q, const bf16* __restrict__ k_new, const bf16* __restrict__ v_new,
     const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
-    float* __restrict__ partial, int n_split, int cap, int n_meta, int window, int Hq, int Hkv) {
+    float* __restrict__ partial, int n_split, int cap, int n_meta, int window, int Hq, int Hkv, float base) {
   constexpr int BT = kDecodeTile;
   constexpr int NT = 256;
   constexpr int KROWB = kHd * 2, VROWB = DV * 2;        // bytes per K / V row
@@ -893,6 +888,7 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
   // one from the loads into the other
   __shared__ __attribute__((aligned(16))) char lds_stage0[STAGE];
   __shared__ __attribute__((aligned(16))) char lds_stage1[STAGE];
+  __shared__ float rope_c[kHd / 2], rope_s[kHd / 2];
   lds_char* const stage0 = (lds_char*)lds_stage0;
   lds_char* const stage1 = (lds_char*)lds_stage1;
   auto ksw = [](int row) { return (row >> 1) & (KCH - 1); };
@@ -947,23 +943,52 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
     }
   };
 
-  // Q^T operand: lane (column lq = query head of the group, half hh) holds
-  // Q[16 kc + 8 hh .. +7] scaled by log2(e)/sqrt(64); columns past the group are zero
   typedef Mma<bf16> M;
   fetch(t0, stage0);
+  // raw q of this lane's column and (threads < KCH) the new key's dims 8 tid ..
+  // and their rotation partners, loaded while cos/sin of position p are formed
+  const bool qv = lq < group;   // (a column past the group reads head 0 and ends up zero)
+  const bf16* qrow = q + (b * Hq + g * group + (qv ? lq : 0)) * kHd;
+  u32x4_t qraw[4];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) qraw[kc] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * kc + 8 * hh);
+  const bool has_new = vi_new / BT < t1;   // (then it is in this split's last tile)
+  u32x4_t kraw = {0u, 0u, 0u, 0u}, kpart = {0u, 0u, 0u, 0u};
+  u32x4_t new_v = {0u, 0u, 0u, 0u};
+  if (has_new) {
+    const bf16* krow = k_new + (b * Hkv + g) * kHd;
+    if (tid < KCH) {
+      kraw = *reinterpret_cast<const u32x4_t*>(krow + 8 * tid);
+      kpart = *reinterpret_cast<const u32x4_t*>(krow + 8 * (tid ^ (KCH / 2)));
+    } else if (tid < KCH + VCH) {
+      new_v = *reinterpret_cast<const u32x4_t*>(v_new + (b * Hkv + g) * DV + 8 * (tid - KCH));
+    }
+  }
+  if (tid < kHd / 2) rope_cs(p, tid, base, &rope_c[tid], &rope_s[tid]);
+  __syncthreads();
+  // Q^T operand: lane (column lq = query head of the group, half hh) holds the
+  // rotated Q[16 kc + 8 hh .. +7] scaled by log2(e)/sqrt(64): dims i and i + 32
+  // (chunks kc and kc + 2) are a rotation pair, both in this lane
   M::Frag qf[4];
   {
-    const bool qv = lq < group;
-    const float sc = qv ? kScaleLog2e : 0.f;   // (a column past the group reads head 0 and zeroes it)
-    const float* qrow = q_rot + (b * Hq + g * group + (qv ? lq : 0)) * kHd;
+    const float sc = qv ? kScaleLog2e : 0.f;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      float v8[8];
-      load16(qrow + 16 * kc + 8 * hh, v8);
-      load16(qrow + 16 * kc + 8 * hh + 4, v8 + 4);
+    for (int kc = 0; kc < 2; ++kc) {
+      float lo[8], hi[8], olo[8], ohi[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) v8[t] *= sc;
-      qf[kc] = M::from_f32(v8);
+      for (int e = 0; e < 4; ++e) {
+        lo[2 * e] = bf16_lo(qraw[kc][e]); lo[2 * e + 1] = bf16_hi(qraw[kc][e]);
+        hi[2 * e] = bf16_lo(qraw[kc + 2][e]); hi[2 * e + 1] = bf16_hi(qraw[kc + 2][e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 16 * kc + 8 * hh + e;
+        const float c = rope_c[i], sn = rope_s[i];
+        olo[e] = (lo[e] * c - hi[e] * sn) * sc;
+        ohi[e] = (hi[e] * c + lo[e] * sn) * sc;
+      }
+      qf[kc] = M::from_f32(olo);
+      qf[kc + 2] = M::from_f32(ohi);
     }
   }
   // per-lane LDS offsets of the operand reads (the swizzles depend on the lane only)
@@ -983,20 +1008,23 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
   float m = -INFINITY, l = 0.f;
-  // the new row's K (rotated, fp32 -> bf16) and V chunks, loaded now so that
-  // writing them into their tile later waits for nothing else
-  const bool has_new = vi_new / BT < t1;   // (then it is in this split's last tile)
+  // the new key rotated (threads < KCH: dims 8 tid .. + 7), written into its
+  // tile later, when that tile is current
   M::Frag new_k = M::zero();
-  u32x4_t new_v = {0u, 0u, 0u, 0u};
-  if (has_new) {
-    if (tid < KCH) {
-      float v8[8];
-      load16(k_rot + (b * Hkv + g) * kHd + 8 * tid, v8);
-      load16(k_rot + (b * Hkv + g) * kHd + 8 * tid + 4, v8 + 4);
-      new_k = M::from_f32(v8);
-    } else if (tid < KCH + VCH) {
-      new_v = *reinterpret_cast<const u32x4_t*>(v_new + (b * Hkv + g) * DV + 8 * (tid - KCH));
+  if (has_new && tid < KCH) {
+    float x[8], xp[8], o[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_lo(kraw[e]); x[2 * e + 1] = bf16_hi(kraw[e]);
+      xp[2 * e] = bf16_lo(kpart[e]); xp[2 * e + 1] = bf16_hi(kpart[e]);
     }
+    const bool low = tid < KCH / 2;   // dims below 32: x' = x c - x_{+32} s, else x c + x_{-32} s
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = (8 * tid + e) & (kHd / 2 - 1);
+      o[e] = low ? x[e] * rope_c[i] - xp[e] * rope_s[i] : x[e] * rope_c[i] + xp[e] * rope_s[i];
+    }
+    new_k = M::from_f32(o);
   }
   wait_loads();
   __syncthreads();
@@ -1239,18 +1267,21 @@ hipError_t attn_decode_t(const AttnDecodeArgs& a, hipStream_t stream, Timing tm)
   Timing t_first, t_last;   // the stage's start on its first kernel, its end on its last
   t_first.start = tm.start;
   t_last.stop = tm.stop;
+  if constexpr (sizeof(T) == 2) {
+    // rotation inside the attention kernel: one launch for the stage
+    HYMBA_LAUNCH((attn_decode_flash_kernel<DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream, tm,
+                 (const bf16*)a.q, (const bf16*)a.k_new, (const bf16*)a.v_new, (const bf16*)a.k_cache,
+                 (const bf16*)a.v_cache, a.cache_len, a.partial, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads,
+                 a.n_kv_heads, a.rope_base);
+    return hipGetLastError();
+  }
   const int64_t n = (int64_t)a.batch * (a.n_q_heads + a.n_kv_heads) * (kHd / 2);
   HYMBA_LAUNCH(decode_rope_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, t_first, (const T*)a.q,
                      (const T*)a.k_new, a.cache_len, a.q_rot, a.k_rot, a.batch, a.n_q_heads, a.n_kv_heads, a.cap,
                      a.rope_base);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (sizeof(T) == 2)
-    HYMBA_LAUNCH((attn_decode_flash_kernel<DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream, t_last,
-                 a.q_rot, a.k_rot, (const bf16*)a.v_new, (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.cache_len,
-                 a.partial, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads, a.n_kv_heads);
-  else
-    HYMBA_LAUNCH((attn_decode_kernel<T, DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream, t_last,
+  HYMBA_LAUNCH((attn_decode_kernel<T, DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream, t_last,
                  a.q_rot, a.k_rot, (const T*)a.v_new, (const T*)a.k_cache, (const T*)a.v_cache, a.cache_len,
                  a.partial, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads, a.n_kv_heads);
   return hipGetLastError();
