@@ -156,6 +156,18 @@ __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70
 // flight (a __syncthreads() would wait for them, loads into LDS included):
 // lgkmcnt 0 (vmcnt and expcnt at their maximum), then s_barrier; the empty asm
 // statements keep the compiler from moving memory accesses across it.
+// Workgroup barrier for a tile pipeline: this wave first waits until at most
+// N of its global loads are outstanding (later tiles' loads may stay in
+// flight; a load into LDS has landed once it is no longer counted) and its LDS
+// operations are done; then as lds_barrier.
+template <int N>
+__device__ __forceinline__ void tile_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);   // vmcnt(N) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);
   asm volatile("" ::: "memory");
@@ -868,14 +880,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 // attn_decode_kernel, one per split. The rotation of q and of the new key to
 // position p is done here, from cos/sin formed once per workgroup while the
 // first tile loads.
-constexpr int kDecodeTile = 64;
+constexpr int kDecodeTile = 32;     // keys per tile
+constexpr int kDecodeStages = 2;    // tiles in LDS: one used, kDecodeStages - 1 loading
 
 template <int DV>
 __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_new, const bf16* __restrict__ v_new,
     const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
     float* __restrict__ partial, int n_split, int cap, int n_meta, int window, int Hq, int Hkv, float base) {
-  constexpr int BT = kDecodeTile;
+  // (a tile is whole 16-byte loads of all 256 threads: 64 keys for dv 32)
+  constexpr int BT = kDecodeTile * (DV / 8) % 256 == 0 ? kDecodeTile : 64, NS = kDecodeStages;
+  constexpr int NKB = BT / 32;                          // 32-key blocks per tile
   constexpr int NT = 256;
   constexpr int KROWB = kHd * 2, VROWB = DV * 2;        // bytes per K / V row
   constexpr int KCH = KROWB / 16, VCH = VROWB / 16;     // 16-byte chunks per row
@@ -883,14 +898,19 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
   constexpr int KSTAGE = BT * KROWB, STAGE = KSTAGE + BT * VROWB;
   constexpr int NDB = DV / 32;                          // 32-wide dv blocks
   constexpr int VRPB = VROWB >= 256 ? 1 : 256 / VROWB;  // V rows per 256-byte bank sweep
-  static_assert(BT * KCH % NT == 0 && BT * VCH % NT == 0 && BT == 64, "tile shape");
+  static_assert(BT * KCH % NT == 0 && BT * VCH % NT == 0 && (BT == 32 || BT == 64), "tile shape");
+  static_assert(NS >= 2 && NS <= 4, "stages");
   // the stages are separate objects, so that the compiler can tell reads of
-  // one from the loads into the other
+  // one from the loads into another
   __shared__ __attribute__((aligned(16))) char lds_stage0[STAGE];
   __shared__ __attribute__((aligned(16))) char lds_stage1[STAGE];
+  __shared__ __attribute__((aligned(16))) char lds_stage2[NS > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char lds_stage3[NS > 3 ? STAGE : 16];
   __shared__ float rope_c[kHd / 2], rope_s[kHd / 2];
   lds_char* const stage0 = (lds_char*)lds_stage0;
   lds_char* const stage1 = (lds_char*)lds_stage1;
+  lds_char* const stage2 = (lds_char*)lds_stage2;
+  lds_char* const stage3 = (lds_char*)lds_stage3;
   auto ksw = [](int row) { return (row >> 1) & (KCH - 1); };
   auto vsw = [](int row) { return (4 * ((row & 3) / VRPB)) & (VCH - 1); };
 
@@ -944,7 +964,13 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
   };
 
   typedef Mma<bf16> M;
+  // the first NS - 1 tiles (past the split: rows that are loaded and never used)
   fetch(t0, stage0);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NS > 2) fetch(t0 + 1, stage1);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NS > 3) fetch(t0 + 2, stage2);
+  __builtin_amdgcn_sched_barrier(0);
   // raw q of this lane's column and (threads < KCH) the new key's dims 8 tid ..
   // and their rotation partners, loaded while cos/sin of position p are formed
   const bool qv = lq < group;   // (a column past the group reads head 0 and ends up zero)
@@ -1029,8 +1055,10 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
   wait_loads();
   __syncthreads();
 
+  // tile t is in stage cur; tile t + NS - 1 loads into nxt
   auto tile = [&](int t, lds_char* cur, lds_char* nxt) __attribute__((always_inline)) {
-    fetch(t + 1, nxt);   // (past the split: rows that are loaded and never used)
+    fetch(t + NS - 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
     const int vbase = BT * t;
     if (has_new && vi_new - vbase < BT) {   // the new row's K and V into this tile
       const int rn = vi_new - vbase;
@@ -1041,9 +1069,9 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
       lds_barrier();
     }
     // scores: lane holds keys 32 h2 + 8 (r / 4) + 4 hh + r % 4 of column lq
-    f32x16_t sc[2];
+    f32x16_t sc[NKB];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < NKB; ++h2) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[h2][r] = 0.f;
 #pragma unroll
@@ -1056,7 +1084,7 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
     // keys past the visible ones (last tile only); online softmax of the column
     float tmx = -INFINITY;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int h2 = 0; h2 < NKB; ++h2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = vbase + 32 * h2 + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -1072,9 +1100,9 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
     for (int i = 0; i < NDW; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
-    M::Frag pf[4];   // P^T operands, 16 keys each
+    M::Frag pf[2 * NKB];   // P^T operands, 16 keys each
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < NKB; ++h2) {
       float pv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -1091,7 +1119,7 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
       const int d = wave + 4 * i;
       if (d < NDB) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 2 * NKB; ++kk) {
           const lds_char* vp = cur + ((vro ^ (d << 6)) + 16 * kk * VROWB);
           const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)vp);
           const v4i16_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp + 8 * VROWB));
@@ -1100,16 +1128,25 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
         }
       }
     }
-    wait_loads();
-    __syncthreads();
+    // tile t + 1 has landed (the loads of later tiles may still be in flight)
+    tile_barrier<(KN + VN) * (NS - 2)>();
   };
-  // two tiles per trip, so that each stage is a fixed object in each half
+  // NS tiles per trip, so that every stage is a fixed object in each part
   for (int t = t0;;) {
-    tile(t, stage0, stage1);
+    tile(t, stage0, NS == 2 ? stage1 : NS == 3 ? stage2 : stage3);
     if (++t >= t1) break;
-    tile(t, stage1, stage0);
+    tile(t, stage1, NS == 2 ? stage0 : NS == 3 ? stage0 : stage0);
     if (++t >= t1) break;
+    if constexpr (NS > 2) {
+      tile(t, stage2, stage1);
+      if (++t >= t1) break;
+    }
+    if constexpr (NS > 3) {
+      tile(t, stage3, stage2);
+      if (++t >= t1) break;
+    }
   }
+  wait_loads();   // no load into LDS outlives the workgroup
 
   l += __shfl_xor(l, 32, 64);
   if (lq < group) {
@@ -1336,10 +1373,13 @@ int decode_active_splits(const AttnDecodeArgs& a) {
   const int64_t max_vis = decode_max_visible(a.n_meta, a.window, a.cap);
   if (a.act != HYMBA_BF16)   // one split per kKeysPerSplit keys
     return (int)((max_vis + kKeysPerSplit - 1) / kKeysPerSplit);
-  // about three workgroups per compute unit, each streaming whole tiles
+  // as many workgroups as fit the chip at once (LDS bounds them), each
+  // streaming whole tiles
+  const int64_t stage = (int64_t)kDecodeTile * (kHd + a.head_dim_v) * 2;
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / (kDecodeStages * stage + 512)));
   const int64_t tiles = (max_vis + kDecodeTile - 1) / kDecodeTile;
   const int64_t rows = (int64_t)a.batch * a.n_kv_heads;
-  const int64_t want = std::max<int64_t>(1, (3 * (int64_t)a.n_cu) / std::max<int64_t>(1, rows));
+  const int64_t want = std::max<int64_t>(1, (per_cu * a.n_cu) / std::max<int64_t>(1, rows));
   return (int)std::min(tiles, want);
 }
 

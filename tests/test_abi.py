@@ -72,8 +72,8 @@ def test_workspace_sizes(lib):
     got = H.hymba_mixer_prefill_workspace_bytes(d)
     assert expect <= got <= expect + 7 * 256
     dd = c1_desc(batch=64)
-    # room for a partial (o, m, l) per query head and 64-key tile of the 128 + 1024 visible keys
-    n_split = (128 + 1024 + 63) // 64
+    # room for a partial (o, m, l) per query head and 32-key tile of the 128 + 1024 visible keys
+    n_split = (128 + 1024 + 31) // 32
     expect = 64 * 25 * n_split * 130 * 4 + 2 * 64 * 3200 * 2 + 64 * (25 + 5) * 64 * 4
     got = H.hymba_mixer_decode_workspace_bytes(dd)
     assert expect <= got <= expect + 5 * 256
