@@ -929,6 +929,7 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
   const int t0 = min(n_tiles, s * per), t1 = min(n_tiles, t0 + per);
   float* outp = partial + (((b * Hq) + g * group) * n_split + s) * (DV + 2);
   const int64_t pstride = (int64_t)n_split * (DV + 2);  // between query heads
+
   if (t0 >= t1) {   // (whole workgroup, before any barrier)
     for (int t = tid; t < group * (DV + 2); t += blockDim.x) {
       const int hq = t / (DV + 2), e = t % (DV + 2);

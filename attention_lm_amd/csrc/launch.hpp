@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "../../include/hymba_mixer.h"
+#include "ssm_step.hpp"
 
 namespace hymba {
 
@@ -65,6 +66,14 @@ struct SsmDecodeArgs {
   hymba_dtype act;
 };
 hipError_t launch_ssm_decode(const SsmDecodeArgs& a, hipStream_t stream, Timing tm = {});
+template <typename T>
+inline ssm_step::Ptrs<T> ssm_step_ptrs(const SsmDecodeArgs& a) {
+  ssm_step::Ptrs<T> p;
+  p.x = (const T*)a.x; p.z = (const T*)a.z; p.dt = (const T*)a.dt; p.B = (const T*)a.B; p.C = (const T*)a.C;
+  p.A = a.A; p.D = a.D; p.conv_w = a.conv_w; p.state = a.state; p.conv_state = (T*)a.conv_state; p.y = (T*)a.y;
+  p.d_inner = a.d_inner;
+  return p;
+}
 
 // attn.hip ------------------------------------------------------------------
 struct RopeArgs {

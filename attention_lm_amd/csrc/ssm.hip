@@ -20,6 +20,7 @@
 // The conv history of a chunk is re-read from x (3 rows before it).
 #include "common.hpp"
 #include "launch.hpp"
+#include "ssm_step.hpp"
 
 namespace hymba {
 
@@ -351,75 +352,28 @@ __global__ __launch_bounds__(64 * kCarrySegs) void ssm_chunk_carry_kernel(const 
   }
 }
 
-// Decode step: a lane quad per (sequence, channel), 4 states per lane, and
-// kDecodeChanPerQuad channels per quad (channel i and i + n_quad), so that the
-// whole step is one round of workgroups; every load of a lane is issued
-// before its first use.
+// Decode step (ssm_step.hpp): a lane quad per (sequence, channel), 4 states
+// per lane, and kDecodeChanPerQuad channels per quad (channel i and i +
+// n_quad), so that the whole step is one round of workgroups; every load of a
+// lane is issued before its first use.
 constexpr int kDecodeChanPerQuad = 2;
 
 template <typename T>
-__global__ __launch_bounds__(256) void ssm_decode_kernel(
-    const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ dt,
-    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ A,
-    const float* __restrict__ Dp, const float* __restrict__ conv_w, float* __restrict__ state,
-    T* __restrict__ conv_state, T* __restrict__ y, int batch, int Dch, int64_t n_quad) {
+__global__ __launch_bounds__(256) void ssm_decode_kernel(ssm_step::Ptrs<T> p, int batch, int64_t n_quad) {
   constexpr int K = kDecodeChanPerQuad;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int q = (int)(gid & 3);
   const int64_t qi = gid >> 2;
-  const int64_t n_bc = (int64_t)batch * Dch;
-  bool ok[K];
-  int64_t bc[K];
-  float cs[K][kConv - 1], w[K][kConv], Bv[K][4], Cv[K][4], xn[K], d[K], zn[K], Dc[K];
-  float4 h4[K], a4[K];
-  T xr[K];
+  const int64_t n_bc = (int64_t)batch * p.d_inner;
+  ssm_step::Item<T> it[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int64_t i = qi + k * n_quad;
-    ok[k] = qi < n_quad && i < n_bc;   // uniform over each quad (the grid is rounded up past n_quad)
-    bc[k] = ok[k] ? i : 0;
-    const int c = (int)(bc[k] % Dch);
-    const int64_t b = bc[k] / Dch;
-#pragma unroll
-    for (int j = 0; j < kConv - 1; ++j) cs[k][j] = to_f32(conv_state[bc[k] * (kConv - 1) + j]);
-    xr[k] = x[bc[k]];
-    d[k] = to_f32(dt[bc[k]]);
-    zn[k] = to_f32(z[bc[k]]);
-    Dc[k] = Dp[c];
-    const float4 w4 = *reinterpret_cast<const float4*>(conv_w + (int64_t)c * kConv);
-    w[k][0] = w4.x; w[k][1] = w4.y; w[k][2] = w4.z; w[k][3] = w4.w;
-    h4[k] = *reinterpret_cast<const float4*>(state + bc[k] * kStates + 4 * q);
-    a4[k] = *reinterpret_cast<const float4*>(A + (int64_t)c * kStates + 4 * q);
-    load_n<4>(Bm + b * kStates + 4 * q, Bv[k]);
-    load_n<4>(Cm + b * kStates + 4 * q, Cv[k]);
+    const bool ok = qi < n_quad && i < n_bc;   // uniform over each quad (the grid is rounded up past n_quad)
+    ssm_step::load(p, it[k], ok ? i / p.d_inner : 0, ok ? (int)(i % p.d_inner) : 0, q, ok);
   }
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    xn[k] = to_f32(xr[k]);
-    float u = w[k][kConv - 1] * xn[k];
-#pragma unroll
-    for (int j = 0; j < kConv - 1; ++j) u = fmaf(w[k][j], cs[k][j], u);
-    const float du = d[k] * u;
-    float h[4] = {h4[k].x, h4[k].y, h4[k].z, h4[k].w};
-    const float a[4] = {a4[k].x, a4[k].y, a4[k].z, a4[k].w};
-    float part = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      h[j] = fmaf(fast_exp2(d[k] * a[j] * kLog2e), h[j], du * Bv[k][j]);
-      part = fmaf(Cv[k][j], h[j], part);
-    }
-    part += __shfl_xor(part, 1, 64);
-    part += __shfl_xor(part, 2, 64);
-    if (!ok[k]) continue;
-    *reinterpret_cast<float4*>(state + bc[k] * kStates + 4 * q) = make_float4(h[0], h[1], h[2], h[3]);
-    if (q == 0) {
-      y[bc[k]] = from_f32<T>(fmaf(Dc[k], u, part) * silu(zn[k]));
-      T* cp = conv_state + bc[k] * (kConv - 1);
-#pragma unroll
-      for (int j = 0; j < kConv - 2; ++j) cp[j] = from_f32<T>(cs[k][j + 1]);
-      cp[kConv - 2] = xr[k];
-    }
-  }
+  for (int k = 0; k < K; ++k) ssm_step::finish(p, it[k], q);
 }
 
 template <typename T>
@@ -481,16 +435,11 @@ hipError_t launch_ssm_chunk_out(const SsmPrefillArgs& a, hipStream_t stream, Tim
 
 hipError_t launch_ssm_decode(const SsmDecodeArgs& a, hipStream_t stream, Timing tm) {
   const int64_t n_quad = ((int64_t)a.batch * a.d_inner + kDecodeChanPerQuad - 1) / kDecodeChanPerQuad;
-  const int64_t threads = n_quad * 4;
-  dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  dim3 grid((unsigned)((n_quad * 4 + 255) / 256)), block(256);
   if (a.act == HYMBA_BF16)
-    HYMBA_LAUNCH(ssm_decode_kernel<bf16>, grid, block, 0, stream, tm, (const bf16*)a.x, (const bf16*)a.z,
-                       (const bf16*)a.dt, (const bf16*)a.B, (const bf16*)a.C, a.A, a.D, a.conv_w, a.state,
-                       (bf16*)a.conv_state, (bf16*)a.y, a.batch, a.d_inner, n_quad);
+    HYMBA_LAUNCH(ssm_decode_kernel<bf16>, grid, block, 0, stream, tm, ssm_step_ptrs<bf16>(a), a.batch, n_quad);
   else
-    HYMBA_LAUNCH(ssm_decode_kernel<float>, grid, block, 0, stream, tm, (const float*)a.x, (const float*)a.z,
-                       (const float*)a.dt, (const float*)a.B, (const float*)a.C, a.A, a.D, a.conv_w, a.state,
-                       (float*)a.conv_state, (float*)a.y, a.batch, a.d_inner, n_quad);
+    HYMBA_LAUNCH(ssm_decode_kernel<float>, grid, block, 0, stream, tm, ssm_step_ptrs<float>(a), a.batch, n_quad);
   return hipGetLastError();
 }
 
