@@ -203,6 +203,26 @@ def test_decode_small_global_f32():
     run_decode_parity(cfg, cache_len=np.array([199, 4, 130], np.int32))
 
 
+DECODE_EDGE = [
+    # dv 32 (64-key tiles), a global layer, one sequence: many one-tile splits
+    dict(batch=1, d_inner=64, n_q_heads=2, n_kv_heads=1, n_meta=3, window=0, cache_capacity=500, cache=[437]),
+    # no GQA (G = 1), dv 128, no meta rows; an empty cache, one row, a full cache (p = capacity)
+    dict(batch=4, d_inner=256, n_q_heads=2, n_kv_heads=2, n_meta=0, window=7, cache_capacity=64,
+         cache=[0, 1, 63, 64]),
+    # the largest group (8 query heads per kv head), dv 32, window wider than the cache
+    dict(batch=2, d_inner=256, n_q_heads=8, n_kv_heads=1, n_meta=16, window=4096, cache_capacity=100,
+         cache=[17, 100]),
+]
+
+
+@pytest.mark.parametrize("kw", DECODE_EDGE, ids=[f"edge{i}" for i in range(len(DECODE_EDGE))])
+def test_decode_bf16_edge_shapes(kw):
+    kw = dict(kw)
+    cache = np.array(kw.pop("cache"), np.int32)
+    cfg = synth.config("decode").with_(**kw, name="dedge")
+    run_decode_parity(cfg, cache_len=cache)
+
+
 def test_decode_full_config():
     run_decode_parity(synth.config("decode"))
 
