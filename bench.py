@@ -463,7 +463,7 @@ def main():
             "workload": dcfg.workload,
             "us_per_step": round(dms * 1e3, 2),
             "layers_per_step": dcfg.n_layers,
-            "branches": "concurrent",
+            "branches": "one stream (SSM step, attention, epilogue in order)",
             "us_per_call_serialized": [round(x * 1e3, 2) for x in per_layer],
             "hbm_GBs_per_call": round(dw["total_bytes"] / (call_us * 1e-6) / 1e9, 1),
             "hbm_frac_per_call": round(dw["total_bytes"] / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
