@@ -15,6 +15,7 @@ from .hymba_oracle import (  # noqa: F401
     visible,
     mask_ranges,
     attention,
+    shared_key_affine,
     rms_fuse,
     mixer_prefill,
     mixer_decode,

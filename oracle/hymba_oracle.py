@@ -220,6 +220,24 @@ def attention(q_rot, k_rot, v, n_meta: int, window: int, rows: Optional[np.ndarr
     return out
 
 
+def shared_key_affine(k_rot, k_scale=None, k_bias=None) -> np.ndarray:
+    """Keys as a secondary layer sees a primary layer's shared cache: the
+    head-specific affine K~ = K (.) w_scale + b_bias (Hymba guide, "Systems
+    Mechanics: Cross-Layer KV Cache Sharing", "1. The KV Sharing Mechanism").
+
+    Reading: w_scale and b_bias are per kv head vectors over the key
+    dimension, [Hkv, d], applied element-wise to the keys as the cache holds
+    them (rotated); the values are shared unchanged (the pages' formula names
+    the keys only). None = identity. k_rot: [..., Hkv, d].
+    """
+    k = _f64(k_rot)
+    if k_scale is not None:
+        k = k * _f64(k_scale)
+    if k_bias is not None:
+        k = k + _f64(k_bias)
+    return k
+
+
 # ---------------------------------------------------------------------------
 # Fusion of the two branches
 
@@ -255,6 +273,9 @@ def mixer_prefill(cfg, inp: Dict[str, np.ndarray], batches: Optional[Iterable[in
 
     ``batches`` restricts to some sequences; ``rows`` restricts the attention
     and fused outputs to some query rows (the scan always runs over all rows).
+    Optional inp["k_scale"], inp["k_bias"] ([Hkv, d]): the attention reads the
+    keys through shared_key_affine (a secondary layer); k_rot, the keys a
+    cache would store, are returned without it.
     Returns float64 arrays: y_ssm [b, L, D], ssm_state [b, D, N],
     conv_state [b, D, K-1] (last K-1 raw x rows, oldest first),
     k_rot [b, L, Hkv, d], and for the selected rows y_attn [b, R, D] and
@@ -280,7 +301,8 @@ def mixer_prefill(cfg, inp: Dict[str, np.ndarray], batches: Optional[Iterable[in
     res["k_rot"] = k_rot
     if with_attention:
         q_rot = rope(_f64(inp["q"])[bsel], pos, cfg.rope_base)
-        ya = attention(q_rot, k_rot, _f64(inp["v"])[bsel], cfg.n_meta, cfg.window, rows=rsel)
+        k_att = shared_key_affine(k_rot, inp.get("k_scale"), inp.get("k_bias"))
+        ya = attention(q_rot, k_att, _f64(inp["v"])[bsel], cfg.n_meta, cfg.window, rows=rsel)
         y_attn = ya.reshape(len(bsel), len(rsel), cfg.n_q_heads * cfg.head_dim_v)  # head-major concat
         res["y_attn"] = y_attn
         res["out"] = rms_fuse(y_attn, y_ssm[:, rsel, :], inp["beta_attn"], inp["beta_ssm"], cfg.norm_eps)
@@ -298,6 +320,10 @@ def mixer_decode(cfg, layer_inp: Dict[str, np.ndarray], k_cache, v_cache, k_new,
     layers that share a cache read the same key/value tensors). Visibility is
     the prefill rule at query row p. Conv state holds the last K-1 raw x rows,
     oldest first, and both states are advanced by one row.
+
+    Optional layer_inp["k_scale"], ["k_bias"] ([Hkv, d]): this layer is a
+    secondary one and reads the shared keys (the new row's included) through
+    shared_key_affine.
 
     Returns out, y_attn, y_ssm [B, D] and the new ssm_state [B, D, N],
     conv_state [B, D, K-1] (float64).
@@ -321,6 +347,7 @@ def mixer_decode(cfg, layer_inp: Dict[str, np.ndarray], k_cache, v_cache, k_new,
         q_rot = rope(_f64(li["q"])[b][None, None], pos, cfg.rope_base)          # [1,1,Hq,d]
         kn = rope(_f64(k_new)[b][None, None], pos, cfg.rope_base)[0]             # [1,Hkv,d]
         keys = np.concatenate([_f64(k_cache[b, :p]), kn], axis=0)[None]          # [1,p+1,Hkv,d]
+        keys = shared_key_affine(keys, li.get("k_scale"), li.get("k_bias"))
         vals = np.concatenate([_f64(v_cache[b, :p]), _f64(v_new)[b][None]], axis=0)[None]
         ya = attention(q_rot, keys, vals, cfg.n_meta, cfg.window, rows=np.array([0]),
                        key_positions=np.arange(p + 1), query_positions=pos)

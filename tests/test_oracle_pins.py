@@ -402,3 +402,76 @@ def test_kv_cache_worked_examples():
         if "ratio_to_previous_approx" in e:
             assert abs(b / prev - e["ratio_to_previous_approx"]) <= e["ratio_tolerance"], e["cite"]
         prev = b
+
+
+# ---------------------------------------------------------------------------
+# shared-KV key affine of a secondary layer (Hymba guide, "Systems Mechanics:
+# Cross-Layer KV Cache Sharing")
+
+
+def _affine(cfg, g, scale=True, bias=True):
+    Hkv, d = cfg.n_kv_heads, cfg.head_dim
+    ks = (0.5 + g.random((Hkv, d))) if scale else None
+    kb = g.standard_normal((Hkv, d)) if bias else None
+    return ks, kb
+
+
+def test_key_affine_identity_and_bias_shift_invariance():
+    """Unit scale and zero bias change nothing; a bias adds q . b to every
+    score of a query row, a constant over its keys, which softmax removes."""
+    cfg = _tiny_cfg(window=4)
+    inp = synth.make_prefill_inputs(cfg)
+    g = np.random.default_rng(5)
+    plain = O.mixer_prefill(cfg, inp)
+    unit = O.mixer_prefill(cfg, {**inp, "k_scale": np.ones((cfg.n_kv_heads, cfg.head_dim)),
+                                 "k_bias": np.zeros((cfg.n_kv_heads, cfg.head_dim))})
+    np.testing.assert_array_equal(unit["y_attn"], plain["y_attn"])
+    ks, kb = _affine(cfg, g)
+    scaled = O.mixer_prefill(cfg, {**inp, "k_scale": ks})
+    both = O.mixer_prefill(cfg, {**inp, "k_scale": ks, "k_bias": kb})
+    np.testing.assert_allclose(both["y_attn"], scaled["y_attn"], rtol=1e-11, atol=1e-13)
+    # and the scale does change the result (it reshapes every head's scores)
+    assert np.max(np.abs(scaled["y_attn"] - plain["y_attn"])) > 1e-3
+    # the cache content a prefill returns is the plain rotated keys
+    np.testing.assert_array_equal(both["k_rot"], plain["k_rot"])
+
+
+def test_key_affine_scale_equals_query_scale_of_its_group():
+    """(q . (k (.) w)) = ((q (.) w) . k): scaling every query head of kv group
+    g by w[g] instead of the keys gives the same attention, which pins the
+    head-to-group mapping of the per-kv-head vectors."""
+    cfg = _tiny_cfg(window=0, n_q_heads=4, n_kv_heads=2)
+    inp = synth.make_prefill_inputs(cfg)
+    g = np.random.default_rng(6)
+    ks, _ = _affine(cfg, g, bias=False)
+    L = cfg.seq_rows
+    pos = np.arange(L)
+    q_rot = O.rope(inp["q"], pos, cfg.rope_base)
+    k_rot = O.rope(inp["k"], pos, cfg.rope_base)
+    group = cfg.n_q_heads // cfg.n_kv_heads
+    q_scaled = q_rot * np.repeat(ks, group, axis=0)[None, None]     # query head h uses w[h // group]
+    via_q = O.attention(q_scaled, k_rot, inp["v"], cfg.n_meta, cfg.window)
+    via_k = O.attention(q_rot, O.shared_key_affine(k_rot, ks), inp["v"], cfg.n_meta, cfg.window)
+    np.testing.assert_allclose(via_k, via_q, rtol=1e-12, atol=1e-13)
+    ref = O.mixer_prefill(cfg, {**inp, "k_scale": ks})
+    np.testing.assert_allclose(ref["y_attn"], via_k.reshape(cfg.batch, L, -1), rtol=1e-13, atol=1e-14)
+
+
+def test_key_affine_decode_equals_prefill_of_one_more_row():
+    """A secondary layer's decode step (affine over the shared cache and the
+    new key) equals its prefill of one more row."""
+    cfg = _tiny_cfg(window=4)
+    L = cfg.seq_rows
+    full = synth.make_prefill_inputs(cfg)
+    ks, kb = _affine(cfg, np.random.default_rng(7))
+    ref = O.mixer_prefill(cfg, {**full, "k_scale": ks, "k_bias": kb})
+    short_cfg = cfg.with_(n_tokens=cfg.n_tokens - 1)
+    short = {k: (v[:, :L - 1] if k in ("x", "z", "dt", "B", "C", "q", "k", "v") else v) for k, v in full.items()}
+    pre = O.mixer_prefill(short_cfg, short)
+    layer = {k: full[k][:, L - 1] for k in ("x", "z", "dt", "B", "C", "q")}
+    layer.update(ssm_state=pre["ssm_state"], conv_state=pre["conv_state"], k_scale=ks, k_bias=kb,
+                 **{k: full[k] for k in ("A", "conv_w", "D", "beta_attn", "beta_ssm")})
+    dec = O.mixer_decode(cfg, layer, pre["k_rot"], full["v"][:, :L - 1], full["k"][:, L - 1], full["v"][:, L - 1],
+                         np.full(cfg.batch, L - 1))
+    np.testing.assert_allclose(dec["y_attn"], ref["y_attn"][:, L - 1], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dec["out"], ref["out"][:, L - 1], rtol=1e-12, atol=1e-13)
