@@ -43,7 +43,8 @@ class MixerDesc(ctypes.Structure):
 
 
 class MixerParams(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("A", "D", "conv_w", "conv_b", "beta_attn", "beta_ssm")]
+    _fields_ = [(n, ctypes.c_void_p)
+                for n in ("A", "D", "conv_w", "conv_b", "beta_attn", "beta_ssm", "k_scale", "k_bias")]
 
 
 class HymbaError(RuntimeError):
@@ -103,8 +104,10 @@ def make_desc(batch, n_meta, n_tokens, d_inner, n_q_heads, n_kv_heads, window, a
                      head_dim_v, window, cache_capacity, rope_base, norm_eps, act_code)
 
 
-def make_params(A, D, conv_w, beta_attn, beta_ssm) -> MixerParams:
-    return MixerParams(_ptr(A), _ptr(D), _ptr(conv_w), None, _ptr(beta_attn), _ptr(beta_ssm))
+def make_params(A, D, conv_w, beta_attn, beta_ssm, k_scale=None, k_bias=None) -> MixerParams:
+    """k_scale / k_bias: [n_kv_heads, head_dim] fp32 affine on shared keys, or None."""
+    return MixerParams(_ptr(A), _ptr(D), _ptr(conv_w), None, _ptr(beta_attn), _ptr(beta_ssm), _ptr(k_scale),
+                       _ptr(k_bias))
 
 
 def _ptr(t) -> Optional[int]:

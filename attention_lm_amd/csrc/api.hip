@@ -117,7 +117,7 @@ int check_params(const hymba_mixer_params* p) {
   if (!p || !p->A || !p->D || !p->conv_w || !p->beta_attn || !p->beta_ssm) return HYMBA_EINVAL;
   if (p->conv_b) return HYMBA_EUNSUPPORTED;
   if (!aligned16(p->A) || !aligned16(p->D) || !aligned16(p->conv_w) || !aligned16(p->beta_attn) ||
-      !aligned16(p->beta_ssm))
+      !aligned16(p->beta_ssm) || !aligned16(p->k_scale))
     return HYMBA_EALIGN;
   return HYMBA_OK;
 }
@@ -249,7 +249,7 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
 
   hymba::RopeArgs ra;
   ra.q = q; ra.k = k; ra.v = v; ra.q_rot = q_rot; ra.k_rot = k_rot; ra.v_copy = v_cache;
-  ra.k_rows = k_rows; ra.v_rows = desc->cache_capacity;
+  ra.k_rows = k_rows; ra.v_rows = desc->cache_capacity; ra.k_scale = params->k_scale;
   ra.batch = desc->batch; ra.L = L; ra.n_q_heads = desc->n_q_heads; ra.n_kv_heads = desc->n_kv_heads;
   ra.head_dim = desc->head_dim; ra.head_dim_v = desc->head_dim_v; ra.rope_base = desc->rope_base;
   ra.act = desc->act;
@@ -313,7 +313,7 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
 
   hymba::AttnDecodeArgs aa;
   aa.q = q; aa.k_new = k_new; aa.v_new = v_new; aa.k_cache = k_cache; aa.v_cache = v_cache;
-  aa.cache_len = cache_len; aa.partial = partial;
+  aa.cache_len = cache_len; aa.partial = partial; aa.k_scale = params->k_scale;
   aa.q_rot = (float*)(wsb + ws.q_rot); aa.k_rot = (float*)(wsb + ws.k_rot); aa.n_split = ws.n_split; aa.keys_per_split = ws.keys_per_split;
   aa.batch = desc->batch; aa.cap = desc->cache_capacity; aa.n_meta = desc->n_meta; aa.window = desc->window;
   aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;

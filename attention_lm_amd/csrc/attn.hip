@@ -60,8 +60,8 @@ constexpr int kRopeThreads = 256;
 template <typename T>
 __global__ __launch_bounds__(kRopeThreads) void rope_prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ q_rot,
-    T* __restrict__ k_rot, T* __restrict__ v_copy, int64_t k_rows, int64_t v_rows, int L, int Hq, int Hkv,
-    int dv, float base, float q_scale) {
+    T* __restrict__ k_rot, T* __restrict__ v_copy, int64_t k_rows, int64_t v_rows,
+    const float* __restrict__ k_scale, int L, int Hq, int Hkv, int dv, float base, float q_scale) {
   __shared__ float cs[kRopeRows][kHd / 2];
   __shared__ float sn[kRopeRows][kHd / 2];
   const int r0 = blockIdx.x * kRopeRows;
@@ -90,14 +90,22 @@ __global__ __launch_bounds__(kRopeThreads) void rope_prefill_kernel(
     const bool has_r = it < rot_items;
     const int g8 = it & 3, hr = it >> 2, hd = hr % H, rr = hr / H;
     T* dst = nullptr;
-    float sc = 1.f, lo[8], hi[8];
+    float slo[8], shi[8], lo[8], hi[8];   // per-dim output scale of the pair's two halves
+#pragma unroll
+    for (int e = 0; e < 8; ++e) slo[e] = shi[e] = 1.f;
     if (has_r) {
       const int row = r0 + rr;
       const T* src;
       if (hd < Hq) {
         src = q + ((b * L + row) * Hq + hd) * kHd;
         dst = q_rot + ((b * L + row) * Hq + hd) * kHd;
-        sc = q_scale;
+        if (k_scale) {   // shared-key affine: q (.) w of the head's kv group
+          const float* w = k_scale + (hd / (Hq / Hkv)) * kHd;
+          load8(w + 8 * g8, slo);
+          load8(w + 32 + 8 * g8, shi);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { slo[e] *= q_scale; shi[e] *= q_scale; }
       } else {
         src = k + ((b * L + row) * Hkv + (hd - Hq)) * kHd;
         dst = k_rot + ((b * k_rows + row) * Hkv + (hd - Hq)) * kHd;
@@ -110,8 +118,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_prefill_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float c = cs[rr][8 * g8 + e], s = sn[rr][8 * g8 + e];
-        olo[e] = (lo[e] * c - hi[e] * s) * sc;
-        ohi[e] = (hi[e] * c + lo[e] * s) * sc;
+        olo[e] = (lo[e] * c - hi[e] * s) * slo[e];
+        ohi[e] = (hi[e] * c + lo[e] * s) * shi[e];
       }
       store8(dst + 8 * g8, olo);
       store8(dst + 32 + 8 * g8, ohi);
@@ -743,7 +751,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void decode_rope_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
                                                           const int32_t* __restrict__ cache_len,
                                                           float* __restrict__ q_rot, float* __restrict__ k_rot,
-                                                          int batch, int Hq, int Hkv, int cap, float base) {
+                                                          const float* __restrict__ k_scale, int batch, int Hq,
+                                                          int Hkv, int cap, float base) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, head, i)
   const int H = Hq + Hkv;
   if (idx >= (int64_t)batch * H * (kHd / 2)) return;
@@ -756,8 +765,14 @@ __global__ __launch_bounds__(256) void decode_rope_kernel(const T* __restrict__ 
   const T* src = hd < Hq ? q + (b * Hq + hd) * kHd : k_new + (b * Hkv + (hd - Hq)) * kHd;
   float* dst = hd < Hq ? q_rot + (b * Hq + hd) * kHd : k_rot + (b * Hkv + (hd - Hq)) * kHd;
   const float lo = to_f32(src[i]), hi = to_f32(src[i + 32]);
-  dst[i] = lo * c - hi * sn;
-  dst[i + 32] = hi * c + lo * sn;
+  float wlo = 1.f, whi = 1.f;   // shared-key affine on the query side: q (.) w of its kv group
+  if (k_scale && hd < Hq) {
+    const float* w = k_scale + (hd / (Hq / Hkv)) * kHd;
+    wlo = w[i];
+    whi = w[i + 32];
+  }
+  dst[i] = (lo * c - hi * sn) * wlo;
+  dst[i + 32] = (hi * c + lo * sn) * whi;
 }
 
 template <typename T, int DV>
@@ -882,12 +897,16 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 // first tile loads.
 constexpr int kDecodeTile = 32;     // keys per tile
 constexpr int kDecodeStages = 2;    // tiles in LDS: one used, kDecodeStages - 1 loading
+constexpr int kMaxGroupFlash = 8;   // query heads per kv head (larger groups are rejected up front)
 
+// (dv >= 64: five waves per SIMD fit in 96 registers without spills)
 template <int DV>
-__global__ __launch_bounds__(256) void attn_decode_flash_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DV >= 64 ? 5 : 1)))
+void attn_decode_flash_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_new, const bf16* __restrict__ v_new,
     const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
-    float* __restrict__ partial, int n_split, int cap, int n_meta, int window, int Hq, int Hkv, float base) {
+    float* __restrict__ partial, const float* __restrict__ k_scale, int n_split, int cap, int n_meta, int window,
+    int Hq, int Hkv, float base) {
   // (a tile is whole 16-byte loads of all 256 threads: 64 keys for dv 32)
   constexpr int BT = kDecodeTile * (DV / 8) % 256 == 0 ? kDecodeTile : 64, NS = kDecodeStages;
   constexpr int NKB = BT / 32;                          // 32-key blocks per tile
@@ -907,6 +926,7 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
   __shared__ __attribute__((aligned(16))) char lds_stage2[NS > 2 ? STAGE : 16];
   __shared__ __attribute__((aligned(16))) char lds_stage3[NS > 3 ? STAGE : 16];
   __shared__ float rope_c[kHd / 2], rope_s[kHd / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kMaxGroupFlash][kHd];   // bf16 bits
   lds_char* const stage0 = (lds_char*)lds_stage0;
   lds_char* const stage1 = (lds_char*)lds_stage1;
   lds_char* const stage2 = (lds_char*)lds_stage2;
@@ -972,13 +992,19 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (NS > 3) fetch(t0 + 2, stage2);
   __builtin_amdgcn_sched_barrier(0);
-  // raw q of this lane's column and (threads < KCH) the new key's dims 8 tid ..
-  // and their rotation partners, loaded while cos/sin of position p are formed
-  const bool qv = lq < group;   // (a column past the group reads head 0 and ends up zero)
-  const bf16* qrow = q + (b * Hq + g * group + (qv ? lq : 0)) * kHd;
-  u32x4_t qraw[4];
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) qraw[kc] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * kc + 8 * hh);
+  // thread 32 h + i: raw dims i and i + 32 (a rotation pair) of query head h
+  // of the group and their shared-key affine weights w[g]; threads < KCH also
+  // the new key's dims 8 tid .. and their rotation partners. All are loaded
+  // while cos/sin of position p are formed.
+  const int qh = tid >> 5, qi = tid & (kHd / 2 - 1);
+  const bool q_in = qh < group;
+  const bf16* qrow = q + (b * Hq + g * group + (q_in ? qh : 0)) * kHd;
+  const uint16_t qlo_bits = qrow[qi].u, qhi_bits = qrow[qi + kHd / 2].u;
+  float wl = 1.f, wh = 1.f;
+  if (k_scale) {
+    wl = k_scale[g * kHd + qi];
+    wh = k_scale[g * kHd + qi + kHd / 2];
+  }
   const bool has_new = vi_new / BT < t1;   // (then it is in this split's last tile)
   u32x4_t kraw = {0u, 0u, 0u, 0u}, kpart = {0u, 0u, 0u, 0u};
   u32x4_t new_v = {0u, 0u, 0u, 0u};
@@ -993,30 +1019,12 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
   }
   if (tid < kHd / 2) rope_cs(p, tid, base, &rope_c[tid], &rope_s[tid]);
   __syncthreads();
-  // Q^T operand: lane (column lq = query head of the group, half hh) holds the
-  // rotated Q[16 kc + 8 hh .. +7] scaled by log2(e)/sqrt(64): dims i and i + 32
-  // (chunks kc and kc + 2) are a rotation pair, both in this lane
-  M::Frag qf[4];
-  {
-    const float sc = qv ? kScaleLog2e : 0.f;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      float lo[8], hi[8], olo[8], ohi[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo[2 * e] = bf16_lo(qraw[kc][e]); lo[2 * e + 1] = bf16_hi(qraw[kc][e]);
-        hi[2 * e] = bf16_lo(qraw[kc + 2][e]); hi[2 * e + 1] = bf16_hi(qraw[kc + 2][e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = 16 * kc + 8 * hh + e;
-        const float c = rope_c[i], sn = rope_s[i];
-        olo[e] = (lo[e] * c - hi[e] * sn) * sc;
-        ohi[e] = (hi[e] * c + lo[e] * sn) * sc;
-      }
-      qf[kc] = M::from_f32(olo);
-      qf[kc + 2] = M::from_f32(ohi);
-    }
+  // the group's queries rotated, times w[g] and log2(e)/sqrt(64), as bf16 in LDS
+  if (q_in) {
+    const float lo = __uint_as_float((uint32_t)qlo_bits << 16), hi = __uint_as_float((uint32_t)qhi_bits << 16);
+    const float c = rope_c[qi], sn = rope_s[qi];
+    q_lds[qh][qi] = f32_to_bf16_bits((lo * c - hi * sn) * wl * kScaleLog2e);
+    q_lds[qh][qi + kHd / 2] = f32_to_bf16_bits((hi * c + lo * sn) * wh * kScaleLog2e);
   }
   // per-lane LDS offsets of the operand reads (the swizzles depend on the lane only)
   const int kro = lq * KROWB + 16 * (hh ^ ksw(lq));
@@ -1055,6 +1063,19 @@ __global__ __launch_bounds__(256) void attn_decode_flash_kernel(
   }
   wait_loads();
   __syncthreads();
+  // Q^T operand: lane (column lq = query head of the group, half hh) holds
+  // dims 16 kc + 8 hh .. + 7; columns past the group are zero
+  M::Frag qf[4];
+  {
+    const bool qv = lq < group;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const M::Frag f =
+          *(const __attribute__((address_space(3))) M::Frag*)((lds_char*)q_lds + (qv ? lq : 0) * (kHd * 2) +
+                                                              32 * kc + 16 * hh);
+      qf[kc] = qv ? f : M::zero();
+    }
+  }
 
   // tile t is in stage cur; tile t + NS - 1 loads into nxt
   auto tile = [&](int t, lds_char* cur, lds_char* nxt) __attribute__((always_inline)) {
@@ -1284,7 +1305,8 @@ template <typename T>
 hipError_t rope_t(const RopeArgs& a, hipStream_t stream, Timing tm) {
   dim3 grid((a.L + kRopeRows - 1) / kRopeRows, a.batch);
   HYMBA_LAUNCH(rope_prefill_kernel<T>, grid, dim3(kRopeThreads), 0, stream, tm, (const T*)a.q, (const T*)a.k,
-                     (const T*)a.v, (T*)a.q_rot, (T*)a.k_rot, (T*)a.v_copy, a.k_rows, a.v_rows, a.L, a.n_q_heads,
+                     (const T*)a.v, (T*)a.q_rot, (T*)a.k_rot, (T*)a.v_copy, a.k_rows, a.v_rows, a.k_scale, a.L,
+                     a.n_q_heads,
                      a.n_kv_heads, a.head_dim_v, a.rope_base, kScaleLog2e);
   return hipGetLastError();
 }
@@ -1309,13 +1331,15 @@ hipError_t attn_decode_t(const AttnDecodeArgs& a, hipStream_t stream, Timing tm)
     // rotation inside the attention kernel: one launch for the stage
     HYMBA_LAUNCH((attn_decode_flash_kernel<DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream, tm,
                  (const bf16*)a.q, (const bf16*)a.k_new, (const bf16*)a.v_new, (const bf16*)a.k_cache,
-                 (const bf16*)a.v_cache, a.cache_len, a.partial, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads,
+                 (const bf16*)a.v_cache, a.cache_len, a.partial, a.k_scale, a.n_split, a.cap, a.n_meta, a.window,
+                 a.n_q_heads,
                  a.n_kv_heads, a.rope_base);
     return hipGetLastError();
   }
   const int64_t n = (int64_t)a.batch * (a.n_q_heads + a.n_kv_heads) * (kHd / 2);
   HYMBA_LAUNCH(decode_rope_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, t_first, (const T*)a.q,
-                     (const T*)a.k_new, a.cache_len, a.q_rot, a.k_rot, a.batch, a.n_q_heads, a.n_kv_heads, a.cap,
+                     (const T*)a.k_new, a.cache_len, a.q_rot, a.k_rot, a.k_scale, a.batch, a.n_q_heads,
+                     a.n_kv_heads, a.cap,
                      a.rope_base);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -82,6 +82,7 @@ struct RopeArgs {
   void* k_rot;             // rows with stride k_rows per sequence
   void* v_copy;            // optional, rows with stride v_rows per sequence
   int64_t k_rows, v_rows;  // rows per sequence of k_rot / v_copy (>= L)
+  const float* k_scale;    // [Hkv, 64] or null: query heads of kv head g are scaled by row g
   int batch, L, n_q_heads, n_kv_heads, head_dim, head_dim_v;
   float rope_base;
   hymba_dtype act;
@@ -107,6 +108,7 @@ struct AttnDecodeArgs {
   float* q_rot;                        // workspace [batch, Hq, 64]
   float* k_rot;                        // workspace [batch, Hkv, 64]
   float* partial;                      // [batch, Hq, n_split, dv + 2]
+  const float* k_scale;                // [Hkv, 64] or null (query scale of the shared-key affine)
   int n_split, keys_per_split;         // n_split: splits of this launch (decode_active_splits)
   int n_cu;                            // compute units of the device (split count)
   int batch, cap, n_meta, window, n_q_heads, n_kv_heads, head_dim_v;

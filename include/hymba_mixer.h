@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define HYMBA_ABI_VERSION 1
+#define HYMBA_ABI_VERSION 2
 #define HYMBA_PREFILL_STAGES 6
 #define HYMBA_DECODE_STAGES 3
 
@@ -99,10 +99,20 @@ typedef struct {
  *  D          [d_inner] skip weight
  *  conv_w     [d_inner, d_conv]; tap d_conv-1 multiplies the current row
  *  conv_b     must be NULL (the conv has no bias)
- *  beta_attn, beta_ssm   [d_inner] per-channel scales of the fusion        */
+ *  beta_attn, beta_ssm   [d_inner] per-channel scales of the fusion
+ *  k_scale, k_bias       [n_kv_heads, head_dim] or NULL: the head-specific
+ *      affine a layer applies to keys it reads from another layer's shared
+ *      cache, K' = K * k_scale + k_bias on the rotated keys (Hymba guide,
+ *      "Systems Mechanics: Cross-Layer KV Cache Sharing", section 1). Values
+ *      are shared unchanged. NULL k_scale = all ones. The library scales the
+ *      rotated queries by k_scale of their kv head instead of touching the
+ *      keys; k_bias adds q . k_bias to every score of a query, which the
+ *      softmax removes, so it is accepted and never read. The cache and
+ *      k_rot outputs always hold the keys without the affine.             */
 typedef struct {
   const float *A, *D, *conv_w, *conv_b;
   const float *beta_attn, *beta_ssm;
+  const float *k_scale, *k_bias;
 } hymba_mixer_params;
 
 /* Bytes of caller-provided device workspace the call needs for this geometry

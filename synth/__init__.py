@@ -30,6 +30,7 @@ __all__ = [
     "round_bf16",
     "make_prefill_inputs",
     "make_decode_inputs",
+    "key_affine",
     "POISON",
 ]
 
@@ -41,7 +42,7 @@ POISON = 8.0
 _TID = {
     "x": 1, "z": 2, "dt": 3, "B": 4, "C": 5, "q": 6, "k": 7, "v": 8,
     "A": 9, "conv_w": 10, "ssm_state": 11, "conv_state": 12,
-    "k_cache": 13, "v_cache": 14,
+    "k_cache": 13, "v_cache": 14, "k_affine": 15,
 }
 
 
@@ -71,6 +72,8 @@ class MixerConfig:
     cache_len: int = 0     # decode: rows already in the cache (new token's position)
     cache_capacity: int = 0
     n_layers: int = 1      # decode: layers sharing one KV cache
+    key_affine: bool = False   # decode: layers after the first read the shared keys through
+                               # their own affine (k_scale, k_bias); prefill: the layer does
     workload: str = ""
 
     @property
@@ -114,9 +117,10 @@ CONFIGS: Dict[str, MixerConfig] = {
     "decode": MixerConfig(
         name="decode", batch=64, n_meta=128, n_tokens=1, d_inner=3200,
         n_q_heads=25, n_kv_heads=5, head_dim=64, window=1024, act="bf16", seed=4,
-        decode=True, cache_len=8192, cache_capacity=8192, n_layers=2,
+        decode=True, cache_len=8192, cache_capacity=8192, n_layers=2, key_affine=True,
         workload="decode step, batch 64, cache 8192 rows (window 1024 + 128 meta), "
-                 "25q/5kv x 64, KV cache shared read-only by two layers"),
+                 "25q/5kv x 64, KV cache shared read-only by two layers, the second "
+                 "reading its keys through a per-head affine"),
 }
 
 CONFIG_ORDER = ["tiny_f32", "swa_layer", "global_layer", "batched_prefill", "decode"]
@@ -181,6 +185,15 @@ def _params(cfg: MixerConfig, layer: int) -> Dict[str, np.ndarray]:
     }
 
 
+def key_affine(cfg: MixerConfig, layer: int) -> Dict[str, np.ndarray]:
+    """Head-specific affine of a layer that reads another layer's keys:
+    k_scale U[0.5, 1.5) and k_bias N(0, 1), each [Hkv, hd] fp32."""
+    g = _rng(cfg, layer, "k_affine")
+    shape = (cfg.n_kv_heads, cfg.head_dim)
+    return {"k_scale": (np.float32(0.5) + g.random(size=shape, dtype=np.float32)).astype(np.float32),
+            "k_bias": g.standard_normal(size=shape, dtype=np.float32)}
+
+
 def make_prefill_inputs(cfg: MixerConfig, layer: int = 0) -> Dict[str, np.ndarray]:
     """x, z, dt [B,L,D]; B, C [B,L,N]; q [B,L,Hq,hd]; k [B,L,Hkv,hd]; v [B,L,Hkv,dv]
     in the activation dtype's values, plus fp32 parameters."""
@@ -197,6 +210,8 @@ def make_prefill_inputs(cfg: MixerConfig, layer: int = 0) -> Dict[str, np.ndarra
         "v": _act(cfg, _normal(cfg, layer, "v", (Bsz, L, Hkv, dv))),
     }
     out.update(_params(cfg, layer))
+    if cfg.key_affine:
+        out.update(key_affine(cfg, layer))
     return out
 
 
@@ -206,7 +221,8 @@ def make_decode_inputs(cfg: MixerConfig, cache_len: Optional[np.ndarray] = None)
     Shared: k_cache [B,cap,Hkv,hd], v_cache [B,cap,Hkv,dv] (rows treated as already
     rotated), k_new [B,Hkv,hd], v_new [B,Hkv,dv], cache_len [B] int32.
     Per layer l (dict ``layers[l]``): x, z, dt [B,D]; B, C [B,N]; q [B,Hq,hd];
-    ssm_state [B,D,N] fp32; conv_state [B,D,d_conv-1] (act); parameters.
+    ssm_state [B,D,N] fp32; conv_state [B,D,d_conv-1] (act); parameters; with
+    ``cfg.key_affine``, layers after the first also k_scale, k_bias [Hkv,hd].
 
     Rows [0, cache_len[b]) of sequence b hold N(0,1) draws; rows at or beyond
     cache_len[b] have not been written by any earlier step and hold POISON.
@@ -247,6 +263,8 @@ def make_decode_inputs(cfg: MixerConfig, cache_len: Optional[np.ndarray] = None)
             "conv_state": _act(cfg, _normal(cfg, l, "conv_state", (Bsz, D, cfg.d_conv - 1))),
         }
         d.update(_params(cfg, l))
+        if cfg.key_affine and l > 0:
+            d.update(key_affine(cfg, l))
         layers.append(d)
     shared["layers"] = layers
     return shared

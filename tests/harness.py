@@ -61,7 +61,11 @@ class Prefill:
             self.o["k_cache"] = torch.full((Bsz, self.cap, cfg.n_kv_heads, cfg.head_dim), 7.0, dtype=dt_, device="cuda")
             self.o["v_cache"] = torch.full((Bsz, self.cap, cfg.n_kv_heads, cfg.head_dim_v), 7.0, dtype=dt_, device="cuda")
         self.desc = desc_for(cfg, cache_capacity=self.cap)
-        self.params = H.make_params(self.p["A"], self.p["D"], self.p["conv_w"], self.p["beta_attn"], self.p["beta_ssm"])
+        for k in ("k_scale", "k_bias"):
+            if inp.get(k) is not None:
+                self.p[k] = dev(inp[k])
+        self.params = H.make_params(self.p["A"], self.p["D"], self.p["conv_w"], self.p["beta_attn"], self.p["beta_ssm"],
+                                    self.p.get("k_scale"), self.p.get("k_bias"))
         self.ws = torch.empty(max(H.hymba_mixer_prefill_workspace_bytes(self.desc), 256), dtype=torch.uint8,
                               device="cuda")
 
@@ -94,9 +98,11 @@ class Decode:
         for li in inp["layers"]:
             L = {k: dev(li[k], act) for k in ("x", "z", "dt", "B", "C", "q", "conv_state")}
             L["ssm_state"] = dev(li["ssm_state"])
-            L["params_t"] = {k: dev(li[k]) for k in ("A", "D", "conv_w", "beta_attn", "beta_ssm")}
+            L["params_t"] = {k: dev(li[k]) for k in ("A", "D", "conv_w", "beta_attn", "beta_ssm", "k_scale", "k_bias")
+                             if li.get(k) is not None}
             pt = L["params_t"]
-            L["params"] = H.make_params(pt["A"], pt["D"], pt["conv_w"], pt["beta_attn"], pt["beta_ssm"])
+            L["params"] = H.make_params(pt["A"], pt["D"], pt["conv_w"], pt["beta_attn"], pt["beta_ssm"],
+                                        pt.get("k_scale"), pt.get("k_bias"))
             L["out"] = torch.empty((Bsz, D), dtype=dt_, device="cuda")
             L["y_attn_out"] = torch.empty((Bsz, D), dtype=dt_, device="cuda")
             L["y_ssm_out"] = torch.empty((Bsz, D), dtype=dt_, device="cuda")

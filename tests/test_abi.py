@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert H.hymba_abi_version() == 1
+    assert H.hymba_abi_version() == 2
     assert H.hymba_status_string(0) == "ok"
     for s in (-1, -2, -3, -4, -5):
         assert H.hymba_status_string(s) != "unknown status"
@@ -116,6 +116,8 @@ def test_prefill_rejects_pointers_and_workspace(lib):
     assert call(ok, params=bad) == -2                        # conv bias unsupported
     nullp = _lib.MixerParams(None, fake, fake, None, fake, fake)
     assert call(ok, params=nullp) == -1
+    skew = _lib.MixerParams(fake, fake, fake, None, fake, fake, fake + 4, None)
+    assert call(ok, params=skew) == -3                       # misaligned k_scale
     # k_cache without v_cache, and a cache too short for L rows
     st = lib.hymba_mixer_prefill(ctypes.byref(d), ctypes.byref(p), *ok, None, None, fake, None, None, None, fake,
                                  1 << 40, None, None)

@@ -123,6 +123,24 @@ def test_prefill_small_shapes(kw):
     run_prefill_parity(cfg)
 
 
+AFFINE_PREFILL = [
+    # two kv heads with two query heads each: a head must take its own group's w
+    dict(batch=2, n_meta=5, n_tokens=130, d_inner=256, n_q_heads=4, n_kv_heads=2, window=40, act="bf16", seed=41),
+    dict(batch=1, n_meta=8, n_tokens=75, d_inner=256, n_q_heads=4, n_kv_heads=2, window=0, act="f32", seed=42),
+]
+
+
+@pytest.mark.parametrize("kw", AFFINE_PREFILL, ids=["bf16_swa", "f32_global"])
+def test_prefill_shared_key_affine(kw):
+    """A layer reading shared keys through its affine K w + b: attention as the
+    oracle computes it (bias included), cache rows without the affine."""
+    cfg = synth.config("tiny_f32").with_(**kw, key_affine=True, name="affine")
+    run, inp, got = run_prefill_parity(cfg)
+    plain = {k: v for k, v in inp.items() if k not in ("k_scale", "k_bias")}
+    ref_plain = O.mixer_prefill(cfg, plain)
+    assert rel_l2(got["y_attn_out"], ref_plain["y_attn"]) > 20 * TOL[cfg.act]   # the affine is not a no-op
+
+
 def test_prefill_swa_layer_full():
     run_prefill_parity(synth.config("swa_layer"))
 
@@ -188,6 +206,11 @@ def run_decode_parity(cfg, cache_len=None):
         check("out", host(L["out"]), ref["out"], tol)
         check("ssm_state", host(L["ssm_state"]), ref["ssm_state"], tol)
         check("conv_state", host(L["conv_state"]), ref["conv_state"], 0.0)
+        if inp["layers"][l].get("k_scale") is not None:   # a secondary layer: its affine matters
+            plain = {k: v for k, v in inp["layers"][l].items() if k not in ("k_scale", "k_bias")}
+            ref_plain = O.mixer_decode(cfg, plain, inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"],
+                                       inp["cache_len"])
+            assert rel_l2(host(L["y_attn_out"]), ref_plain["y_attn"]) > 20 * tol
     return run
 
 
