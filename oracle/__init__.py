@@ -18,7 +18,12 @@ from .hymba_oracle import (  # noqa: F401
     shared_key_affine,
     rms_fuse,
     mixer_prefill,
+    mixer_prefill_continue,
     mixer_decode,
+    ring_slot,
+    cache_rows,
+    cache_store,
+    visible_history,
     kv_cache_bytes,
     ssm_state_bytes,
 )

@@ -309,8 +309,109 @@ def mixer_prefill(cfg, inp: Dict[str, np.ndarray], batches: Optional[Iterable[in
     return res
 
 
+# ---------------------------------------------------------------------------
+# KV cache layouts: one row per position, or the compact sliding-window form
+
+
+def ring_slot(positions, n_meta: int, window: int) -> np.ndarray:
+    """Cache row of absolute position p in the compact cache of a sliding-window
+    layer (Hymba-1.5B article, section 1: SWA layers keep a compact cache).
+
+    Reading: a query at position i sees the meta rows and the positions
+    i - window + 1 .. i, so a cache of n_meta + window rows suffices: meta
+    rows keep their own row, later positions share a ring of ``window`` rows,
+    p -> n_meta + (p - n_meta) mod window. Positions ``window`` apart share a
+    row and the later one replaces the earlier, which no query can still see.
+    """
+    if window <= 0:
+        raise ValueError("a compact cache needs a sliding window (window > 0)")
+    p = np.asarray(positions, np.int64)
+    return np.where(p < n_meta, p, n_meta + (p - n_meta) % window)
+
+
+def cache_rows(positions, n_meta: int, window: int, ring: bool) -> np.ndarray:
+    """Cache row of each position: the position itself, or its ring_slot."""
+    p = np.asarray(positions, np.int64)
+    return ring_slot(p, n_meta, window) if ring else p
+
+
+def cache_store(cache, rows, positions, n_meta: int, window: int, ring: bool) -> np.ndarray:
+    """A copy of ``cache`` [B, cap, H, d] with rows[:, i] stored at the row of
+    positions[i], in increasing position order (so a later position replaces
+    an earlier one that shares its ring row)."""
+    out = _f64(cache).copy()
+    pos = np.asarray(positions, np.int64)
+    order = np.argsort(pos, kind="stable")
+    dst = cache_rows(pos, n_meta, window, ring)
+    for i in order:
+        out[:, dst[i]] = _f64(rows)[:, i]
+    return out
+
+
+def visible_history(p: int, n_meta: int, window: int) -> np.ndarray:
+    """Positions below p that a query at position p (>= n_meta) can see: the
+    meta rows and, under a window, p - window + 1 .. p - 1 (``visible``)."""
+    j = np.arange(p)
+    return j[visible(p, j, n_meta, window)]
+
+
+def mixer_prefill_continue(cfg, inp: Dict[str, np.ndarray], pos0: int, ssm_state, conv_state, k_cache, v_cache,
+                           ring: bool = False) -> Dict[str, np.ndarray]:
+    """Prefill of T further rows per sequence at positions pos0 .. pos0 + T - 1
+    (T = inp["x"].shape[1]), continuing an earlier prefill (or decode steps)
+    from its state.
+
+    The Mamba branch resumes from the carried state: conv history and SSM state
+    after row pos0 - 1 (Hymba guide, "2. Learnable Meta-Tokens": the state
+    carries what came before; Lecture 04, section 2: a fixed-size state is all
+    the scan needs). Attention sees the cached rotated keys and values of
+    earlier positions and the new rows under the usual visibility rule
+    (Lecture 04, section 1: the cache grows per token). Reading: pos0 is the
+    same for every sequence and pos0 >= n_meta (the meta rows were in the
+    first call). The cache is one row per position, or the ring of
+    ``ring_slot`` when ``ring``.
+
+    inp: x, z, dt [B,T,D]; B, C [B,T,N]; q [B,T,Hq,d]; k [B,T,Hkv,d];
+    v [B,T,Hkv,dv]; parameters; optional k_scale, k_bias (shared_key_affine).
+    ssm_state [B,D,N]; conv_state [B,D,K-1] (oldest first); k_cache, v_cache
+    [B,cap,Hkv,d(v)] with the rows of positions < pos0.
+    Returns y_ssm, y_attn, out [B,T,D]; ssm_state, conv_state after the last
+    row; k_rot [B,T,Hkv,d] of the new rows; k_cache, v_cache with the new rows
+    stored (copies).
+    """
+    n_meta, window = cfg.n_meta, cfg.window
+    if pos0 < n_meta:
+        raise ValueError("a continuation starts at or after the meta rows")
+    x = _f64(inp["x"])
+    Bsz, T, D = x.shape
+    K = cfg.d_conv
+    hist = np.transpose(_f64(conv_state), (0, 2, 1))                      # [B,K-1,D]
+    u = causal_conv1d(x, inp["conv_w"], history=hist)
+    y, h = selective_scan(u, _f64(inp["dt"]), inp["A"], _f64(inp["B"]), _f64(inp["C"]), inp["D"],
+                          h0=ssm_state)
+    y_ssm = silu_gate(y, _f64(inp["z"]))
+    xh = np.concatenate([hist, x], axis=1)                                # rows pos0-K+1 .. pos0+T-1
+    new_conv = np.transpose(xh[:, -(K - 1):, :], (0, 2, 1))
+    pos = pos0 + np.arange(T)
+    q_rot = rope(_f64(inp["q"]), pos, cfg.rope_base)
+    k_rot = rope(_f64(inp["k"]), pos, cfg.rope_base)
+    old = visible_history(pos0, n_meta, window)                           # what any new row may still see
+    src = cache_rows(old, n_meta, window, ring)
+    keys = np.concatenate([_f64(k_cache)[:, src], k_rot], axis=1)
+    vals = np.concatenate([_f64(v_cache)[:, src], _f64(inp["v"])], axis=1)
+    keys = shared_key_affine(keys, inp.get("k_scale"), inp.get("k_bias"))
+    ya = attention(q_rot, keys, vals, n_meta, window, key_positions=np.concatenate([old, pos]),
+                   query_positions=pos)
+    y_attn = ya.reshape(Bsz, T, cfg.n_q_heads * cfg.head_dim_v)
+    out = rms_fuse(y_attn, y_ssm, inp["beta_attn"], inp["beta_ssm"], cfg.norm_eps)
+    return {"y_ssm": y_ssm, "y_attn": y_attn, "out": out, "ssm_state": h, "conv_state": new_conv,
+            "k_rot": k_rot,
+            "k_cache": cache_store(k_cache, k_rot, pos, n_meta, window, ring),
+            "v_cache": cache_store(v_cache, inp["v"], pos, n_meta, window, ring)}
+
+
 def mixer_decode(cfg, layer_inp: Dict[str, np.ndarray], k_cache, v_cache, k_new, v_new,
-                 cache_len) -> Dict[str, np.ndarray]:
+                 cache_len, ring: bool = False) -> Dict[str, np.ndarray]:
     """One new row per sequence at position p = cache_len[b].
 
     Lecture 04, section 1: the new token attends over the cached keys and
@@ -323,7 +424,8 @@ def mixer_decode(cfg, layer_inp: Dict[str, np.ndarray], k_cache, v_cache, k_new,
 
     Optional layer_inp["k_scale"], ["k_bias"] ([Hkv, d]): this layer is a
     secondary one and reads the shared keys (the new row's included) through
-    shared_key_affine.
+    shared_key_affine. With ``ring`` the cache is the compact form of
+    ``ring_slot`` and only the positions the new row can see are read from it.
 
     Returns out, y_attn, y_ssm [B, D] and the new ssm_state [B, D, N],
     conv_state [B, D, K-1] (float64).
@@ -346,11 +448,13 @@ def mixer_decode(cfg, layer_inp: Dict[str, np.ndarray], k_cache, v_cache, k_new,
         pos = np.array([p])
         q_rot = rope(_f64(li["q"])[b][None, None], pos, cfg.rope_base)          # [1,1,Hq,d]
         kn = rope(_f64(k_new)[b][None, None], pos, cfg.rope_base)[0]             # [1,Hkv,d]
-        keys = np.concatenate([_f64(k_cache[b, :p]), kn], axis=0)[None]          # [1,p+1,Hkv,d]
+        old = visible_history(p, cfg.n_meta, cfg.window) if ring else np.arange(p)
+        src = cache_rows(old, cfg.n_meta, cfg.window, ring)
+        keys = np.concatenate([_f64(k_cache[b])[src], kn], axis=0)[None]         # [1,n+1,Hkv,d]
         keys = shared_key_affine(keys, li.get("k_scale"), li.get("k_bias"))
-        vals = np.concatenate([_f64(v_cache[b, :p]), _f64(v_new)[b][None]], axis=0)[None]
+        vals = np.concatenate([_f64(v_cache[b])[src], _f64(v_new)[b][None]], axis=0)[None]
         ya = attention(q_rot, keys, vals, cfg.n_meta, cfg.window, rows=np.array([0]),
-                       key_positions=np.arange(p + 1), query_positions=pos)
+                       key_positions=np.append(old, p), query_positions=pos)
         y_attn[b] = ya.reshape(Hq * dv)
     out = rms_fuse(y_attn, y_ssm, li["beta_attn"], li["beta_ssm"], cfg.norm_eps)
     return {"out": out, "y_attn": y_attn, "y_ssm": y_ssm, "ssm_state": h, "conv_state": new_conv}

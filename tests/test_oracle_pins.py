@@ -475,3 +475,113 @@ def test_key_affine_decode_equals_prefill_of_one_more_row():
                          np.full(cfg.batch, L - 1))
     np.testing.assert_allclose(dec["y_attn"], ref["y_attn"][:, L - 1], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(dec["out"], ref["out"][:, L - 1], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# continuing a prefill from its state, and the compact sliding-window cache
+# (Hymba-1.5B article, section 1; Lecture 04, sections 1 and 2)
+
+_PER_ROW = ("x", "z", "dt", "B", "C", "q", "k", "v")
+
+
+def _rows(full, a, b):
+    return {k: (v[:, a:b] if k in _PER_ROW else v) for k, v in full.items()}
+
+
+def _chain(cfg, full, cuts, ring):
+    """Prefill of rows [0, cuts[0]) then one continuation per later cut; the
+    cache is one row per position or the compact ring. Returns the
+    concatenated outputs, the final states and the cache."""
+    L, M, W = cfg.seq_rows, cfg.n_meta, cfg.window
+    Hkv, d, dv = cfg.n_kv_heads, cfg.head_dim, cfg.head_dim_v
+    cap = M + W if ring else L
+    pre = O.mixer_prefill(cfg.with_(n_tokens=cuts[0] - M), _rows(full, 0, cuts[0]))
+    first = np.arange(cuts[0])
+    kc = O.cache_store(np.zeros((cfg.batch, cap, Hkv, d)), pre["k_rot"], first, M, W, ring)
+    vc = O.cache_store(np.zeros((cfg.batch, cap, Hkv, dv)), full["v"][:, :cuts[0]], first, M, W, ring)
+    outs = {k: [pre[k]] for k in ("y_ssm", "y_attn", "out")}
+    state, conv = pre["ssm_state"], pre["conv_state"]
+    for a, b in zip(cuts, list(cuts[1:]) + [L]):
+        r = O.mixer_prefill_continue(cfg.with_(n_tokens=b - a), _rows(full, a, b), a, state, conv, kc, vc,
+                                     ring=ring)
+        for k in outs:
+            outs[k].append(r[k])
+        state, conv, kc, vc = r["ssm_state"], r["conv_state"], r["k_cache"], r["v_cache"]
+    res = {k: np.concatenate(v, axis=1) for k, v in outs.items()}
+    res.update(ssm_state=state, conv_state=conv, k_cache=kc, v_cache=vc)
+    return res
+
+
+@pytest.mark.parametrize("ring", [False, True])
+@pytest.mark.parametrize("cuts", [[3], [3, 4, 5], [5, 6, 11], [8, 12]])
+def test_continuation_equals_one_prefill(ring, cuts):
+    """Cutting a prefill anywhere after the meta rows and continuing from the
+    carried state (SSM state, conv history, cache) gives the rows of one
+    prefill: chunks of one row (conv history from the state) and chunks
+    longer than the window (ring rows replaced within a chunk) included."""
+    cfg = _tiny_cfg(n_meta=3, n_tokens=11, window=4)
+    full = synth.make_prefill_inputs(cfg)
+    ref = O.mixer_prefill(cfg, full)
+    got = _chain(cfg, full, cuts, ring)
+    for k in ("y_ssm", "y_attn", "out"):
+        np.testing.assert_allclose(got[k], ref[k], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got["ssm_state"], ref["ssm_state"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(got["conv_state"], ref["conv_state"])
+    L, M, W = cfg.seq_rows, cfg.n_meta, cfg.window
+    if ring:   # the meta rows and the last W positions, each in its ring row
+        keep = np.concatenate([np.arange(M), np.arange(L - W, L)])
+        rows = O.ring_slot(keep, M, W)
+        np.testing.assert_array_equal(np.sort(rows), np.arange(M + W))
+        np.testing.assert_allclose(got["k_cache"][:, rows], ref["k_rot"][:, keep], rtol=0, atol=1e-14)
+        np.testing.assert_array_equal(got["v_cache"][:, rows], full["v"][:, keep])
+    else:
+        np.testing.assert_allclose(got["k_cache"], ref["k_rot"], rtol=0, atol=1e-14)
+        np.testing.assert_array_equal(got["v_cache"], full["v"])
+
+
+def test_continuation_global_layer_and_sequences_independent():
+    cfg = _tiny_cfg(n_meta=2, n_tokens=9, window=0, batch=3)
+    full = synth.make_prefill_inputs(cfg)
+    ref = O.mixer_prefill(cfg, full)
+    got = _chain(cfg, full, [4, 9], ring=False)
+    np.testing.assert_allclose(got["out"], ref["out"], rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.ring_slot([5], 2, 0)   # a global layer has no compact form
+
+
+def test_ring_slot_closed_form_and_no_visible_row_lost():
+    M, W = 3, 4
+    p = np.arange(40)
+    s = O.ring_slot(p, M, W)
+    np.testing.assert_array_equal(s[:M + W], np.arange(M + W))          # first pass fills the rows in order
+    np.testing.assert_array_equal(s[M:], M + (p[M:] - M) % W)
+    assert s.max() == M + W - 1                                        # capacity n_meta + window
+    for q in range(M, 40 - W):                                         # W consecutive positions: W distinct rows
+        assert len(set(s[q:q + W])) == W
+    # storing positions 0 .. p - 1 in order leaves every position that a query
+    # at p can see in its row (no later position below p took that row)
+    for pq in range(M, 40):
+        owner = {}
+        for q in range(pq):
+            owner[int(s[q])] = q
+        for q in O.visible_history(pq, M, W):
+            assert owner[int(s[q])] == q, (pq, q)
+        assert len(O.visible_history(pq, M, W)) == min(pq, M + W - 1)
+
+
+@pytest.mark.parametrize("window", [4, 1])
+def test_decode_on_the_ring_equals_decode_on_the_full_cache(window):
+    """A decode step reads the same keys from the compact ring as from one row
+    per position, also far past the ring's capacity."""
+    cfg = _tiny_cfg(n_meta=3, window=window).with_(decode=True, cache_capacity=64, n_layers=1)
+    for p in (3, 5, 3 + window, 29, 63):
+        inp = synth.make_decode_inputs(cfg, cache_len=np.full(cfg.batch, p, np.int32))
+        ring_k = O.cache_store(np.zeros((cfg.batch, cfg.n_meta + window, cfg.n_kv_heads, cfg.head_dim)),
+                               inp["k_cache"][:, :p], np.arange(p), cfg.n_meta, window, True)
+        ring_v = O.cache_store(np.zeros((cfg.batch, cfg.n_meta + window, cfg.n_kv_heads, cfg.head_dim_v)),
+                               inp["v_cache"][:, :p], np.arange(p), cfg.n_meta, window, True)
+        lay = inp["layers"][0]
+        a = O.mixer_decode(cfg, lay, inp["k_cache"], inp["v_cache"], inp["k_new"], inp["v_new"], inp["cache_len"])
+        b = O.mixer_decode(cfg, lay, ring_k, ring_v, inp["k_new"], inp["v_new"], inp["cache_len"], ring=True)
+        np.testing.assert_allclose(b["out"], a["out"], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(b["y_attn"], a["y_attn"], rtol=1e-13, atol=1e-14)
