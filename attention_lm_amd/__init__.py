@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     hymba_mixer_decode_workspace_bytes,
     hymba_mixer_prefill,
     hymba_mixer_prefill_chunk_rows,
+    hymba_mixer_prefill_continue,
     hymba_mixer_prefill_workspace_bytes,
     hymba_status_string,
     load_library,

@@ -23,6 +23,7 @@ _EXPORTS = [
     "hymba_mixer_prefill_workspace_bytes",
     "hymba_mixer_decode_workspace_bytes",
     "hymba_mixer_prefill",
+    "hymba_mixer_prefill_continue",
     "hymba_mixer_decode",
     "hymba_fuse_heads",
     "hymba_debug_mask_ranges",
@@ -39,6 +40,7 @@ class MixerDesc(ctypes.Structure):
         ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("head_dim_v", ctypes.c_int32), ("window", ctypes.c_int32), ("cache_capacity", ctypes.c_int32),
         ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float), ("act", ctypes.c_int),
+        ("cache_ring", ctypes.c_int32),
     ]
 
 
@@ -74,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hymba_mixer_decode_workspace_bytes.restype = sz
     lib.hymba_mixer_prefill.argtypes = [pdesc, pparams] + [vp] * 8 + [vp] + [vp] * 6 + [vp, sz, vp, vp]
     lib.hymba_mixer_prefill.restype = ctypes.c_int
+    lib.hymba_mixer_prefill_continue.argtypes = [pdesc, pparams, i32] + [vp] * 8 + [vp] + [vp] * 6 + [vp, sz, vp]
+    lib.hymba_mixer_prefill_continue.restype = ctypes.c_int
     lib.hymba_mixer_decode.argtypes = [pdesc, pparams] + [vp] * 8 + [vp, vp, vp] + [vp, vp] + [vp, vp, vp] + [vp, sz, vp, vp]
     lib.hymba_mixer_decode.restype = ctypes.c_int
     lib.hymba_fuse_heads.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, ctypes.c_int, vp, vp]
@@ -96,12 +100,12 @@ DECODE_STAGES = ("ssm_decode", "attn_decode", "decode_merge_fuse")
 
 def make_desc(batch, n_meta, n_tokens, d_inner, n_q_heads, n_kv_heads, window, act, head_dim=64,
               head_dim_v=None, d_state=16, d_conv=4, cache_capacity=0, rope_base=10000.0,
-              norm_eps=1e-6) -> MixerDesc:
+              norm_eps=1e-6, cache_ring=False) -> MixerDesc:
     if head_dim_v is None:
         head_dim_v = d_inner // n_q_heads
     act_code = {"f32": HYMBA_F32, "bf16": HYMBA_BF16}.get(act, act)
     return MixerDesc(batch, n_meta, n_tokens, d_inner, d_state, d_conv, n_q_heads, n_kv_heads, head_dim,
-                     head_dim_v, window, cache_capacity, rope_base, norm_eps, act_code)
+                     head_dim_v, window, cache_capacity, rope_base, norm_eps, act_code, int(bool(cache_ring)))
 
 
 def make_params(A, D, conv_w, beta_attn, beta_ssm, k_scale=None, k_bias=None) -> MixerParams:
@@ -165,6 +169,20 @@ def hymba_mixer_prefill(desc: MixerDesc, params: MixerParams, x, z, dt, B, C, q,
         _ptr(y_attn_out), _ptr(y_ssm_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         stage_events, _stream(stream))
     _check("hymba_mixer_prefill", st)
+
+
+def hymba_mixer_prefill_continue(desc: MixerDesc, params: MixerParams, pos0: int, x, z, dt, B, C, q, k, v, out,
+                                 ssm_state, conv_state, k_cache, v_cache, y_attn_out=None, y_ssm_out=None,
+                                 workspace=None, stream=None):
+    lib = load_library()
+    if workspace is None:
+        workspace = _workspace(hymba_mixer_prefill_workspace_bytes(desc), out.device)
+    st = lib.hymba_mixer_prefill_continue(
+        ctypes.byref(desc), ctypes.byref(params), int(pos0), _ptr(x), _ptr(z), _ptr(dt), _ptr(B), _ptr(C),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ssm_state), _ptr(conv_state), _ptr(k_cache), _ptr(v_cache),
+        _ptr(y_attn_out), _ptr(y_ssm_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check("hymba_mixer_prefill_continue", st)
 
 
 def hymba_mixer_decode(desc: MixerDesc, params: MixerParams, x, z, dt, B, C, q, k_new, v_new, k_cache,

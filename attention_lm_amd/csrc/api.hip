@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <unordered_map>
 
@@ -93,6 +94,10 @@ int check_desc(const hymba_mixer_desc* d, bool decode) {
   if (!(d->rope_base > 0.f) || !(d->norm_eps >= 0.f)) return HYMBA_EINVAL;
   if (d->cache_capacity < 0) return HYMBA_EINVAL;
   if (decode && d->cache_capacity < 1) return HYMBA_EINVAL;
+  if (d->cache_ring != 0 && d->cache_ring != 1) return HYMBA_EINVAL;
+  // the compact cache exists for sliding-window layers and holds n_meta + window rows
+  if (d->cache_ring && (d->window <= 0 || (int64_t)d->cache_capacity < (int64_t)d->n_meta + d->window))
+    return HYMBA_EINVAL;
   // what this build has kernels for
   if (d->d_state != 16 || d->d_conv != 4 || d->head_dim != 64) return HYMBA_EUNSUPPORTED;
   if (d->head_dim_v != 32 && d->head_dim_v != 64 && d->head_dim_v != 128) return HYMBA_EUNSUPPORTED;
@@ -122,9 +127,15 @@ int check_params(const hymba_mixer_params* p) {
   return HYMBA_OK;
 }
 
+// Workspace of both prefill entry points: a fresh prefill has L = n_meta +
+// n_tokens rows, a continuation n_tokens rows (and, with the compact cache,
+// an assembly of the meta rows, up to window - 1 earlier rows and the new rows
+// that its attention reads).
 struct PrefillWs {
-  size_t q_rot, k_rot, y_attn, y_ssm, agg, sdt, carry, total;
-  int chunk_rows;
+  size_t q_rot, k_rot, y_attn, y_ssm, agg, sdt, carry, conv_in, asm_k, asm_v, total;
+  int chunk_rows;        // fresh prefill
+  int chunk_rows_cont;   // continuation
+  int asm_rows;          // rows per sequence of the assembly (0 without the compact cache)
   bool carry_ok;
 };
 PrefillWs prefill_ws(const hymba_mixer_desc* d) {
@@ -138,13 +149,26 @@ PrefillWs prefill_ws(const hymba_mixer_desc* d) {
   w.agg = w.y_ssm + round256(rows * d->d_inner * es);
   const int L = d->n_meta + d->n_tokens;
   w.chunk_rows = hymba::ssm_prefill_chunk_rows(d->batch, L, d->d_inner);
-  const size_t nchunk = (size_t)((L + w.chunk_rows - 1) / w.chunk_rows);
+  w.chunk_rows_cont = hymba::ssm_prefill_chunk_rows(d->batch, d->n_tokens > 0 ? d->n_tokens : 1, d->d_inner);
+  const size_t nchunk = std::max((size_t)((L + w.chunk_rows - 1) / w.chunk_rows),
+                                 (size_t)((d->n_tokens + w.chunk_rows_cont - 1) / w.chunk_rows_cont));
   const size_t chans = (size_t)d->batch * d->d_inner;
   w.sdt = w.agg + round256(nchunk * chans * 16 * sizeof(float));
   w.carry = w.sdt + round256(nchunk * chans * sizeof(float));
-  w.total = w.carry + round256(nchunk * chans * 16 * sizeof(float));
+  w.conv_in = w.carry + round256(nchunk * chans * 16 * sizeof(float));
+  w.asm_k = w.conv_in + round256(chans * (d->d_conv - 1) * es);
+  w.asm_rows = d->cache_ring ? d->n_meta + d->window - 1 + d->n_tokens : 0;
+  const size_t arows = (size_t)d->batch * w.asm_rows;
+  w.asm_v = w.asm_k + round256(arows * d->n_kv_heads * d->head_dim * es);
+  w.total = w.asm_v + round256(arows * d->n_kv_heads * d->head_dim_v * es);
   w.carry_ok = nchunk * chans * 16 * sizeof(float) <= (size_t)INT32_MAX;   // 32-bit offsets in the carry chain
   return w;
+}
+
+// bytes of one cache row (all kv heads) of the wider of K and V
+int64_t kv_row_bytes(const hymba_mixer_desc* d) {
+  return (int64_t)d->n_kv_heads * (d->head_dim > d->head_dim_v ? d->head_dim : d->head_dim_v) *
+         (int64_t)act_bytes(d->act);
 }
 
 struct DecodeWs {
@@ -184,6 +208,177 @@ size_t hymba_mixer_decode_workspace_bytes(const hymba_mixer_desc* desc) {
   return decode_ws(desc).total;
 }
 
+}  // extern "C"
+
+namespace {
+
+// One prefill call, fresh (pos0 = 0, no carried state) or continuing.
+struct PrefillCall {
+  const void *x, *z, *dt, *B, *C, *q, *k, *v;
+  void* out;
+  int pos0;                       // position of the call's first row
+  bool cont;                      // continuation: rows are n_tokens rows at pos0 ..
+  const float* state_in;          // continuation: carried SSM state (may equal state_out)
+  const void* conv_in;            // continuation: carried conv history (may equal conv_out)
+  float* state_out;
+  void* conv_out;
+  void *k_cache, *v_cache;
+  void *y_attn_out, *y_ssm_out;
+  void* workspace;
+  size_t workspace_bytes;
+  hipEvent_t* stage_events;
+};
+
+int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params, const PrefillCall& c,
+                 hipStream_t stream) {
+  const int M = desc->n_meta, W = desc->window;
+  const bool ring = desc->cache_ring != 0;
+  const int L = c.cont ? desc->n_tokens : M + desc->n_tokens;   // rows in this call
+  const PrefillWs ws = prefill_ws(desc);
+  if (!ws.carry_ok) return HYMBA_EUNSUPPORTED;
+  if (!c.workspace || c.workspace_bytes < ws.total) return HYMBA_EWORKSPACE;
+  if (((uintptr_t)c.workspace & 255u) != 0) return HYMBA_EALIGN;
+
+  char* wsb = (char*)c.workspace;
+  void* q_rot = wsb + ws.q_rot;
+  void* y_attn = c.y_attn_out ? c.y_attn_out : (void*)(wsb + ws.y_attn);
+  void* y_ssm = c.y_ssm_out ? c.y_ssm_out : (void*)(wsb + ws.y_ssm);
+
+  // stage i's kernel records stage_events[2i] when it starts and [2i+1] when it ends
+  auto tm = [&](int i) -> hymba::Timing {
+    hymba::Timing t;
+    if (c.stage_events) {
+      t.start = c.stage_events[2 * i];
+      t.stop = c.stage_events[2 * i + 1];
+    }
+    return t;
+  };
+  // The two branches are independent until the fusion: without stage events the
+  // Mamba branch runs on a second stream, concurrently with the attention branch.
+  ForkCtx* fc = nullptr;
+  if (!c.stage_events) HYMBA_TRY(fork_ctx(&fc));
+  hipStream_t ssm_stream = stream;
+  if (fc) {
+    HYMBA_TRY(hipEventRecord(fc->fork, stream));
+    HYMBA_TRY(hipStreamWaitEvent(fc->aux, fc->fork, 0));
+    ssm_stream = fc->aux;
+  }
+  hymba::SsmPrefillArgs sa;
+  sa.x = c.x; sa.z = c.z; sa.dt = c.dt; sa.B = c.B; sa.C = c.C;
+  sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
+  sa.y = y_ssm; sa.state_out = c.state_out; sa.conv_state_out = c.conv_out;
+  sa.state_in = c.state_in;
+  sa.conv_in = nullptr;
+  if (c.conv_in) {   // a private copy: the output pass writes the caller's buffer while it is still read
+    void* staged = wsb + ws.conv_in;
+    HYMBA_TRY(hipMemcpyAsync(staged, c.conv_in,
+                             (size_t)desc->batch * desc->d_inner * (desc->d_conv - 1) * act_bytes(desc->act),
+                             hipMemcpyDeviceToDevice, ssm_stream));
+    sa.conv_in = staged;
+  }
+  sa.agg = (float*)(wsb + ws.agg); sa.sdt = (float*)(wsb + ws.sdt); sa.carry = (float*)(wsb + ws.carry);
+  sa.chunk_rows = c.cont ? ws.chunk_rows_cont : ws.chunk_rows;
+  sa.batch = desc->batch; sa.L = L; sa.d_inner = desc->d_inner; sa.act = desc->act;
+  HYMBA_TRY(hymba::launch_ssm_chunk_end(sa, ssm_stream, tm(0)));
+  HYMBA_TRY(hymba::launch_ssm_chunk_carry(sa, ssm_stream, tm(1)));
+  HYMBA_TRY(hymba::launch_ssm_chunk_out(sa, ssm_stream, tm(2)));
+  if (fc) HYMBA_TRY(hipEventRecord(fc->join, fc->aux));
+
+  // Attention branch. Where the rotated keys and the values that attention
+  // reads live (row j of k_src / v_src = position j - shift):
+  //  * fresh, cache of one row per position: the cache itself (rope stores there);
+  //  * fresh otherwise: the workspace keys and the input values;
+  //  * continuation, one row per position: the cache (rope appends the new rows);
+  //  * continuation, compact ring: an assembly of meta rows, the earlier rows
+  //    the new ones can see, and the new rows.
+  hymba::RopeArgs ra;
+  ra.q = c.q; ra.k = c.k; ra.v = c.v; ra.q_rot = q_rot;
+  ra.k_scale = params->k_scale;
+  ra.batch = desc->batch; ra.L = L; ra.n_q_heads = desc->n_q_heads; ra.n_kv_heads = desc->n_kv_heads;
+  ra.head_dim = desc->head_dim; ra.head_dim_v = desc->head_dim_v; ra.rope_base = desc->rope_base;
+  ra.act = desc->act;
+  ra.pos0 = c.pos0;
+  hymba::AttnPrefillArgs aa;
+  aa.q_rot = q_rot; aa.y = y_attn;
+  aa.batch = desc->batch; aa.L = L; aa.n_meta = M; aa.window = W;
+  aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
+  aa.act = desc->act;
+  HYMBA_TRY(device_cus(&aa.n_cu));
+  hymba::KvCopyArgs kc;   // rows into the compact ring (fresh prefill, continuation)
+  kc.n = 0;
+  kc.n_meta = M; kc.window = W; kc.batch = desc->batch; kc.n_kv_heads = desc->n_kv_heads;
+  kc.head_dim_v = desc->head_dim_v; kc.act = desc->act;
+  kc.dst.k = c.k_cache; kc.dst.v = c.v_cache; kc.dst.k_rows = kc.dst.v_rows = desc->cache_capacity;
+  kc.dst.mode = hymba::KvSide::kRing; kc.dst.base = 0;
+  const int64_t cap = desc->cache_capacity;
+
+  if (!c.cont) {
+    if (c.k_cache && !ring) {
+      ra.k_rot = c.k_cache; ra.k_rows = cap; ra.v_copy = c.v_cache; ra.v_rows = cap;
+    } else {
+      ra.k_rot = wsb + ws.k_rot; ra.k_rows = L; ra.v_copy = nullptr; ra.v_rows = L;
+    }
+    ra.k_row0 = ra.v_row0 = 0;
+    aa.k_rot = ra.k_rot; aa.k_rows = ra.k_rows; aa.v = c.v; aa.v_rows = L; aa.q_pos0 = 0;
+    if (c.k_cache && ring) {   // the meta rows and the last `window` rows survive in the ring
+      kc.src.k = ra.k_rot; kc.src.v = c.v; kc.src.k_rows = L; kc.src.v_rows = L;
+      kc.src.mode = hymba::KvSide::kLinear; kc.src.base = 0;
+      kc.na = std::min(M, L); kc.pa = 0; kc.pb = std::max(M, L - W);
+      kc.n = kc.na + (L - kc.pb);
+    }
+    HYMBA_TRY(hymba::launch_rope_prefill(ra, stream, tm(3)));
+  } else if (!ring) {
+    ra.k_rot = c.k_cache; ra.k_rows = cap; ra.v_copy = c.v_cache; ra.v_rows = cap;
+    ra.k_row0 = ra.v_row0 = c.pos0;
+    aa.k_rot = c.k_cache; aa.k_rows = cap; aa.v = c.v_cache; aa.v_rows = cap; aa.q_pos0 = c.pos0;
+    HYMBA_TRY(hymba::launch_rope_prefill(ra, stream, tm(3)));
+  } else {
+    // assembly row r: position r below n_meta, then a0 + (r - n_meta); the
+    // attention runs on assembly rows as positions (the window rule depends on
+    // position differences only, and every key was rotated at its true position)
+    const int a0 = std::max(M, c.pos0 - W + 1), nw = c.pos0 - a0;
+    const int R = ws.asm_rows;
+    void* asm_k = wsb + ws.asm_k;
+    void* asm_v = wsb + ws.asm_v;
+    hymba::KvCopyArgs g = kc;   // ring -> assembly: meta rows, then positions a0 .. pos0 - 1
+    g.src = kc.dst;
+    g.dst.k = asm_k; g.dst.v = asm_v; g.dst.k_rows = g.dst.v_rows = R; g.dst.mode = hymba::KvSide::kIndex;
+    g.dst.base = 0;
+    g.na = M; g.pa = 0; g.pb = a0; g.n = M + nw;
+    HYMBA_TRY(hymba::launch_kv_copy(g, stream));
+    ra.k_rot = asm_k; ra.k_rows = R; ra.v_copy = asm_v; ra.v_rows = R;
+    ra.k_row0 = ra.v_row0 = M + nw;
+    aa.k_rot = asm_k; aa.k_rows = R; aa.v = asm_v; aa.v_rows = R; aa.q_pos0 = M + nw;
+    HYMBA_TRY(hymba::launch_rope_prefill(ra, stream, tm(3)));
+    // the new rows that stay: the last `window` positions (after the gather above)
+    kc.src.k = asm_k; kc.src.v = asm_v; kc.src.k_rows = kc.src.v_rows = R;
+    kc.src.mode = hymba::KvSide::kLinear; kc.src.base = c.pos0 - (M + nw);
+    kc.pb = std::max(c.pos0, c.pos0 + L - W); kc.na = 0; kc.pa = 0;
+    kc.n = c.pos0 + L - kc.pb;
+  }
+  HYMBA_TRY(hymba::launch_kv_copy(kc, stream));
+  HYMBA_TRY(hymba::launch_attn_prefill(aa, stream, tm(4)));
+  if (fc) HYMBA_TRY(hipStreamWaitEvent(stream, fc->join, 0));
+
+  HYMBA_TRY(hymba::launch_fuse(y_attn, y_ssm, params->beta_attn, params->beta_ssm, (int64_t)desc->batch * L,
+                               desc->d_inner, desc->norm_eps, desc->act, c.out, stream, tm(5)));
+  return HYMBA_OK;
+}
+
+int check_prefill_io(const void* const* req, int n_req, const void* const* opt, int n_opt) {
+  for (int i = 0; i < n_req; ++i)
+    if (!req[i]) return HYMBA_EINVAL;
+  for (int i = 0; i < n_req; ++i)
+    if (!aligned16(req[i])) return HYMBA_EALIGN;
+  for (int i = 0; i < n_opt; ++i)
+    if (opt[i] && !aligned16(opt[i])) return HYMBA_EALIGN;
+  return HYMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* params, const void* x,
                         const void* z, const void* dt, const void* B, const void* C, const void* q, const void* k,
                         const void* v, void* out, float* ssm_state_out, void* conv_state_out, void* k_cache,
@@ -194,79 +389,51 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
   st = check_params(params);
   if (st != HYMBA_OK) return st;
   const void* req[] = {x, z, dt, B, C, q, k, v, out};
-  for (const void* p : req)
-    if (!p) return HYMBA_EINVAL;
-  for (const void* p : req)
-    if (!aligned16(p)) return HYMBA_EALIGN;
   const void* opt[] = {ssm_state_out, conv_state_out, k_cache, v_cache, y_attn_out, y_ssm_out};
-  for (const void* p : opt)
-    if (p && !aligned16(p)) return HYMBA_EALIGN;
+  st = check_prefill_io(req, 9, opt, 6);
+  if (st != HYMBA_OK) return st;
   if ((k_cache == nullptr) != (v_cache == nullptr)) return HYMBA_EINVAL;
   const int L = desc->n_meta + desc->n_tokens;
-  if (k_cache && desc->cache_capacity < L) return HYMBA_EINVAL;
-  const PrefillWs ws = prefill_ws(desc);
-  if (!ws.carry_ok) return HYMBA_EUNSUPPORTED;
-  if (!workspace || workspace_bytes < ws.total) return HYMBA_EWORKSPACE;
-  if (((uintptr_t)workspace & 255u) != 0) return HYMBA_EALIGN;
+  if (k_cache && !desc->cache_ring && desc->cache_capacity < L) return HYMBA_EINVAL;
+  PrefillCall c = {};
+  c.x = x; c.z = z; c.dt = dt; c.B = B; c.C = C; c.q = q; c.k = k; c.v = v; c.out = out;
+  c.pos0 = 0; c.cont = false;
+  c.state_out = ssm_state_out; c.conv_out = conv_state_out;
+  c.k_cache = k_cache; c.v_cache = v_cache;
+  c.y_attn_out = y_attn_out; c.y_ssm_out = y_ssm_out;
+  c.workspace = workspace; c.workspace_bytes = workspace_bytes; c.stage_events = stage_events;
+  return prefill_impl(desc, params, c, stream);
+}
 
-  char* wsb = (char*)workspace;
-  void* q_rot = wsb + ws.q_rot;
-  void* k_rot = k_cache ? k_cache : (void*)(wsb + ws.k_rot);
-  const int64_t k_rows = k_cache ? desc->cache_capacity : L;
-  void* y_attn = y_attn_out ? y_attn_out : (void*)(wsb + ws.y_attn);
-  void* y_ssm = y_ssm_out ? y_ssm_out : (void*)(wsb + ws.y_ssm);
-
-  // stage i's kernel records stage_events[2i] when it starts and [2i+1] when it ends
-  auto tm = [&](int i) -> hymba::Timing {
-    hymba::Timing t;
-    if (stage_events) {
-      t.start = stage_events[2 * i];
-      t.stop = stage_events[2 * i + 1];
-    }
-    return t;
-  };
-  // The two branches are independent until the fusion: without stage events the
-  // Mamba branch runs on a second stream, concurrently with the attention branch.
-  ForkCtx* fc = nullptr;
-  if (!stage_events) HYMBA_TRY(fork_ctx(&fc));
-  hipStream_t ssm_stream = stream;
-  if (fc) {
-    HYMBA_TRY(hipEventRecord(fc->fork, stream));
-    HYMBA_TRY(hipStreamWaitEvent(fc->aux, fc->fork, 0));
-    ssm_stream = fc->aux;
-  }
-  hymba::SsmPrefillArgs sa;
-  sa.x = x; sa.z = z; sa.dt = dt; sa.B = B; sa.C = C;
-  sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
-  sa.y = y_ssm; sa.state_out = ssm_state_out; sa.conv_state_out = conv_state_out;
-  sa.agg = (float*)(wsb + ws.agg); sa.sdt = (float*)(wsb + ws.sdt); sa.carry = (float*)(wsb + ws.carry);
-  sa.chunk_rows = ws.chunk_rows;
-  sa.batch = desc->batch; sa.L = L; sa.d_inner = desc->d_inner; sa.act = desc->act;
-  HYMBA_TRY(hymba::launch_ssm_chunk_end(sa, ssm_stream, tm(0)));
-  HYMBA_TRY(hymba::launch_ssm_chunk_carry(sa, ssm_stream, tm(1)));
-  HYMBA_TRY(hymba::launch_ssm_chunk_out(sa, ssm_stream, tm(2)));
-  if (fc) HYMBA_TRY(hipEventRecord(fc->join, fc->aux));
-
-  hymba::RopeArgs ra;
-  ra.q = q; ra.k = k; ra.v = v; ra.q_rot = q_rot; ra.k_rot = k_rot; ra.v_copy = v_cache;
-  ra.k_rows = k_rows; ra.v_rows = desc->cache_capacity; ra.k_scale = params->k_scale;
-  ra.batch = desc->batch; ra.L = L; ra.n_q_heads = desc->n_q_heads; ra.n_kv_heads = desc->n_kv_heads;
-  ra.head_dim = desc->head_dim; ra.head_dim_v = desc->head_dim_v; ra.rope_base = desc->rope_base;
-  ra.act = desc->act;
-  HYMBA_TRY(hymba::launch_rope_prefill(ra, stream, tm(3)));
-
-  hymba::AttnPrefillArgs aa;
-  aa.q_rot = q_rot; aa.k_rot = k_rot; aa.v = v; aa.k_rows = k_rows; aa.v_rows = L; aa.y = y_attn;
-  aa.batch = desc->batch; aa.L = L; aa.n_meta = desc->n_meta; aa.window = desc->window;
-  aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
-  aa.act = desc->act;
-  HYMBA_TRY(device_cus(&aa.n_cu));
-  HYMBA_TRY(hymba::launch_attn_prefill(aa, stream, tm(4)));
-  if (fc) HYMBA_TRY(hipStreamWaitEvent(stream, fc->join, 0));
-
-  HYMBA_TRY(hymba::launch_fuse(y_attn, y_ssm, params->beta_attn, params->beta_ssm, (int64_t)desc->batch * L,
-                               desc->d_inner, desc->norm_eps, desc->act, out, stream, tm(5)));
-  return HYMBA_OK;
+int hymba_mixer_prefill_continue(const hymba_mixer_desc* desc, const hymba_mixer_params* params, int32_t pos0,
+                                 const void* x, const void* z, const void* dt, const void* B, const void* C,
+                                 const void* q, const void* k, const void* v, void* out, float* ssm_state,
+                                 void* conv_state, void* k_cache, void* v_cache, void* y_attn_out, void* y_ssm_out,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_desc(desc, false);
+  if (st != HYMBA_OK) return st;
+  st = check_params(params);
+  if (st != HYMBA_OK) return st;
+  const void* req[] = {x, z, dt, B, C, q, k, v, out, ssm_state, conv_state, k_cache, v_cache};
+  const void* opt[] = {y_attn_out, y_ssm_out};
+  st = check_prefill_io(req, 13, opt, 2);
+  if (st != HYMBA_OK) return st;
+  const int T = desc->n_tokens;
+  if (T < 1 || pos0 < desc->n_meta || (int64_t)pos0 + T > INT32_MAX / 2) return HYMBA_EINVAL;
+  // rows the attention addresses with 32-bit byte offsets: positions below
+  // pos0 + T in the cache, or the assembly of the compact form
+  const int64_t key_rows = desc->cache_ring ? (int64_t)prefill_ws(desc).asm_rows : (int64_t)pos0 + T;
+  if (!desc->cache_ring && desc->cache_capacity < (int64_t)pos0 + T) return HYMBA_EINVAL;
+  if (key_rows * kv_row_bytes(desc) > INT32_MAX) return HYMBA_EUNSUPPORTED;
+  PrefillCall c = {};
+  c.x = x; c.z = z; c.dt = dt; c.B = B; c.C = C; c.q = q; c.k = k; c.v = v; c.out = out;
+  c.pos0 = pos0; c.cont = true;
+  c.state_in = ssm_state; c.conv_in = conv_state;
+  c.state_out = ssm_state; c.conv_out = conv_state;
+  c.k_cache = k_cache; c.v_cache = v_cache;
+  c.y_attn_out = y_attn_out; c.y_ssm_out = y_ssm_out;
+  c.workspace = workspace; c.workspace_bytes = workspace_bytes; c.stage_events = nullptr;
+  return prefill_impl(desc, params, c, stream);
 }
 
 int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* params, const void* x,
@@ -317,7 +484,7 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
   aa.q_rot = (float*)(wsb + ws.q_rot); aa.k_rot = (float*)(wsb + ws.k_rot); aa.n_split = ws.n_split; aa.keys_per_split = ws.keys_per_split;
   aa.batch = desc->batch; aa.cap = desc->cache_capacity; aa.n_meta = desc->n_meta; aa.window = desc->window;
   aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
-  aa.rope_base = desc->rope_base; aa.act = desc->act;
+  aa.rope_base = desc->rope_base; aa.act = desc->act; aa.ring = desc->cache_ring;
   HYMBA_TRY(device_cus(&aa.n_cu));
   aa.n_split = hymba::decode_active_splits(aa);   // <= ws.n_split partial slots
   HYMBA_TRY(hymba::launch_attn_decode(aa, stream, tm(1)));

@@ -60,8 +60,8 @@ constexpr int kRopeThreads = 256;
 template <typename T>
 __global__ __launch_bounds__(kRopeThreads) void rope_prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ q_rot,
-    T* __restrict__ k_rot, T* __restrict__ v_copy, int64_t k_rows, int64_t v_rows,
-    const float* __restrict__ k_scale, int L, int Hq, int Hkv, int dv, float base, float q_scale) {
+    T* __restrict__ k_rot, T* __restrict__ v_copy, int64_t k_rows, int64_t v_rows, int64_t k_row0, int64_t v_row0,
+    const float* __restrict__ k_scale, int L, int pos0, int Hq, int Hkv, int dv, float base, float q_scale) {
   __shared__ float cs[kRopeRows][kHd / 2];
   __shared__ float sn[kRopeRows][kHd / 2];
   const int r0 = blockIdx.x * kRopeRows;
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_prefill_kernel(
   const int tid = threadIdx.x;
   for (int t = tid; t < kRopeRows * (kHd / 2); t += blockDim.x) {
     const int r = t / (kHd / 2), i = t % (kHd / 2);
-    rope_cs(r0 + r, i, base, &cs[r][i], &sn[r][i]);
+    rope_cs(pos0 + r0 + r, i, base, &cs[r][i], &sn[r][i]);
   }
   __syncthreads();
   const int nrows = min(kRopeRows, L - r0);
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_prefill_kernel(
     if (has_v) {
       const int r = it / per_row, e = it % per_row;
       load8(v + (b * L + r0 + r) * (int64_t)(Hkv * dv) + 8 * e, vf);
-      v_dst = (b * v_rows + r0 + r) * (int64_t)(Hkv * dv) + 8 * e;
+      v_dst = (b * v_rows + v_row0 + r0 + r) * (int64_t)(Hkv * dv) + 8 * e;
     }
     const bool has_r = it < rot_items;
     const int g8 = it & 3, hr = it >> 2, hd = hr % H, rr = hr / H;
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_prefill_kernel(
         for (int e = 0; e < 8; ++e) { slo[e] *= q_scale; shi[e] *= q_scale; }
       } else {
         src = k + ((b * L + row) * Hkv + (hd - Hq)) * kHd;
-        dst = k_rot + ((b * k_rows + row) * Hkv + (hd - Hq)) * kHd;
+        dst = k_rot + ((b * k_rows + k_row0 + row) * Hkv + (hd - Hq)) * kHd;
       }
       load8(src + 8 * g8, lo);
       load8(src + 32 + 8 * g8, hi);
@@ -527,7 +527,8 @@ __device__ __forceinline__ void mask_scores(f32x16_t& s, const LaneKeys& lk, int
 template <typename T, int DV>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
     const T* __restrict__ q_rot, const T* __restrict__ k_rot, const T* __restrict__ v, T* __restrict__ y,
-    int64_t k_rows, int64_t v_rows, int L, int n_meta, int window, int Hq, int Hkv, int batch, int n_cu) {
+    int64_t k_rows, int64_t v_rows, int Lq, int q_pos0, int n_meta, int window, int Hq, int Hkv, int batch,
+    int n_cu) {
   typedef Mma<T> M;
   typedef typename M::Frag Frag;
   constexpr int NDB = DV / 32;
@@ -553,7 +554,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   // of them fit at once (at most two per CU), the first n_cu workgroups (one
   // per CU) take the heaviest items and the rest the lightest, in ascending
   // order, so that heavy items share a CU with light ones.
-  const int nxb = (L + P - 1) / P;
+  // query row r is at position q_pos0 + r; key row j of k_rot / v is at
+  // position j; positions below L = q_pos0 + Lq exist
+  const int L = q_pos0 + Lq;
+  const int nxb = (Lq + P - 1) / P;
   const int hb_n = Hkv * batch;
   const int n_items = nxb * hb_n;
   const int wg = (int)blockIdx.x;
@@ -562,7 +566,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   const int pb = nxb - 1 - rank / hb_n;
   const int g = (rank % hb_n) % Hkv;
   const int64_t b = (rank % hb_n) / Hkv;
-  const int p0 = pb * P;
+  const int p0 = q_pos0 + pb * P;
   const int p1 = min(p0 + P, L);
   const int col = 32 * wave + lq;
   const bool col_ok = col < P * G;
@@ -582,7 +586,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   Frag qf[4];
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc)
-    qf[kc] = my_q < L ? M::frag_at(q_rot + ((b * L + my_q) * Hq + h) * kHd + 16 * kc + 8 * hh) : M::zero();
+    qf[kc] = my_q < L ? M::frag_at(q_rot + ((b * Lq + my_q - q_pos0) * Hq + h) * kHd + 16 * kc + 8 * hh)
+                      : M::zero();
 
   SoftmaxState<NDB> st;
   st.init();
@@ -707,7 +712,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   const float l_tot = st.l + __shfl_xor(st.l, 32, 64);   // the column's sum over both lane halves
   if (my_q < L) {
     const float inv = 1.0f / l_tot;
-    T* yrow = y + ((b * L + my_q) * Hq + h) * DV;
+    T* yrow = y + ((b * Lq + my_q - q_pos0) * Hq + h) * DV;
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
 #pragma unroll
@@ -746,20 +751,32 @@ constexpr int kKeysPerSplit = 128;
 constexpr int kMaxGroup = 10;
 
 __device__ __forceinline__ int clamp_pos(int p, int cap) { return p < 0 ? 0 : (p > cap ? cap : p); }
+// Position of a decode step's new row: cache_len, clamped so that no cache
+// access leaves the buffer (a cache of one row per position holds rows < p;
+// the compact ring holds any position, so only p >= 0 is needed there).
+__device__ __forceinline__ int decode_pos(int cache_len, int cap, bool ring) {
+  return ring ? max(cache_len, 0) : clamp_pos(cache_len, cap);
+}
+// Cache row of position j < p: the position itself, or, in the compact cache
+// of a sliding-window layer, its row in the ring of `window` rows after the
+// n_meta meta rows.
+__device__ __forceinline__ int cache_row(int j, int n_meta, int window, bool ring) {
+  return ring && j >= n_meta ? n_meta + (j - n_meta) % window : j;
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void decode_rope_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
                                                           const int32_t* __restrict__ cache_len,
                                                           float* __restrict__ q_rot, float* __restrict__ k_rot,
                                                           const float* __restrict__ k_scale, int batch, int Hq,
-                                                          int Hkv, int cap, float base) {
+                                                          int Hkv, int cap, int ring, float base) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, head, i)
   const int H = Hq + Hkv;
   if (idx >= (int64_t)batch * H * (kHd / 2)) return;
   const int i = (int)(idx % (kHd / 2));
   const int hd = (int)((idx / (kHd / 2)) % H);
   const int64_t b = idx / ((kHd / 2) * H);
-  const int p = clamp_pos(cache_len[b], cap);
+  const int p = decode_pos(cache_len[b], cap, ring);
   float c, sn;
   rope_cs(p, i, base, &c, &sn);
   const T* src = hd < Hq ? q + (b * Hq + hd) * kHd : k_new + (b * Hkv + (hd - Hq)) * kHd;
@@ -779,7 +796,7 @@ template <typename T, int DV>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
     const float* __restrict__ q_rot, const float* __restrict__ k_rot, const T* __restrict__ v_new,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
-    float* __restrict__ partial, int n_split, int cap, int n_meta, int window, int Hq, int Hkv) {
+    float* __restrict__ partial, int n_split, int cap, int n_meta, int window, int ring, int Hq, int Hkv) {
   constexpr int KS = kKeysPerSplit;
   constexpr int E = Vec16<T>::n;            // elements per 16-byte load
   __shared__ float qs[kMaxGroup][kHd];
@@ -790,7 +807,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   const int64_t b = blockIdx.z;
   const int group = Hq / Hkv;
   const int tid = threadIdx.x;
-  const int p = clamp_pos(cache_len[b], cap);
+  const int p = decode_pos(cache_len[b], cap, ring);
   const MaskRange mr = mask_range(p, n_meta, window);
   const int n_vis = mr.meta_end + (mr.win_end - mr.win_begin);
   const int i0 = s * KS;
@@ -812,7 +829,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   for (int it = tid; it < nk * VCH; it += blockDim.x) {
     const int kk = it / VCH, ch = it % VCH;
     const int j = key_row(i0 + kk);
-    const T* src = j == p ? v_new + (b * Hkv + g) * DV : v_cache + ((b * cap + j) * Hkv + g) * DV;
+    const T* src = j == p ? v_new + (b * Hkv + g) * DV
+                          : v_cache + ((b * cap + cache_row(j, n_meta, window, ring)) * Hkv + g) * DV;
     *reinterpret_cast<uint4*>(&Vs[kk][ch * E]) = *reinterpret_cast<const uint4*>(src + ch * E);
   }
   for (int t = tid; t < group * kHd; t += blockDim.x) qs[t / kHd][t % kHd] = q_rot[(b * Hq + g * group) * kHd + t];
@@ -825,7 +843,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll
       for (int d = 0; d < kHd; ++d) kr[d] = k_rot[(b * Hkv + g) * kHd + d];
     } else {
-      const T* src = k_cache + ((b * cap + j) * Hkv + g) * kHd;
+      const T* src = k_cache + ((b * cap + cache_row(j, n_meta, window, ring)) * Hkv + g) * kHd;
 #pragma unroll
       for (int ch = 0; ch < kHd / E; ++ch) load16(src + ch * E, kr + ch * E);
     }
@@ -899,9 +917,10 @@ constexpr int kDecodeTile = 32;     // keys per tile
 constexpr int kDecodeStages = 2;    // tiles in LDS: one used, kDecodeStages - 1 loading
 constexpr int kMaxGroupFlash = 8;   // query heads per kv head (larger groups are rejected up front)
 
-// (dv >= 64: five waves per SIMD fit in 96 registers without spills)
-template <int DV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DV >= 64 ? 5 : 1)))
+// (dv >= 64: five waves per SIMD fit in 96 registers without spills; RING:
+// the cache is the compact ring of n_meta + window rows)
+template <int DV, bool RING>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DV >= 64 && !RING ? 5 : 1)))
 void attn_decode_flash_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_new, const bf16* __restrict__ v_new,
     const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
@@ -941,7 +960,7 @@ void attn_decode_flash_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hh = lane >> 5;
-  const int p = clamp_pos(cache_len[b], cap);
+  const int p = decode_pos(cache_len[b], cap, RING);
   const MaskRange mr = mask_range(p, n_meta, window);
   const int n_vis = mr.meta_end + (mr.win_end - mr.win_begin);
   const int n_tiles = (n_vis + BT - 1) / BT;
@@ -957,7 +976,17 @@ void attn_decode_flash_kernel(
     }
     return;
   }
-  auto key_row = [&](int vi) { return vi < mr.meta_end ? vi : mr.win_begin + (vi - mr.meta_end); };
+  // cache row of visible key vi (meta keys first, then the window in order);
+  // in the ring, window key o is at ring row w0 + o folded once into [0, window)
+  const int w0 = RING ? (mr.win_begin - n_meta) % window : 0;
+  auto key_row = [&](int vi) {
+    if constexpr (RING) {
+      const int r = w0 + (vi - mr.meta_end);
+      return vi < mr.meta_end ? vi : n_meta + (r >= window ? r - window : r);
+    } else {
+      return vi < mr.meta_end ? vi : mr.win_begin + (vi - mr.meta_end);
+    }
+  };
   const int vi_new = n_vis - 1;   // the new row p is the last visible key
 
   // Tile t: row r is visible key 64 t + r. Rows past the visible keys and the
@@ -1301,12 +1330,51 @@ __global__ __launch_bounds__(kCombineMaxThreads) void decode_combine_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// KV row copies between a cache (one row per position, or the compact ring)
+// and the rows the prefill attention reads. Workgroup = (copy index, sequence);
+// 16-byte pieces of the K row, then of the V row.
+__device__ __forceinline__ int64_t kv_side_row(int mode, int base, int i, int P, int n_meta, int window) {
+  if (mode == KvSide::kIndex) return i;
+  if (mode == KvSide::kLinear) return P - base;
+  return cache_row(P, n_meta, window, true);
+}
+
+__global__ __launch_bounds__(64) void kv_copy_kernel(KvCopyArgs a, int k_row_bytes, int v_row_bytes) {
+  const int i = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const int P = i < a.na ? a.pa + i : a.pb + (i - a.na);
+  const int64_t sr = kv_side_row(a.src.mode, a.src.base, i, P, a.n_meta, a.window);
+  const int64_t dr = kv_side_row(a.dst.mode, a.dst.base, i, P, a.n_meta, a.window);
+  const char* sk = (const char*)a.src.k + (b * a.src.k_rows + sr) * k_row_bytes;
+  const char* sv = (const char*)a.src.v + (b * a.src.v_rows + sr) * v_row_bytes;
+  char* dk = (char*)a.dst.k + (b * a.dst.k_rows + dr) * k_row_bytes;
+  char* dv = (char*)a.dst.v + (b * a.dst.v_rows + dr) * v_row_bytes;
+  for (int o = 16 * (int)threadIdx.x; o < k_row_bytes; o += 16 * 64)
+    *reinterpret_cast<uint4*>(dk + o) = *reinterpret_cast<const uint4*>(sk + o);
+  for (int o = 16 * (int)threadIdx.x; o < v_row_bytes; o += 16 * 64)
+    *reinterpret_cast<uint4*>(dv + o) = *reinterpret_cast<const uint4*>(sv + o);
+}
+
+}  // namespace
+
+hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t stream) {
+  if (a.n <= 0 || a.batch <= 0) return hipSuccess;
+  const int es = a.act == HYMBA_BF16 ? 2 : 4;
+  const int k_row_bytes = a.n_kv_heads * kHd * es, v_row_bytes = a.n_kv_heads * a.head_dim_v * es;
+  hipLaunchKernelGGL(kv_copy_kernel, dim3((unsigned)a.n, (unsigned)a.batch), dim3(64), 0, stream, a, k_row_bytes,
+                     v_row_bytes);
+  return hipGetLastError();
+}
+
+namespace {
+
 template <typename T>
 hipError_t rope_t(const RopeArgs& a, hipStream_t stream, Timing tm) {
   dim3 grid((a.L + kRopeRows - 1) / kRopeRows, a.batch);
   HYMBA_LAUNCH(rope_prefill_kernel<T>, grid, dim3(kRopeThreads), 0, stream, tm, (const T*)a.q, (const T*)a.k,
-                     (const T*)a.v, (T*)a.q_rot, (T*)a.k_rot, (T*)a.v_copy, a.k_rows, a.v_rows, a.k_scale, a.L,
-                     a.n_q_heads,
+                     (const T*)a.v, (T*)a.q_rot, (T*)a.k_rot, (T*)a.v_copy, a.k_rows, a.v_rows, a.k_row0,
+                     a.v_row0, a.k_scale, a.L, a.pos0, a.n_q_heads,
                      a.n_kv_heads, a.head_dim_v, a.rope_base, kScaleLog2e);
   return hipGetLastError();
 }
@@ -1317,8 +1385,8 @@ hipError_t attn_prefill_t(const AttnPrefillArgs& a, hipStream_t stream, Timing t
   const int P = kAttnCols / G;   // positions per workgroup
   const int64_t n_items = (int64_t)((a.L + P - 1) / P) * a.n_kv_heads * a.batch;
   HYMBA_LAUNCH((attn_prefill_kernel<T, DV>), dim3((unsigned)n_items), dim3(64 * kAttnWaves), 0, stream, tm,
-                     (const T*)a.q_rot, (const T*)a.k_rot, (const T*)a.v, (T*)a.y, a.k_rows, a.v_rows, a.L, a.n_meta,
-                     a.window, a.n_q_heads, a.n_kv_heads, a.batch, a.n_cu);
+                     (const T*)a.q_rot, (const T*)a.k_rot, (const T*)a.v, (T*)a.y, a.k_rows, a.v_rows, a.L, a.q_pos0,
+                     a.n_meta, a.window, a.n_q_heads, a.n_kv_heads, a.batch, a.n_cu);
   return hipGetLastError();
 }
 
@@ -1329,23 +1397,28 @@ hipError_t attn_decode_t(const AttnDecodeArgs& a, hipStream_t stream, Timing tm)
   t_last.stop = tm.stop;
   if constexpr (sizeof(T) == 2) {
     // rotation inside the attention kernel: one launch for the stage
-    HYMBA_LAUNCH((attn_decode_flash_kernel<DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream, tm,
-                 (const bf16*)a.q, (const bf16*)a.k_new, (const bf16*)a.v_new, (const bf16*)a.k_cache,
-                 (const bf16*)a.v_cache, a.cache_len, a.partial, a.k_scale, a.n_split, a.cap, a.n_meta, a.window,
-                 a.n_q_heads,
-                 a.n_kv_heads, a.rope_base);
+    if (a.ring)
+      HYMBA_LAUNCH((attn_decode_flash_kernel<DV, true>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream,
+                   tm, (const bf16*)a.q, (const bf16*)a.k_new, (const bf16*)a.v_new, (const bf16*)a.k_cache,
+                   (const bf16*)a.v_cache, a.cache_len, a.partial, a.k_scale, a.n_split, a.cap, a.n_meta, a.window,
+                   a.n_q_heads, a.n_kv_heads, a.rope_base);
+    else
+      HYMBA_LAUNCH((attn_decode_flash_kernel<DV, false>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0,
+                   stream, tm, (const bf16*)a.q, (const bf16*)a.k_new, (const bf16*)a.v_new, (const bf16*)a.k_cache,
+                   (const bf16*)a.v_cache, a.cache_len, a.partial, a.k_scale, a.n_split, a.cap, a.n_meta, a.window,
+                   a.n_q_heads, a.n_kv_heads, a.rope_base);
     return hipGetLastError();
   }
   const int64_t n = (int64_t)a.batch * (a.n_q_heads + a.n_kv_heads) * (kHd / 2);
   HYMBA_LAUNCH(decode_rope_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, t_first, (const T*)a.q,
                      (const T*)a.k_new, a.cache_len, a.q_rot, a.k_rot, a.k_scale, a.batch, a.n_q_heads,
-                     a.n_kv_heads, a.cap,
+                     a.n_kv_heads, a.cap, a.ring,
                      a.rope_base);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   HYMBA_LAUNCH((attn_decode_kernel<T, DV>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream, t_last,
                  a.q_rot, a.k_rot, (const T*)a.v_new, (const T*)a.k_cache, (const T*)a.v_cache, a.cache_len,
-                 a.partial, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads, a.n_kv_heads);
+                 a.partial, a.n_split, a.cap, a.n_meta, a.window, a.ring, a.n_q_heads, a.n_kv_heads);
   return hipGetLastError();
 }
 

@@ -42,6 +42,8 @@ struct SsmPrefillArgs {
   void* y;                 // [batch, L, d_inner] act
   float* state_out;        // optional [batch, d_inner, 16]
   void* conv_state_out;    // optional [batch, d_inner, 3]
+  const float* state_in;   // optional [batch, d_inner, 16] state before row 0 (else zero)
+  const void* conv_in;     // optional [batch, d_inner, 3] raw x of rows -3..-1 (else zero); not conv_state_out
   float* agg;              // workspace [n_chunks, batch, d_inner, 16]
   float* sdt;              // workspace [n_chunks, batch, d_inner]
   float* carry;            // workspace [n_chunks, batch, d_inner, 16]
@@ -81,21 +83,24 @@ struct RopeArgs {
   void* q_rot;             // [batch, L, Hq, hd] act
   void* k_rot;             // rows with stride k_rows per sequence
   void* v_copy;            // optional, rows with stride v_rows per sequence
-  int64_t k_rows, v_rows;  // rows per sequence of k_rot / v_copy (>= L)
+  int64_t k_rows, v_rows;  // rows per sequence of k_rot / v_copy
+  int64_t k_row0, v_row0;  // rows of k_rot / v_copy that receive input row 0
   const float* k_scale;    // [Hkv, 64] or null: query heads of kv head g are scaled by row g
   int batch, L, n_q_heads, n_kv_heads, head_dim, head_dim_v;
+  int pos0;                // position of input row 0 (rotation angle)
   float rope_base;
   hymba_dtype act;
 };
 hipError_t launch_rope_prefill(const RopeArgs& a, hipStream_t stream, Timing tm = {});
 
 struct AttnPrefillArgs {
-  const void* q_rot;       // [batch, L, Hq, 64]
-  const void* k_rot;       // [batch, k_rows, Hkv, 64]
+  const void* q_rot;       // [batch, L, Hq, 64]: query row r is at position q_pos0 + r
+  const void* k_rot;       // [batch, k_rows, Hkv, 64]: key row j is at position j
   const void* v;           // [batch, v_rows, Hkv, dv]
   int64_t k_rows, v_rows;
   void* y;                 // [batch, L, Hq*dv] act
   int batch, L, n_meta, window, n_q_heads, n_kv_heads, head_dim_v;
+  int q_pos0;
   int n_cu;                // compute units of the device (work ordering)
   hymba_dtype act;
 };
@@ -112,6 +117,7 @@ struct AttnDecodeArgs {
   int n_split, keys_per_split;         // n_split: splits of this launch (decode_active_splits)
   int n_cu;                            // compute units of the device (split count)
   int batch, cap, n_meta, window, n_q_heads, n_kv_heads, head_dim_v;
+  int ring;                            // cache is the compact ring of n_meta + window rows
   float rope_base;
   hymba_dtype act;
 };
@@ -120,6 +126,25 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream, Timin
 void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_per_split);
 // splits (partials per head) one launch uses, at most the plan's slot count
 int decode_active_splits(const AttnDecodeArgs& a);
+
+// Whole K and V rows (all kv heads) of n positions per sequence, from one
+// buffer to another. The positions are [pa, pa + na) then [pb, pb + n - na).
+// Each side locates position P of copy index i as kIndex (row i), kLinear
+// (row P - base) or kRing (cache row of P in the compact ring).
+struct KvSide {
+  enum Mode { kIndex = 0, kLinear = 1, kRing = 2 };
+  const void* k;
+  const void* v;
+  int64_t k_rows, v_rows;  // rows per sequence
+  int mode, base;
+};
+struct KvCopyArgs {
+  KvSide src, dst;         // (dst.k, dst.v are written)
+  int n, na, pa, pb;
+  int n_meta, window, batch, n_kv_heads, head_dim_v;
+  hymba_dtype act;
+};
+hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t stream);
 
 // decode epilogue: merge of the split partials + fusion with the Mamba output
 struct DecodeCombineArgs {

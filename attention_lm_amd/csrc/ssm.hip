@@ -94,9 +94,9 @@ template <typename T, bool OUT>
 __global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_kernel(
     const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ dt, const T* __restrict__ Bm,
     const T* __restrict__ Cm, const float* __restrict__ A, const float* __restrict__ Dp,
-    const float* __restrict__ conv_w, const float* __restrict__ carry, float* __restrict__ agg,
-    float* __restrict__ sdt, T* __restrict__ y, float* __restrict__ state_out, T* __restrict__ conv_state_out,
-    int L, int Dch, int CT) {
+    const float* __restrict__ conv_w, const T* __restrict__ conv_in, const float* __restrict__ carry,
+    float* __restrict__ agg, float* __restrict__ sdt, T* __restrict__ y, float* __restrict__ state_out,
+    T* __restrict__ conv_state_out, int L, int Dch, int CT) {
   constexpr int E = Vec16<T>::n;                  // elements per 16-byte vector
   constexpr int RV = kChanPerBlock / E;           // vectors per 128-channel row
   constexpr int XR = kRowBlock + kConv - 1;       // x rows per block (with conv history)
@@ -179,6 +179,11 @@ __global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_kernel(
   const int nblk = (t1 - t0 + kRowBlock - 1) / kRowBlock;
   fetch(t0);
   __syncthreads();
+  if (conv_in && t0 == 0) {   // rows -3 .. -1: the carried conv history (oldest first)
+#pragma unroll
+    for (int r = 0; r < kConv - 1; ++r) xs[r][tid] = conv_in[((int64_t)b * Dch + cc) * (kConv - 1) + r];
+    __syncthreads();
+  }
   for (int ib = 0; ib < nblk; ++ib) {
     const int tb = t0 + ib * kRowBlock;
     // this block's per-channel inputs, LDS -> registers, before any scalar
@@ -251,12 +256,14 @@ __global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_kernel(
 #pragma unroll
       for (int q = 0; q < kStates / 4; ++q) sp[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
     }
-    if (conv_state_out) {   // raw x of rows L-3, L-2, L-1 (zero before row 0)
+    if (conv_state_out) {   // raw x of rows L-3, L-2, L-1 (before row 0: the carried history, or zero)
       T* csp = conv_state_out + ((int64_t)b * Dch + c) * (kConv - 1);
 #pragma unroll
       for (int j = 0; j < kConv - 1; ++j) {
         const int t = L - (kConv - 1) + j;
-        csp[j] = t >= 0 ? x[(seq + t) * Dch + c] : from_f32<T>(0.f);
+        csp[j] = t >= 0  ? x[(seq + t) * Dch + c]
+                 : conv_in ? conv_in[((int64_t)b * Dch + c) * (kConv - 1) + (kConv - 1) + t]
+                           : from_f32<T>(0.f);
       }
     }
   }
@@ -277,6 +284,7 @@ constexpr int kCarryBatch = 24;
 __global__ __launch_bounds__(64 * kCarrySegs) void ssm_chunk_carry_kernel(const float* __restrict__ A,
                                                                          const float* __restrict__ agg,
                                                                          const float* __restrict__ sdt,
+                                                                         const float* __restrict__ state_in,
                                                                          float* __restrict__ carry, int nchunk,
                                                                          int batch, int Dch) {
   constexpr int KB = kCarryBatch;
@@ -303,7 +311,8 @@ __global__ __launch_bounds__(64 * kCarrySegs) void ssm_chunk_carry_kernel(const 
   const __amdgpu_buffer_rsrc_t srs =
       make_rsrc(sdt + k0 * (per / kStates), (uint32_t)(nseg * (per / kStates) * sizeof(float)));
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(carry + (k0 + 1) * per, (uint32_t)(nseg * per * sizeof(float)));
-  if (seg == 0 && valid) carry[idx] = 0.f;
+  const float h_in = state_in ? state_in[ci] : 0.f;   // the state entering chunk 0
+  if (seg == 0 && valid) carry[idx] = h_in;
   auto load = [&](int kb, float* av, float* sv) {   // steps kb .. kb + KB - 1 of the segment
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(64 * kCarrySegs) void ssm_chunk_carry_kernel(const 
   seg_s[seg][lane] = S;
   __syncthreads();
   // the state entering this segment: the earlier segments, in order
-  float H0 = 0.f;
+  float H0 = h_in;
   for (int s = 0; s < seg; ++s) H0 = fmaf(fast_exp2(a2 * seg_s[s][lane]), H0, seg_h[s][lane]);
   // second walk from the true start, storing carry[k + 1]
   H = H0;
@@ -384,8 +393,8 @@ hipError_t chunk_end_t(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
   const int cblocks = (a.d_inner + kChanPerBlock - 1) / kChanPerBlock;
   HYMBA_LAUNCH((ssm_chunk_kernel<T, false>), dim3(cblocks, nchunk - 1, a.batch), dim3(kChanPerBlock), 0, stream, tm,
                      (const T*)a.x, (const T*)a.z, (const T*)a.dt, (const T*)a.B, (const T*)a.C, a.A, a.D, a.conv_w,
-                     (const float*)nullptr, a.agg, a.sdt, (T*)nullptr, (float*)nullptr, (T*)nullptr, a.L, a.d_inner,
-                     CT);
+                     (const T*)a.conv_in, (const float*)nullptr, a.agg, a.sdt, (T*)nullptr, (float*)nullptr,
+                     (T*)nullptr, a.L, a.d_inner, CT);
   return hipGetLastError();
 }
 
@@ -397,8 +406,8 @@ hipError_t chunk_out_t(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
   // the output pass covers every chunk (the grid's y extent is nchunk)
   HYMBA_LAUNCH((ssm_chunk_kernel<T, true>), dim3(cblocks, nchunk, a.batch), dim3(kChanPerBlock), 0, stream, tm,
                      (const T*)a.x, (const T*)a.z, (const T*)a.dt, (const T*)a.B, (const T*)a.C, a.A, a.D, a.conv_w,
-                     a.carry, (float*)nullptr, (float*)nullptr, (T*)a.y, a.state_out, (T*)a.conv_state_out, a.L,
-                     a.d_inner, CT);
+                     (const T*)a.conv_in, a.carry, (float*)nullptr, (float*)nullptr, (T*)a.y, a.state_out,
+                     (T*)a.conv_state_out, a.L, a.d_inner, CT);
   return hipGetLastError();
 }
 
@@ -424,7 +433,7 @@ hipError_t launch_ssm_chunk_carry(const SsmPrefillArgs& a, hipStream_t stream, T
   const int nchunk = (a.L + a.chunk_rows - 1) / a.chunk_rows;
   const int64_t per = (int64_t)a.batch * a.d_inner * kStates;
   HYMBA_LAUNCH(ssm_chunk_carry_kernel, dim3((unsigned)((per + 63) / 64)), dim3(64 * kCarrySegs), 0, stream, tm,
-               a.A, a.agg, a.sdt, a.carry, nchunk, a.batch, a.d_inner);
+               a.A, a.agg, a.sdt, a.state_in, a.carry, nchunk, a.batch, a.d_inner);
   return hipGetLastError();
 }
 

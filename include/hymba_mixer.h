@@ -69,7 +69,8 @@ typedef enum {
  *  n_meta      meta-token rows at the start of every sequence (Hymba guide,
  *              "2. Learnable Meta-Tokens": prepended to the prompt)
  *  n_tokens    prompt rows after the meta rows (prefill); L = n_meta + n_tokens
- *              rows per sequence. Decode ignores it.
+ *              rows per sequence. A continuation call processes n_tokens rows.
+ *              Decode ignores it.
  *  d_inner     Mamba channels; also the attention output width (n_q_heads * head_dim_v)
  *  d_state     SSM state size per channel: 16 (Hymba-1.5B article, section 2)
  *  d_conv      conv taps: 4
@@ -83,6 +84,13 @@ typedef enum {
  *  rope_base   rotary base (10000); rotation pairs element i with i + head_dim/2
  *  norm_eps    added to the mean square in the RMS norm (1e-6)
  *  act         dtype of every activation tensor and of the KV cache
+ *  cache_ring  0: cache row p holds position p. 1: the compact cache of a
+ *              sliding-window layer (Hymba-1.5B article, section 1): position
+ *              p < n_meta at row p, later positions in a ring of `window` rows,
+ *              row n_meta + (p - n_meta) % window. A query at position p needs
+ *              no older row, so the cache holds n_meta + window rows whatever
+ *              the context length. Needs window > 0 and
+ *              cache_capacity >= n_meta + window.
  */
 typedef struct {
   int32_t batch, n_meta, n_tokens;
@@ -92,6 +100,7 @@ typedef struct {
   int32_t cache_capacity;
   float rope_base, norm_eps;
   hymba_dtype act;
+  int32_t cache_ring;
 } hymba_mixer_desc;
 
 /* Per-layer fp32 parameters, device pointers.
@@ -141,9 +150,11 @@ int hymba_mixer_prefill_chunk_rows(const hymba_mixer_desc* desc);
  *  ssm_state_out   [batch, d_inner, d_state] fp32 state after row L-1
  *  conv_state_out  [batch, d_inner, d_conv-1] raw x of rows L-3..L-1, oldest
  *                  first (zeros where the row index is negative)
- *  k_cache, v_cache  [batch, cache_capacity, n_kv_heads, head_dim(_v)]: rows
- *                  0..L-1 receive the rotated keys and the values; needs
- *                  cache_capacity >= L. Pass both or neither.
+ *  k_cache, v_cache  [batch, cache_capacity, n_kv_heads, head_dim(_v)]: the
+ *                  rotated keys and the values of rows 0..L-1 are stored, at
+ *                  rows 0..L-1 (needs cache_capacity >= L) or, with
+ *                  cache_ring, the meta rows and the last `window` rows in
+ *                  their ring rows. Pass both or neither.
  *  y_attn_out      [batch, L, d_inner] attention branch before the fusion,
  *                  head-major (channel c = head c / head_dim_v, dim c % head_dim_v)
  *  y_ssm_out       [batch, L, d_inner] Mamba branch before the fusion
@@ -169,6 +180,36 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
                         void* workspace, size_t workspace_bytes,
                         hipEvent_t* stage_events, hipStream_t stream);
 
+/* Prefill continued from an earlier call's state: n_tokens further rows per
+ * sequence at positions pos0 .. pos0 + n_tokens - 1, the same pos0 for every
+ * sequence (chunked prefill). The Mamba branch resumes from the carried SSM
+ * state and conv history ("Lecture 04 - Beyond the Dense Transformer",
+ * section 2: the fixed-size state is all the scan carries); attention sees the
+ * cached rotated keys and values of earlier positions and the new rows under
+ * the prefill visibility rule (section 1: the cache grows per token).
+ *  pos0        rows already processed per sequence; n_meta <= pos0 (the meta
+ *              rows belong to the first call)
+ *  x .. v, out as hymba_mixer_prefill, with n_tokens rows (no meta rows)
+ *  ssm_state   IN/OUT [batch, d_inner, d_state] fp32: the state after row
+ *              pos0 - 1 on entry, after the last new row on return
+ *  conv_state  IN/OUT [batch, d_inner, d_conv-1] raw x of the 3 rows before
+ *              pos0, oldest first; the last 3 rows on return
+ *  k_cache, v_cache  IN/OUT: rotated keys and values of the positions below
+ *              pos0 that a new row can see (rows as cache_ring says); the new
+ *              rows are stored the same way. Without cache_ring needs
+ *              cache_capacity >= pos0 + n_tokens.
+ *  y_attn_out, y_ssm_out  optional, [batch, n_tokens, d_inner]
+ *  workspace   hymba_mixer_prefill_workspace_bytes(desc) bytes, 256-byte aligned
+ * The two branches run concurrently as in hymba_mixer_prefill.               */
+int hymba_mixer_prefill_continue(const hymba_mixer_desc* desc, const hymba_mixer_params* params, int32_t pos0,
+                                 const void* x, const void* z, const void* dt, const void* B, const void* C,
+                                 const void* q, const void* k, const void* v,
+                                 void* out,
+                                 float* ssm_state, void* conv_state,
+                                 void* k_cache, void* v_cache,
+                                 void* y_attn_out, void* y_ssm_out,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* One decode step: one new row per sequence at position p_b = cache_len[b]
  * ("Lecture 04 - Beyond the Dense Transformer", section 1: the new token
  * attends over the cached rows and itself; section 2: the SSM state is updated
@@ -178,13 +219,15 @@ int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* 
  *  v_new      [batch, n_kv_heads, head_dim_v]   (q, k_new not rotated: both are
  *             rotated to position p_b inside)
  *  k_cache, v_cache  READ-ONLY [batch, cache_capacity, n_kv_heads, head_dim(_v)]
- *             holding rotated keys and values of rows < p_b. Several layers may
+ *             holding rotated keys and values of rows < p_b (with cache_ring:
+ *             of the positions p_b can see, in their ring rows). Several layers may
  *             pass the same buffers (Hymba guide, "Systems Mechanics: Cross-Layer
  *             KV Cache Sharing"); the library never writes them. Appending the
  *             new row is the caller's job.
  *  cache_len  [batch] int32 on the device; n_meta <= p_b <= cache_capacity is the
- *             caller's contract. Out-of-range values are clamped to
- *             [0, cache_capacity] so that no access leaves the buffers.
+ *             caller's contract (with cache_ring, any p_b >= n_meta). Values
+ *             that break it are clamped to [0, cache_capacity] (ring: to
+ *             p_b >= 0) so that no access leaves the buffers.
  *  ssm_state  IN/OUT [batch, d_inner, d_state] fp32, updated in place
  *  conv_state IN/OUT [batch, d_inner, d_conv-1] raw x, oldest first, shifted in place
  *  out        [batch, d_inner]; y_attn_out, y_ssm_out optional [batch, d_inner]

@@ -67,10 +67,15 @@ def test_workspace_sizes(lib):
     # rotated q and k, both branch outputs (bf16), then the scan's per-chunk
     # end states, summed dt and carried-in states (fp32): 25 channel blocks of
     # 128 -> ~2048/25 = 82 chunks wanted -> 27 rows, rounded up to 32 -> 68 chunks
+    # (then a copy of a carried conv history, 3 rows, for a continuation)
     n_chunk = (L + 31) // 32
-    expect = (L * 25 * 64 + L * 5 * 64 + 2 * L * 3200) * 2 + n_chunk * 3200 * (16 + 1 + 16) * 4
+    expect = (L * 25 * 64 + L * 5 * 64 + 2 * L * 3200) * 2 + n_chunk * 3200 * (16 + 1 + 16) * 4 + 3200 * 3 * 2
     got = H.hymba_mixer_prefill_workspace_bytes(d)
-    assert expect <= got <= expect + 7 * 256
+    assert expect <= got <= expect + 10 * 256
+    # the compact cache adds the rows a continuation's attention reads: the
+    # meta rows, up to window - 1 earlier rows and the new rows, K and V
+    ring = H.hymba_mixer_prefill_workspace_bytes(c1_desc(cache_capacity=128 + 1024, cache_ring=True))
+    assert ring - got == pytest.approx((128 + 1023 + 2048) * 5 * (64 + 128) * 2, abs=2 * 256)
     dd = c1_desc(batch=64)
     # room for a partial (o, m, l) per query head and 32-key tile of the 128 + 1024 visible keys
     n_split = (128 + 1024 + 31) // 32
@@ -152,3 +157,47 @@ def test_fuse_and_mask_validation(lib):
     d = c1_desc()
     assert lib.hymba_debug_mask_ranges(ctypes.byref(d), None, None) == -1
     assert lib.hymba_debug_mask_ranges(ctypes.byref(d), fake + 4, None) == -3
+
+
+def test_continue_and_compact_cache_validation(lib):
+    fake = 0x100000
+    p = _lib.MixerParams(fake, fake, fake, None, fake, fake)
+
+    def cont(desc, pos0, ptrs=None, ws=fake, wsb=1 << 40):
+        ptrs = ptrs or [fake] * 13   # x z dt B C q k v out ssm_state conv_state k_cache v_cache
+        return lib.hymba_mixer_prefill_continue(ctypes.byref(desc), ctypes.byref(p), pos0, *ptrs, None, None, ws,
+                                                wsb, None)
+
+    d = c1_desc(n_tokens=512)
+    assert cont(d, 127) == -1                       # starts inside the meta rows
+    assert cont(d, 8192 - 511) == -1                # one row per position: needs pos0 + n_tokens rows
+    assert cont(d, 8192 - 512, ws=None) == -5       # valid up to the workspace
+    for i in (9, 10, 11, 12):                       # states and cache are required
+        ptrs = [fake] * 13
+        ptrs[i] = None
+        assert cont(d, 1000, ptrs) == -1
+    ptrs = [fake] * 13
+    ptrs[10] = fake + 2
+    assert cont(d, 1000, ptrs) == -3
+    assert cont(c1_desc(n_tokens=0), 1000) == -1
+    # the compact cache: sliding-window layers only, at least n_meta + window rows
+    assert cont(c1_desc(window=0, cache_ring=True), 1000) == -1
+    assert cont(c1_desc(cache_capacity=1151, cache_ring=True), 1000) == -1
+    ring = c1_desc(n_tokens=512, cache_capacity=1152, cache_ring=True)
+    assert cont(ring, 100000, ws=None) == -5        # any position past the meta rows
+    bad = c1_desc()
+    bad.cache_ring = 2
+    assert cont(bad, 1000) == -1
+    # a fresh prefill into the compact cache needs n_meta + window rows, not L
+    st = lib.hymba_mixer_prefill(ctypes.byref(c1_desc(cache_capacity=1152, cache_ring=True)), ctypes.byref(p),
+                                 *([fake] * 9), None, None, fake, fake, None, None, None, 1 << 40, None, None)
+    assert st == -5
+    # decode reads it the same way
+    dd = c1_desc(batch=64, cache_capacity=1152, cache_ring=True)
+    st = lib.hymba_mixer_decode(ctypes.byref(dd), ctypes.byref(p), *([fake] * 14), None, None, None, 1 << 40,
+                                None, None)
+    assert st == -5
+    dd.cache_capacity = 1151
+    st = lib.hymba_mixer_decode(ctypes.byref(dd), ctypes.byref(p), *([fake] * 14), None, None, fake, 1 << 40,
+                                None, None)
+    assert st == -1
