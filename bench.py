@@ -323,6 +323,88 @@ def bench_decode(cfg, steps, warmup, n_sets, ev):
     return wall / steps * 1e3, per_layer_ms, stage_ms
 
 
+def bench_continue(cfg, steps, warmup, ring):
+    """A prefill continued from its state: rows [M + W, L) of ``cfg`` after a
+    first call over [0, M + W) (the chunk sees a full window of history), with
+    the cache one row per position or the compact ring. Times the
+    continuation call (inputs resident; state and cache are updated in place,
+    so every call does the same work)."""
+    import torch
+    from harness import TORCH_DT, desc_for, dev
+    import attention_lm_amd as H
+    import synth
+
+    per_row = ("x", "z", "dt", "B", "C", "q", "k", "v")
+    M, W, L = cfg.n_meta, cfg.window, cfg.seq_rows
+    a = M + W
+    T = L - a
+    act, dt_ = cfg.act, TORCH_DT[cfg.act]
+    inp = synth.make_prefill_inputs(cfg)
+    cap = M + W if ring else L
+    par = {k: dev(inp[k]) for k in ("A", "D", "conv_w", "beta_attn", "beta_ssm")}
+    params = H.make_params(par["A"], par["D"], par["conv_w"], par["beta_attn"], par["beta_ssm"])
+    Hkv, D = cfg.n_kv_heads, cfg.d_inner
+    kc = torch.zeros((cfg.batch, cap, Hkv, cfg.head_dim), dtype=dt_, device="cuda")
+    vc = torch.zeros((cfg.batch, cap, Hkv, cfg.head_dim_v), dtype=dt_, device="cuda")
+    state = torch.empty((cfg.batch, D, cfg.d_state), dtype=torch.float32, device="cuda")
+    conv = torch.empty((cfg.batch, D, cfg.d_conv - 1), dtype=dt_, device="cuda")
+    first = {k: dev(inp[k][:, :a], act) for k in per_row}
+    out0 = torch.empty((cfg.batch, a, D), dtype=dt_, device="cuda")
+    d0 = desc_for(cfg.with_(n_tokens=a - M), cache_capacity=cap, cache_ring=ring)
+    H.hymba_mixer_prefill(d0, params, *[first[k] for k in per_row], out0, ssm_state_out=state,
+                          conv_state_out=conv, k_cache=kc, v_cache=vc)
+    rest = {k: dev(inp[k][:, a:], act) for k in per_row}
+    out = torch.empty((cfg.batch, T, D), dtype=dt_, device="cuda")
+    desc = desc_for(cfg.with_(n_tokens=T), cache_capacity=cap, cache_ring=ring)
+    ws = torch.empty(max(H.hymba_mixer_prefill_workspace_bytes(desc), 256), dtype=torch.uint8, device="cuda")
+
+    def step():
+        H.hymba_mixer_prefill_continue(desc, params, a, *[rest[k] for k in per_row], out, state, conv, kc, vc,
+                                       workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    return {"us_per_call": round(us, 2), "tokens_per_s": round(cfg.batch * T / (us * 1e-6), 1),
+            "cache_rows_per_seq": cap}
+
+
+def bench_decode_ring(cfg, steps, warmup):
+    """The decode step over the compact cache: n_meta + window rows per
+    sequence instead of cache_len, every sequence at position cache_len."""
+    import torch
+    from harness import Decode, desc_for
+    import attention_lm_amd as H
+    import synth
+
+    cap = cfg.n_meta + cfg.window
+    rcfg = cfg.with_(cache_capacity=cap, cache_len=cap)
+    run = Decode(rcfg, synth.make_decode_inputs(rcfg))
+    run.cache_len.fill_(cfg.cache_len)
+    run.desc = desc_for(rcfg, cache_ring=True)
+    run.ws = torch.empty(max(H.hymba_mixer_decode_workspace_bytes(run.desc), 256), dtype=torch.uint8,
+                         device="cuda")
+
+    def step():
+        for l in range(rcfg.n_layers):
+            run.call(l, with_branches=False)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    return {"us_per_step": round(us, 2), "cache_rows_per_seq": cap, "position": cfg.cache_len}
+
+
 def cpu_baseline(cfg, min_seconds=10.0):
     import numpy as np
     import synth
@@ -370,6 +452,8 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated through the timed steps")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-continue", action="store_true",
+                    help="skip the continued prefill and the compact-cache decode")
     ap.add_argument("--serial", action="store_true",
                     help="time the prefill steps with the branches serialized (per-kernel events in every "
                          "step, as in the per-kernel pass): for profiles whose kernel averages must match")
@@ -470,6 +554,17 @@ def main():
             "bytes_per_call": dw["total_bytes"],
             "kernels": dk,
         }
+    if not args.no_continue:
+        log("[bench] prefill continuation")
+        res["continue"] = {
+            "workload": f"{cfg.workload}: rows {cfg.n_meta + cfg.window}..{cfg.seq_rows - 1} continuing a first "
+                        f"call over rows 0..{cfg.n_meta + cfg.window - 1} (a full window of history)",
+            "rows": bench_continue(cfg, args.steps, args.warmup, ring=False),
+            "ring": bench_continue(cfg, args.steps, args.warmup, ring=True),
+        }
+        if not args.no_decode:
+            log("[bench] decode over the compact cache")
+            res["decode"]["ring"] = bench_decode_ring(synth.config("decode"), args.steps, args.warmup)
     ev.close()
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
