@@ -9,6 +9,7 @@ holds no arithmetic of the method).
 from .hymba_oracle import (  # noqa: F401
     causal_conv1d,
     selective_scan,
+    ssd_scan,
     silu_gate,
     rope,
     rope_angles,

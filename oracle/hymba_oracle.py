@@ -101,6 +101,45 @@ def selective_scan(u, dt, A, Bm, Cm, D, h0=None):
     return y, h
 
 
+def ssd_scan(u, dt, A, Bm, Cm, D, h0=None):
+    """The Mamba-2 form of the selective SSM, one time step after another
+    (Lecture 04, section 3: the state matrix is a scalar times the identity,
+    with heads as in attention; the recurrence is one of the two ways to
+    compute the layer, the block-matmul form the other).
+
+    Channels are grouped into H heads of P = D / H consecutive channels; head
+    h has one decay rate A[h] and one step size dt[:, t, h], so a step decays
+    the head's whole P x N state by the scalar exp(dt A):
+      h_t = exp(dt_t A) h_{t-1} + dt_t x_t B_t^T,  y_t = h_t C_t + D x_t.
+    B and C are shared by all heads.
+
+    u: [B, L, D]; dt: [B, L, H]; A: [H]; Bm, Cm: [B, L, N]; D: [D];
+    h0: [B, D, N] or None (row c of the state belongs to head c // P).
+    Returns y [B, L, D] (before the gate) and the final state [B, D, N].
+    """
+    u, dt, A, Bm, Cm, D = map(_f64, (u, dt, A, Bm, Cm, D))
+    Bsz, L, Dch = u.shape
+    H = A.shape[0]
+    P = Dch // H
+    N = Bm.shape[2]
+    h = np.zeros((Bsz, H, P, N), F64) if h0 is None else _f64(h0).reshape(Bsz, H, P, N).copy()
+    y = np.zeros((Bsz, L, Dch), F64)
+    for t in range(L):
+        decay = np.exp(dt[:, t, :] * A[None, :])                              # [B, H]: one scalar per head
+        xt = u[:, t, :].reshape(Bsz, H, P)
+        h = decay[:, :, None, None] * h + (dt[:, t, :, None, None] * xt[..., None]) * Bm[:, t, None, None, :]
+        y[:, t, :] = np.einsum("bhpn,bn->bhp", h, Cm[:, t, :]).reshape(Bsz, Dch) + D[None, :] * u[:, t, :]
+    return y, h.reshape(Bsz, Dch, N)
+
+
+def _scan(cfg, u, dt, A, Bm, Cm, D, h0=None):
+    """The Mamba branch's scan for this workload: the Mamba-2 form when the
+    configuration has SSM heads, else the selective scan per (channel, state)."""
+    if getattr(cfg, "ssm_heads", 0) > 0:
+        return ssd_scan(u, dt, A, Bm, Cm, D, h0=h0)
+    return selective_scan(u, dt, A, Bm, Cm, D, h0=h0)
+
+
 def silu_gate(y, z) -> np.ndarray:
     """Output gate of the Mamba branch: y * silu(z), silu(z) = z / (1 + exp(-z)).
     Not described on the pages; the plain reading of a silu(z) gate."""
@@ -286,8 +325,7 @@ def mixer_prefill(cfg, inp: Dict[str, np.ndarray], batches: Optional[Iterable[in
     rsel = np.arange(L) if rows is None else np.asarray(rows)
     x = _f64(inp["x"])[bsel]
     u = causal_conv1d(x, inp["conv_w"])
-    y, h = selective_scan(u, _f64(inp["dt"])[bsel], inp["A"], _f64(inp["B"])[bsel],
-                          _f64(inp["C"])[bsel], inp["D"])
+    y, h = _scan(cfg, u, _f64(inp["dt"])[bsel], inp["A"], _f64(inp["B"])[bsel], _f64(inp["C"])[bsel], inp["D"])
     y_ssm = silu_gate(y, _f64(inp["z"])[bsel])
     K = cfg.d_conv
     conv_state = np.zeros((len(bsel), cfg.d_inner, K - 1), F64)
@@ -387,8 +425,7 @@ def mixer_prefill_continue(cfg, inp: Dict[str, np.ndarray], pos0: int, ssm_state
     K = cfg.d_conv
     hist = np.transpose(_f64(conv_state), (0, 2, 1))                      # [B,K-1,D]
     u = causal_conv1d(x, inp["conv_w"], history=hist)
-    y, h = selective_scan(u, _f64(inp["dt"]), inp["A"], _f64(inp["B"]), _f64(inp["C"]), inp["D"],
-                          h0=ssm_state)
+    y, h = _scan(cfg, u, _f64(inp["dt"]), inp["A"], _f64(inp["B"]), _f64(inp["C"]), inp["D"], h0=ssm_state)
     y_ssm = silu_gate(y, _f64(inp["z"]))
     xh = np.concatenate([hist, x], axis=1)                                # rows pos0-K+1 .. pos0+T-1
     new_conv = np.transpose(xh[:, -(K - 1):, :], (0, 2, 1))
@@ -436,8 +473,8 @@ def mixer_decode(cfg, layer_inp: Dict[str, np.ndarray], k_cache, v_cache, k_new,
     x = _f64(li["x"])[:, None, :]                                   # [B,1,D]
     hist = np.transpose(_f64(li["conv_state"]), (0, 2, 1))          # [B,K-1,D]
     u = causal_conv1d(x, li["conv_w"], history=hist)
-    y, h = selective_scan(u, _f64(li["dt"])[:, None, :], li["A"], _f64(li["B"])[:, None, :],
-                          _f64(li["C"])[:, None, :], li["D"], h0=li["ssm_state"])
+    y, h = _scan(cfg, u, _f64(li["dt"])[:, None, :], li["A"], _f64(li["B"])[:, None, :],
+                 _f64(li["C"])[:, None, :], li["D"], h0=li["ssm_state"])
     y_ssm = silu_gate(y, _f64(li["z"])[:, None, :])[:, 0, :]
     new_conv = np.concatenate([_f64(li["conv_state"])[:, :, 1:], _f64(li["x"])[:, :, None]], axis=2)
 

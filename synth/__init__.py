@@ -72,6 +72,7 @@ class MixerConfig:
     cache_len: int = 0     # decode: rows already in the cache (new token's position)
     cache_capacity: int = 0
     n_layers: int = 1      # decode: layers sharing one KV cache
+    ssm_heads: int = 0     # > 0: Mamba-2 form, A a scalar per head, dt per head (head width d_inner / ssm_heads)
     key_affine: bool = False   # decode: layers after the first read the shared keys through
                                # their own affine (k_scale, k_bias); prefill: the layer does
     workload: str = ""
@@ -174,7 +175,8 @@ def _act(cfg: MixerConfig, a: np.ndarray) -> np.ndarray:
 def _params(cfg: MixerConfig, layer: int) -> Dict[str, np.ndarray]:
     D, N, K = cfg.d_inner, cfg.d_state, cfg.d_conv
     g = _rng(cfg, layer, "A")
-    A = -np.exp(g.uniform(np.log(1.0), np.log(16.0), size=(D, N))).astype(np.float32)
+    a_shape = (cfg.ssm_heads,) if cfg.ssm_heads > 0 else (D, N)   # per head, or per (channel, state)
+    A = -np.exp(g.uniform(np.log(1.0), np.log(16.0), size=a_shape)).astype(np.float32)
     conv_w = _normal(cfg, layer, "conv_w", (D, K), sigma=cfg.conv_sigma)
     return {
         "A": A,
@@ -196,13 +198,15 @@ def key_affine(cfg: MixerConfig, layer: int) -> Dict[str, np.ndarray]:
 
 def make_prefill_inputs(cfg: MixerConfig, layer: int = 0) -> Dict[str, np.ndarray]:
     """x, z, dt [B,L,D]; B, C [B,L,N]; q [B,L,Hq,hd]; k [B,L,Hkv,hd]; v [B,L,Hkv,dv]
-    in the activation dtype's values, plus fp32 parameters."""
+    in the activation dtype's values, plus fp32 parameters. With ssm_heads > 0
+    dt is [B,L,ssm_heads] and A [ssm_heads]."""
     Bsz, L, D, N = cfg.batch, cfg.seq_rows, cfg.d_inner, cfg.d_state
+    Ddt = cfg.ssm_heads if cfg.ssm_heads > 0 else D
     Hq, Hkv, hd, dv = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.head_dim_v
     out = {
         "x": _act(cfg, _normal(cfg, layer, "x", (Bsz, L, D))),
         "z": _act(cfg, _normal(cfg, layer, "z", (Bsz, L, D))),
-        "dt": _act(cfg, _softplus32(_normal(cfg, layer, "dt", (Bsz, L, D), cfg.dt_mu, cfg.dt_sigma))),
+        "dt": _act(cfg, _softplus32(_normal(cfg, layer, "dt", (Bsz, L, Ddt), cfg.dt_mu, cfg.dt_sigma))),
         "B": _act(cfg, _normal(cfg, layer, "B", (Bsz, L, N))),
         "C": _act(cfg, _normal(cfg, layer, "C", (Bsz, L, N))),
         "q": _act(cfg, _normal(cfg, layer, "q", (Bsz, L, Hq, hd))),
@@ -251,11 +255,12 @@ def make_decode_inputs(cfg: MixerConfig, cache_len: Optional[np.ndarray] = None)
         "cache_len": cache_len,
     }
     layers = []
+    Ddt = cfg.ssm_heads if cfg.ssm_heads > 0 else D
     for l in range(cfg.n_layers):
         d = {
             "x": _act(cfg, _normal(cfg, l, "x", (Bsz, D))),
             "z": _act(cfg, _normal(cfg, l, "z", (Bsz, D))),
-            "dt": _act(cfg, _softplus32(_normal(cfg, l, "dt", (Bsz, D), cfg.dt_mu, cfg.dt_sigma))),
+            "dt": _act(cfg, _softplus32(_normal(cfg, l, "dt", (Bsz, Ddt), cfg.dt_mu, cfg.dt_sigma))),
             "B": _act(cfg, _normal(cfg, l, "B", (Bsz, N))),
             "C": _act(cfg, _normal(cfg, l, "C", (Bsz, N))),
             "q": _act(cfg, _normal(cfg, l, "q", (Bsz, Hq, hd))),

@@ -585,3 +585,100 @@ def test_decode_on_the_ring_equals_decode_on_the_full_cache(window):
         b = O.mixer_decode(cfg, lay, ring_k, ring_v, inp["k_new"], inp["v_new"], inp["cache_len"], ring=True)
         np.testing.assert_allclose(b["out"], a["out"], rtol=1e-13, atol=1e-14)
         np.testing.assert_allclose(b["y_attn"], a["y_attn"], rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# the Mamba-2 form: one decay rate and one step size per head (Lecture 04,
+# section 3: scalar-times-identity state matrix, recurrence and matmul forms)
+
+
+def _ssd_case(seed, Bsz=2, L=13, H=3, P=4, N=5):
+    g = np.random.default_rng(seed)
+    return dict(u=g.standard_normal((Bsz, L, H * P)), dt=g.uniform(0.01, 0.6, (Bsz, L, H)),
+                A=-g.uniform(0.3, 4.0, H), Bm=g.standard_normal((Bsz, L, N)), Cm=g.standard_normal((Bsz, L, N)),
+                D=g.standard_normal(H * P), h0=g.standard_normal((Bsz, H * P, N)), P=P)
+
+
+def test_ssd_is_the_selective_scan_with_one_rate_per_head():
+    c = _ssd_case(31)
+    P, N = c["P"], c["Bm"].shape[2]
+    A_exp = np.repeat(c["A"], P)[:, None] * np.ones((1, N))          # A[c, n] = A[c // P]
+    dt_exp = np.repeat(c["dt"], P, axis=2)                            # dt[b, t, c] = dt[b, t, c // P]
+    for h0 in (None, c["h0"]):
+        y1, s1 = O.ssd_scan(c["u"], c["dt"], c["A"], c["Bm"], c["Cm"], c["D"], h0=h0)
+        y2, s2 = O.selective_scan(c["u"], dt_exp, A_exp, c["Bm"], c["Cm"], c["D"], h0=h0)
+        np.testing.assert_allclose(y1, y2, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(s1, s2, rtol=1e-12, atol=1e-12)
+
+
+def test_ssd_dual_form_is_a_masked_product():
+    """Zero initial state: per head, Y = (Lmask . (C B^T)) (dt x) + D x with
+    Lmask[i, j] = exp(A (s_i - s_j)) for j <= i and 0 above the diagonal,
+    s the running sum of dt: the quadratic, attention-like way to compute
+    the same layer."""
+    c = _ssd_case(32)
+    u, dt, A, Bm, Cm, D, P = c["u"], c["dt"], c["A"], c["Bm"], c["Cm"], c["D"], c["P"]
+    Bsz, L, Dch = u.shape
+    y_ref, _ = O.ssd_scan(u, dt, A, Bm, Cm, D)
+    y = np.zeros_like(u)
+    for b in range(Bsz):
+        for h in range(len(A)):
+            s = np.cumsum(dt[b, :, h])
+            i, j = np.meshgrid(np.arange(L), np.arange(L), indexing="ij")
+            Lm = np.where(j <= i, np.exp(A[h] * (s[i] - s[j])), 0.0)
+            X = u[b, :, h * P:(h + 1) * P]
+            y[b, :, h * P:(h + 1) * P] = (Lm * (Cm[b] @ Bm[b].T)) @ (dt[b, :, h, None] * X) + D[h * P:(h + 1) * P] * X
+    np.testing.assert_allclose(y, y_ref, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("Q", [1, 4, 5, 13])
+def test_ssd_block_decomposition(Q):
+    """The chunked form: within a chunk the masked product, plus the carried
+    state decayed to each row; chunk end states chained by the chunk's total
+    decay. Equal to the recurrence for any chunk length."""
+    c = _ssd_case(33)
+    u, dt, A, Bm, Cm, D, P, h0 = c["u"], c["dt"], c["A"], c["Bm"], c["Cm"], c["D"], c["P"], c["h0"]
+    Bsz, L, Dch = u.shape
+    H, N = len(A), Bm.shape[2]
+    y_ref, s_ref = O.ssd_scan(u, dt, A, Bm, Cm, D, h0=h0)
+    y = np.zeros_like(u)
+    state = h0.reshape(Bsz, H, P, N).copy()
+    for t0 in range(0, L, Q):
+        t1 = min(t0 + Q, L)
+        for b in range(Bsz):
+            for h in range(H):
+                S = A[h] * np.cumsum(dt[b, t0:t1, h])                  # inclusive, from the chunk start
+                X = u[b, t0:t1, h * P:(h + 1) * P] * dt[b, t0:t1, h, None]
+                i, j = np.meshgrid(np.arange(t1 - t0), np.arange(t1 - t0), indexing="ij")
+                M = np.where(j <= i, np.exp(S[i] - S[j]), 0.0) * (Cm[b, t0:t1] @ Bm[b, t0:t1].T)
+                Hs = state[b, h]                                       # [P, N], entering the chunk
+                y[b, t0:t1, h * P:(h + 1) * P] = (M @ X + np.exp(S)[:, None] * (Cm[b, t0:t1] @ Hs.T)
+                                                  + D[h * P:(h + 1) * P] * u[b, t0:t1, h * P:(h + 1) * P])
+                w = np.exp(S[-1] - S)                                  # decay of each row to the chunk end
+                state[b, h] = np.exp(S[-1]) * Hs + (X * w[:, None]).T @ Bm[b, t0:t1]
+    np.testing.assert_allclose(y, y_ref, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(state.reshape(Bsz, Dch, N), s_ref, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("ring", [False, True])
+def test_ssd_mixer_continuation_and_decode(ring):
+    """The mixer with the Mamba-2 form: a continued prefill equals one prefill,
+    and a decode step equals the prefill of one more row."""
+    cfg = _tiny_cfg(n_meta=3, n_tokens=11, window=4, ssm_heads=2)
+    full = synth.make_prefill_inputs(cfg)
+    assert full["A"].shape == (2,) and full["dt"].shape == (cfg.batch, cfg.seq_rows, 2)
+    ref = O.mixer_prefill(cfg, full)
+    got = _chain(cfg, full, [5, 6, 11], ring)
+    for k in ("y_ssm", "y_attn", "out"):
+        np.testing.assert_allclose(got[k], ref[k], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got["ssm_state"], ref["ssm_state"], rtol=1e-12, atol=1e-13)
+    L = cfg.seq_rows
+    short = {k: (v[:, :L - 1] if k in _PER_ROW else v) for k, v in full.items()}
+    pre = O.mixer_prefill(cfg.with_(n_tokens=cfg.n_tokens - 1), short)
+    layer = {k: full[k][:, L - 1] for k in ("x", "z", "dt", "B", "C", "q")}
+    layer.update(ssm_state=pre["ssm_state"], conv_state=pre["conv_state"],
+                 **{k: full[k] for k in ("A", "conv_w", "D", "beta_attn", "beta_ssm")})
+    dec = O.mixer_decode(cfg, layer, pre["k_rot"], full["v"][:, :L - 1], full["k"][:, L - 1], full["v"][:, L - 1],
+                         np.full(cfg.batch, L - 1))
+    np.testing.assert_allclose(dec["out"], ref["out"][:, L - 1], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dec["ssm_state"], ref["ssm_state"], rtol=1e-12, atol=1e-13)
