@@ -40,7 +40,7 @@ class MixerDesc(ctypes.Structure):
         ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("head_dim_v", ctypes.c_int32), ("window", ctypes.c_int32), ("cache_capacity", ctypes.c_int32),
         ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float), ("act", ctypes.c_int),
-        ("cache_ring", ctypes.c_int32),
+        ("cache_ring", ctypes.c_int32), ("ssm_heads", ctypes.c_int32),
     ]
 
 
@@ -100,12 +100,13 @@ DECODE_STAGES = ("ssm_decode", "attn_decode", "decode_merge_fuse")
 
 def make_desc(batch, n_meta, n_tokens, d_inner, n_q_heads, n_kv_heads, window, act, head_dim=64,
               head_dim_v=None, d_state=16, d_conv=4, cache_capacity=0, rope_base=10000.0,
-              norm_eps=1e-6, cache_ring=False) -> MixerDesc:
+              norm_eps=1e-6, cache_ring=False, ssm_heads=0) -> MixerDesc:
     if head_dim_v is None:
         head_dim_v = d_inner // n_q_heads
     act_code = {"f32": HYMBA_F32, "bf16": HYMBA_BF16}.get(act, act)
     return MixerDesc(batch, n_meta, n_tokens, d_inner, d_state, d_conv, n_q_heads, n_kv_heads, head_dim,
-                     head_dim_v, window, cache_capacity, rope_base, norm_eps, act_code, int(bool(cache_ring)))
+                     head_dim_v, window, cache_capacity, rope_base, norm_eps, act_code, int(bool(cache_ring)),
+                     int(ssm_heads))
 
 
 def make_params(A, D, conv_w, beta_attn, beta_ssm, k_scale=None, k_bias=None) -> MixerParams:

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhymba_mixer.so")
-SOURCES = ["api.hip", "fuse.hip", "ssm.hip", "attn.hip"]
+SOURCES = ["api.hip", "fuse.hip", "ssm.hip", "ssd.hip", "attn.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -95,6 +95,11 @@ int check_desc(const hymba_mixer_desc* d, bool decode) {
   if (d->cache_capacity < 0) return HYMBA_EINVAL;
   if (decode && d->cache_capacity < 1) return HYMBA_EINVAL;
   if (d->cache_ring != 0 && d->cache_ring != 1) return HYMBA_EINVAL;
+  if (d->ssm_heads < 0 || (d->ssm_heads > 0 && d->d_inner % d->ssm_heads != 0)) return HYMBA_EINVAL;
+  if (d->ssm_heads > 0) {   // Mamba-2 heads: widths with a kernel
+    const int P = d->d_inner / d->ssm_heads;
+    if (P != 32 && P != 64 && P != 128) return HYMBA_EUNSUPPORTED;
+  }
   // the compact cache exists for sliding-window layers and holds n_meta + window rows
   if (d->cache_ring && (d->window <= 0 || (int64_t)d->cache_capacity < (int64_t)d->n_meta + d->window))
     return HYMBA_EINVAL;
@@ -148,10 +153,15 @@ PrefillWs prefill_ws(const hymba_mixer_desc* d) {
   w.y_ssm = w.y_attn + round256(rows * d->d_inner * es);
   w.agg = w.y_ssm + round256(rows * d->d_inner * es);
   const int L = d->n_meta + d->n_tokens;
-  w.chunk_rows = hymba::ssm_prefill_chunk_rows(d->batch, L, d->d_inner);
-  w.chunk_rows_cont = hymba::ssm_prefill_chunk_rows(d->batch, d->n_tokens > 0 ? d->n_tokens : 1, d->d_inner);
-  const size_t nchunk = std::max((size_t)((L + w.chunk_rows - 1) / w.chunk_rows),
-                                 (size_t)((d->n_tokens + w.chunk_rows_cont - 1) / w.chunk_rows_cont));
+  if (d->ssm_heads > 0) {   // Mamba-2 form: fixed chunks
+    w.chunk_rows = w.chunk_rows_cont = hymba::ssd_chunk_rows();
+  } else {
+    w.chunk_rows = hymba::ssm_prefill_chunk_rows(d->batch, L, d->d_inner);
+    w.chunk_rows_cont = hymba::ssm_prefill_chunk_rows(d->batch, d->n_tokens > 0 ? d->n_tokens : 1, d->d_inner);
+  }
+  // (one slot more than chunks: the Mamba-2 form's carry chain also yields the final state)
+  const size_t nchunk = 1 + std::max((size_t)((L + w.chunk_rows - 1) / w.chunk_rows),
+                                     (size_t)((d->n_tokens + w.chunk_rows_cont - 1) / w.chunk_rows_cont));
   const size_t chans = (size_t)d->batch * d->d_inner;
   w.sdt = w.agg + round256(nchunk * chans * 16 * sizeof(float));
   w.carry = w.sdt + round256(nchunk * chans * sizeof(float));
@@ -279,9 +289,14 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
   sa.agg = (float*)(wsb + ws.agg); sa.sdt = (float*)(wsb + ws.sdt); sa.carry = (float*)(wsb + ws.carry);
   sa.chunk_rows = c.cont ? ws.chunk_rows_cont : ws.chunk_rows;
   sa.batch = desc->batch; sa.L = L; sa.d_inner = desc->d_inner; sa.act = desc->act;
-  HYMBA_TRY(hymba::launch_ssm_chunk_end(sa, ssm_stream, tm(0)));
-  HYMBA_TRY(hymba::launch_ssm_chunk_carry(sa, ssm_stream, tm(1)));
-  HYMBA_TRY(hymba::launch_ssm_chunk_out(sa, ssm_stream, tm(2)));
+  sa.head_width = desc->ssm_heads > 0 ? desc->d_inner / desc->ssm_heads : 0;
+  if (sa.head_width > 0) {
+    HYMBA_TRY(hymba::launch_ssd_prefill(sa, ssm_stream, tm(0), tm(1), tm(2)));
+  } else {
+    HYMBA_TRY(hymba::launch_ssm_chunk_end(sa, ssm_stream, tm(0)));
+    HYMBA_TRY(hymba::launch_ssm_chunk_carry(sa, ssm_stream, tm(1)));
+    HYMBA_TRY(hymba::launch_ssm_chunk_out(sa, ssm_stream, tm(2)));
+  }
   if (fc) HYMBA_TRY(hipEventRecord(fc->join, fc->aux));
 
   // Attention branch. Where the rotated keys and the values that attention
@@ -476,6 +491,7 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
   sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
   sa.state = ssm_state; sa.conv_state = conv_state; sa.y = y_ssm;
   sa.batch = desc->batch; sa.d_inner = desc->d_inner; sa.act = desc->act;
+  sa.head_width = desc->ssm_heads > 0 ? desc->d_inner / desc->ssm_heads : 0;
   HYMBA_TRY(hymba::launch_ssm_decode(sa, stream, tm(0)));
 
   hymba::AttnDecodeArgs aa;

@@ -12,6 +12,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "mma.hpp"
 
 namespace hymba {
 
@@ -185,56 +186,6 @@ __device__ __forceinline__ void lds_barrier() {
 
 // slot s of a 16-key chunk holds key kperm(s); an involution
 __device__ __forceinline__ int kperm(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
-
-template <typename T>
-struct Mma;
-template <>
-struct Mma<bf16> {
-  typedef bf16x8_t Frag;   // 8 bf16 per lane
-  static __device__ __forceinline__ Frag frag_at(const bf16* p) {
-    return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4_t*>(p));
-  }
-  static __device__ __forceinline__ Frag zero() { return __builtin_bit_cast(Frag, u32x4_t{0u, 0u, 0u, 0u}); }
-  static __device__ __forceinline__ Frag from_f32(const float* v) {
-    u32x4_t u;
-    u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
-    u.z = pack_bf16x2(v[4], v[5]); u.w = pack_bf16x2(v[6], v[7]);
-    return __builtin_bit_cast(Frag, u);
-  }
-  static __device__ __forceinline__ f32x16_t mma(const Frag& a, const Frag& b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-};
-struct F32x8 { float v[8]; };
-template <>
-struct Mma<float> {
-  typedef F32x8 Frag;      // 8 fp32 per lane; slot t of lane half h is k = 8h + t
-  static __device__ __forceinline__ Frag frag_at(const float* p) {
-    Frag f;
-    float4 a = *reinterpret_cast<const float4*>(p);
-    float4 b = *reinterpret_cast<const float4*>(p + 4);
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-    return f;
-  }
-  static __device__ __forceinline__ Frag zero() {
-    Frag f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) f.v[t] = 0.f;
-    return f;
-  }
-  static __device__ __forceinline__ Frag from_f32(const float* v) {
-    Frag f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) f.v[t] = v[t];
-    return f;
-  }
-  static __device__ __forceinline__ f32x16_t mma(const Frag& a, const Frag& b, f32x16_t c) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[t], b.v[t], c, 0, 0, 0);
-    return c;
-  }
-};
 
 // Staging of one 64-key K/V tile in LDS (two stages, double-buffered).
 //

@@ -49,6 +49,8 @@ struct SsmPrefillArgs {
   float* carry;            // workspace [n_chunks, batch, d_inner, 16]
   int chunk_rows;          // from ssm_prefill_chunk_rows()
   int batch, L, d_inner;
+  int head_width;          // 0: A [d_inner, 16], dt per channel; > 0: Mamba-2 heads of this many channels,
+                           // A [d_inner / head_width], dt [batch, L, d_inner / head_width]
   hymba_dtype act;
 };
 int ssm_prefill_chunk_rows(int batch, int L, int d_inner);
@@ -57,6 +59,16 @@ int ssm_prefill_chunk_rows(int batch, int L, int d_inner);
 hipError_t launch_ssm_chunk_end(const SsmPrefillArgs& a, hipStream_t stream, Timing tm = {});
 hipError_t launch_ssm_chunk_carry(const SsmPrefillArgs& a, hipStream_t stream, Timing tm = {});
 hipError_t launch_ssm_chunk_out(const SsmPrefillArgs& a, hipStream_t stream, Timing tm = {});
+// The chunk carry chain alone: carry[0] = state_in (or 0), carry[k + 1] =
+// exp(a sdt[k]) carry[k] + agg[k] for k < n_slots - 1, per (sequence, channel,
+// state); a = A[c, n], or A[c / head_width] when head_width > 0.
+hipError_t launch_ssm_carry_chain(const float* A, const float* agg, const float* sdt, const float* state_in,
+                                  float* carry, int n_slots, int batch, int d_inner, int head_width,
+                                  hipStream_t stream, Timing tm = {});
+// Mamba-2 form (ssd.hip): chunk states, carry chain, outputs; rows per chunk
+int ssd_chunk_rows();
+hipError_t launch_ssd_prefill(const SsmPrefillArgs& a, hipStream_t stream, Timing tm_state = {}, Timing tm_carry = {},
+                              Timing tm_out = {});
 
 struct SsmDecodeArgs {
   const void *x, *z, *dt, *B, *C;
@@ -65,6 +77,7 @@ struct SsmDecodeArgs {
   void* conv_state;        // in/out [batch, d_inner, 3] act
   void* y;                 // [batch, d_inner] act
   int batch, d_inner;
+  int head_width;          // > 0: Mamba-2 heads (A and dt per head)
   hymba_dtype act;
 };
 hipError_t launch_ssm_decode(const SsmDecodeArgs& a, hipStream_t stream, Timing tm = {});
@@ -74,6 +87,7 @@ inline ssm_step::Ptrs<T> ssm_step_ptrs(const SsmDecodeArgs& a) {
   p.x = (const T*)a.x; p.z = (const T*)a.z; p.dt = (const T*)a.dt; p.B = (const T*)a.B; p.C = (const T*)a.C;
   p.A = a.A; p.D = a.D; p.conv_w = a.conv_w; p.state = a.state; p.conv_state = (T*)a.conv_state; p.y = (T*)a.y;
   p.d_inner = a.d_inner;
+  p.head_width = a.head_width;
   return p;
 }
 

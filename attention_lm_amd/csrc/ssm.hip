@@ -286,7 +286,7 @@ __global__ __launch_bounds__(64 * kCarrySegs) void ssm_chunk_carry_kernel(const 
                                                                          const float* __restrict__ sdt,
                                                                          const float* __restrict__ state_in,
                                                                          float* __restrict__ carry, int nchunk,
-                                                                         int batch, int Dch) {
+                                                                         int batch, int Dch, int head_width) {
   constexpr int KB = kCarryBatch;
   __shared__ float seg_h[kCarrySegs][64], seg_s[kCarrySegs][64];
   const int lane = threadIdx.x & 63;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * kCarrySegs) void ssm_chunk_carry_kernel(const 
   const int n = (int)(ci % kStates);
   const int64_t bc = ci / kStates;
   const int c = (int)(bc % Dch);
-  const float a2 = A[(int64_t)c * kStates + n] * kLog2e;
+  const float a2 = (head_width > 0 ? A[c / head_width] : A[(int64_t)c * kStates + n]) * kLog2e;
   const int steps = nchunk - 1;   // chunks 0 .. nchunk-2 feed a later chunk
   const int seg_len = (steps + kCarrySegs - 1) / kCarrySegs;
   const int k0 = min(steps, seg * seg_len), k1 = min(steps, k0 + seg_len);
@@ -429,12 +429,18 @@ hipError_t launch_ssm_chunk_end(const SsmPrefillArgs& a, hipStream_t stream, Tim
   return chunk_end_t<float>(a, stream, tm);
 }
 
+hipError_t launch_ssm_carry_chain(const float* A, const float* agg, const float* sdt, const float* state_in,
+                                  float* carry, int n_slots, int batch, int d_inner, int head_width,
+                                  hipStream_t stream, Timing tm) {
+  const int64_t per = (int64_t)batch * d_inner * kStates;
+  HYMBA_LAUNCH(ssm_chunk_carry_kernel, dim3((unsigned)((per + 63) / 64)), dim3(64 * kCarrySegs), 0, stream, tm, A,
+               agg, sdt, state_in, carry, n_slots, batch, d_inner, head_width);
+  return hipGetLastError();
+}
+
 hipError_t launch_ssm_chunk_carry(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
   const int nchunk = (a.L + a.chunk_rows - 1) / a.chunk_rows;
-  const int64_t per = (int64_t)a.batch * a.d_inner * kStates;
-  HYMBA_LAUNCH(ssm_chunk_carry_kernel, dim3((unsigned)((per + 63) / 64)), dim3(64 * kCarrySegs), 0, stream, tm,
-               a.A, a.agg, a.sdt, a.state_in, a.carry, nchunk, a.batch, a.d_inner);
-  return hipGetLastError();
+  return launch_ssm_carry_chain(a.A, a.agg, a.sdt, a.state_in, a.carry, nchunk, a.batch, a.d_inner, 0, stream, tm);
 }
 
 hipError_t launch_ssm_chunk_out(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {

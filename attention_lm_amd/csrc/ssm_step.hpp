@@ -17,12 +17,13 @@ constexpr int kConv = 4;
 
 template <typename T>
 struct Ptrs {
-  const T *x, *z, *dt, *B, *C;   // [batch, d_inner] / [batch, 16]
-  const float *A, *D, *conv_w;   // [d_inner, 16], [d_inner], [d_inner, 4]
+  const T *x, *z, *dt, *B, *C;   // [batch, d_inner] (dt: [batch, heads] with heads) / [batch, 16]
+  const float *A, *D, *conv_w;   // [d_inner, 16] (or [heads]), [d_inner], [d_inner, 4]
   float* state;                  // in/out [batch, d_inner, 16]
   T* conv_state;                 // in/out [batch, d_inner, 3]
   T* y;                          // out [batch, d_inner]
   int d_inner;
+  int head_width;                // > 0: Mamba-2 heads of this many channels, one A and dt per head
 };
 
 // Everything a lane needs for its item, loaded by load() and used by finish(),
@@ -56,12 +57,18 @@ __device__ __forceinline__ void load(const Ptrs<T>& p, Item<T>& it, int64_t b, i
 #pragma unroll
   for (int j = 0; j < kConv - 1; ++j) it.cs[j] = to_f32(p.conv_state[it.bc * (kConv - 1) + j]);
   it.x = p.x[it.bc];
-  it.d = to_f32(p.dt[it.bc]);
+  const int hw = p.head_width;
+  it.d = to_f32(hw > 0 ? p.dt[b * (p.d_inner / hw) + c / hw] : p.dt[it.bc]);
   it.z = to_f32(p.z[it.bc]);
   it.Dc = p.D[c];
   load4(p.conv_w + (int64_t)c * kConv, it.w);
   it.h4 = *reinterpret_cast<const float4*>(p.state + it.bc * kStates + 4 * q);
-  it.a4 = *reinterpret_cast<const float4*>(p.A + (int64_t)c * kStates + 4 * q);
+  if (hw > 0) {
+    const float a = p.A[c / hw];
+    it.a4 = make_float4(a, a, a, a);
+  } else {
+    it.a4 = *reinterpret_cast<const float4*>(p.A + (int64_t)c * kStates + 4 * q);
+  }
   load4(p.B + b * kStates + 4 * q, it.B);
   load4(p.C + b * kStates + 4 * q, it.C);
 }

@@ -40,7 +40,8 @@ EXP_SLOTS = 4
 SCAN_END_SLOTS_PER_ELEM = 3 + EXP_SLOTS   # mul(dt*A) + exp + mul(dt*u*B) + fma(h)
 SCAN_OUT_SLOTS_PER_ELEM = 4 + EXP_SLOTS   # ... + fma(C.h)
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
-KERNEL_SOURCES = ["common.hpp", "launch.hpp", "ssm_step.hpp", "ssm.hip", "attn.hip", "fuse.hip", "api.hip"]
+KERNEL_SOURCES = ["common.hpp", "launch.hpp", "ssm_step.hpp", "mma.hpp", "ssm.hip", "ssd.hip", "attn.hip", "fuse.hip",
+                  "api.hip"]
 
 
 def log(*a):

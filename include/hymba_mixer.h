@@ -91,6 +91,14 @@ typedef enum {
  *              no older row, so the cache holds n_meta + window rows whatever
  *              the context length. Needs window > 0 and
  *              cache_capacity >= n_meta + window.
+ *  ssm_heads   0: the selective scan with A [d_inner, d_state] and dt per
+ *              channel. > 0: the Mamba-2 form ("Lecture 04 - Beyond the Dense
+ *              Transformer", section 3): ssm_heads heads of P = d_inner /
+ *              ssm_heads consecutive channels, each with one decay rate and
+ *              one step size, so A is [ssm_heads] and dt [.., ssm_heads]
+ *              (prefill [batch, L, ssm_heads], decode [batch, ssm_heads]);
+ *              states keep their [batch, d_inner, d_state] layout. This build
+ *              has kernels for P = 32, 64, 128.
  */
 typedef struct {
   int32_t batch, n_meta, n_tokens;
@@ -101,6 +109,7 @@ typedef struct {
   float rope_base, norm_eps;
   hymba_dtype act;
   int32_t cache_ring;
+  int32_t ssm_heads;
 } hymba_mixer_desc;
 
 /* Per-layer fp32 parameters, device pointers.
@@ -133,7 +142,9 @@ size_t hymba_mixer_decode_workspace_bytes(const hymba_mixer_desc* desc);
 /* Rows per chunk of the prefill selective scan: the sequence is cut into
  * chunks of this many rows that are scanned in parallel (the first pass
  * computes the end state of every chunk but the last, a carry pass chains
- * them, the output pass rescans every chunk from its carried-in state).
+ * them, the output pass rescans every chunk from its carried-in state; in the
+ * Mamba-2 form the first pass covers every chunk and the output pass is block
+ * matrix products).
  * Host-side query for sizing and work accounting; 0 if desc is invalid. */
 int hymba_mixer_prefill_chunk_rows(const hymba_mixer_desc* desc);
 

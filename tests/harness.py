@@ -33,7 +33,8 @@ def desc_for(cfg, **kw):
     d = dict(batch=cfg.batch, n_meta=cfg.n_meta, n_tokens=cfg.n_tokens, d_inner=cfg.d_inner,
              n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads, window=cfg.window, act=cfg.act,
              head_dim=cfg.head_dim, d_state=cfg.d_state, d_conv=cfg.d_conv,
-             cache_capacity=cfg.cache_capacity, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps)
+             cache_capacity=cfg.cache_capacity, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps,
+             ssm_heads=cfg.ssm_heads)
     d.update(kw)
     return H.make_desc(**d)
 

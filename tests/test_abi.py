@@ -67,8 +67,9 @@ def test_workspace_sizes(lib):
     # rotated q and k, both branch outputs (bf16), then the scan's per-chunk
     # end states, summed dt and carried-in states (fp32): 25 channel blocks of
     # 128 -> ~2048/25 = 82 chunks wanted -> 27 rows, rounded up to 32 -> 68 chunks
-    # (then a copy of a carried conv history, 3 rows, for a continuation)
-    n_chunk = (L + 31) // 32
+    # (one slot more than chunks: the Mamba-2 form's chain also yields the
+    # final state), then a copy of a carried conv history, 3 rows, for a continuation
+    n_chunk = (L + 31) // 32 + 1
     expect = (L * 25 * 64 + L * 5 * 64 + 2 * L * 3200) * 2 + n_chunk * 3200 * (16 + 1 + 16) * 4 + 3200 * 3 * 2
     got = H.hymba_mixer_prefill_workspace_bytes(d)
     assert expect <= got <= expect + 10 * 256
@@ -85,6 +86,7 @@ def test_workspace_sizes(lib):
     assert H.hymba_mixer_prefill_workspace_bytes(c1_desc(n_q_heads=24)) == 0     # invalid -> 0
     assert H.hymba_mixer_prefill_chunk_rows(d) == 32
     assert H.hymba_mixer_prefill_chunk_rows(c1_desc(n_q_heads=24)) == 0
+    assert H.hymba_mixer_prefill_chunk_rows(c1_desc(ssm_heads=50)) == 64   # Mamba-2 form: 64-row chunks
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -95,6 +97,9 @@ def test_workspace_sizes(lib):
     (dict(d_state=8), -2),
     (dict(head_dim=128), -2),
     (dict(act=7), -1),
+    (dict(ssm_heads=-1), -1),
+    (dict(ssm_heads=3), -1),           # d_inner % ssm_heads != 0
+    (dict(ssm_heads=128), -2),         # head width 25: no kernel
 ])
 def test_prefill_rejects_bad_geometry(lib, kw, status):
     d = c1_desc(**kw)

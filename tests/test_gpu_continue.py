@@ -195,3 +195,12 @@ def test_ring_prefill_then_decode():
     check("y_ssm", host(run.layers[0]["y_ssm_out"]), ref["y_ssm"][:, L - 1], 5e-3)
     check("y_attn", host(run.layers[0]["y_attn_out"]), ref["y_attn"][:, 0], 5e-3)
     check("out", host(run.layers[0]["out"]), ref["out"][:, 0], 5e-3)
+
+
+@pytest.mark.parametrize("ring", [False, True], ids=["rows", "ring"])
+def test_continuation_chain_ssd(ring):
+    """A chain of calls with the Mamba-2 form: the carried state enters the
+    block form's chain, the conv history its first chunk."""
+    cfg = synth.config("tiny_f32").with_(batch=2, n_meta=5, n_tokens=200, d_inner=256, n_q_heads=2, n_kv_heads=1,
+                                         window=40, act="bf16", seed=65, ssm_heads=4, name="chain_ssd")
+    check_chain(cfg, [55, 57, 140], ring)

@@ -280,3 +280,41 @@ def test_decode_continues_prefill():
     check("y_ssm", host(run.layers[0]["y_ssm_out"]), ref["y_ssm"][:, L - 1], 5e-3)
     check("y_attn", host(run.layers[0]["y_attn_out"]), ref["y_attn"][:, 0], 5e-3)
     check("out", host(run.layers[0]["out"]), ref["out"][:, 0], 5e-3)
+
+
+# ---------------------------------------------------------------------------
+# the Mamba-2 form of the scan (one decay rate and step size per head)
+
+SSD_SMALL = [
+    # head width 64, several 64-row chunks and a ragged tail
+    dict(batch=2, n_meta=5, n_tokens=150, d_inner=256, n_q_heads=2, n_kv_heads=1, window=40, act="bf16", seed=61,
+         ssm_heads=4),
+    # fp32, head width 32, one partial chunk
+    dict(batch=1, n_meta=8, n_tokens=40, d_inner=128, n_q_heads=2, n_kv_heads=1, window=16, act="f32", seed=62,
+         ssm_heads=4),
+    # fp32, head width 128, chunks of 64 with a 1-row tail
+    dict(batch=2, n_meta=3, n_tokens=126, d_inner=256, n_q_heads=4, n_kv_heads=2, window=0, act="f32", seed=63,
+         ssm_heads=2),
+    # bf16, head width 32, 8 heads
+    dict(batch=1, n_meta=16, n_tokens=300, d_inner=256, n_q_heads=8, n_kv_heads=2, window=64, act="bf16", seed=64,
+         ssm_heads=8),
+]
+
+
+@pytest.mark.parametrize("kw", SSD_SMALL, ids=[f"ssd{i}" for i in range(len(SSD_SMALL))])
+def test_prefill_ssd_small_shapes(kw):
+    cfg = synth.config("tiny_f32").with_(**kw, name="ssd")
+    run_prefill_parity(cfg)
+
+
+def test_prefill_ssd_swa_layer_full():
+    """The 1.5B-shaped window-1024 layer with its Mamba branch in the Mamba-2
+    form: 50 heads of 64 channels."""
+    run_prefill_parity(synth.config("swa_layer").with_(ssm_heads=50, name="swa_ssd"))
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_decode_ssd(act):
+    cfg = synth.config("decode").with_(batch=5, d_inner=320, n_q_heads=5, n_kv_heads=1, n_meta=8, window=50,
+                                       cache_capacity=300, act=act, ssm_heads=5, name="dssd")
+    run_decode_parity(cfg, cache_len=np.array([300, 8, 9, 57, 120], np.int32))
