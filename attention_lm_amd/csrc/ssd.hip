@@ -49,48 +49,123 @@ __device__ __forceinline__ float wave_scan(float v, int lane) {
   return v;
 }
 
-// What both passes stage for chunk k of head h of sequence b: per row, dt and
-// S (in log2 units, A log2(e) times the running dt sum); the conv input rows
-// t0 - 3 .. t0 + 63 of the head's channels; the conv taps.
+// What both passes stage for chunk k of head h of sequence b, in LDS: per
+// row, dt and S (log2 units: A log2(e) times the running dt sum); the conv
+// input rows t0 - 3 .. t0 + 63 of the head's channels (fp32); the conv taps;
+// the chunk's B rows (and, for the output pass, C rows).
 template <typename T, int P>
 struct ChunkIn {
-  T xs[kQ + kTaps - 1][P];
+  float xs[kQ + kTaps - 1][P];
+  float bs[kQ][kSt];
   float s2[kQ], dts[kQ];
   float cw[P][kTaps];
   float total;   // dt sum over the chunk
 };
 
+// Global loads of a chunk, issued together into registers (buffer loads: rows
+// at or past L read zeros), then written to LDS by commit().
 template <typename T, int P>
-__device__ __forceinline__ void stage_chunk(ChunkIn<T, P>& ci, const T* __restrict__ x, const T* __restrict__ dt,
-                                            const float* __restrict__ A, const float* __restrict__ conv_w,
-                                            const T* __restrict__ conv_in, int64_t b, int h, int t0, int nr, int L,
-                                            int D, int H) {
-  const int tid = threadIdx.x;
-  const int c0 = h * P;
-  if (tid < 64) {
-    const float d = tid < nr ? to_f32(dt[((b * L) + t0 + tid) * H + h]) : 0.f;
-    const float cum = wave_scan(d, tid);
-    ci.dts[tid] = d;
-    ci.s2[tid] = A[h] * kLog2e * cum;
-    if (tid == 63) ci.total = cum;
+struct ChunkLoads {
+  static constexpr int E = Vec16<T>::n;                          // elements per 16-byte load
+  static constexpr int XV = P / E;                                // 16-byte pieces per x row
+  static constexpr int NX = ((kQ + kTaps - 1) * XV + kSsdThreads - 1) / kSsdThreads;
+  static constexpr int BV = kSt / E;                              // pieces per B/C row
+  static constexpr int NB = (kQ * BV + kSsdThreads - 1) / kSsdThreads;
+  u32x4_t xv[NX], bv[NB], cv[NB];
+  float dt;
+
+  __device__ __forceinline__ void issue(const T* x, const T* dtp, const T* Bm, const T* Cm, int64_t b, int h,
+                                        int t0, int L, int D, int H, bool with_c) {
+    const int tid = threadIdx.x;
+    const int c0 = h * P;
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + b * L * D, (uint32_t)((int64_t)L * D * sizeof(T)));
+#pragma unroll
+    for (int q = 0; q < NX; ++q) {
+      const int it = tid + q * kSsdThreads, r = it / XV, v = it % XV, t = t0 - (kTaps - 1) + r;
+      const bool ok = it < (kQ + kTaps - 1) * XV && t >= 0;
+      xv[q] = buf_load16(xrs, ok ? (uint32_t)(((int64_t)t * D + c0 + v * E) * sizeof(T)) : kBufferNowhere);
+    }
+    const uint32_t rowb = kSt * sizeof(T);
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(Bm + b * L * kSt, (uint32_t)L * rowb);
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(Cm + b * L * kSt, (uint32_t)L * rowb);
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int it = tid + q * kSsdThreads, j = it / BV, v = it % BV;
+      const uint32_t off = it < kQ * BV ? (uint32_t)(t0 + j) * rowb + 16u * v : kBufferNowhere;
+      bv[q] = buf_load16(brs, off);
+      if (with_c) cv[q] = buf_load16(crs, off);
+    }
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dtp + b * L * H, (uint32_t)((int64_t)L * H * sizeof(T)));
+    dt = 0.f;
+    if (tid < 64) {
+      const uint32_t off = (uint32_t)(((int64_t)(t0 + tid) * H + h) * sizeof(T));
+      if constexpr (sizeof(T) == 2)
+        dt = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(drs, off, 0, 0) << 16);
+      else
+        dt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(drs, off, 0, 0));
+    }
   }
-  for (int e = tid; e < (kQ + kTaps - 1) * P; e += kSsdThreads) {
-    const int r = e / P, p = e % P, t = t0 - (kTaps - 1) + r;
-    T v = from_f32<T>(0.f);
-    if (t >= 0 && t < L)
-      v = x[(b * L + t) * D + c0 + p];
-    else if (t < 0 && conv_in)
-      v = conv_in[(b * D + c0 + p) * (kTaps - 1) + (kTaps - 1) + t];
-    ci.xs[r][p] = v;
+
+  __device__ __forceinline__ static void unpack(u32x4_t w, float* o) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { o[2 * e] = bf16_lo(w[e]); o[2 * e + 1] = bf16_hi(w[e]); }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(w[e]);
+    }
   }
-  for (int e = tid; e < P * kTaps; e += kSsdThreads) ci.cw[e / kTaps][e % kTaps] = conv_w[(int64_t)c0 * kTaps + e];
-}
+
+  // LDS writes; rows before row 0 come from the carried history when given
+  __device__ __forceinline__ void commit(ChunkIn<T, P>& ci, float (*cs)[kSt], const float* A, const float* conv_w,
+                                         const T* conv_in, int64_t b, int h, int t0, int D) {
+    const int tid = threadIdx.x;
+    const int c0 = h * P;
+#pragma unroll
+    for (int q = 0; q < NX; ++q) {
+      const int it = tid + q * kSsdThreads, r = it / XV, v = it % XV, t = t0 - (kTaps - 1) + r;
+      if (it < (kQ + kTaps - 1) * XV) {
+        float f[E];
+        unpack(xv[q], f);
+        if (t < 0 && conv_in) {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            f[e] = to_f32(conv_in[(b * D + c0 + v * E + e) * (kTaps - 1) + (kTaps - 1) + t]);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) ci.xs[r][v * E + e] = f[e];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int it = tid + q * kSsdThreads, j = it / BV, v = it % BV;
+      if (it < kQ * BV) {
+        float f[E];
+        unpack(bv[q], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) ci.bs[j][v * E + e] = f[e];
+        if (cs) {
+          unpack(cv[q], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) cs[j][v * E + e] = f[e];
+        }
+      }
+    }
+    if (tid < 64) {
+      const float cum = wave_scan(dt, tid);
+      ci.dts[tid] = dt;
+      ci.s2[tid] = A[h] * kLog2e * cum;
+      if (tid == 63) ci.total = cum;
+    }
+    for (int e = tid; e < P * kTaps; e += kSsdThreads) ci.cw[e / kTaps][e % kTaps] = conv_w[(int64_t)c0 * kTaps + e];
+  }
+};
 
 template <typename T, int P>
 __device__ __forceinline__ float conv_at(const ChunkIn<T, P>& ci, int j, int p) {
   float u = 0.f;
 #pragma unroll
-  for (int k = 0; k < kTaps; ++k) u = fmaf(ci.cw[p][k], to_f32(ci.xs[j + k][p]), u);
+  for (int k = 0; k < kTaps; ++k) u = fmaf(ci.cw[p][k], ci.xs[j + k][p], u);
   return u;
 }
 
@@ -103,21 +178,22 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
     float* __restrict__ sdt, int L, int D, int H, int batch) {
   __shared__ ChunkIn<T, P> ci;
   __shared__ __attribute__((aligned(16))) float us[kQ][P + kRowPad];   // u_j dt_j exp(S_last - S_j)
-  __shared__ __attribute__((aligned(16))) float bs[kQ][kSt];
+  __shared__ float wj[kQ];                                              // dt_j exp(S_last - S_j)
   const int k = blockIdx.x, h = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int t0 = k * kQ, nr = min(kQ, L - t0);
-  stage_chunk(ci, x, dt, A, conv_w, conv_in, b, h, t0, nr, L, D, H);
-  for (int e = tid; e < kQ * kSt; e += kSsdThreads) {
-    const int j = e / kSt;
-    bs[j][e % kSt] = j < nr ? to_f32(Bm[(b * L + t0 + j) * kSt + e % kSt]) : 0.f;
+  const int t0 = k * kQ;
+  {
+    ChunkLoads<T, P> ld;
+    ld.issue(x, dt, Bm, nullptr, b, h, t0, L, D, H, false);
+    ld.commit(ci, nullptr, A, conv_w, conv_in, b, h, t0, D);
   }
   __syncthreads();
-  const float s2_last = ci.s2[kQ - 1];
+  if (tid < kQ) wj[tid] = ci.dts[tid] * __builtin_amdgcn_exp2f(ci.s2[kQ - 1] - ci.s2[tid]);
+  __syncthreads();
   for (int e = tid; e < kQ * P; e += kSsdThreads) {
     const int j = e / P, p = e % P;
-    us[j][p] = conv_at(ci, j, p) * ci.dts[j] * __builtin_amdgcn_exp2f(s2_last - ci.s2[j]);
+    us[j][p] = conv_at(ci, j, p) * wj[j];
   }
   __syncthreads();
   const int c0 = h * P;
@@ -128,8 +204,8 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
 #pragma unroll 8
     for (int j = 0; j < kQ; ++j) {
       const float u = us[j][p];
-      const float4 bv = *reinterpret_cast<const float4*>(&bs[j][n0]);
-      a0 = fmaf(u, bv.x, a0); a1 = fmaf(u, bv.y, a1); a2 = fmaf(u, bv.z, a2); a3 = fmaf(u, bv.w, a3);
+      const float4 bq = *reinterpret_cast<const float4*>(&ci.bs[j][n0]);
+      a0 = fmaf(u, bq.x, a0); a1 = fmaf(u, bq.y, a1); a2 = fmaf(u, bq.z, a2); a3 = fmaf(u, bq.w, a3);
     }
     *reinterpret_cast<float4*>(agg + (row0 + p) * kSt + n0) = make_float4(a0, a1, a2, a3);
   }
@@ -145,78 +221,88 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(
     T* __restrict__ y, float* __restrict__ state_out, T* __restrict__ conv_state_out, int L, int D, int H,
     int batch, int nchunk) {
   typedef Mma<T> M;
+  constexpr int NTP = P / 32;
   __shared__ ChunkIn<T, P> ci;
   __shared__ __attribute__((aligned(16))) float ut[P][kQ + kRowPad];   // u, [channel][row]
   __shared__ __attribute__((aligned(16))) float ms[kQ][kQ + kRowPad];  // M[i][j]
-  __shared__ __attribute__((aligned(16))) float bs[kQ][kSt];
   __shared__ __attribute__((aligned(16))) float cs[kQ][kSt];
   __shared__ __attribute__((aligned(16))) float hs[P][kSt];            // entering state
   const int k = blockIdx.x, h = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lq = lane & 31, hh = lane >> 5;
   const int t0 = k * kQ, nr = min(kQ, L - t0);
   const int c0 = h * P;
-  stage_chunk(ci, x, dt, A, conv_w, conv_in, b, h, t0, nr, L, D, H);
-  for (int e = tid; e < kQ * kSt; e += kSsdThreads) {
-    const int j = e / kSt, n = e % kSt;
-    const bool in = j < nr;
-    bs[j][n] = in ? to_f32(Bm[(b * L + t0 + j) * kSt + n]) : 0.f;
-    cs[j][n] = in ? to_f32(Cm[(b * L + t0 + j) * kSt + n]) : 0.f;
+  {
+    ChunkLoads<T, P> ld;
+    ld.issue(x, dt, Bm, Cm, b, h, t0, L, D, H, true);
+    const float4* hin = reinterpret_cast<const float4*>(carry + (((int64_t)k * batch + b) * D + c0) * kSt);
+    float4 hv[(P * kSt / 4 + kSsdThreads - 1) / kSsdThreads];
+#pragma unroll
+    for (int q = 0; q < (int)(sizeof(hv) / sizeof(hv[0])); ++q) {
+      const int it = tid + q * kSsdThreads;
+      if (it < P * kSt / 4) hv[q] = hin[it];
+    }
+    ld.commit(ci, cs, A, conv_w, conv_in, b, h, t0, D);
+#pragma unroll
+    for (int q = 0; q < (int)(sizeof(hv) / sizeof(hv[0])); ++q) {
+      const int it = tid + q * kSsdThreads;
+      if (it < P * kSt / 4) reinterpret_cast<float4*>(&hs[0][0])[it] = hv[q];
+    }
   }
-  const float* hin = carry + (((int64_t)k * batch + b) * D + c0) * kSt;
-  for (int e = tid; e < P * kSt; e += kSsdThreads) hs[e / kSt][e % kSt] = hin[e];
   __syncthreads();
-  // u (transposed) and the masked, decayed C B^T block: each thread a 4 x 4
-  // block of (i, j)
+  // u, transposed to [channel][row]
   for (int e = tid; e < kQ * P; e += kSsdThreads) {
     const int j = e / P, p = e % P;
     ut[p][j] = conv_at(ci, j, p);
   }
+  // M = C B^T on the matrix cores (one 32 x 32 tile per wave), masked below
+  // the diagonal and decayed: M[i][j] = (C_i . B_j) exp(S_i - S_j) dt_j
   {
-    const int i0 = 4 * (tid / 16), j0 = 4 * (tid % 16);
-    float g[4][4] = {};
+    const int ti = wave >> 1, tj = wave & 1;
+    f32x16_t g;
 #pragma unroll
-    for (int q = 0; q < kSt / 4; ++q) {
-      float4 cr[4], br[4];
+    for (int r = 0; r < 16; ++r) g[r] = 0.f;
+    if (tj <= ti) g = M::mma(M::from_f32(&cs[32 * ti + lq][8 * hh]), M::from_f32(&ci.bs[32 * tj + lq][8 * hh]), g);
+    const int j = 32 * tj + lq;
+    const float s2j = ci.s2[j], dtj = ci.dts[j];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        cr[a] = *reinterpret_cast<const float4*>(&cs[i0 + a][4 * q]);
-        br[a] = *reinterpret_cast<const float4*>(&bs[j0 + a][4 * q]);
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          g[a][c] = fmaf(cr[a].x, br[c].x, fmaf(cr[a].y, br[c].y, fmaf(cr[a].z, br[c].z, fmaf(cr[a].w, br[c].w, g[a][c]))));
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int i = i0 + a;
-      float m4[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int j = j0 + c;
-        m4[c] = j <= i ? g[a][c] * __builtin_amdgcn_exp2f(ci.s2[i] - ci.s2[j]) * ci.dts[j] : 0.f;
-      }
-      *reinterpret_cast<float4*>(&ms[i][j0]) = make_float4(m4[0], m4[1], m4[2], m4[3]);
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * ti + 8 * (r >> 2) + 4 * hh + (r & 3);
+      ms[i][j] = j <= i ? g[r] * __builtin_amdgcn_exp2f(ci.s2[i] - s2j) * dtj : 0.f;
     }
   }
+  // this lane's gate inputs, loaded while the block products run
+  const uint32_t rowb = (uint32_t)(D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(z + (b * L + t0) * D, (uint32_t)nr * rowb);
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + (b * L + t0) * D, (uint32_t)nr * rowb);
   __syncthreads();
   // Y tiles of 32 rows x 32 channels, one per wave in turn
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, lq = lane & 31, hh = lane >> 5;
-  constexpr int NTP = P / 32;
   for (int tile = wave; tile < 2 * NTP; tile += kSsdThreads / 64) {
     const int ti = tile / NTP, tp = tile % NTP;
     const int ia = 32 * ti + lq, pb = 32 * tp + lq;   // this lane's A row and B column
+    const uint32_t col = (uint32_t)((c0 + pb) * sizeof(T));
+    float zv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * ti + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const uint32_t off = (uint32_t)i * rowb + col;
+      if constexpr (sizeof(T) == 2)
+        zv[r] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(zrs, off, 0, 0) << 16);
+      else
+        zv[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(zrs, off, 0, 0));
+    }
     f32x16_t acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < kQ / 16; ++kb) {
-      const typename M::Frag fa = M::from_f32(&ms[ia][16 * kb + 8 * hh]);
-      const typename M::Frag fb = M::from_f32(&ut[pb][16 * kb + 8 * hh]);
-      acc = M::mma(fa, fb, acc);
+      if (kb <= (2 * ti + 1)) {   // key blocks past this tile's last row are all zero
+        const typename M::Frag fa = M::from_f32(&ms[ia][16 * kb + 8 * hh]);
+        const typename M::Frag fb = M::from_f32(&ut[pb][16 * kb + 8 * hh]);
+        acc = M::mma(fa, fb, acc);
+      }
     }
     {   // the entering state: rows of C scaled by exp(S_i), against H^T
       const float es = __builtin_amdgcn_exp2f(ci.s2[ia]);
@@ -225,15 +311,11 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(
       for (int e = 0; e < 8; ++e) cv[e] = cs[ia][8 * hh + e] * es;
       acc = M::mma(M::from_f32(cv), M::from_f32(&hs[pb][8 * hh]), acc);
     }
-    const int c = c0 + pb;
-    const float Dc = Dp[c];
+    const float Dc = Dp[c0 + pb];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 32 * ti + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (i < nr) {
-        const int64_t o = (b * L + t0 + i) * D + c;
-        y[o] = from_f32<T>(fmaf(Dc, ut[pb][i], acc[r]) * ssd_silu(to_f32(z[o])));
-      }
+      buf_store(yrs, (uint32_t)i * rowb + col, from_f32<T>(fmaf(Dc, ut[pb][i], acc[r]) * ssd_silu(zv[r])));
     }
   }
   if (k == nchunk - 1) {

@@ -127,6 +127,28 @@ def prefill_work(cfg, chunk_rows):
     }
 
 
+def ssd_work(cfg):
+    """Algorithmic work of the Mamba-2 form's three kernels (64-row chunks):
+    every input read once, every output written once; the output pass's block
+    products (the masked C B^T-weighted product and the entering-state term)
+    as matrix-core flops, counted on each chunk's real rows."""
+    es = 2 if cfg.act == "bf16" else 4
+    B, L, D, N, H = cfg.batch, cfg.seq_rows, cfg.d_inner, cfg.d_state, cfg.ssm_heads
+    P, Q = D // H, 64
+    rows = B * L
+    nchunk = -(-L // Q)
+    state = B * D * N * 4
+    params = (H + D * 5) * 4                              # A per head, D, conv taps
+    in_rows = rows * (D * es + H * es)                    # x and dt
+    state_bytes = in_rows + rows * N * es + nchunk * (state + B * D * 4) + params
+    carry_bytes = nchunk * (state + B * D * 4) + (nchunk + 1) * state + H * 4
+    out_bytes = in_rows + rows * (2 * D * es + 2 * N * es) + nchunk * state + state + B * D * 3 * es + params
+    nr = [min(Q, L - k * Q) for k in range(nchunk)]
+    flops = B * H * sum(2 * r * r * P + 2 * r * N * P for r in nr)
+    return {"ssd_state": {"bytes": state_bytes}, "ssd_carry": {"bytes": carry_bytes},
+            "ssd_out": {"bytes": out_bytes, "flops": flops}}
+
+
 def decode_work(cfg):
     es = 2 if cfg.act == "bf16" else 4
     B, D, N = cfg.batch, cfg.d_inner, cfg.d_state
@@ -453,6 +475,7 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated through the timed steps")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-ssd", action="store_true", help="skip the prefill with the Mamba-2 form of the scan")
     ap.add_argument("--no-continue", action="store_true",
                     help="skip the continued prefill and the compact-cache decode")
     ap.add_argument("--serial", action="store_true",
@@ -554,6 +577,24 @@ def main():
             "hbm_frac_per_call": round(dw["total_bytes"] / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_call": dw["total_bytes"],
             "kernels": dk,
+        }
+    if not args.no_ssd:
+        scfg = cfg.with_(ssm_heads=50, name="swa_layer_ssd")
+        log("[bench] prefill with the Mamba-2 form of the scan")
+        sms, sstage, sserial = bench_prefill(scfg, args.steps, args.warmup, args.sets, ev)
+        sw = ssd_work(scfg)
+        names = {"ssm_chunk_end": "ssd_state", "ssm_chunk_carry": "ssd_carry", "ssm_chunk_out": "ssd_out"}
+        sk = {}
+        for k, v in sstage.items():
+            n = names.get(k, k)
+            sk[n] = kernel_report(n, v, sw[n] if n in sw else work[k], scfg.act)
+        res["ssd"] = {
+            "workload": f"{cfg.workload}, Mamba branch in the Mamba-2 form: 50 heads of 64 channels, "
+                        f"one decay rate and step size per head",
+            "tokens_per_s": round(scfg.batch * scfg.n_tokens / (sms * 1e-3), 1),
+            "ms_per_step": round(sms, 4),
+            "serial_ms_per_step": round(sserial, 4),
+            "kernels": sk,
         }
     if not args.no_continue:
         log("[bench] prefill continuation")
