@@ -76,6 +76,13 @@ int hip_status(hipError_t e) {
     if (e_ != hipSuccess) return hip_status(e_); \
   } while (0)
 
+// inside a function returning hipError_t
+#define TRY_E(expr)                  \
+  do {                               \
+    hipError_t e_ = (expr);          \
+    if (e_ != hipSuccess) return e_; \
+  } while (0)
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t act_bytes(hymba_dtype t) { return t == HYMBA_BF16 ? 2 : 4; }
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -273,106 +280,124 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
     HYMBA_TRY(hipStreamWaitEvent(fc->aux, fc->fork, 0));
     ssm_stream = fc->aux;
   }
-  hymba::SsmPrefillArgs sa;
-  sa.x = c.x; sa.z = c.z; sa.dt = c.dt; sa.B = c.B; sa.C = c.C;
-  sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
-  sa.y = y_ssm; sa.state_out = c.state_out; sa.conv_state_out = c.conv_out;
-  sa.state_in = c.state_in;
-  sa.conv_in = nullptr;
-  if (c.conv_in) {   // a private copy: the output pass writes the caller's buffer while it is still read
-    void* staged = wsb + ws.conv_in;
-    HYMBA_TRY(hipMemcpyAsync(staged, c.conv_in,
-                             (size_t)desc->batch * desc->d_inner * (desc->d_conv - 1) * act_bytes(desc->act),
-                             hipMemcpyDeviceToDevice, ssm_stream));
-    sa.conv_in = staged;
-  }
-  sa.agg = (float*)(wsb + ws.agg); sa.sdt = (float*)(wsb + ws.sdt); sa.carry = (float*)(wsb + ws.carry);
-  sa.chunk_rows = c.cont ? ws.chunk_rows_cont : ws.chunk_rows;
-  sa.batch = desc->batch; sa.L = L; sa.d_inner = desc->d_inner; sa.act = desc->act;
-  sa.head_width = desc->ssm_heads > 0 ? desc->d_inner / desc->ssm_heads : 0;
-  if (sa.head_width > 0) {
-    HYMBA_TRY(hymba::launch_ssd_prefill(sa, ssm_stream, tm(0), tm(1), tm(2)));
-  } else {
-    HYMBA_TRY(hymba::launch_ssm_chunk_end(sa, ssm_stream, tm(0)));
-    HYMBA_TRY(hymba::launch_ssm_chunk_carry(sa, ssm_stream, tm(1)));
-    HYMBA_TRY(hymba::launch_ssm_chunk_out(sa, ssm_stream, tm(2)));
-  }
-  if (fc) HYMBA_TRY(hipEventRecord(fc->join, fc->aux));
-
-  // Attention branch. Where the rotated keys and the values that attention
-  // reads live (row j of k_src / v_src = position j - shift):
-  //  * fresh, cache of one row per position: the cache itself (rope stores there);
-  //  * fresh otherwise: the workspace keys and the input values;
-  //  * continuation, one row per position: the cache (rope appends the new rows);
-  //  * continuation, compact ring: an assembly of meta rows, the earlier rows
-  //    the new ones can see, and the new rows.
-  hymba::RopeArgs ra;
-  ra.q = c.q; ra.k = c.k; ra.v = c.v; ra.q_rot = q_rot;
-  ra.k_scale = params->k_scale;
-  ra.batch = desc->batch; ra.L = L; ra.n_q_heads = desc->n_q_heads; ra.n_kv_heads = desc->n_kv_heads;
-  ra.head_dim = desc->head_dim; ra.head_dim_v = desc->head_dim_v; ra.rope_base = desc->rope_base;
-  ra.act = desc->act;
-  ra.pos0 = c.pos0;
-  hymba::AttnPrefillArgs aa;
-  aa.q_rot = q_rot; aa.y = y_attn;
-  aa.batch = desc->batch; aa.L = L; aa.n_meta = M; aa.window = W;
-  aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
-  aa.act = desc->act;
-  HYMBA_TRY(device_cus(&aa.n_cu));
-  hymba::KvCopyArgs kc;   // rows into the compact ring (fresh prefill, continuation)
-  kc.n = 0;
-  kc.n_meta = M; kc.window = W; kc.batch = desc->batch; kc.n_kv_heads = desc->n_kv_heads;
-  kc.head_dim_v = desc->head_dim_v; kc.act = desc->act;
-  kc.dst.k = c.k_cache; kc.dst.v = c.v_cache; kc.dst.k_rows = kc.dst.v_rows = desc->cache_capacity;
-  kc.dst.mode = hymba::KvSide::kRing; kc.dst.base = 0;
-  const int64_t cap = desc->cache_capacity;
-
-  if (!c.cont) {
-    if (c.k_cache && !ring) {
-      ra.k_rot = c.k_cache; ra.k_rows = cap; ra.v_copy = c.v_cache; ra.v_rows = cap;
+  // Mamba branch (conv + scan), on ssm_stream
+  auto mamba_branch = [&]() -> hipError_t {
+    hymba::SsmPrefillArgs sa;
+    sa.x = c.x; sa.z = c.z; sa.dt = c.dt; sa.B = c.B; sa.C = c.C;
+    sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
+    sa.y = y_ssm; sa.state_out = c.state_out; sa.conv_state_out = c.conv_out;
+    sa.state_in = c.state_in;
+    sa.conv_in = nullptr;
+    if (c.conv_in) {   // a private copy: the output pass writes the caller's buffer while it is still read
+      void* staged = wsb + ws.conv_in;
+      TRY_E(hipMemcpyAsync(staged, c.conv_in,
+                           (size_t)desc->batch * desc->d_inner * (desc->d_conv - 1) * act_bytes(desc->act),
+                           hipMemcpyDeviceToDevice, ssm_stream));
+      sa.conv_in = staged;
+    }
+    sa.agg = (float*)(wsb + ws.agg); sa.sdt = (float*)(wsb + ws.sdt); sa.carry = (float*)(wsb + ws.carry);
+    sa.chunk_rows = c.cont ? ws.chunk_rows_cont : ws.chunk_rows;
+    sa.batch = desc->batch; sa.L = L; sa.d_inner = desc->d_inner; sa.act = desc->act;
+    sa.head_width = desc->ssm_heads > 0 ? desc->d_inner / desc->ssm_heads : 0;
+    if (sa.head_width > 0) {
+      TRY_E(hymba::launch_ssd_prefill(sa, ssm_stream, tm(0), tm(1), tm(2)));
     } else {
-      ra.k_rot = wsb + ws.k_rot; ra.k_rows = L; ra.v_copy = nullptr; ra.v_rows = L;
+      TRY_E(hymba::launch_ssm_chunk_end(sa, ssm_stream, tm(0)));
+      TRY_E(hymba::launch_ssm_chunk_carry(sa, ssm_stream, tm(1)));
+      TRY_E(hymba::launch_ssm_chunk_out(sa, ssm_stream, tm(2)));
     }
-    ra.k_row0 = ra.v_row0 = 0;
-    aa.k_rot = ra.k_rot; aa.k_rows = ra.k_rows; aa.v = c.v; aa.v_rows = L; aa.q_pos0 = 0;
-    if (c.k_cache && ring) {   // the meta rows and the last `window` rows survive in the ring
-      kc.src.k = ra.k_rot; kc.src.v = c.v; kc.src.k_rows = L; kc.src.v_rows = L;
-      kc.src.mode = hymba::KvSide::kLinear; kc.src.base = 0;
-      kc.na = std::min(M, L); kc.pa = 0; kc.pb = std::max(M, L - W);
-      kc.n = kc.na + (L - kc.pb);
+    return hipSuccess;
+  };
+
+  auto attention_branch = [&]() -> hipError_t {
+    // Attention branch. Where the rotated keys and the values that attention
+    // reads live (row j of k_src / v_src = position j - shift):
+    //  * fresh, cache of one row per position: the cache itself (rope stores there);
+    //  * fresh otherwise: the workspace keys and the input values;
+    //  * continuation, one row per position: the cache (rope appends the new rows);
+    //  * continuation, compact ring: an assembly of meta rows, the earlier rows
+    //    the new ones can see, and the new rows.
+    hymba::RopeArgs ra;
+    ra.q = c.q; ra.k = c.k; ra.v = c.v; ra.q_rot = q_rot;
+    ra.k_scale = params->k_scale;
+    ra.batch = desc->batch; ra.L = L; ra.n_q_heads = desc->n_q_heads; ra.n_kv_heads = desc->n_kv_heads;
+    ra.head_dim = desc->head_dim; ra.head_dim_v = desc->head_dim_v; ra.rope_base = desc->rope_base;
+    ra.act = desc->act;
+    ra.pos0 = c.pos0;
+    hymba::AttnPrefillArgs aa;
+    aa.q_rot = q_rot; aa.y = y_attn;
+    aa.batch = desc->batch; aa.L = L; aa.n_meta = M; aa.window = W;
+    aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
+    aa.act = desc->act;
+    TRY_E(device_cus(&aa.n_cu));
+    hymba::KvCopyArgs kc;   // rows into the compact ring (fresh prefill, continuation)
+    kc.n = 0;
+    kc.n_meta = M; kc.window = W; kc.batch = desc->batch; kc.n_kv_heads = desc->n_kv_heads;
+    kc.head_dim_v = desc->head_dim_v; kc.act = desc->act;
+    kc.dst.k = c.k_cache; kc.dst.v = c.v_cache; kc.dst.k_rows = kc.dst.v_rows = desc->cache_capacity;
+    kc.dst.mode = hymba::KvSide::kRing; kc.dst.base = 0;
+    const int64_t cap = desc->cache_capacity;
+
+    if (!c.cont) {
+      if (c.k_cache && !ring) {
+        ra.k_rot = c.k_cache; ra.k_rows = cap; ra.v_copy = c.v_cache; ra.v_rows = cap;
+      } else {
+        ra.k_rot = wsb + ws.k_rot; ra.k_rows = L; ra.v_copy = nullptr; ra.v_rows = L;
+      }
+      ra.k_row0 = ra.v_row0 = 0;
+      aa.k_rot = ra.k_rot; aa.k_rows = ra.k_rows; aa.v = c.v; aa.v_rows = L; aa.q_pos0 = 0;
+      if (c.k_cache && ring) {   // the meta rows and the last `window` rows survive in the ring
+        kc.src.k = ra.k_rot; kc.src.v = c.v; kc.src.k_rows = L; kc.src.v_rows = L;
+        kc.src.mode = hymba::KvSide::kLinear; kc.src.base = 0;
+        kc.na = std::min(M, L); kc.pa = 0; kc.pb = std::max(M, L - W);
+        kc.n = kc.na + (L - kc.pb);
+      }
+      TRY_E(hymba::launch_rope_prefill(ra, stream, tm(3)));
+    } else if (!ring) {
+      ra.k_rot = c.k_cache; ra.k_rows = cap; ra.v_copy = c.v_cache; ra.v_rows = cap;
+      ra.k_row0 = ra.v_row0 = c.pos0;
+      aa.k_rot = c.k_cache; aa.k_rows = cap; aa.v = c.v_cache; aa.v_rows = cap; aa.q_pos0 = c.pos0;
+      TRY_E(hymba::launch_rope_prefill(ra, stream, tm(3)));
+    } else {
+      // assembly row r: position r below n_meta, then a0 + (r - n_meta); the
+      // attention runs on assembly rows as positions (the window rule depends on
+      // position differences only, and every key was rotated at its true position)
+      const int a0 = std::max(M, c.pos0 - W + 1), nw = c.pos0 - a0;
+      const int R = ws.asm_rows;
+      void* asm_k = wsb + ws.asm_k;
+      void* asm_v = wsb + ws.asm_v;
+      hymba::KvCopyArgs g = kc;   // ring -> assembly: meta rows, then positions a0 .. pos0 - 1
+      g.src = kc.dst;
+      g.dst.k = asm_k; g.dst.v = asm_v; g.dst.k_rows = g.dst.v_rows = R; g.dst.mode = hymba::KvSide::kIndex;
+      g.dst.base = 0;
+      g.na = M; g.pa = 0; g.pb = a0; g.n = M + nw;
+      TRY_E(hymba::launch_kv_copy(g, stream));
+      ra.k_rot = asm_k; ra.k_rows = R; ra.v_copy = asm_v; ra.v_rows = R;
+      ra.k_row0 = ra.v_row0 = M + nw;
+      aa.k_rot = asm_k; aa.k_rows = R; aa.v = asm_v; aa.v_rows = R; aa.q_pos0 = M + nw;
+      TRY_E(hymba::launch_rope_prefill(ra, stream, tm(3)));
+      // the new rows that stay: the last `window` positions (after the gather above)
+      kc.src.k = asm_k; kc.src.v = asm_v; kc.src.k_rows = kc.src.v_rows = R;
+      kc.src.mode = hymba::KvSide::kLinear; kc.src.base = c.pos0 - (M + nw);
+      kc.pb = std::max(c.pos0, c.pos0 + L - W); kc.na = 0; kc.pa = 0;
+      kc.n = c.pos0 + L - kc.pb;
     }
-    HYMBA_TRY(hymba::launch_rope_prefill(ra, stream, tm(3)));
-  } else if (!ring) {
-    ra.k_rot = c.k_cache; ra.k_rows = cap; ra.v_copy = c.v_cache; ra.v_rows = cap;
-    ra.k_row0 = ra.v_row0 = c.pos0;
-    aa.k_rot = c.k_cache; aa.k_rows = cap; aa.v = c.v_cache; aa.v_rows = cap; aa.q_pos0 = c.pos0;
-    HYMBA_TRY(hymba::launch_rope_prefill(ra, stream, tm(3)));
+    TRY_E(hymba::launch_kv_copy(kc, stream));
+    TRY_E(hymba::launch_attn_prefill(aa, stream, tm(4)));
+    return hipSuccess;
+  };
+  // Enqueued attention first when the branches run concurrently: its
+  // workgroups then take their slots before the scan's fill the chip, and
+  // scan waves still fit beside them (attention is register-limited to two
+  // waves per SIMD). With stage events, the order of the stage list.
+  if (fc) {
+    HYMBA_TRY(attention_branch());
+    HYMBA_TRY(mamba_branch());
+    HYMBA_TRY(hipEventRecord(fc->join, fc->aux));
   } else {
-    // assembly row r: position r below n_meta, then a0 + (r - n_meta); the
-    // attention runs on assembly rows as positions (the window rule depends on
-    // position differences only, and every key was rotated at its true position)
-    const int a0 = std::max(M, c.pos0 - W + 1), nw = c.pos0 - a0;
-    const int R = ws.asm_rows;
-    void* asm_k = wsb + ws.asm_k;
-    void* asm_v = wsb + ws.asm_v;
-    hymba::KvCopyArgs g = kc;   // ring -> assembly: meta rows, then positions a0 .. pos0 - 1
-    g.src = kc.dst;
-    g.dst.k = asm_k; g.dst.v = asm_v; g.dst.k_rows = g.dst.v_rows = R; g.dst.mode = hymba::KvSide::kIndex;
-    g.dst.base = 0;
-    g.na = M; g.pa = 0; g.pb = a0; g.n = M + nw;
-    HYMBA_TRY(hymba::launch_kv_copy(g, stream));
-    ra.k_rot = asm_k; ra.k_rows = R; ra.v_copy = asm_v; ra.v_rows = R;
-    ra.k_row0 = ra.v_row0 = M + nw;
-    aa.k_rot = asm_k; aa.k_rows = R; aa.v = asm_v; aa.v_rows = R; aa.q_pos0 = M + nw;
-    HYMBA_TRY(hymba::launch_rope_prefill(ra, stream, tm(3)));
-    // the new rows that stay: the last `window` positions (after the gather above)
-    kc.src.k = asm_k; kc.src.v = asm_v; kc.src.k_rows = kc.src.v_rows = R;
-    kc.src.mode = hymba::KvSide::kLinear; kc.src.base = c.pos0 - (M + nw);
-    kc.pb = std::max(c.pos0, c.pos0 + L - W); kc.na = 0; kc.pa = 0;
-    kc.n = c.pos0 + L - kc.pb;
+    HYMBA_TRY(mamba_branch());
+    HYMBA_TRY(attention_branch());
   }
-  HYMBA_TRY(hymba::launch_kv_copy(kc, stream));
-  HYMBA_TRY(hymba::launch_attn_prefill(aa, stream, tm(4)));
   if (fc) HYMBA_TRY(hipStreamWaitEvent(stream, fc->join, 0));
 
   HYMBA_TRY(hymba::launch_fuse(y_attn, y_ssm, params->beta_attn, params->beta_ssm, (int64_t)desc->batch * L,
