@@ -1176,9 +1176,10 @@ void attn_decode_flash_kernel(
 // does (RMS-normalise each branch over the row, scale by the betas, average),
 // from the merged values in registers.
 constexpr int kCombineMaxThreads = 1024;
-constexpr int kCombineItems = 4;   // (head, 4 dv) items per thread: up to 16384 channels
+constexpr int kCombineItems = 4;   // (head, 4 dv) items per thread at most: up to 16384 channels
+constexpr int kMergeBatch = 8;     // split partials loaded together
 
-template <typename T, int DV>
+template <typename T, int DV, int KI>
 __global__ __launch_bounds__(kCombineMaxThreads) void decode_combine_kernel(
     const float* __restrict__ partial, const T* __restrict__ ys, const float* __restrict__ ba,
     const float* __restrict__ bs, float eps, int n_split, int Hq, T* __restrict__ y_attn, T* __restrict__ out) {
@@ -1189,11 +1190,11 @@ __global__ __launch_bounds__(kCombineMaxThreads) void decode_combine_kernel(
   const int nt = blockDim.x;   // whole waves
   const int width = Hq * DV;
   const int n_items = Hq * NQ;
-  float ya[kCombineItems][4], yv[kCombineItems][4], bav[kCombineItems][4], bsv[kCombineItems][4];
+  float ya[KI][4], yv[KI][4], bav[KI][4], bsv[KI][4];
   float sa = 0.f, ss = 0.f;
   // the Mamba output and the betas first: their loads overlap the merge's
 #pragma unroll
-  for (int k = 0; k < kCombineItems; ++k) {
+  for (int k = 0; k < KI; ++k) {
     const int it = tid + k * nt;
     if (it < n_items) {
       const int c = (it / NQ) * DV + 4 * (it % NQ);
@@ -1208,23 +1209,38 @@ __global__ __launch_bounds__(kCombineMaxThreads) void decode_combine_kernel(
     }
   }
 #pragma unroll
-  for (int k = 0; k < kCombineItems; ++k) {
+  for (int k = 0; k < KI; ++k) {
     const int it = tid + k * nt;
     if (it < n_items) {
       const int h = it / NQ, dq = it % NQ;
       const float* ph = partial + ((b * Hq) + h) * (int64_t)n_split * (DV + 2);
-      float m = -INFINITY;
-#pragma unroll 4
-      for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, ph[sp * (DV + 2) + DV]);
-      float l = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-#pragma unroll 4
-      for (int sp = 0; sp < n_split; ++sp) {
-        const float* q = ph + sp * (DV + 2);
-        const float ms = q[DV];
-        const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - m);   // empty splits weigh nothing
-        const float4 o4 = *reinterpret_cast<const float4*>(q + 4 * dq);
-        l = fmaf(q[DV + 1], f, l);
-        o0 = fmaf(o4.x, f, o0); o1 = fmaf(o4.y, f, o1); o2 = fmaf(o4.z, f, o2); o3 = fmaf(o4.w, f, o3);
+      // the splits in batches of kMergeBatch, every load of a batch issued
+      // before the first use (past n_split: the last split again, weighted 0)
+      float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+      for (int s0 = 0; s0 < n_split; s0 += kMergeBatch) {
+        float ms[kMergeBatch], ls[kMergeBatch];
+        float4 os[kMergeBatch];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+          const float* q = ph + min(s0 + j, n_split - 1) * (DV + 2);
+          ms[j] = q[DV];
+          ls[j] = q[DV + 1];
+          os[j] = *reinterpret_cast<const float4*>(q + 4 * dq);
+        }
+        float mb = m;
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) mb = fmaxf(mb, s0 + j < n_split ? ms[j] : -INFINITY);
+        if (mb != -INFINITY) {   // (else every split so far is empty)
+          const float fo = m == -INFINITY ? 0.f : fast_exp2(m - mb);
+          l *= fo; o0 *= fo; o1 *= fo; o2 *= fo; o3 *= fo;
+#pragma unroll
+          for (int j = 0; j < kMergeBatch; ++j) {
+            const float f = (s0 + j < n_split && ms[j] != -INFINITY) ? fast_exp2(ms[j] - mb) : 0.f;
+            l = fmaf(ls[j], f, l);
+            o0 = fmaf(os[j].x, f, o0); o1 = fmaf(os[j].y, f, o1); o2 = fmaf(os[j].z, f, o2); o3 = fmaf(os[j].w, f, o3);
+          }
+          m = mb;
+        }
       }
       const float il = 1.0f / l;
       ya[k][0] = o0 * il; ya[k][1] = o1 * il; ya[k][2] = o2 * il; ya[k][3] = o3 * il;
@@ -1262,7 +1278,7 @@ __global__ __launch_bounds__(kCombineMaxThreads) void decode_combine_kernel(
   const float ra = 0.5f / sqrtf(sa * inv_w + eps);
   const float rs = 0.5f / sqrtf(ss * inv_w + eps);
 #pragma unroll
-  for (int k = 0; k < kCombineItems; ++k) {
+  for (int k = 0; k < KI; ++k) {
     const int it = tid + k * nt;
     if (it < n_items) {
       const int c = (it / NQ) * DV + 4 * (it % NQ);
@@ -1375,12 +1391,23 @@ hipError_t attn_decode_t(const AttnDecodeArgs& a, hipStream_t stream, Timing tm)
 
 template <typename T, int DV>
 hipError_t combine_t(const DecodeCombineArgs& a, hipStream_t stream, Timing tm) {
-  // whole waves, kCombineItems (head, 4 dv) items per thread
+  // whole waves, one (head, 4 dv) item per thread while that fits in one
+  // workgroup, else up to kCombineItems each (the row stays in registers)
   const int n_items = a.n_q_heads * (DV / 4);
-  const int threads = std::max(64, (n_items + 64 * kCombineItems - 1) / (64 * kCombineItems) * 64);
+  const int per = (n_items + kCombineMaxThreads - 1) / kCombineMaxThreads;
+  const int threads = std::max(64, (n_items + 64 * per - 1) / (64 * per) * 64);
+  if (per > kCombineItems) return hipErrorInvalidValue;
   if (threads > kCombineMaxThreads) return hipErrorInvalidValue;
-  HYMBA_LAUNCH((decode_combine_kernel<T, DV>), dim3(a.batch), dim3(threads), 0, stream, tm, a.partial,
-               (const T*)a.y_ssm, a.beta_attn, a.beta_ssm, a.eps, a.n_split, a.n_q_heads, (T*)a.y_attn, (T*)a.out);
+#define HYMBA_COMBINE(KI)                                                                                    \
+  HYMBA_LAUNCH((decode_combine_kernel<T, DV, KI>), dim3(a.batch), dim3(threads), 0, stream, tm, a.partial,   \
+               (const T*)a.y_ssm, a.beta_attn, a.beta_ssm, a.eps, a.n_split, a.n_q_heads, (T*)a.y_attn, (T*)a.out)
+  if (per == 1)
+    HYMBA_COMBINE(1);
+  else if (per == 2)
+    HYMBA_COMBINE(2);
+  else
+    HYMBA_COMBINE(4);
+#undef HYMBA_COMBINE
   return hipGetLastError();
 }
 
