@@ -362,27 +362,21 @@ __global__ __launch_bounds__(64 * kCarrySegs) void ssm_chunk_carry_kernel(const 
 }
 
 // Decode step (ssm_step.hpp): a lane quad per (sequence, channel), 4 states
-// per lane, and kDecodeChanPerQuad channels per quad (channel i and i +
-// n_quad), so that the whole step is one round of workgroups; every load of a
-// lane is issued before its first use.
-constexpr int kDecodeChanPerQuad = 2;
-
+// per lane, and two channels per quad (c and c + d_inner / 2), so that the
+// whole step is one round of workgroups; every load of a lane is issued
+// before its first use. Grid: (channel-pair blocks, sequences).
 template <typename T>
-__global__ __launch_bounds__(256) void ssm_decode_kernel(ssm_step::Ptrs<T> p, int batch, int64_t n_quad) {
-  constexpr int K = kDecodeChanPerQuad;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int q = (int)(gid & 3);
-  const int64_t qi = gid >> 2;
-  const int64_t n_bc = (int64_t)batch * p.d_inner;
-  ssm_step::Item<T> it[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int64_t i = qi + k * n_quad;
-    const bool ok = qi < n_quad && i < n_bc;   // uniform over each quad (the grid is rounded up past n_quad)
-    ssm_step::load(p, it[k], ok ? i / p.d_inner : 0, ok ? (int)(i % p.d_inner) : 0, q, ok);
-  }
-#pragma unroll
-  for (int k = 0; k < K; ++k) ssm_step::finish(p, it[k], q);
+__global__ __launch_bounds__(256) void ssm_decode_kernel(ssm_step::Ptrs<T> p) {
+  const int q = threadIdx.x & 3;
+  const int qi = blockIdx.x * 64 + (threadIdx.x >> 2);   // channel pair within the sequence
+  const int64_t b = blockIdx.y;
+  const int half = p.d_inner / 2;                          // (d_inner is a multiple of 8)
+  const bool ok = qi < half;                               // the same for the whole quad
+  ssm_step::Item<T> it[2];
+  ssm_step::load(p, it[0], b, ok ? qi : 0, q, ok);
+  ssm_step::load(p, it[1], b, ok ? qi + half : 0, q, ok);
+  ssm_step::finish(p, it[0], q);
+  ssm_step::finish(p, it[1], q);
 }
 
 template <typename T>
@@ -449,12 +443,11 @@ hipError_t launch_ssm_chunk_out(const SsmPrefillArgs& a, hipStream_t stream, Tim
 }
 
 hipError_t launch_ssm_decode(const SsmDecodeArgs& a, hipStream_t stream, Timing tm) {
-  const int64_t n_quad = ((int64_t)a.batch * a.d_inner + kDecodeChanPerQuad - 1) / kDecodeChanPerQuad;
-  dim3 grid((unsigned)((n_quad * 4 + 255) / 256)), block(256);
+  const dim3 grid((unsigned)((a.d_inner / 2 + 63) / 64), (unsigned)a.batch), block(256);
   if (a.act == HYMBA_BF16)
-    HYMBA_LAUNCH(ssm_decode_kernel<bf16>, grid, block, 0, stream, tm, ssm_step_ptrs<bf16>(a), a.batch, n_quad);
+    HYMBA_LAUNCH(ssm_decode_kernel<bf16>, grid, block, 0, stream, tm, ssm_step_ptrs<bf16>(a));
   else
-    HYMBA_LAUNCH(ssm_decode_kernel<float>, grid, block, 0, stream, tm, ssm_step_ptrs<float>(a), a.batch, n_quad);
+    HYMBA_LAUNCH(ssm_decode_kernel<float>, grid, block, 0, stream, tm, ssm_step_ptrs<float>(a));
   return hipGetLastError();
 }
 
