@@ -55,7 +55,11 @@ __device__ __forceinline__ float wave_scan(float v, int lane) {
 // the chunk's B rows (and, for the output pass, C rows).
 template <typename T, int P>
 struct ChunkIn {
-  float xs[kQ + kTaps - 1][P];
+  // (rows enough for the output pass to place its 64 x 68 M block here once
+  // the x rows are dead)
+  static constexpr int kXRows = (kQ + kTaps - 1) > (kQ * (kQ + kRowPad) + P - 1) / P
+                                    ? (kQ + kTaps - 1) : (kQ * (kQ + kRowPad) + P - 1) / P;
+  float xs[kXRows][P];
   float bs[kQ][kSt];
   float s2[kQ], dts[kQ];
   float cw[P][kTaps];
@@ -170,15 +174,15 @@ __device__ __forceinline__ float conv_at(const ChunkIn<T, P>& ci, int j, int p) 
 }
 
 // Pass 1: agg[k][b][c][n] = sum_j exp(S_last - S_j) dt_j u_j[c] B_j[n] for the
-// head's channels c, and sdt[k][b][c] = the chunk's dt sum.
+// head's channels c, and sdt[k][b][c] = the chunk's dt sum. Thread (c, 4
+// states) walks the chunk's rows with the conv window in registers.
 template <typename T, int P>
 __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
     const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm, const float* __restrict__ A,
     const float* __restrict__ conv_w, const T* __restrict__ conv_in, float* __restrict__ agg,
     float* __restrict__ sdt, int L, int D, int H, int batch) {
   __shared__ ChunkIn<T, P> ci;
-  __shared__ __attribute__((aligned(16))) float us[kQ][P + kRowPad];   // u_j dt_j exp(S_last - S_j)
-  __shared__ float wj[kQ];                                              // dt_j exp(S_last - S_j)
+  __shared__ float wj[kQ];   // dt_j exp(S_last - S_j)
   const int k = blockIdx.x, h = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -191,21 +195,20 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
   __syncthreads();
   if (tid < kQ) wj[tid] = ci.dts[tid] * __builtin_amdgcn_exp2f(ci.s2[kQ - 1] - ci.s2[tid]);
   __syncthreads();
-  for (int e = tid; e < kQ * P; e += kSsdThreads) {
-    const int j = e / P, p = e % P;
-    us[j][p] = conv_at(ci, j, p) * wj[j];
-  }
-  __syncthreads();
   const int c0 = h * P;
   const int64_t row0 = ((int64_t)k * batch + b) * D + c0;   // (chunk, sequence, first channel of the head)
   for (int o = tid; o < P * (kSt / 4); o += kSsdThreads) {
     const int p = o / (kSt / 4), n0 = 4 * (o % (kSt / 4));
+    const float w0 = ci.cw[p][0], w1 = ci.cw[p][1], w2 = ci.cw[p][2], w3 = ci.cw[p][3];
+    float x0 = ci.xs[0][p], x1 = ci.xs[1][p], x2 = ci.xs[2][p];
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll 8
     for (int j = 0; j < kQ; ++j) {
-      const float u = us[j][p];
+      const float x3 = ci.xs[j + 3][p];
+      const float u = fmaf(w0, x0, fmaf(w1, x1, fmaf(w2, x2, w3 * x3))) * wj[j];
       const float4 bq = *reinterpret_cast<const float4*>(&ci.bs[j][n0]);
       a0 = fmaf(u, bq.x, a0); a1 = fmaf(u, bq.y, a1); a2 = fmaf(u, bq.z, a2); a3 = fmaf(u, bq.w, a3);
+      x0 = x1; x1 = x2; x2 = x3;
     }
     *reinterpret_cast<float4*>(agg + (row0 + p) * kSt + n0) = make_float4(a0, a1, a2, a3);
   }
@@ -224,7 +227,6 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(
   constexpr int NTP = P / 32;
   __shared__ ChunkIn<T, P> ci;
   __shared__ __attribute__((aligned(16))) float ut[P][kQ + kRowPad];   // u, [channel][row]
-  __shared__ __attribute__((aligned(16))) float ms[kQ][kQ + kRowPad];  // M[i][j]
   __shared__ __attribute__((aligned(16))) float cs[kQ][kSt];
   __shared__ __attribute__((aligned(16))) float hs[P][kSt];            // entering state
   const int k = blockIdx.x, h = blockIdx.y;
@@ -257,6 +259,10 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(
     const int j = e / P, p = e % P;
     ut[p][j] = conv_at(ci, j, p);
   }
+  __syncthreads();   // the staged x rows are dead: M takes their place
+  typedef float MRow[kQ + kRowPad];
+  static_assert(sizeof(ci.xs) >= sizeof(float) * kQ * (kQ + kRowPad), "M fits where x was staged");
+  MRow* const ms = reinterpret_cast<MRow*>(&ci.xs[0][0]);
   // M = C B^T on the matrix cores (one 32 x 32 tile per wave), masked below
   // the diagonal and decayed: M[i][j] = (C_i . B_j) exp(S_i - S_j) dt_j
   {
