@@ -67,7 +67,7 @@ constexpr int kStates = 16;
 constexpr int kConv = 4;
 
 constexpr int kChanPerBlock = 128;   // one lane per channel
-constexpr int kRowBlock = 16;        // rows staged in LDS per step
+constexpr int kRowBlock = 8;         // rows staged in LDS per step
 
 // Row t of B or C (16 values, the same for every channel) as raw 32-bit words:
 // a uniform address, so the compiler reads it with scalar loads into SGPRs and
@@ -408,14 +408,23 @@ hipError_t chunk_out_t(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
 }  // namespace
 
 int ssm_prefill_chunk_rows(int batch, int L, int d_inner) {
-  // enough (sequence, channel block, chunk) workgroups to fill the chip
-  // several times over, without making the carry chain long
+  // Every (sequence, channel block, chunk) workgroup is two waves and all of
+  // them are resident at once, so a SIMD's time is its number of waves times
+  // the rows per chunk. Ask for at least 2048 workgroups (four waves on each
+  // of the 1024 SIMDs of a 256-CU chip: enough to hide the scan's latency),
+  // then round the rows per chunk down to whole staging blocks: rounding up
+  // would drop below four waves per SIMD, where the busiest SIMDs hold a
+  // whole wave more than the average (2176 rows, 25 channel blocks: 24-row
+  // chunks give 4.4 waves per SIMD, 32-row chunks 3.3).
   const int64_t per_chunk = (int64_t)batch * ((d_inner + kChanPerBlock - 1) / kChanPerBlock);
   const int64_t want = (2048 + per_chunk - 1) / per_chunk;   // chunks per sequence
-  int64_t ct = (L + want - 1) / want;
-  ct = (ct + 15) / 16 * 16;
-  if (ct < 16) ct = 16;
-  return (int)ct;
+  int64_t ct = L / want / kRowBlock * kRowBlock;
+  if (ct < kRowBlock) ct = kRowBlock;
+  // the carry chain keeps a whole segment in registers up to kCarryBatch
+  // steps per segment; past that it reads every end state twice
+  const int64_t max_chunks = (int64_t)kCarrySegs * kCarryBatch + 1;
+  const int64_t ct_chain = ((L + max_chunks - 1) / max_chunks + kRowBlock - 1) / kRowBlock * kRowBlock;
+  return (int)std::max(ct, ct_chain);
 }
 
 hipError_t launch_ssm_chunk_end(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {

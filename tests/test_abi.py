@@ -66,10 +66,11 @@ def test_workspace_sizes(lib):
     L = 2176
     # rotated q and k, both branch outputs (bf16), then the scan's per-chunk
     # end states, summed dt and carried-in states (fp32): 25 channel blocks of
-    # 128 -> ~2048/25 = 82 chunks wanted -> 27 rows, rounded up to 32 -> 68 chunks
-    # (one slot more than chunks: the Mamba-2 form's chain also yields the
-    # final state), then a copy of a carried conv history, 3 rows, for a continuation
-    n_chunk = (L + 31) // 32 + 1
+    # 128 -> ~2048/25 = 82 chunks wanted -> 26.5 rows, rounded down to whole
+    # 8-row staging blocks: 24 rows -> 91 chunks (one slot more than chunks:
+    # the Mamba-2 form's chain also yields the final state), then a copy of a
+    # carried conv history, 3 rows, for a continuation
+    n_chunk = (L + 23) // 24 + 1
     expect = (L * 25 * 64 + L * 5 * 64 + 2 * L * 3200) * 2 + n_chunk * 3200 * (16 + 1 + 16) * 4 + 3200 * 3 * 2
     got = H.hymba_mixer_prefill_workspace_bytes(d)
     assert expect <= got <= expect + 10 * 256
@@ -84,7 +85,10 @@ def test_workspace_sizes(lib):
     got = H.hymba_mixer_decode_workspace_bytes(dd)
     assert expect <= got <= expect + 5 * 256
     assert H.hymba_mixer_prefill_workspace_bytes(c1_desc(n_q_heads=24)) == 0     # invalid -> 0
-    assert H.hymba_mixer_prefill_chunk_rows(d) == 32
+    assert H.hymba_mixer_prefill_chunk_rows(d) == 24
+    # never below one staging block; a larger batch gives longer chunks
+    assert H.hymba_mixer_prefill_chunk_rows(c1_desc(n_tokens=64, n_meta=0)) == 8
+    assert H.hymba_mixer_prefill_chunk_rows(c1_desc(batch=4)) == 96   # 21 chunks wanted -> 103.6 -> 96
     assert H.hymba_mixer_prefill_chunk_rows(c1_desc(n_q_heads=24)) == 0
     assert H.hymba_mixer_prefill_chunk_rows(c1_desc(ssm_heads=50)) == 64   # Mamba-2 form: 64-row chunks
 
