@@ -46,6 +46,24 @@ __device__ __forceinline__ void rope_cs(int pos, int i, float base, float* c, fl
   *s = (float)sd;
 }
 
+// The same cos/sin from the frequency step r = base^(-2/64) (formed on the
+// host in fp64): the frequency r^i by repeated squaring, the angle in fp64,
+// reduced by 2 pi in fp64 (two-part constant), then sin/cos of the reduced
+// angle in fp32 (the fp64 angle carries the same error as in rope_cs).
+__device__ __forceinline__ void rope_cs_step(int pos, int i, double r, float* c, float* s) {
+  double f = 1.0, x = r;
+#pragma unroll
+  for (int bit = 0; bit < 5; ++bit) {   // i < 32
+    if (i & (1 << bit)) f *= x;
+    x *= x;
+  }
+  const double ang = (double)pos * f;
+  constexpr double kInv2Pi = 0.15915494309189533577, k2PiHi = 6.283185307179586232, k2PiLo = 2.4492935982947064e-16;
+  const double n = rint(ang * kInv2Pi);
+  const double red = fma(-n, k2PiLo, fma(-n, k2PiHi, ang));
+  sincosf((float)red, s, c);
+}
+
 // ---------------------------------------------------------------------------
 // RoPE prologue (prefill): q -> q_rot, k -> k_rot (e.g. straight into the KV
 // cache), optionally v -> v_copy. Rotate-half pairs (i, i+32). The rotated
@@ -848,80 +866,96 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
 }
 
-// bf16 decode attention on the matrix cores, flash-decoding style: one
-// workgroup of 4 waves per (split, kv head, sequence), where a split is a run
-// of 64-key tiles of the row's visible keys (meta keys first, then window
-// keys), and few splits per row: enough workgroups for about three per
-// compute unit, each streaming many tiles. Tiles go from the cache straight
-// into LDS (buffer loads with the LDS destination, 16-byte chunks of each row
-// XOR-swizzled by the row as in the prefill tiles), double-buffered, so that
-// the next tile loads while this one is used; the new row p, not in the
-// cache, is written into its tile from the rotated k and v_new. Every wave
-// scores the tile against the group's query heads (S^T = K Q^T, the heads as
-// MFMA columns padded to 32) and keeps an online softmax; wave w accumulates
-// the 32-wide dv blocks w, w + 4, ... of O^T = V^T P^T, V's operand coming
-// from transposing LDS reads. Writes the same partials (o, m, l) as
-// attn_decode_kernel, one per split. The rotation of q and of the new key to
-// position p is done here, from cos/sin formed once per workgroup while the
-// first tile loads.
-constexpr int kDecodeTile = 32;     // keys per tile
-constexpr int kDecodeStages = 2;    // tiles in LDS: one used, kDecodeStages - 1 loading
+constexpr int kDecodeTile = 32;     // keys per partial slot in the workspace (the most splits a launch uses)
 constexpr int kMaxGroupFlash = 8;   // query heads per kv head (larger groups are rejected up front)
 
-// (dv >= 64: five waves per SIMD fit in 96 registers without spills; RING:
-// the cache is the compact ring of n_meta + window rows)
+// Flash-decoding, one wave per split: the wave of (split s, kv head g,
+// sequence b) streams its own run of 32-key tiles and keeps every dv block, so
+// no score or softmax work is repeated across waves (the heads of a group are
+// the MFMA columns, padded to 32). K goes from the cache straight into the
+// operand registers (a lane holds one key row, 16 bytes per 16 dims); V is
+// staged in LDS, two 32-row stages per wave, for the transposing operand
+// reads. The new row p, absent from the read-only cache, opens split 0's
+// online softmax before its first tile. The running maximum is raised only
+// when a tile's maximum exceeds it by more than kRescaleSlack (base-2 units),
+// so most tiles skip rescaling the accumulators. Writes the same partials
+// (o, m, l) per split as the other decode kernels.
+constexpr int kWaveTile = 32;   // keys per tile
+
 template <int DV, bool RING>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DV >= 64 && !RING ? 5 : 1)))
-void attn_decode_flash_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_decode_wave_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_new, const bf16* __restrict__ v_new,
     const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
     float* __restrict__ partial, const float* __restrict__ k_scale, int n_split, int cap, int n_meta, int window,
-    int Hq, int Hkv, float base) {
-  // (a tile is whole 16-byte loads of all 256 threads: 64 keys for dv 32)
-  constexpr int BT = kDecodeTile * (DV / 8) % 256 == 0 ? kDecodeTile : 64, NS = kDecodeStages;
-  constexpr int NKB = BT / 32;                          // 32-key blocks per tile
-  constexpr int NT = 256;
+    int Hq, int Hkv, double freq_step) {
+  typedef Mma<bf16> M;
   constexpr int KROWB = kHd * 2, VROWB = DV * 2;        // bytes per K / V row
-  constexpr int KCH = KROWB / 16, VCH = VROWB / 16;     // 16-byte chunks per row
-  constexpr int KN = BT * KCH / NT, VN = BT * VCH / NT; // loads per thread per tile
-  constexpr int KSTAGE = BT * KROWB, STAGE = KSTAGE + BT * VROWB;
+  constexpr int VCH = VROWB / 16;                       // 16-byte chunks per V row
+  constexpr int VN = kWaveTile * VCH / 64;              // V loads per lane per tile
+  constexpr int VSTAGE = kWaveTile * VROWB;
   constexpr int NDB = DV / 32;                          // 32-wide dv blocks
   constexpr int VRPB = VROWB >= 256 ? 1 : 256 / VROWB;  // V rows per 256-byte bank sweep
-  static_assert(BT * KCH % NT == 0 && BT * VCH % NT == 0 && (BT == 32 || BT == 64), "tile shape");
-  static_assert(NS >= 2 && NS <= 4, "stages");
-  // the stages are separate objects, so that the compiler can tell reads of
-  // one from the loads into another
-  __shared__ __attribute__((aligned(16))) char lds_stage0[STAGE];
-  __shared__ __attribute__((aligned(16))) char lds_stage1[STAGE];
-  __shared__ __attribute__((aligned(16))) char lds_stage2[NS > 2 ? STAGE : 16];
-  __shared__ __attribute__((aligned(16))) char lds_stage3[NS > 3 ? STAGE : 16];
+  static_assert(kWaveTile * VCH % 64 == 0 && VN + 4 < 64, "tile shape");
+  __shared__ __attribute__((aligned(16))) char lds_v0[VSTAGE];
+  __shared__ __attribute__((aligned(16))) char lds_v1[VSTAGE];
   __shared__ float rope_c[kHd / 2], rope_s[kHd / 2];
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[kMaxGroupFlash][kHd];   // bf16 bits
-  lds_char* const stage0 = (lds_char*)lds_stage0;
-  lds_char* const stage1 = (lds_char*)lds_stage1;
-  lds_char* const stage2 = (lds_char*)lds_stage2;
-  lds_char* const stage3 = (lds_char*)lds_stage3;
-  auto ksw = [](int row) { return (row >> 1) & (KCH - 1); };
+  lds_char* const vst0 = (lds_char*)lds_v0;
+  lds_char* const vst1 = (lds_char*)lds_v1;
   auto vsw = [](int row) { return (4 * ((row & 3) / VRPB)) & (VCH - 1); };
 
   const int s = blockIdx.x, g = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int group = Hq / Hkv;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x;
   const int lq = lane & 31, hh = lane >> 5;
-  const int p = decode_pos(cache_len[b], cap, RING);
+  const bool has_new = s == 0;
+  const int len = cache_len[b];
+  // The wave's small inputs are loaded first, all together and without
+  // branches, ahead of the cache stream that the whole chip starts at once
+  // (behind it they would wait as long as a tile): the group's query pairs
+  // (dims i, i + 32 of head h for item 32 h + i; kQItems items per lane) with
+  // their shared-key weights (a null k_scale reads as zeros from an empty
+  // descriptor: weight 1), the new row's key (all 64 dims) and this lane's
+  // values of v_new (used by split 0 only).
+  constexpr int kQItems = kMaxGroupFlash * (kHd / 2) / 64;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + (b * Hq + g * group) * kHd, (uint32_t)(group * kHd * 2));
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(k_scale ? k_scale + g * kHd : nullptr, k_scale ? kHd * 4 : 0);
+  const float w_one = k_scale ? 0.f : 1.f;
+  uint32_t qlo[kQItems], qhi[kQItems];
+  float wpl[kQItems], wph[kQItems];
+#pragma unroll
+  for (int j = 0; j < kQItems; ++j) {
+    const int it = lane + 64 * j, qh = it / (kHd / 2), qi = it % (kHd / 2);
+    const uint32_t off = qh < group ? (uint32_t)(qh * kHd + qi) * 2 : kBufferNowhere;
+    qlo[j] = __builtin_amdgcn_raw_buffer_load_b16(qrs, off, 0, 0);
+    qhi[j] = __builtin_amdgcn_raw_buffer_load_b16(qrs, off + kHd, 0, 0);
+    wpl[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wrs, (uint32_t)qi * 4, 0, 0));
+    wph[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wrs, (uint32_t)(qi + kHd / 2) * 4, 0, 0));
+  }
+  const __amdgpu_buffer_rsrc_t knrs = make_rsrc(k_new + (b * Hkv + g) * kHd, kHd * 2);
+  const __amdgpu_buffer_rsrc_t vnrs = make_rsrc(v_new + (b * Hkv + g) * DV, DV * 2);
+  u32x4_t knew[kHd / 8];
+#pragma unroll
+  for (int c = 0; c < kHd / 8; ++c) knew[c] = buf_load16(knrs, 16 * c);
+  u32x2_t vnew[DV / 32][4];
+#pragma unroll
+  for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      vnew[d][rr] = __builtin_amdgcn_raw_buffer_load_b64(vnrs, (uint32_t)(32 * d + 8 * rr + 4 * hh) * 2, 0, 0);
+  const int p = decode_pos(len, cap, RING);
   const MaskRange mr = mask_range(p, n_meta, window);
-  const int n_vis = mr.meta_end + (mr.win_end - mr.win_begin);
-  const int n_tiles = (n_vis + BT - 1) / BT;
+  // visible keys held in the cache: all but the last visible key, the new row p
+  const int n_old = mr.meta_end + (mr.win_end - mr.win_begin) - 1;
+  const int n_tiles = (n_old + kWaveTile - 1) / kWaveTile;
   const int per = (n_tiles + n_split - 1) / n_split;
   const int t0 = min(n_tiles, s * per), t1 = min(n_tiles, t0 + per);
   float* outp = partial + (((b * Hq) + g * group) * n_split + s) * (DV + 2);
-  const int64_t pstride = (int64_t)n_split * (DV + 2);  // between query heads
-
-  if (t0 >= t1) {   // (whole workgroup, before any barrier)
-    for (int t = tid; t < group * (DV + 2); t += blockDim.x) {
+  const int64_t pstride = (int64_t)n_split * (DV + 2);   // between query heads
+  if (t0 >= t1 && !has_new) {
+    for (int t = lane; t < group * (DV + 2); t += 64) {
       const int hq = t / (DV + 2), e = t % (DV + 2);
       outp[hq * pstride + e] = e == DV ? -INFINITY : 0.f;
     }
@@ -938,234 +972,209 @@ void attn_decode_flash_kernel(
       return vi < mr.meta_end ? vi : mr.win_begin + (vi - mr.meta_end);
     }
   };
-  const int vi_new = n_vis - 1;   // the new row p is the last visible key
-
-  // Tile t: row r is visible key 64 t + r. Rows past the visible keys and the
-  // new row read as zeros here (offset out of range).
+  // tile t: row r is visible key 32 t + r; rows at or past n_old read zeros
   const uint32_t kv_row = (uint32_t)Hkv * KROWB, vv_row = (uint32_t)Hkv * VROWB;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(k_cache + b * cap * Hkv * kHd, (uint32_t)cap * kv_row);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v_cache + b * cap * Hkv * DV, (uint32_t)cap * vv_row);
-  auto fetch = [&](int t, lds_char* dst) {
-#pragma unroll
-    for (int r = 0; r < KN; ++r) {
-      const int it = r * NT + tid, row = it / KCH, cp = it % KCH, vi = BT * t + row;
-      const bool in = vi < vi_new;
-      const uint32_t off =
-          in ? (uint32_t)key_row(vi) * kv_row + (uint32_t)(g * KROWB + 16 * (cp ^ ksw(row))) : kBufferNowhere;
-      buf_load16_lds(krs, off, dst + (r * NT + 64 * wave) * 16);
-    }
+  // V rows into LDS with the 16-byte chunks of row r XOR-swizzled by vsw(r)
+  auto fetch_v = [&](int t, lds_char* dst) {
 #pragma unroll
     for (int r = 0; r < VN; ++r) {
-      const int it = r * NT + tid, row = it / VCH, cp = it % VCH, vi = BT * t + row;
-      const bool in = vi < vi_new;
-      const uint32_t off =
-          in ? (uint32_t)key_row(vi) * vv_row + (uint32_t)(g * VROWB + 16 * (cp ^ vsw(row))) : kBufferNowhere;
-      buf_load16_lds(vrs, off, dst + KSTAGE + (r * NT + 64 * wave) * 16);
+      const int it = r * 64 + lane, row = it / VCH, cp = it % VCH, vi = kWaveTile * t + row;
+      const uint32_t off = vi < n_old ? (uint32_t)key_row(vi) * vv_row + (uint32_t)(g * VROWB + 16 * (cp ^ vsw(row)))
+                                      : kBufferNowhere;
+      buf_load16_lds(vrs, off, dst + r * 64 * 16);
     }
   };
-
-  typedef Mma<bf16> M;
-  // the first NS - 1 tiles (past the split: rows that are loaded and never used)
-  fetch(t0, stage0);
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (NS > 2) fetch(t0 + 1, stage1);
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (NS > 3) fetch(t0 + 2, stage2);
-  __builtin_amdgcn_sched_barrier(0);
-  // thread 32 h + i: raw dims i and i + 32 (a rotation pair) of query head h
-  // of the group and their shared-key affine weights w[g]; threads < KCH also
-  // the new key's dims 8 tid .. and their rotation partners. All are loaded
-  // while cos/sin of position p are formed.
-  const int qh = tid >> 5, qi = tid & (kHd / 2 - 1);
-  const bool q_in = qh < group;
-  const bf16* qrow = q + (b * Hq + g * group + (q_in ? qh : 0)) * kHd;
-  const uint16_t qlo_bits = qrow[qi].u, qhi_bits = qrow[qi + kHd / 2].u;
-  float wl = 1.f, wh = 1.f;
-  if (k_scale) {
-    wl = k_scale[g * kHd + qi];
-    wh = k_scale[g * kHd + qi + kHd / 2];
+  // the K operand: lane (row lq, half hh) holds dims 16 kc + 8 hh .. + 7 of key 32 t + lq
+  auto fetch_k = [&](int t, M::Frag* kf) {
+    const int vi = kWaveTile * t + lq;
+    const uint32_t off = vi < n_old ? (uint32_t)key_row(vi) * kv_row + (uint32_t)(g * KROWB + 16 * hh) : kBufferNowhere;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) kf[kc] = __builtin_bit_cast(M::Frag, buf_load16(krs, off + 32 * kc));
+  };
+  // loads in a fixed order (V then K), so that a wait for the K operand of
+  // tile t also covers tile t's V rows; the first two tiles go out before the
+  // prologue's own work
+  M::Frag kfa[4], kfb[4];
+  if (t0 < t1) {
+    fetch_v(t0, vst0);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_k(t0, kfa);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  const bool has_new = vi_new / BT < t1;   // (then it is in this split's last tile)
-  u32x4_t kraw = {0u, 0u, 0u, 0u}, kpart = {0u, 0u, 0u, 0u};
-  u32x4_t new_v = {0u, 0u, 0u, 0u};
-  if (has_new) {
-    const bf16* krow = k_new + (b * Hkv + g) * kHd;
-    if (tid < KCH) {
-      kraw = *reinterpret_cast<const u32x4_t*>(krow + 8 * tid);
-      kpart = *reinterpret_cast<const u32x4_t*>(krow + 8 * (tid ^ (KCH / 2)));
-    } else if (tid < KCH + VCH) {
-      new_v = *reinterpret_cast<const u32x4_t*>(v_new + (b * Hkv + g) * DV + 8 * (tid - KCH));
+  if (t0 + 1 < t1) {
+    fetch_v(t0 + 1, vst1);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_k(t0 + 1, kfb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // the group's queries at position p, times the shared-key weights w[g] and
+  // log2(e)/sqrt(64), as bf16 in LDS: item (head h, pair i) rotates dims i, i + 32
+  if (lane < kHd / 2) rope_cs_step(p, lane, freq_step, &rope_c[lane], &rope_s[lane]);
+  lds_barrier();   // (a __syncthreads() would also wait for the tile in flight)
+#pragma unroll
+  for (int j = 0; j < kQItems; ++j) {
+    const int it = lane + 64 * j, qh = it / (kHd / 2), qi = it % (kHd / 2);
+    if (qh < group) {
+      const float lo = __uint_as_float(qlo[j] << 16), hi = __uint_as_float(qhi[j] << 16);
+      const float c = rope_c[qi], sn = rope_s[qi];
+      q_lds[qh][qi] = f32_to_bf16_bits((lo * c - hi * sn) * (wpl[j] + w_one) * kScaleLog2e);
+      q_lds[qh][qi + kHd / 2] = f32_to_bf16_bits((hi * c + lo * sn) * (wph[j] + w_one) * kScaleLog2e);
     }
   }
-  if (tid < kHd / 2) rope_cs(p, tid, base, &rope_c[tid], &rope_s[tid]);
-  __syncthreads();
-  // the group's queries rotated, times w[g] and log2(e)/sqrt(64), as bf16 in LDS
-  if (q_in) {
-    const float lo = __uint_as_float((uint32_t)qlo_bits << 16), hi = __uint_as_float((uint32_t)qhi_bits << 16);
-    const float c = rope_c[qi], sn = rope_s[qi];
-    q_lds[qh][qi] = f32_to_bf16_bits((lo * c - hi * sn) * wl * kScaleLog2e);
-    q_lds[qh][qi + kHd / 2] = f32_to_bf16_bits((hi * c + lo * sn) * wh * kScaleLog2e);
+  lds_barrier();
+  // Q^T operand: column lq (query head of the group), dims 16 kc + 8 hh .. + 7;
+  // columns past the group are zero
+  const bool qv = lq < group;
+  M::Frag qf[4];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    const M::Frag f = *(const __attribute__((address_space(3))) M::Frag*)((lds_char*)q_lds + (qv ? lq : 0) * (kHd * 2) +
+                                                                          32 * kc + 16 * hh);
+    qf[kc] = qv ? f : M::zero();
   }
-  // per-lane LDS offsets of the operand reads (the swizzles depend on the lane only)
-  const int kro = lq * KROWB + 16 * (hh ^ ksw(lq));
+
+  // accumulators: O^T block d, register r holds dv 32 d + 8 (r / 4) + 4 hh + r % 4 of column lq
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  if (has_new) {
+    // score of the new key (rotated, rounded to bf16 like a cached key) against
+    // this column's query, over this lane's 32 dims, then both lane halves
+    auto kval = [&](int dim) {   // raw dim of the new key (lane-uniform register index after unrolling)
+      const uint32_t w = knew[dim >> 3][(dim >> 1) & 3];
+      return (dim & 1) ? bf16_hi(w) : bf16_lo(w);
+    };
+    float dot = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dim0 = 16 * kc + e;                 // this lane's dim is dim0 + 8 hh
+        const int dim = dim0 + 8 * hh, i = dim & (kHd / 2 - 1);
+        const float x = hh ? kval(dim0 + 8) : kval(dim0);
+        const float xp = hh ? kval((dim0 + 8) ^ (kHd / 2)) : kval(dim0 ^ (kHd / 2));
+        const float kr = dim < kHd / 2 ? x * rope_c[i] - xp * rope_s[i] : x * rope_c[i] + xp * rope_s[i];
+        const float qd = __uint_as_float((uint32_t)q_lds[qv ? lq : 0][dim] << 16);
+        dot = fmaf(qv ? qd : 0.f, __uint_as_float((uint32_t)f32_to_bf16_bits(kr) << 16), dot);
+      }
+    m = dot + __shfl_xor(dot, 32, 64);
+    l = hh == 0 ? 1.f : 0.f;   // its weight 2^(s - m) = 1, counted once per column
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const u32x2_t w2 = vnew[d][rr];
+        acc[d][4 * rr] = bf16_lo(w2.x);
+        acc[d][4 * rr + 1] = bf16_hi(w2.x);
+        acc[d][4 * rr + 2] = bf16_lo(w2.y);
+        acc[d][4 * rr + 3] = bf16_hi(w2.y);
+      }
+  }
+  float thr = m + kRescaleSlack;   // -inf without the new key: the first tile sets the maximum
+
+  // per-lane LDS offset of the V operand reads: in each 16-lane group gi, lane
+  // j = 4 k + q reads V[4 (gi / 2) + k][16 (gi % 2) + 4 q .. + 3] (transposed)
   const int gi = lane >> 4, jj = lane & 15;
-  const int vrow = 4 * (gi >> 1) + (jj >> 2);
+  const int vrow_l = 4 * (gi >> 1) + (jj >> 2);
   const int vdv = 16 * (gi & 1) + 4 * (jj & 3);
-  const int vro = KSTAGE + vrow * VROWB + 16 * ((vdv >> 3) ^ vsw(vrow)) + 8 * ((vdv >> 2) & 1);
+  const int vro = vrow_l * VROWB + 16 * ((vdv >> 3) ^ vsw(vrow_l)) + 8 * ((vdv >> 2) & 1);
   typedef __attribute__((address_space(3))) v4i16_t lds_v4;
-  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
   typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
-  constexpr int NDW = (NDB + 3) / 4;   // dv blocks per wave (some waves have none when NDB < 4)
-  f32x16_t acc[NDW];
-#pragma unroll
-  for (int i = 0; i < NDW; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
-  // the new key rotated (threads < KCH: dims 8 tid .. + 7), written into its
-  // tile later, when that tile is current
-  M::Frag new_k = M::zero();
-  if (has_new && tid < KCH) {
-    float x[8], xp[8], o[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = bf16_lo(kraw[e]); x[2 * e + 1] = bf16_hi(kraw[e]);
-      xp[2 * e] = bf16_lo(kpart[e]); xp[2 * e + 1] = bf16_hi(kpart[e]);
+  // tile t from (cur, kf); tile t + 1 loads into (nxt, kn) (for the first
+  // tile it is already on its way)
+  auto tile = [&](int t, lds_char* cur, lds_char* nxt, const M::Frag* kf, M::Frag* kn) __attribute__((always_inline)) {
+    if (t > t0 && t + 1 < t1) {
+      fetch_v(t + 1, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_k(t + 1, kn);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const bool low = tid < KCH / 2;   // dims below 32: x' = x c - x_{+32} s, else x c + x_{-32} s
+    // scores: lane holds keys 32 t + 8 (r / 4) + 4 hh + r % 4 of column lq
+    f32x16_t sc;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int i = (8 * tid + e) & (kHd / 2 - 1);
-      o[e] = low ? x[e] * rope_c[i] - xp[e] * rope_s[i] : x[e] * rope_c[i] + xp[e] * rope_s[i];
-    }
-    new_k = M::from_f32(o);
-  }
-  wait_loads();
-  __syncthreads();
-  // Q^T operand: lane (column lq = query head of the group, half hh) holds
-  // dims 16 kc + 8 hh .. + 7; columns past the group are zero
-  M::Frag qf[4];
-  {
-    const bool qv = lq < group;
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const M::Frag f =
-          *(const __attribute__((address_space(3))) M::Frag*)((lds_char*)q_lds + (qv ? lq : 0) * (kHd * 2) +
-                                                              32 * kc + 16 * hh);
-      qf[kc] = qv ? f : M::zero();
-    }
-  }
-
-  // tile t is in stage cur; tile t + NS - 1 loads into nxt
-  auto tile = [&](int t, lds_char* cur, lds_char* nxt) __attribute__((always_inline)) {
-    fetch(t + NS - 1, nxt);
-    __builtin_amdgcn_sched_barrier(0);
-    const int vbase = BT * t;
-    if (has_new && vi_new - vbase < BT) {   // the new row's K and V into this tile
-      const int rn = vi_new - vbase;
-      if (tid < KCH)
-        *(__attribute__((address_space(3))) M::Frag*)(cur + rn * KROWB + 16 * (tid ^ ksw(rn))) = new_k;
-      else if (tid < KCH + VCH)
-        *(lds_u32x4*)(cur + KSTAGE + rn * VROWB + 16 * ((tid - KCH) ^ vsw(rn))) = new_v;
-      lds_barrier();
-    }
-    // scores: lane holds keys 32 h2 + 8 (r / 4) + 4 hh + r % 4 of column lq
-    f32x16_t sc[NKB];
-#pragma unroll
-    for (int h2 = 0; h2 < NKB; ++h2) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[h2][r] = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const M::Frag kf =
-            __builtin_bit_cast(M::Frag, *(const lds_u32x4*)(cur + ((kro ^ (kc << 5)) + h2 * 32 * KROWB)));
-        sc[h2] = M::mma(kf, qf[kc], sc[h2]);
-      }
-    }
-    // keys past the visible ones (last tile only); online softmax of the column
-    float tmx = -INFINITY;
-#pragma unroll
-    for (int h2 = 0; h2 < NKB; ++h2)
+    for (int kc = 0; kc < 4; ++kc) sc = M::mma(kf[kc], qf[kc], sc);
+    const int vbase = kWaveTile * t;
+    if (vbase + kWaveTile > n_old) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = vbase + 32 * h2 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        sc[h2][r] = key < n_vis ? sc[h2][r] : -INFINITY;
-        tmx = fmaxf(tmx, sc[h2][r]);
-      }
-    tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));   // a tile has a visible key: finite
-    const float mn = fmaxf(m, tmx);
-    const float alpha = fast_exp2(m - mn);       // 0 on the first tile
-    m = mn;
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < NDW; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
-    M::Frag pf[2 * NKB];   // P^T operands, 16 keys each
-#pragma unroll
-    for (int h2 = 0; h2 < NKB; ++h2) {
-      float pv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pv[r] = fast_exp2(sc[h2][r] - m);
-        l += pv[r];
-      }
-      pf[2 * h2] = M::from_f32(&pv[0]);
-      pf[2 * h2 + 1] = M::from_f32(&pv[8]);
-    }
-    // O^T blocks of this wave; in each 16-lane group gi, lane j = 4 k + q reads
-    // V[key0 + 4 (gi / 2) + k][32 d + 16 (gi % 2) + 4 q .. + 3] (transposed to lane j)
-#pragma unroll
-    for (int i = 0; i < NDW; ++i) {
-      const int d = wave + 4 * i;
-      if (d < NDB) {
-#pragma unroll
-        for (int kk = 0; kk < 2 * NKB; ++kk) {
-          const lds_char* vp = cur + ((vro ^ (d << 6)) + 16 * kk * VROWB);
-          const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)vp);
-          const v4i16_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp + 8 * VROWB));
-          const v8i16_t v8 = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-          acc[i] = M::mma(__builtin_bit_cast(M::Frag, v8), pf[kk], acc[i]);
-        }
+        const int key = vbase + 8 * (r >> 2) + 4 * hh + (r & 3);
+        sc[r] = key < n_old ? sc[r] : -INFINITY;
       }
     }
-    // tile t + 1 has landed (the loads of later tiles may still be in flight)
-    tile_barrier<(KN + VN) * (NS - 2)>();
+    float tm[4] = {sc[0], sc[1], sc[2], sc[3]};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tm[r] = max3f(tm[r], sc[4 + r], sc[8 + r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tm[r] = fmaxf(tm[r], sc[12 + r]);
+    const float tmx = max3f(tm[0], tm[1], fmaxf(tm[2], tm[3]));
+    if (__any(tmx > thr)) {
+      const float mn = fmaxf(m, fmaxf(tmx, __shfl_xor(tmx, 32, 64)));   // the column's maximum
+      const float alpha = fast_exp2(m - mn);                             // 0 while m = -inf
+      m = mn;
+      thr = mn + kRescaleSlack;
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+    }
+    float pv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(sc[r] - m);
+    float a8[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) a8[r] = pv[r] + pv[r + 8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a8[r] += a8[r + 4];
+    l += (a8[0] + a8[1]) + (a8[2] + a8[3]);
+    const M::Frag pf0 = M::from_f32(&pv[0]), pf1 = M::from_f32(&pv[8]);
+    // tile t's V rows have landed once at most this many loads are outstanding
+    // (tile t + 1's V and K, issued after them)
+    __builtin_amdgcn_s_waitcnt(((VN + 4) & 15) | (((VN + 4) >> 4) << 14) | 0x0F70);   // vmcnt(VN + 4)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const lds_char* vp = cur + ((vro ^ (d << 6)) + 16 * kk * VROWB);
+        const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)vp);
+        const v4i16_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp + 8 * VROWB));
+        const v8i16_t v8 = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+        acc[d] = M::mma(__builtin_bit_cast(M::Frag, v8), kk ? pf1 : pf0, acc[d]);
+      }
+    }
+    // the V reads of this stage are done before a later tile loads into it
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
   };
-  // NS tiles per trip, so that every stage is a fixed object in each part
-  for (int t = t0;;) {
-    tile(t, stage0, NS == 2 ? stage1 : NS == 3 ? stage2 : stage3);
+  for (int t = t0; t < t1;) {
+    tile(t, vst0, vst1, kfa, kfb);
     if (++t >= t1) break;
-    tile(t, stage1, NS == 2 ? stage0 : NS == 3 ? stage0 : stage0);
-    if (++t >= t1) break;
-    if constexpr (NS > 2) {
-      tile(t, stage2, stage1);
-      if (++t >= t1) break;
-    }
-    if constexpr (NS > 3) {
-      tile(t, stage3, stage2);
-      if (++t >= t1) break;
-    }
+    tile(t, vst1, vst0, kfb, kfa);
+    ++t;
   }
-  wait_loads();   // no load into LDS outlives the workgroup
 
   l += __shfl_xor(l, 32, 64);
-  if (lq < group) {
+  if (qv) {
+    float* o = outp + lq * pstride;
 #pragma unroll
-    for (int i = 0; i < NDW; ++i) {
-      const int d = wave + 4 * i;
-      if (d < NDB) {
-        float* o = outp + lq * pstride + 32 * d + 4 * hh;
+    for (int d = 0; d < NDB; ++d)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<float4*>(o + 8 * q4) =
-              make_float4(acc[i][4 * q4], acc[i][4 * q4 + 1], acc[i][4 * q4 + 2], acc[i][4 * q4 + 3]);
-      }
-    }
-    if (wave == 0 && hh == 0) {
-      outp[lq * pstride + DV] = m;
-      outp[lq * pstride + DV + 1] = l;
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4*>(o + 32 * d + 8 * q4 + 4 * hh) =
+            make_float4(acc[d][4 * q4], acc[d][4 * q4 + 1], acc[d][4 * q4 + 2], acc[d][4 * q4 + 3]);
+    if (hh == 0) {
+      o[DV] = m;
+      o[DV + 1] = l;
     }
   }
 }
@@ -1364,16 +1373,17 @@ hipError_t attn_decode_t(const AttnDecodeArgs& a, hipStream_t stream, Timing tm)
   t_last.stop = tm.stop;
   if constexpr (sizeof(T) == 2) {
     // rotation inside the attention kernel: one launch for the stage
+    const double freq_step = std::pow((double)a.rope_base, -2.0 / kHd);
     if (a.ring)
-      HYMBA_LAUNCH((attn_decode_flash_kernel<DV, true>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0, stream,
+      HYMBA_LAUNCH((attn_decode_wave_kernel<DV, true>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(64), 0, stream,
                    tm, (const bf16*)a.q, (const bf16*)a.k_new, (const bf16*)a.v_new, (const bf16*)a.k_cache,
                    (const bf16*)a.v_cache, a.cache_len, a.partial, a.k_scale, a.n_split, a.cap, a.n_meta, a.window,
-                   a.n_q_heads, a.n_kv_heads, a.rope_base);
+                   a.n_q_heads, a.n_kv_heads, freq_step);
     else
-      HYMBA_LAUNCH((attn_decode_flash_kernel<DV, false>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(256), 0,
+      HYMBA_LAUNCH((attn_decode_wave_kernel<DV, false>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(64), 0,
                    stream, tm, (const bf16*)a.q, (const bf16*)a.k_new, (const bf16*)a.v_new, (const bf16*)a.k_cache,
                    (const bf16*)a.v_cache, a.cache_len, a.partial, a.k_scale, a.n_split, a.cap, a.n_meta, a.window,
-                   a.n_q_heads, a.n_kv_heads, a.rope_base);
+                   a.n_q_heads, a.n_kv_heads, freq_step);
     return hipGetLastError();
   }
   const int64_t n = (int64_t)a.batch * (a.n_q_heads + a.n_kv_heads) * (kHd / 2);
@@ -1439,7 +1449,7 @@ static int64_t decode_max_visible(int n_meta, int window, int cap) {
 }
 
 void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_per_split) {
-  // room for one partial per 64-key tile: the most splits any launch uses
+  // room for one partial per 32-key tile: the most splits any launch uses
   const int64_t max_vis = decode_max_visible(n_meta, window, cap);
   *keys_per_split = kDecodeTile;
   *n_split = (int)((max_vis + kDecodeTile - 1) / kDecodeTile);
@@ -1449,11 +1459,11 @@ int decode_active_splits(const AttnDecodeArgs& a) {
   const int64_t max_vis = decode_max_visible(a.n_meta, a.window, a.cap);
   if (a.act != HYMBA_BF16)   // one split per kKeysPerSplit keys
     return (int)((max_vis + kKeysPerSplit - 1) / kKeysPerSplit);
-  // as many workgroups as fit the chip at once (LDS bounds them), each
-  // streaming whole tiles
-  const int64_t stage = (int64_t)kDecodeTile * (kHd + a.head_dim_v) * 2;
-  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / (kDecodeStages * stage + 512)));
-  const int64_t tiles = (max_vis + kDecodeTile - 1) / kDecodeTile;
+  // one wave per split, as many as fit the chip at once: two per SIMD
+  // (registers), fewer where the two V stages of a wave run short of LDS
+  const int64_t stage = (int64_t)kWaveTile * a.head_dim_v * 2;
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / (2 * stage + 1536)));
+  const int64_t tiles = (max_vis + kWaveTile - 1) / kWaveTile;
   const int64_t rows = (int64_t)a.batch * a.n_kv_heads;
   const int64_t want = std::max<int64_t>(1, (per_cu * a.n_cu) / std::max<int64_t>(1, rows));
   return (int)std::min(tiles, want);

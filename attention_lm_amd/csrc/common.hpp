@@ -19,6 +19,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // register-friendly 16 bytes
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float((uint32_t)v.u << 16); }
