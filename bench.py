@@ -346,12 +346,14 @@ def bench_decode(cfg, steps, warmup, n_sets, ev):
     return wall / steps * 1e3, per_layer_ms, stage_ms
 
 
-def bench_continue(cfg, steps, warmup, ring):
+def bench_continue(cfg, steps, warmup, ring, n_sets=3):
     """A prefill continued from its state: rows [M + W, L) of ``cfg`` after a
     first call over [0, M + W) (the chunk sees a full window of history), with
     the cache one row per position or the compact ring. Times the
     continuation call (inputs resident; state and cache are updated in place,
-    so every call does the same work)."""
+    so every call does the same work). Several sets (state, cache, inputs) are
+    rotated, as in the prefill step, so that a call does not re-read the last
+    call's data from the last-level cache."""
     import torch
     from harness import TORCH_DT, desc_for, dev
     import attention_lm_amd as H
@@ -367,37 +369,41 @@ def bench_continue(cfg, steps, warmup, ring):
     par = {k: dev(inp[k]) for k in ("A", "D", "conv_w", "beta_attn", "beta_ssm")}
     params = H.make_params(par["A"], par["D"], par["conv_w"], par["beta_attn"], par["beta_ssm"])
     Hkv, D = cfg.n_kv_heads, cfg.d_inner
-    kc = torch.zeros((cfg.batch, cap, Hkv, cfg.head_dim), dtype=dt_, device="cuda")
-    vc = torch.zeros((cfg.batch, cap, Hkv, cfg.head_dim_v), dtype=dt_, device="cuda")
-    state = torch.empty((cfg.batch, D, cfg.d_state), dtype=torch.float32, device="cuda")
-    conv = torch.empty((cfg.batch, D, cfg.d_conv - 1), dtype=dt_, device="cuda")
-    first = {k: dev(inp[k][:, :a], act) for k in per_row}
-    out0 = torch.empty((cfg.batch, a, D), dtype=dt_, device="cuda")
     d0 = desc_for(cfg.with_(n_tokens=a - M), cache_capacity=cap, cache_ring=ring)
-    H.hymba_mixer_prefill(d0, params, *[first[k] for k in per_row], out0, ssm_state_out=state,
-                          conv_state_out=conv, k_cache=kc, v_cache=vc)
-    rest = {k: dev(inp[k][:, a:], act) for k in per_row}
-    out = torch.empty((cfg.batch, T, D), dtype=dt_, device="cuda")
     desc = desc_for(cfg.with_(n_tokens=T), cache_capacity=cap, cache_ring=ring)
-    ws = torch.empty(max(H.hymba_mixer_prefill_workspace_bytes(desc), 256), dtype=torch.uint8, device="cuda")
+    sets = []
+    for _ in range(n_sets):
+        kc = torch.zeros((cfg.batch, cap, Hkv, cfg.head_dim), dtype=dt_, device="cuda")
+        vc = torch.zeros((cfg.batch, cap, Hkv, cfg.head_dim_v), dtype=dt_, device="cuda")
+        state = torch.empty((cfg.batch, D, cfg.d_state), dtype=torch.float32, device="cuda")
+        conv = torch.empty((cfg.batch, D, cfg.d_conv - 1), dtype=dt_, device="cuda")
+        first = {k: dev(inp[k][:, :a], act) for k in per_row}
+        out0 = torch.empty((cfg.batch, a, D), dtype=dt_, device="cuda")
+        H.hymba_mixer_prefill(d0, params, *[first[k] for k in per_row], out0, ssm_state_out=state,
+                              conv_state_out=conv, k_cache=kc, v_cache=vc)
+        rest = {k: dev(inp[k][:, a:], act) for k in per_row}
+        out = torch.empty((cfg.batch, T, D), dtype=dt_, device="cuda")
+        ws = torch.empty(max(H.hymba_mixer_prefill_workspace_bytes(desc), 256), dtype=torch.uint8, device="cuda")
+        sets.append((rest, out, state, conv, kc, vc, ws))
 
-    def step():
+    def step(st):
+        rest, out, state, conv, kc, vc, ws = st
         H.hymba_mixer_prefill_continue(desc, params, a, *[rest[k] for k in per_row], out, state, conv, kc, vc,
                                        workspace=ws)
 
-    for _ in range(warmup):
-        step()
+    for i in range(warmup):
+        step(sets[i % n_sets])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
+    for i in range(steps):
+        step(sets[i % n_sets])
     torch.cuda.synchronize()
     us = (time.perf_counter() - t0) / steps * 1e6
     return {"us_per_call": round(us, 2), "tokens_per_s": round(cfg.batch * T / (us * 1e-6), 1),
             "cache_rows_per_seq": cap}
 
 
-def bench_decode_ring(cfg, steps, warmup):
+def bench_decode_ring(cfg, steps, warmup, n_sets=3):
     """The decode step over the compact cache: n_meta + window rows per
     sequence instead of cache_len, every sequence at position cache_len."""
     import torch
@@ -407,22 +413,26 @@ def bench_decode_ring(cfg, steps, warmup):
 
     cap = cfg.n_meta + cfg.window
     rcfg = cfg.with_(cache_capacity=cap, cache_len=cap)
-    run = Decode(rcfg, synth.make_decode_inputs(rcfg))
-    run.cache_len.fill_(cfg.cache_len)
-    run.desc = desc_for(rcfg, cache_ring=True)
-    run.ws = torch.empty(max(H.hymba_mixer_decode_workspace_bytes(run.desc), 256), dtype=torch.uint8,
-                         device="cuda")
+    inp = synth.make_decode_inputs(rcfg)
+    runs = []
+    for _ in range(n_sets):   # rotated like the long-cache step, so no set stays in the last-level cache
+        run = Decode(rcfg, inp)
+        run.cache_len.fill_(cfg.cache_len)
+        run.desc = desc_for(rcfg, cache_ring=True)
+        run.ws = torch.empty(max(H.hymba_mixer_decode_workspace_bytes(run.desc), 256), dtype=torch.uint8,
+                             device="cuda")
+        runs.append(run)
 
-    def step():
+    def step(run):
         for l in range(rcfg.n_layers):
             run.call(l, with_branches=False)
 
-    for _ in range(warmup):
-        step()
+    for i in range(warmup):
+        step(runs[i % n_sets])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
+    for i in range(steps):
+        step(runs[i % n_sets])
     torch.cuda.synchronize()
     us = (time.perf_counter() - t0) / steps * 1e6
     return {"us_per_step": round(us, 2), "cache_rows_per_seq": cap, "position": cfg.cache_len}
