@@ -520,9 +520,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   // Work order: a workgroup's cost grows with its position block (more keys
   // in the causal window, up to the full window); two workgroups fit on a CU.
   // Items are handed out heaviest first (largest-first scheduling). When all
-  // of them fit at once (at most two per CU), the first n_cu workgroups (one
-  // per CU) take the heaviest items and the rest the lightest, in ascending
-  // order, so that heavy items share a CU with light ones.
+  // of them fit at once (between one and two per CU), n_items - n_cu CUs get
+  // a second workgroup (workgroup n_cu + j lands beside workgroup j): the CUs
+  // that keep one workgroup take the heaviest items, and each other CU pairs
+  // one of the next heaviest with one of the lightest.
   // query row r is at position q_pos0 + r; key row j of k_rot / v is at
   // position j; positions below L = q_pos0 + Lq exist
   const int L = q_pos0 + Lq;
@@ -531,7 +532,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   const int n_items = nxb * hb_n;
   const int wg = (int)blockIdx.x;
   int rank = wg;
-  if (n_items <= 2 * n_cu && wg >= n_cu) rank = n_items - 1 - (wg - n_cu);
+  if (n_items > n_cu && n_items <= 2 * n_cu) {
+    const int n_pair = n_items - n_cu, n_single = n_cu - n_pair;
+    if (wg < n_cu) rank = wg < n_pair ? n_single + wg : wg - n_pair;
+    else rank = n_items - 1 - (wg - n_cu);
+  }
   const int pb = nxb - 1 - rank / hb_n;
   const int g = (rank % hb_n) % Hkv;
   const int64_t b = (rank % hb_n) / Hkv;
