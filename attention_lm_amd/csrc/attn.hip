@@ -1464,8 +1464,9 @@ int decode_active_splits(const AttnDecodeArgs& a) {
   const int64_t max_vis = decode_max_visible(a.n_meta, a.window, a.cap);
   if (a.act != HYMBA_BF16)   // one split per kKeysPerSplit keys
     return (int)((max_vis + kKeysPerSplit - 1) / kKeysPerSplit);
-  // one wave per split, as many as fit the chip at once: two per SIMD
-  // (registers), fewer where the two V stages of a wave run short of LDS
+  // one wave per split, all resident at once: eight waves per CU (more were
+  // measured no faster: the step is bound by the memory system), fewer where
+  // the two V stages of a wave run short of LDS
   const int64_t stage = (int64_t)kWaveTile * a.head_dim_v * 2;
   const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / (2 * stage + 1536)));
   const int64_t tiles = (max_vis + kWaveTile - 1) / kWaveTile;
