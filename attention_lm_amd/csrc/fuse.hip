@@ -11,6 +11,20 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;
 
+// The fused row is the step's last write and nothing in the step reads it
+// again: stream it out (non-temporal) instead of keeping it in the caches
+// (10.9 -> 9.6 us on the 2176-row layer).
+__device__ __forceinline__ void store16_stream(bf16* p, const float* r) {
+  const u32x4_t w = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                     pack_bf16x2(r[6], r[7])};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store16_stream(float* p, const float* r) {
+  const f32x4_t w = {r[0], r[1], r[2], r[3]};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t*>(p));
+}
+
+
 // VEC: 16-byte vectors; MAXV > 0: the row fits in MAXV vectors per lane and is
 // kept in registers (all loads issued up front); MAXV == 0: two passes over
 // the row (the second one hits cache).
@@ -77,7 +91,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void fuse_rows_kernel(
         if constexpr (V == 8) load16(sbeta + width + c + 4, bsv + 4);
 #pragma unroll
         for (int e = 0; e < V; ++e) r[e] = fmaf(bav[e] * ra, va[i][e], bsv[e] * rs * vs[i][e]);
-        store16(o + c, r);
+        store16_stream(o + c, r);
       }
     }
   } else {
@@ -113,7 +127,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void fuse_rows_kernel(
 #pragma unroll
       for (int e = 0; e < V; ++e) r[e] = fmaf(ba[c + e] * ra, va[e], bs[c + e] * rs * vs[e]);
       if constexpr (VEC) {
-        store16(o + c, r);
+        store16_stream(o + c, r);
       } else {
         o[c] = from_f32<T>(r[0]);
       }
