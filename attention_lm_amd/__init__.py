@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     MixerParams,
     hymba_abi_version,
     hymba_debug_mask_ranges,
+    hymba_debug_prefill_visibility,
     hymba_fuse_heads,
     hymba_last_hip_error,
     hymba_mixer_decode,

@@ -27,6 +27,7 @@ _EXPORTS = [
     "hymba_mixer_decode",
     "hymba_fuse_heads",
     "hymba_debug_mask_ranges",
+    "hymba_debug_prefill_visibility",
     "hymba_status_string",
     "hymba_last_hip_error",
     "hymba_abi_version",
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hymba_fuse_heads.restype = ctypes.c_int
     lib.hymba_debug_mask_ranges.argtypes = [pdesc, vp, vp]
     lib.hymba_debug_mask_ranges.restype = ctypes.c_int
+    lib.hymba_debug_prefill_visibility.argtypes = [pdesc, i32, vp, vp]
+    lib.hymba_debug_prefill_visibility.restype = ctypes.c_int
     lib.hymba_status_string.argtypes = [ctypes.c_int]
     lib.hymba_status_string.restype = ctypes.c_char_p
     lib.hymba_last_hip_error.argtypes = []
@@ -212,6 +215,11 @@ def hymba_fuse_heads(y_attn, y_ssm, beta_attn, beta_ssm, n_rows: int, width: int
 def hymba_debug_mask_ranges(desc: MixerDesc, ranges, stream=None):
     st = load_library().hymba_debug_mask_ranges(ctypes.byref(desc), _ptr(ranges), _stream(stream))
     _check("hymba_debug_mask_ranges", st)
+
+
+def hymba_debug_prefill_visibility(desc: MixerDesc, pos0: int, out, stream=None):
+    st = load_library().hymba_debug_prefill_visibility(ctypes.byref(desc), int(pos0), _ptr(out), _stream(stream))
+    _check("hymba_debug_prefill_visibility", st)
 
 
 def hymba_status_string(status: int) -> str:

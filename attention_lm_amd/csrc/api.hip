@@ -559,6 +559,21 @@ int hymba_debug_mask_ranges(const hymba_mixer_desc* desc, int32_t* ranges, hipSt
                                               stream));
 }
 
+int hymba_debug_prefill_visibility(const hymba_mixer_desc* desc, int32_t pos0, int32_t* out, hipStream_t stream) {
+  int st = check_desc(desc, false);
+  if (st != HYMBA_OK) return st;
+  if (!out) return HYMBA_EINVAL;
+  if (!aligned16(out)) return HYMBA_EALIGN;
+  if (pos0 < 0 || (pos0 > 0 && (desc->n_tokens < 1 || pos0 < desc->n_meta)) ||
+      (int64_t)pos0 + desc->n_tokens > INT32_MAX / 2)
+    return HYMBA_EINVAL;
+  const int Lq = pos0 > 0 ? desc->n_tokens : desc->n_meta + desc->n_tokens;
+  int n_cu = 0;
+  HYMBA_TRY(device_cus(&n_cu));
+  return hip_status(hymba::launch_prefill_visibility(desc->batch, Lq, pos0, desc->n_meta, desc->window, desc->n_q_heads,
+                                                     desc->n_kv_heads, n_cu, out, stream));
+}
+
 const char* hymba_status_string(int status) {
   switch (status) {
     case HYMBA_OK: return "ok";

@@ -493,6 +493,90 @@ __device__ __forceinline__ void mask_scores(f32x16_t& s, const LaneKeys& lk, int
   }
 }
 
+// The index logic of the prefill attention, shared by the kernel and by the
+// debug export that checks it exactly: the workgroup's item (sequence, kv
+// head, block of P positions) from its launch index, the key tiles it visits
+// (the meta tiles, then the window tiles), each wave's decision per 32-key
+// sub-tile (skip it, or take it without a mask) and each lane's visible key
+// intervals, which mask the remaining sub-tiles in mask_scores.
+//
+// Workgroup = 4 waves = 128 query columns: P = floor(128 / G) consecutive
+// positions times the G query heads of one kv head (column c is position
+// p0 + c / G, head c % G). Query row r is at position q_pos0 + r; key row j
+// is at position j; positions below L = q_pos0 + Lq exist.
+//
+// Work order: a workgroup's cost grows with its position block (more keys in
+// the causal window, up to the full window); two workgroups fit on a CU. Items
+// are handed out heaviest first (largest-first scheduling). When all of them
+// fit at once (between one and two per CU), n_items - n_cu CUs get a second
+// workgroup (workgroup n_cu + j lands beside workgroup j): the CUs that keep
+// one workgroup take the heaviest items, and each other CU pairs one of the
+// next heaviest with one of the lightest.
+struct PrefillIndex {
+  int L, n_meta, window;
+  int64_t b;      // sequence
+  int g;          // kv head
+  int p0, p1;     // the workgroup's positions [p0, p1)
+  int qa, qb;     // positions spanned by this wave's valid columns
+  int my_q;       // this lane's query position (L: the column has no query)
+  int h;          // this lane's query head
+  int n1, k2s, ntiles;   // tiles: [0, n1) of meta keys, then k2s, k2s + 1, .. (64 keys each)
+  LaneKeys lk;
+
+  __device__ __forceinline__ void init(int wg, int n_cu, int Lq, int q_pos0, int n_meta_, int window_, int Hq,
+                                       int Hkv, int batch, int wave, int lane) {
+    n_meta = n_meta_;
+    window = window_;
+    L = q_pos0 + Lq;
+    const int G = Hq / Hkv;                 // query heads per kv head
+    const int P = kAttnCols / G;            // positions per workgroup
+    const int nxb = (Lq + P - 1) / P;
+    const int hb_n = Hkv * batch;
+    const int n_items = nxb * hb_n;
+    int rank = wg;
+    if (n_items > n_cu && n_items <= 2 * n_cu) {
+      const int n_pair = n_items - n_cu, n_single = n_cu - n_pair;
+      if (wg < n_cu) rank = wg < n_pair ? n_single + wg : wg - n_pair;
+      else rank = n_items - 1 - (wg - n_cu);
+    }
+    const int pb = nxb - 1 - rank / hb_n;
+    g = (rank % hb_n) % Hkv;
+    b = (rank % hb_n) / Hkv;
+    p0 = q_pos0 + pb * P;
+    p1 = min(p0 + P, L);
+    const int col = 32 * wave + (lane & 31);
+    const bool col_ok = col < P * G;
+    my_q = col_ok ? p0 + col / G : L;
+    h = g * G + (col_ok ? col % G : 0);
+    const int c_lo = 32 * wave, c_hi = min(32 * wave + 31, P * G - 1);
+    qa = p0 + c_lo / G;
+    qb = c_lo <= c_hi ? min(p0 + c_hi / G + 1, L) : qa;
+    lk.meta_hi = my_q < L ? min(my_q + 1, n_meta) : 0;
+    lk.win_hi = my_q < L ? my_q + 1 : 0;
+    lk.win_lo = window > 0 ? max(my_q - window + 1, n_meta) : n_meta;
+    // key tiles: meta part then window part
+    const int meta_end = min(n_meta, p1);
+    const int wb = window > 0 ? max(n_meta, p0 - window + 1) : n_meta;
+    n1 = (meta_end + BK - 1) / BK;
+    k2s = wb / BK;
+    const int k2e = (p1 + BK - 1) / BK;
+    if (k2s < n1) k2s = n1;
+    ntiles = n1 + max(0, k2e - k2s);
+  }
+  __device__ __forceinline__ int tile_j0(int idx) const { return (idx < n1 ? idx : k2s + (idx - n1)) * BK; }
+  // sub-tile [j0, j0 + 32) against this wave's positions [qa, qb): no key
+  // visible to any column
+  __device__ __forceinline__ bool none_for(int j0) const {
+    const int j1 = j0 + 32;
+    return qa >= qb || (j0 > qb - 1) || (window > 0 && j0 >= n_meta && qa - (j1 - 1) >= window);
+  }
+  // ... or every key visible to every column
+  __device__ __forceinline__ bool full_for(int j0) const {
+    const int j1 = j0 + 32;
+    return qa < qb && (j1 - 1 <= qa) && (window <= 0 || j1 <= n_meta || (qb - 1) - max(j0, n_meta) < window);
+  }
+};
+
 template <typename T, int DV>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
     const T* __restrict__ q_rot, const T* __restrict__ k_rot, const T* __restrict__ v, T* __restrict__ y,
@@ -510,51 +594,17 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   lds_char* const stage0 = (lds_char*)lds_stage0;
   lds_char* const stage1 = (lds_char*)lds_stage1;
 
-  const int G = Hq / Hkv;                 // query heads per kv head
-  const int P = kAttnCols / G;            // positions per workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile decisions are scalar
-  const int lq = lane & 31;   // query column (within the wave) / operand row of this lane
   const int hh = lane >> 5;   // lane half
-  // Work order: a workgroup's cost grows with its position block (more keys
-  // in the causal window, up to the full window); two workgroups fit on a CU.
-  // Items are handed out heaviest first (largest-first scheduling). When all
-  // of them fit at once (between one and two per CU), n_items - n_cu CUs get
-  // a second workgroup (workgroup n_cu + j lands beside workgroup j): the CUs
-  // that keep one workgroup take the heaviest items, and each other CU pairs
-  // one of the next heaviest with one of the lightest.
-  // query row r is at position q_pos0 + r; key row j of k_rot / v is at
-  // position j; positions below L = q_pos0 + Lq exist
   const int L = q_pos0 + Lq;
-  const int nxb = (Lq + P - 1) / P;
-  const int hb_n = Hkv * batch;
-  const int n_items = nxb * hb_n;
-  const int wg = (int)blockIdx.x;
-  int rank = wg;
-  if (n_items > n_cu && n_items <= 2 * n_cu) {
-    const int n_pair = n_items - n_cu, n_single = n_cu - n_pair;
-    if (wg < n_cu) rank = wg < n_pair ? n_single + wg : wg - n_pair;
-    else rank = n_items - 1 - (wg - n_cu);
-  }
-  const int pb = nxb - 1 - rank / hb_n;
-  const int g = (rank % hb_n) % Hkv;
-  const int64_t b = (rank % hb_n) / Hkv;
-  const int p0 = q_pos0 + pb * P;
-  const int p1 = min(p0 + P, L);
-  const int col = 32 * wave + lq;
-  const bool col_ok = col < P * G;
-  const int my_q = col_ok ? p0 + col / G : L;          // position of this lane's column (L = none)
-  const int h = g * G + (col_ok ? col % G : 0);
-  // positions spanned by this wave's valid columns
-  const int c_lo = 32 * wave, c_hi = min(32 * wave + 31, P * G - 1);
-  const int qa = p0 + c_lo / G;
-  const int qb = c_lo <= c_hi ? min(p0 + c_hi / G + 1, L) : qa;
-
-  LaneKeys lk;
-  lk.meta_hi = my_q < L ? min(my_q + 1, n_meta) : 0;
-  lk.win_hi = my_q < L ? my_q + 1 : 0;
-  lk.win_lo = window > 0 ? max(my_q - window + 1, n_meta) : n_meta;
+  PrefillIndex ix;
+  ix.init((int)blockIdx.x, n_cu, Lq, q_pos0, n_meta, window, Hq, Hkv, batch, wave, lane);
+  const int64_t b = ix.b;
+  const int g = ix.g;
+  const int my_q = ix.my_q, h = ix.h;
+  const LaneKeys lk = ix.lk;
 
   // Q^T operand: lane holds Q[my_q][16 kc + 8 hh .. +7] (pre-scaled)
   Frag qf[4];
@@ -566,20 +616,12 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   SoftmaxState<NDB> st;
   st.init();
 
-  // key tiles: meta part then window part
-  const int meta_end = min(n_meta, p1);
-  const int wb = window > 0 ? max(n_meta, p0 - window + 1) : n_meta;
-  const int n1 = (meta_end + BK - 1) / BK;
-  int k2s = wb / BK;
-  const int k2e = (p1 + BK - 1) / BK;
-  if (k2s < n1) k2s = n1;
-  const int ntiles = n1 + max(0, k2e - k2s);
-
+  const int ntiles = ix.ntiles;
   const int64_t kstride = (int64_t)Hkv * kHd, vstride = (int64_t)Hkv * DV;
   Stage stage;
   stage.init(tid, k_rot + (b * k_rows) * kstride + g * kHd, v + (b * v_rows) * vstride + g * DV, kstride, vstride,
              L);
-  auto tile_j0 = [&](int idx) { return (idx < n1 ? idx : k2s + (idx - n1)) * BK; };
+  auto tile_j0 = [&](int idx) { return ix.tile_j0(idx); };
 
   // every workgroup has at least the tile of its own first position (ntiles >= 1)
   stage.fetch(tile_j0(0), stage0);
@@ -587,16 +629,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
   wait_loads();
   __syncthreads();
 
-  // sub-tile [j0, j0 + 32) against this wave's positions [qa, qb): no key
-  // visible to any column, or every key visible to every column
-  auto none_for = [&](int j0) {
-    const int j1 = j0 + 32;
-    return qa >= qb || (j0 > qb - 1) || (window > 0 && j0 >= n_meta && qa - (j1 - 1) >= window);
-  };
-  auto full_for = [&](int j0) {
-    const int j1 = j0 + 32;
-    return qa < qb && (j1 - 1 <= qa) && (window <= 0 || j1 <= n_meta || (qb - 1) - max(j0, n_meta) < window);
-  };
+  auto none_for = [&](int j0) { return ix.none_for(j0); };
+  auto full_for = [&](int j0) { return ix.full_for(j0); };
   // 2^s of 16 shifted scores -> two B operands; l += their sum
   auto probs = [&](const f32x16_t& s, Frag& pa, Frag& pb) {
     float p[16];
@@ -704,6 +738,60 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
         }
       }
     }
+  }
+}
+
+// The prefill attention's visibility decisions, exported for exact tests:
+// the same work order, tile walk, per-wave skip / unmasked decisions and
+// per-lane masking as attn_prefill_kernel, applied to zero scores. For each
+// query column the keys left finite are summarised as
+// [meta_end, win_begin, win_end, count] (the ranges of the visible meta keys
+// [0, meta_end) and window keys [win_begin, win_end), both n_meta when empty;
+// count = keys taken). out: [batch, Lq, Hq, 4].
+__global__ __launch_bounds__(64 * kAttnWaves) void prefill_visibility_kernel(int32_t* __restrict__ out, int Lq,
+                                                                             int q_pos0, int n_meta, int window,
+                                                                             int Hq, int Hkv, int batch, int n_cu) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5;
+  PrefillIndex ix;
+  ix.init((int)blockIdx.x, n_cu, Lq, q_pos0, n_meta, window, Hq, Hkv, batch, wave, lane);
+  int count = 0, meta_end = 0, win_lo = INT32_MAX, win_hi = -1;
+  for (int idx = 0; idx < ix.ntiles; ++idx) {
+    const int jt = ix.tile_j0(idx);
+    if (ix.none_for(jt) && ix.none_for(jt + 32)) continue;
+    for (int half = 0; half < 2; ++half) {
+      const int j0 = jt + 32 * half;
+      f32x16_t sc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+      if (!ix.full_for(j0)) mask_scores(sc, ix.lk, j0, hh, n_meta);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 4 * hh + 8 * (r >> 2) + (r & 3);   // the key of score register r
+        if (sc[r] != -INFINITY) {
+          ++count;
+          if (j < n_meta) {
+            meta_end = max(meta_end, j + 1);
+          } else {
+            win_lo = min(win_lo, j);
+            win_hi = max(win_hi, j + 1);
+          }
+        }
+      }
+    }
+  }
+  count += __shfl_xor(count, 32, 64);
+  meta_end = max(meta_end, __shfl_xor(meta_end, 32, 64));
+  win_lo = min(win_lo, __shfl_xor(win_lo, 32, 64));
+  win_hi = max(win_hi, __shfl_xor(win_hi, 32, 64));
+  if (ix.my_q < ix.L && hh == 0) {
+    const bool any = win_hi >= 0;
+    int32_t* o = out + ((ix.b * Lq + (ix.my_q - q_pos0)) * Hq + ix.h) * 4;
+    o[0] = meta_end;
+    o[1] = any ? win_lo : n_meta;
+    o[2] = any ? win_hi : n_meta;
+    o[3] = count;
   }
 }
 
@@ -1435,6 +1523,16 @@ hipError_t combine_t(const DecodeCombineArgs& a, hipStream_t stream, Timing tm) 
   }
 
 }  // namespace
+
+hipError_t launch_prefill_visibility(int batch, int Lq, int q_pos0, int n_meta, int window, int Hq, int Hkv, int n_cu,
+                                     int32_t* out, hipStream_t stream) {
+  const int P = kAttnCols / (Hq / Hkv);
+  const int64_t n_items = (int64_t)((Lq + P - 1) / P) * Hkv * batch;
+  if (n_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_visibility_kernel, dim3((unsigned)n_items), dim3(64 * kAttnWaves), 0, stream, out, Lq,
+                     q_pos0, n_meta, window, Hq, Hkv, batch, n_cu);
+  return hipGetLastError();
+}
 
 hipError_t launch_rope_prefill(const RopeArgs& a, hipStream_t stream, Timing tm) {
   if (a.act == HYMBA_BF16) return rope_t<bf16>(a, stream, tm);

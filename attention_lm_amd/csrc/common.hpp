@@ -101,7 +101,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Visibility of key row j to query row i (the one rule all kernels use).
+// Visibility of key row j to query row i: the ranges a decode row sees.
 //
 // Causal: j <= i. The meta-token rows j < n_meta are visible to every later
 // row under any window (Hymba guide, "2. Learnable Meta-Tokens"; the
@@ -126,12 +126,6 @@ __host__ __device__ __forceinline__ MaskRange mask_range(int i, int n_meta, int 
   r.win_begin = wb;
   r.win_end = we;
   return r;
-}
-
-__host__ __device__ __forceinline__ bool key_visible(int i, int j, int n_meta, int window) {
-  if (j > i) return false;
-  if (window <= 0 || j < n_meta) return true;
-  return i - j < window;
 }
 
 }  // namespace hymba

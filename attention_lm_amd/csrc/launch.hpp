@@ -54,6 +54,9 @@ struct SsmPrefillArgs {
   hymba_dtype act;
 };
 int ssm_prefill_chunk_rows(int batch, int L, int d_inner);
+// true when the batch alone fills the chip: the prefill scan is then one pass
+// over whole sequences (chunk rows = L, no end-state pass and no carry chain)
+bool ssm_single_pass(int batch, int d_inner);
 // The three kernels of the chunked prefill scan, in this order: chunk end
 // states (nothing to do for a single chunk), carries between chunks, output.
 hipError_t launch_ssm_chunk_end(const SsmPrefillArgs& a, hipStream_t stream, Timing tm = {});
@@ -119,6 +122,10 @@ struct AttnPrefillArgs {
   hymba_dtype act;
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream, Timing tm = {});
+// the prefill attention's visibility decisions per query column, [batch, Lq, Hq, 4]
+// (see prefill_visibility_kernel)
+hipError_t launch_prefill_visibility(int batch, int Lq, int q_pos0, int n_meta, int window, int Hq, int Hkv, int n_cu,
+                                     int32_t* out, hipStream_t stream);
 
 struct AttnDecodeArgs {
   const void *q, *k_new, *v_new;       // [batch, H, d] not rotated

@@ -361,6 +361,226 @@ __global__ __launch_bounds__(64 * kCarrySegs) void ssm_chunk_carry_kernel(const 
   }
 }
 
+// Workgroup barrier for LDS data only: this wave's LDS operations are done
+// (lgkmcnt 0), then s_barrier; global loads in flight, including loads into
+// LDS, are not waited for (a __syncthreads() would wait for all of them). The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most n of this wave's vector memory operations are
+// outstanding (0 <= n; counts of 63 and more wait for nothing). s_waitcnt
+// takes an immediate, so the count is dispatched to constant waits.
+__device__ __forceinline__ void vm_wait_at_most(int n) {
+#define HYMBA_VMW(k) \
+  case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | 0x0F70); break;
+  switch (n) {
+    HYMBA_VMW(0) HYMBA_VMW(1) HYMBA_VMW(2) HYMBA_VMW(3) HYMBA_VMW(4) HYMBA_VMW(5) HYMBA_VMW(6) HYMBA_VMW(7)
+    HYMBA_VMW(8) HYMBA_VMW(9) HYMBA_VMW(10) HYMBA_VMW(11) HYMBA_VMW(12) HYMBA_VMW(13) HYMBA_VMW(14) HYMBA_VMW(15)
+    default: break;
+  }
+#undef HYMBA_VMW
+}
+
+// ---------------------------------------------------------------------------
+// Single-pass scan, for batches whose (sequence, channel) count alone fills
+// the chip: one exp(dt A) per element instead of two, and no carry chain.
+// Workgroup = 32 channels of one sequence x 16 states, 256 lanes: lane l holds
+// channel c0 + l % 32 and the states 2 (l / 32), 2 (l / 32) + 1 in registers
+// for the whole sequence. Per block of kScanRows rows:
+//   A. one lane per (row, channel): the conv output u, dt and dt u as fp32 in
+//      LDS, and the block's B and C rows as fp32, grouped by state pair;
+//   B. every lane advances its two states over the block's rows and leaves its
+//      part of C . h for each row in LDS;
+//   C. one lane per (row, channel): y = the eight parts + D u, times silu(z).
+// Work that is per (row, channel) (conv, dt u, gate) is done once, not once
+// per state. The next block's raw inputs load straight into LDS meanwhile.
+constexpr int kScanChan = 32;
+constexpr int kScanRows = 8;
+constexpr int kScanPairs = kStates / 2;
+constexpr int kScanStages = 4;
+constexpr int kScanRowsLoaded = 4;   // rows of phase B whose LDS values are in registers at once     // staging ring: three blocks in flight ahead of the one in use
+static_assert(kScanChan * kScanRows == 256 && kScanChan * kScanPairs == 256, "one lane per item");
+
+template <typename T>
+struct Scan1Stage {   // one block's inputs as loaded (16-byte pieces, row-major)
+  T x[kScanRows + kConv - 1][kScanChan];   // rows tb - 3 .. tb + kScanRows - 1
+  T dt[kScanRows][kScanChan];
+  T z[kScanRows][kScanChan];
+  T b[kScanRows][kStates];
+  T c[kScanRows][kStates];
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void ssm_scan1_kernel(
+    const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ dt, const T* __restrict__ Bm,
+    const T* __restrict__ Cm, const float* __restrict__ A, const float* __restrict__ Dp,
+    const float* __restrict__ conv_w, const T* __restrict__ conv_in, const float* __restrict__ state_in,
+    T* __restrict__ y, float* __restrict__ state_out, T* __restrict__ conv_state_out, int L, int Dch) {
+  constexpr int E = Vec16<T>::n;                // elements per 16-byte piece
+  constexpr int CP = kScanChan / E;             // pieces per 32-channel row
+  constexpr int SP = kStates / E;               // pieces per B or C row
+  constexpr int R = kScanRows;
+  __shared__ __attribute__((aligned(16))) Scan1Stage<T> stage[kScanStages];
+  __shared__ __attribute__((aligned(16))) float2 dd[R][kScanChan];      // (dt, dt u)
+  __shared__ float us[R][kScanChan];                                    // u, for the D u term
+  __shared__ __attribute__((aligned(16))) float4 bcs[R][kScanPairs];    // (B, B, C, C) of a state pair
+  __shared__ float part[R][kScanPairs][kScanChan];                      // each pair's share of C . h
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cl = tid & (kScanChan - 1);         // channel within the block (all phases)
+  const int sp = tid >> 5;                      // phase B: state pair; phases A, C: row of the block
+  const int c0 = blockIdx.x * kScanChan;
+  const int c = c0 + cl;
+  const bool cv = c < Dch;
+  const int cc = cv ? c : Dch - 1;
+  const int64_t b = blockIdx.y;
+  const int64_t seq = b * L;
+  const uint32_t row_b = (uint32_t)(Dch * sizeof(T));
+  // x over rows [0, L): a row index below 0 wraps past the end and reads zero
+  // (zero conv history); dt and z past L read zero (dt = 0 leaves the state
+  // as it is); y stores past L are dropped.
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + seq * Dch, (uint32_t)L * row_b);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(dt + seq * Dch, (uint32_t)L * row_b);
+  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(z + seq * Dch, (uint32_t)L * row_b);
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(Bm + seq * kStates, (uint32_t)(L * kStates * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(Cm + seq * kStates, (uint32_t)(L * kStates * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + seq * Dch, (uint32_t)L * row_b);
+  const uint32_t col_b = (uint32_t)(c0 * sizeof(T));
+
+  // one array of a block: n 16-byte pieces, piece i at LDS dst + 16 i, loaded by
+  // one wave (lane i of each instruction writes dst + 16 (i0 + i))
+  auto load_array = [&](__amdgpu_buffer_rsrc_t rs, int n, char* dst, auto off) {
+    for (int i0 = 0; i0 < n; i0 += 64)
+      if (i0 + lane < n) buf_load16_lds(rs, off(i0 + lane), dst + 16 * i0);
+  };
+  auto fetch = [&](int tb, Scan1Stage<T>& s) {
+    if (wave == 0)
+      load_array(xrs, (R + kConv - 1) * CP, (char*)&s.x[0][0], [&](int it) {
+        return (uint32_t)(tb - (kConv - 1) + it / CP) * row_b + col_b + (uint32_t)(16 * (it % CP));
+      });
+    if (wave == 1)
+      load_array(drs, R * CP, (char*)&s.dt[0][0], [&](int it) {
+        return (uint32_t)(tb + it / CP) * row_b + col_b + (uint32_t)(16 * (it % CP));
+      });
+    if (wave == 2)
+      load_array(zrs, R * CP, (char*)&s.z[0][0], [&](int it) {
+        return (uint32_t)(tb + it / CP) * row_b + col_b + (uint32_t)(16 * (it % CP));
+      });
+    if (wave == 3) {
+      auto off = [&](int it) { return (uint32_t)((tb * kStates) * (int)sizeof(T) + 16 * it); };
+      load_array(brs, R * SP, (char*)&s.b[0][0], off);
+      load_array(crs, R * SP, (char*)&s.c[0][0], off);
+    }
+  };
+
+  float a0 = A[(int64_t)cc * kStates + 2 * sp] * kLog2e;
+  float a1 = A[(int64_t)cc * kStates + 2 * sp + 1] * kLog2e;
+  float w[kConv];
+#pragma unroll
+  for (int j = 0; j < kConv; ++j) w[j] = conv_w[(int64_t)cc * kConv + j];
+  const float Dc = Dp[cc];
+  float h0 = 0.f, h1 = 0.f;
+  if (state_in) {
+    const float2 s2 = *reinterpret_cast<const float2*>(state_in + (b * Dch + cc) * kStates + 2 * sp);
+    h0 = s2.x;
+    h1 = s2.y;
+  }
+
+  // Staging ring of kScanStages blocks: block ib + kScanStages - 1 is fetched
+  // when block ib starts. Fetches past the sequence read zeros into stages
+  // that are never used, so every wave issues the same loads per block and a
+  // wait can count them. Before block ib, this wave's memory operations issued
+  // after block ib's loads are: the loads of the blocks fetched since (n_ld
+  // instructions per block) and one y store per finished block, at most
+  // kScanStages - 1 of them in flight; vmcnt drains in issue order, so waiting
+  // until that many remain means block ib's loads have landed.
+  const int n_ld = wave == 0 ? (R + kConv - 1) * CP / 64 + ((R + kConv - 1) * CP % 64 != 0)
+                   : wave < 3 ? (R * CP + 63) / 64
+                              : 2 * ((R * SP + 63) / 64);
+  const int nblk = (L + R - 1) / R;
+#pragma unroll
+  for (int k = 0; k < kScanStages - 1; ++k) fetch(k * R, stage[k]);
+  for (int ib = 0; ib < nblk; ++ib) {
+    Scan1Stage<T>& s = stage[ib % kScanStages];
+    vm_wait_at_most((kScanStages - 2) * n_ld + min(ib, kScanStages - 1));
+    lds_barrier();   // block ib has landed (every wave waited for its loads); block ib - 1 is done
+    if (ib == 0 && conv_in) {   // rows -3 .. -1: the carried conv history (oldest first)
+      if (tid < (kConv - 1) * kScanChan) {
+        const int r = tid / kScanChan;
+        s.x[r][cl] = conv_in[(b * Dch + cc) * (kConv - 1) + r];
+      }
+      lds_barrier();
+    }
+    fetch((ib + kScanStages - 1) * R, stage[(ib + kScanStages - 1) % kScanStages]);
+    // A: lane = (row sp, channel cl)
+    {
+      float xv[kConv];
+#pragma unroll
+      for (int j = 0; j < kConv; ++j) xv[j] = to_f32(s.x[sp + j][cl]);
+      const float u = fmaf(w[0], xv[0], fmaf(w[1], xv[1], fmaf(w[2], xv[2], w[3] * xv[3])));
+      const float d = to_f32(s.dt[sp][cl]);
+      dd[sp][cl] = make_float2(d, d * u);
+      us[sp][cl] = u;
+      if (tid < R * kScanPairs) {
+        const int t = tid / kScanPairs, p = tid % kScanPairs;
+        bcs[t][p] = make_float4(to_f32(s.b[t][2 * p]), to_f32(s.b[t][2 * p + 1]), to_f32(s.c[t][2 * p]),
+                                to_f32(s.c[t][2 * p + 1]));
+      }
+    }
+    lds_barrier();
+    // B: lane = (state pair sp, channel cl); the values of kScanRowsLoaded rows
+    // are read from LDS together, so that the row loop waits once per group
+#pragma unroll
+    for (int t0 = 0; t0 < R; t0 += kScanRowsLoaded) {
+      float2 q[kScanRowsLoaded];
+      float4 g[kScanRowsLoaded];
+#pragma unroll
+      for (int t = 0; t < kScanRowsLoaded; ++t) {
+        q[t] = dd[t0 + t][cl];
+        g[t] = bcs[t0 + t][sp];
+      }
+#pragma unroll
+      for (int t = 0; t < kScanRowsLoaded; ++t) {
+        h0 = fmaf(fast_exp2(q[t].x * a0), h0, q[t].y * g[t].x);
+        h1 = fmaf(fast_exp2(q[t].x * a1), h1, q[t].y * g[t].y);
+        part[t0 + t][sp][cl] = fmaf(g[t].z, h0, g[t].w * h1);
+      }
+    }
+    lds_barrier();
+    // C: lane = (row sp, channel cl)
+    {
+      float acc = Dc * us[sp][cl];
+#pragma unroll
+      for (int p = 0; p < kScanPairs; ++p) acc += part[sp][p][cl];
+      const float g = acc * silu(to_f32(s.z[sp][cl]));
+      const uint32_t off = cv ? (uint32_t)(ib * R + sp) * row_b + (uint32_t)(c * sizeof(T)) : kBufferNowhere;
+      buf_store(yrs, off, from_f32<T>(g));
+    }
+  }
+  // the prefetches past the sequence land before the workgroup's LDS is released
+  vm_wait_at_most(0);
+
+  if (!cv) return;
+  if (state_out)
+    *reinterpret_cast<float2*>(state_out + (b * Dch + c) * kStates + 2 * sp) = make_float2(h0, h1);
+  if (conv_state_out && sp == 0) {   // raw x of rows L-3, L-2, L-1 (before row 0: the carried history, or zero)
+    T* csp = conv_state_out + (b * Dch + c) * (kConv - 1);
+#pragma unroll
+    for (int j = 0; j < kConv - 1; ++j) {
+      const int t = L - (kConv - 1) + j;
+      csp[j] = t >= 0    ? x[(seq + t) * Dch + c]
+               : conv_in ? conv_in[(b * Dch + c) * (kConv - 1) + (kConv - 1) + t]
+                         : from_f32<T>(0.f);
+    }
+  }
+}
+
 // Decode step (ssm_step.hpp): a lane quad per (sequence, channel), 4 states
 // per lane, and two channels per quad (c and c + d_inner / 2), so that the
 // whole step is one round of workgroups; every load of a lane is issued
@@ -405,9 +625,25 @@ hipError_t chunk_out_t(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t scan1_t(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
+  const dim3 grid((unsigned)((a.d_inner + kScanChan - 1) / kScanChan), (unsigned)a.batch);
+  HYMBA_LAUNCH(ssm_scan1_kernel<T>, grid, dim3(256), 0, stream, tm, (const T*)a.x, (const T*)a.z, (const T*)a.dt,
+               (const T*)a.B, (const T*)a.C, a.A, a.D, a.conv_w, (const T*)a.conv_in, a.state_in, (T*)a.y,
+               a.state_out, (T*)a.conv_state_out, a.L, a.d_inner);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+bool ssm_single_pass(int batch, int d_inner) {
+  // the single-pass form's workgroups (32 channels of one sequence) fill the
+  // chip on their own: at least four per compute unit of a 256-CU device
+  return (int64_t)batch * ((d_inner + kScanChan - 1) / kScanChan) >= 1024;
+}
+
 int ssm_prefill_chunk_rows(int batch, int L, int d_inner) {
+  if (ssm_single_pass(batch, d_inner)) return L;   // one chunk: the whole sequence
   // Every (sequence, channel block, chunk) workgroup is two waves and all of
   // them are resident at once, so a SIMD's time is its number of waves times
   // the rows per chunk. Ask for at least 2048 workgroups (four waves on each
@@ -442,11 +678,16 @@ hipError_t launch_ssm_carry_chain(const float* A, const float* agg, const float*
 }
 
 hipError_t launch_ssm_chunk_carry(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
+  if (ssm_single_pass(a.batch, a.d_inner)) return no_kernel(stream, tm);   // the state starts in registers
   const int nchunk = (a.L + a.chunk_rows - 1) / a.chunk_rows;
   return launch_ssm_carry_chain(a.A, a.agg, a.sdt, a.state_in, a.carry, nchunk, a.batch, a.d_inner, 0, stream, tm);
 }
 
 hipError_t launch_ssm_chunk_out(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
+  if (ssm_single_pass(a.batch, a.d_inner)) {
+    if (a.act == HYMBA_BF16) return scan1_t<bf16>(a, stream, tm);
+    return scan1_t<float>(a, stream, tm);
+  }
   if (a.act == HYMBA_BF16) return chunk_out_t<bf16>(a, stream, tm);
   return chunk_out_t<float>(a, stream, tm);
 }

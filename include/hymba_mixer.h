@@ -266,7 +266,11 @@ int hymba_fuse_heads(const void* y_attn, const void* y_ssm,
                      int64_t n_rows, int32_t width, float eps, hymba_dtype act,
                      void* out, hipStream_t stream);
 
-/* The visibility rule every attention kernel uses, exported for exact tests.
+/* The visibility rule as the decode attention applies it (one query row at a
+ * position p sees the meta rows [0, min(n_meta, p+1)) and the window rows),
+ * exported for exact tests ("Hymba Guide: NVIDIA Hybrid-Head Mamba &
+ * Attention SLM", "2. Learnable Meta-Tokens": meta rows stay visible to every
+ * later row under any window).
  * For each query row i < L = n_meta + n_tokens writes 4 int32 to ranges[4*i]:
  *   meta_end   visible meta keys are [0, meta_end)         = min(n_meta, i+1)
  *   win_begin, win_end   visible non-meta keys are [win_begin, win_end); both
@@ -274,6 +278,23 @@ int hymba_fuse_heads(const void* y_attn, const void* y_ssm,
  *   count      number of visible keys
  * ranges: device int32 [L, 4].                                               */
 int hymba_debug_mask_ranges(const hymba_mixer_desc* desc, int32_t* ranges, hipStream_t stream);
+
+/* The prefill attention's own visibility decisions, exported for exact tests:
+ * the kernel's work order, key-tile walk, per-wave decisions to skip a 32-key
+ * sub-tile or take it unmasked, and per-lane masking, run on zero scores.
+ * For each sequence b, query row r and query head h writes 4 int32 at
+ * out[((b * Lq + r) * n_q_heads + h) * 4] in the format of
+ * hymba_debug_mask_ranges: [meta_end, win_begin, win_end, count], where count
+ * is the number of keys whose score the kernel keeps (so the kept keys are
+ * exactly the two ranges when count = meta_end + win_end - win_begin).
+ *  pos0   0: a fresh prefill of Lq = n_meta + n_tokens rows at positions
+ *         0 .. Lq-1; > 0: a continuation of Lq = n_tokens rows at positions
+ *         pos0 .. pos0+Lq-1 over a cache of one row per position (n_meta <=
+ *         pos0).
+ *  out    device int32 [batch, Lq, n_q_heads, 4]; entries are written once
+ *         each; rows of a column without a query are not written.
+ * Errors as hymba_mixer_prefill (geometry), HYMBA_EINVAL for a bad pos0.    */
+int hymba_debug_prefill_visibility(const hymba_mixer_desc* desc, int32_t pos0, int32_t* out, hipStream_t stream);
 
 /* Static text for a hymba_status value. */
 const char* hymba_status_string(int status);

@@ -118,6 +118,14 @@ CONFIGS: Dict[str, MixerConfig] = {
     "decode": MixerConfig(
         name="decode", batch=64, n_meta=128, n_tokens=1, d_inner=3200,
         n_q_heads=25, n_kv_heads=5, head_dim=64, window=1024, act="bf16", seed=4,
+        decode=True, cache_len=8192, cache_capacity=8192, n_layers=2,
+        workload="decode step, batch 64, cache 8192 rows (window 1024 + 128 meta), "
+                 "25q/5kv x 64, KV cache shared read-only by two consecutive layers"),
+    # the same step where the second layer reads the shared keys through its
+    # own per-head affine (the cross-layer sharing variant of the Hymba guide)
+    "decode_affine": MixerConfig(
+        name="decode_affine", batch=64, n_meta=128, n_tokens=1, d_inner=3200,
+        n_q_heads=25, n_kv_heads=5, head_dim=64, window=1024, act="bf16", seed=4,
         decode=True, cache_len=8192, cache_capacity=8192, n_layers=2, key_affine=True,
         workload="decode step, batch 64, cache 8192 rows (window 1024 + 128 meta), "
                  "25q/5kv x 64, KV cache shared read-only by two layers, the second "

@@ -18,6 +18,44 @@ def rel_l2(got, ref) -> float:
     return float(np.linalg.norm((got - ref).ravel()) / (den if den > 0 else 1.0))
 
 
+def slice_errors(got, ref, width):
+    """Relative L2 error of each slice: the last axis cut into pieces of
+    ``width`` elements (the whole axis if it does not divide), every other axis
+    kept, so a slice is one (row, head) of the attention output, one block of
+    channels of a row, or one channel's states. A slice whose reference norm is
+    below a tenth of the RMS slice norm is measured against that floor (a
+    decayed state or a near-zero block is not blown up by its own small norm)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    w = ref.shape[-1]
+    sw = width if (width <= w and w % width == 0) else w
+    g = got.reshape(-1, sw)
+    r = ref.reshape(-1, sw)
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.linalg.norm(r, axis=1)
+    floor = 0.1 * np.sqrt(np.mean(den * den)) if den.size else 0.0
+    return num / np.maximum(den, max(floor, 1e-30)), sw
+
+
+def check(name, got, ref, tol, slice_width=128, slice_factor=4.0, say=print):
+    """Relative L2 over the whole tensor <= tol, and over every slice (see
+    slice_errors) <= slice_factor * tol, so that an error confined to one row,
+    head, tile or channel block cannot hide in a large tensor's norm."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), name
+    e = rel_l2(got, ref)
+    se, sw = slice_errors(got, ref, slice_width)
+    worst = int(np.argmax(se)) if se.size else 0
+    ws = float(se[worst]) if se.size else 0.0
+    where = np.unravel_index(worst, ref.shape[:-1] + (ref.shape[-1] // sw,)) if se.size else ()
+    say(f"  {name:14s} rel_l2={e:.3e} (tol {tol:.0e}); worst {sw}-wide slice {ws:.3e} at {tuple(int(i) for i in where)}"
+        f" (tol {slice_factor * tol:.0e})")
+    assert e <= tol, (name, e, tol)
+    assert ws <= slice_factor * tol, (name, "slice", where, ws)
+
+
 def dev(a, act=None, device="cuda"):
     t = torch.from_numpy(np.ascontiguousarray(a))
     if act is not None:

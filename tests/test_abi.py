@@ -166,6 +166,13 @@ def test_fuse_and_mask_validation(lib):
     d = c1_desc()
     assert lib.hymba_debug_mask_ranges(ctypes.byref(d), None, None) == -1
     assert lib.hymba_debug_mask_ranges(ctypes.byref(d), fake + 4, None) == -3
+    # the prefill visibility export validates like a prefill call, then its own arguments
+    assert lib.hymba_debug_prefill_visibility(ctypes.byref(d), 0, None, None) == -1
+    assert lib.hymba_debug_prefill_visibility(ctypes.byref(d), 0, fake + 4, None) == -3
+    assert lib.hymba_debug_prefill_visibility(ctypes.byref(d), -1, fake, None) == -1
+    assert lib.hymba_debug_prefill_visibility(ctypes.byref(d), 100, fake, None) == -1   # pos0 below n_meta
+    bad = c1_desc(n_kv_heads=3)
+    assert lib.hymba_debug_prefill_visibility(ctypes.byref(bad), 0, fake, None) == -1
 
 
 def test_continue_and_compact_cache_validation(lib):

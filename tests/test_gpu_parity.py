@@ -14,6 +14,7 @@ pytestmark = pytest.mark.gpu
 
 H = pytest.importorskip("attention_lm_amd")
 from harness import TOL, Decode, Prefill, dev, host, rel_l2  # noqa: E402
+from harness import check as _check  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -27,11 +28,12 @@ def say(*a):
     print(*a, flush=True)
 
 
-def check(name, got, ref, tol):
-    e = rel_l2(got, ref)
-    say(f"  {name:14s} rel_l2={e:.3e} (tol {tol:.0e})")
-    assert np.all(np.isfinite(got)), name
-    assert e <= tol, (name, e)
+def check(name, got, ref, tol, slice_width=128):
+    if tol == 0.0:   # copies of stored values: bitwise
+        np.testing.assert_array_equal(np.asarray(got), np.asarray(ref), err_msg=name)
+        say(f"  {name:14s} bit-exact")
+        return
+    _check(name, got, ref, tol, slice_width=slice_width, say=say)
 
 
 # ---------------------------------------------------------------------------
@@ -49,6 +51,45 @@ def test_mask_ranges_bit_exact(L, M, W):
     torch.cuda.synchronize()
     ref = O.mask_ranges(Lr, M, W)
     np.testing.assert_array_equal(r.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------------------
+# the prefill attention's own visibility decisions: bit exact
+
+
+VIS_SHAPES = [
+    # (batch, n_meta, n_tokens, Hq, Hkv, window, pos0)
+    (1, 8, 64, 2, 1, 32, 0),            # the tiny workload
+    (2, 5, 150, 5, 1, 40, 0),           # ragged tail, window across tiles
+    (3, 33, 70, 2, 2, 17, 0),           # MHA, meta not a multiple of 32
+    (1, 0, 97, 4, 2, 0, 0),             # no meta rows, global
+    (1, 128, 300, 5, 1, 64, 0),         # meta longer than the window
+    (2, 70, 0, 5, 5, 4, 0),             # meta rows only
+    (1, 60, 50, 8, 1, 7, 0),            # G = 8, n_meta > n_tokens
+    (1, 128, 2048, 25, 5, 1024, 0),     # the SWA layer
+    (1, 128, 8192, 25, 5, 0, 0),        # the global layer
+    (16, 128, 4096, 25, 5, 1024, 0),    # the batched workload
+    (2, 6, 40, 5, 1, 33, 50),           # a continuation: rows at positions 50 .. 89
+    (1, 128, 1024, 25, 5, 1024, 1152),  # a continuation of the SWA layer
+]
+
+
+@pytest.mark.parametrize("shape", VIS_SHAPES, ids=[f"vis{i}" for i in range(len(VIS_SHAPES))])
+def test_prefill_visibility_bit_exact(shape):
+    B, M, T, Hq, Hkv, W, pos0 = shape
+    dv = 128 if Hq == 25 else 64
+    desc = H.make_desc(batch=B, n_meta=M, n_tokens=T, d_inner=Hq * dv, n_q_heads=Hq, n_kv_heads=Hkv, window=W,
+                       act="bf16")
+    Lq = T if pos0 > 0 else M + T
+    say(f"visibility B={B} M={M} Lq={Lq} pos0={pos0} Hq={Hq} Hkv={Hkv} W={W}")
+    out = torch.full((B, Lq, Hq, 4), -7, dtype=torch.int32, device="cuda")
+    H.hymba_debug_prefill_visibility(desc, pos0, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = O.mask_ranges(pos0 + Lq, M, W)[pos0:]
+    np.testing.assert_array_equal(got, np.broadcast_to(ref[None, :, None, :], got.shape))
+    # the kept keys are exactly the two ranges
+    np.testing.assert_array_equal(ref[:, 3], ref[:, 0] + ref[:, 2] - ref[:, 1])
 
 
 # ---------------------------------------------------------------------------
@@ -91,13 +132,14 @@ def run_prefill_parity(cfg, rows=None, batches=None, state_tol=None):
     ref = O.mixer_prefill(cfg, inp, batches=bsel, rows=rows)
     rsel = ref["rows"]
     tol = TOL[cfg.act]
+    dv = cfg.head_dim_v
     check("y_ssm", got["y_ssm_out"][bsel], ref["y_ssm"], tol)
-    check("y_attn", got["y_attn_out"][bsel][:, rsel], ref["y_attn"], tol)
+    check("y_attn", got["y_attn_out"][bsel][:, rsel], ref["y_attn"], tol, slice_width=dv)   # per (row, head)
     check("out", got["out"][bsel][:, rsel], ref["out"], tol)
-    check("ssm_state", got["ssm_state_out"][bsel], ref["ssm_state"], state_tol or tol)
+    check("ssm_state", got["ssm_state_out"][bsel], ref["ssm_state"], state_tol or tol, slice_width=cfg.d_state)
     check("conv_state", got["conv_state_out"][bsel], ref["conv_state"], 0.0)
     L = cfg.seq_rows
-    check("k_cache", got["k_cache"][bsel][:, :L], ref["k_rot"], tol)
+    check("k_cache", got["k_cache"][bsel][:, :L], ref["k_rot"], tol, slice_width=cfg.head_dim)
     np.testing.assert_array_equal(got["v_cache"][bsel][:, :L], inp["v"][bsel])
     return run, inp, got
 
@@ -123,6 +165,21 @@ def test_prefill_small_shapes(kw):
     run_prefill_parity(cfg)
 
 
+# batches whose (sequence, channel) count fills the chip take the single-pass scan
+SINGLE_PASS = [
+    dict(batch=32, n_meta=5, n_tokens=60, d_inner=1024, n_q_heads=8, n_kv_heads=2, window=16, act="bf16", seed=71),
+    dict(batch=40, n_meta=3, n_tokens=27, d_inner=1024, n_q_heads=16, n_kv_heads=4, window=0, act="f32", seed=72),
+    dict(batch=12, n_meta=8, n_tokens=1, d_inner=3200, n_q_heads=25, n_kv_heads=5, window=4, act="bf16", seed=73),
+]
+
+
+@pytest.mark.parametrize("kw", SINGLE_PASS, ids=[f"single{i}" for i in range(len(SINGLE_PASS))])
+def test_prefill_single_pass_scan(kw):
+    cfg = synth.config("tiny_f32").with_(**kw, name="single")
+    run = run_prefill_parity(cfg)[0]
+    assert H.hymba_mixer_prefill_chunk_rows(run.desc) == cfg.seq_rows   # one chunk: the single-pass form ran
+
+
 AFFINE_PREFILL = [
     # two kv heads with two query heads each: a head must take its own group's w
     dict(batch=2, n_meta=5, n_tokens=130, d_inner=256, n_q_heads=4, n_kv_heads=2, window=40, act="bf16", seed=41),
@@ -145,20 +202,34 @@ def test_prefill_swa_layer_full():
     run_prefill_parity(synth.config("swa_layer"))
 
 
+def block_rows(cfg, head=0, tail=0):
+    """One query row from every position block of the prefill attention's work
+    items (a block is 128 // G consecutive positions of one kv group; a row
+    checks every head, so every (sequence, kv group, block) item is covered),
+    at an offset that moves from block to block, plus the first ``head`` and
+    the last ``tail`` rows."""
+    L = cfg.seq_rows
+    P = 128 // cfg.group
+    starts = np.arange(0, L, P)
+    rows = np.minimum(starts + (np.arange(len(starts)) * 7) % P, L - 1)
+    return np.unique(np.concatenate([rows, np.arange(0, min(head, L)), np.arange(max(0, L - tail), L)]))
+
+
 @pytest.mark.slow
-def test_prefill_global_layer_sampled_rows():
+def test_prefill_global_layer_every_block():
+    """The global layer: the scan over every row; attention and the fused
+    output on one row of every work item's position block."""
     cfg = synth.config("global_layer")
-    L = cfg.seq_rows
-    rows = np.unique(np.concatenate([np.arange(0, 130), np.linspace(0, L - 1, 48).astype(int), np.arange(L - 40, L)]))
-    run_prefill_parity(cfg, rows=rows)
+    run_prefill_parity(cfg, rows=block_rows(cfg, head=130, tail=40))
 
 
 @pytest.mark.slow
-def test_prefill_batched_sampled():
+def test_prefill_batched_every_sequence():
+    """The batched workload (single-pass scan): the Mamba branch, final state
+    and conv state of all 16 sequences over every row; attention and the
+    fused output on one row of every position block of every sequence."""
     cfg = synth.config("batched_prefill")
-    L = cfg.seq_rows
-    rows = np.unique(np.concatenate([np.arange(0, 70), np.linspace(0, L - 1, 40).astype(int), np.arange(L - 30, L)]))
-    run_prefill_parity(cfg, rows=rows, batches=[0, 9, 15])
+    run_prefill_parity(cfg, rows=block_rows(cfg, head=20, tail=10))
 
 
 def test_prefill_deterministic_and_branch_isolation():
@@ -202,9 +273,9 @@ def run_decode_parity(cfg, cache_len=None):
         L = run.layers[l]
         say(f" layer {l}")
         check("y_ssm", host(L["y_ssm_out"]), ref["y_ssm"], tol)
-        check("y_attn", host(L["y_attn_out"]), ref["y_attn"], tol)
+        check("y_attn", host(L["y_attn_out"]), ref["y_attn"], tol, slice_width=cfg.head_dim_v)   # per (row, head)
         check("out", host(L["out"]), ref["out"], tol)
-        check("ssm_state", host(L["ssm_state"]), ref["ssm_state"], tol)
+        check("ssm_state", host(L["ssm_state"]), ref["ssm_state"], tol, slice_width=cfg.d_state)
         check("conv_state", host(L["conv_state"]), ref["conv_state"], 0.0)
         if inp["layers"][l].get("k_scale") is not None:   # a secondary layer: its affine matters
             plain = {k: v for k, v in inp["layers"][l].items() if k not in ("k_scale", "k_bias")}
@@ -215,13 +286,13 @@ def run_decode_parity(cfg, cache_len=None):
 
 
 def test_decode_small_ragged_cache_lengths():
-    cfg = synth.config("decode").with_(batch=5, d_inner=320, n_q_heads=5, n_kv_heads=1, n_meta=8, window=50,
+    cfg = synth.config("decode_affine").with_(batch=5, d_inner=320, n_q_heads=5, n_kv_heads=1, n_meta=8, window=50,
                                        cache_capacity=300, cache_len=0, name="dsmall")
     run_decode_parity(cfg, cache_len=np.array([300, 8, 9, 57, 120], np.int32))
 
 
 def test_decode_small_global_f32():
-    cfg = synth.config("decode").with_(batch=3, d_inner=128, n_q_heads=2, n_kv_heads=1, n_meta=4, window=0,
+    cfg = synth.config("decode_affine").with_(batch=3, d_inner=128, n_q_heads=2, n_kv_heads=1, n_meta=4, window=0,
                                        cache_capacity=200, act="f32", name="dglob")
     run_decode_parity(cfg, cache_len=np.array([199, 4, 130], np.int32))
 
@@ -242,12 +313,18 @@ DECODE_EDGE = [
 def test_decode_bf16_edge_shapes(kw):
     kw = dict(kw)
     cache = np.array(kw.pop("cache"), np.int32)
-    cfg = synth.config("decode").with_(**kw, name="dedge")
+    cfg = synth.config("decode_affine").with_(**kw, name="dedge")
     run_decode_parity(cfg, cache_len=cache)
 
 
 def test_decode_full_config():
     run_decode_parity(synth.config("decode"))
+
+
+def test_decode_full_config_key_affine():
+    """The same step with the second layer reading the shared keys through its
+    per-head affine."""
+    run_decode_parity(synth.config("decode_affine"))
 
 
 def test_decode_continues_prefill():
@@ -315,6 +392,6 @@ def test_prefill_ssd_swa_layer_full():
 
 @pytest.mark.parametrize("act", ["bf16", "f32"])
 def test_decode_ssd(act):
-    cfg = synth.config("decode").with_(batch=5, d_inner=320, n_q_heads=5, n_kv_heads=1, n_meta=8, window=50,
+    cfg = synth.config("decode_affine").with_(batch=5, d_inner=320, n_q_heads=5, n_kv_heads=1, n_meta=8, window=50,
                                        cache_capacity=300, act=act, ssm_heads=5, name="dssd")
     run_decode_parity(cfg, cache_len=np.array([300, 8, 9, 57, 120], np.int32))
