@@ -29,6 +29,17 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
+// A VALU instruction may read a matrix-core result only some wait states
+// after the MFMA issues (gfx950: 12 for v_mfma_f32_32x32x16_bf16, 18 for
+// v_mfma_f32_32x32x2_f32). The compiler pads its own instructions, but not
+// the operands of inline asm such as max3f: before max3f reads score
+// registers that an MFMA has just written, this wait (18 states) is placed,
+// and since it takes the registers as in/out operands every later read of them
+// is ordered after it.
+__device__ __forceinline__ void mfma_result_wait(f32x16_t& a) { asm volatile("s_nop 15\n\ts_nop 1" : "+v"(a)); }
+__device__ __forceinline__ void mfma_result_wait(f32x16_t& a, f32x16_t& b) {
+  asm volatile("s_nop 15\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
 
 // 8 consecutive elements <-> fp32
 __device__ __forceinline__ void load8(const bf16* p, float* o) { load16(p, o); }
@@ -666,6 +677,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
       // column of the wave sees ends up all -inf and adds nothing)
       if (!full_for(jt)) mask_scores(s0, lk, jt, hh, n_meta);
       if (!full_for(jt + 32)) mask_scores(s1, lk, jt + 32, hh, n_meta);
+      mfma_result_wait(s0, s1);
       // this lane's max of both sub-tiles: four independent max3 chains
       float tm[4] = {s0[0], s0[1], s0[2], s0[3]};
 #pragma unroll
@@ -1203,6 +1215,7 @@ void attn_decode_wave_kernel(
         sc[r] = key < n_old ? sc[r] : -INFINITY;
       }
     }
+    mfma_result_wait(sc);
     float tm[4] = {sc[0], sc[1], sc[2], sc[3]};
 #pragma unroll
     for (int r = 0; r < 4; ++r) tm[r] = max3f(tm[r], sc[4 + r], sc[8 + r]);

@@ -321,6 +321,38 @@ def test_decode_full_config():
     run_decode_parity(synth.config("decode"))
 
 
+def test_decode_deterministic():
+    """Two identical decode steps of the full workload (fresh copies of the
+    states) give the same bits: no result depends on timing."""
+    cfg = synth.config("decode")
+    inp = synth.make_decode_inputs(cfg)
+    outs = []
+    for _ in range(3):
+        run = Decode(cfg, inp)
+        for l in range(cfg.n_layers):
+            run.call(l)
+        torch.cuda.synchronize()
+        outs.append([{k: host(run.layers[l][k]) for k in ("out", "y_attn_out", "y_ssm_out", "ssm_state")}
+                     for l in range(cfg.n_layers)])
+        del run
+    for other in outs[1:]:
+        for l in range(cfg.n_layers):
+            for k in outs[0][l]:
+                np.testing.assert_array_equal(other[l][k], outs[0][l][k], err_msg=f"layer {l} {k}")
+
+
+def test_prefill_swa_layer_deterministic():
+    cfg = synth.config("swa_layer")
+    inp = synth.make_prefill_inputs(cfg)
+    run = Prefill(cfg, inp)
+    run()
+    a = run.results()
+    run()
+    b = run.results()
+    for k in a:
+        np.testing.assert_array_equal(b[k], a[k], err_msg=k)
+
+
 def test_decode_full_config_key_affine():
     """The same step with the second layer reading the shared keys through its
     per-head affine."""
