@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     hymba_fuse_heads,
     hymba_last_hip_error,
     hymba_mixer_decode,
+    hymba_mixer_decode_noalloc,
     hymba_mixer_decode_workspace_bytes,
     hymba_mixer_prefill,
     hymba_mixer_prefill_chunk_rows,

@@ -25,6 +25,7 @@ _EXPORTS = [
     "hymba_mixer_prefill",
     "hymba_mixer_prefill_continue",
     "hymba_mixer_decode",
+    "hymba_mixer_decode_noalloc",
     "hymba_fuse_heads",
     "hymba_debug_mask_ranges",
     "hymba_debug_prefill_visibility",
@@ -81,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hymba_mixer_prefill_continue.restype = ctypes.c_int
     lib.hymba_mixer_decode.argtypes = [pdesc, pparams] + [vp] * 8 + [vp, vp, vp] + [vp, vp] + [vp, vp, vp] + [vp, sz, vp, vp]
     lib.hymba_mixer_decode.restype = ctypes.c_int
+    lib.hymba_mixer_decode_noalloc.argtypes = [pdesc, pparams] + [vp] * 8 + [vp, vp, vp] + [vp, vp] + [vp, vp, vp] + [vp]
+    lib.hymba_mixer_decode_noalloc.restype = ctypes.c_int
     lib.hymba_fuse_heads.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, ctypes.c_int, vp, vp]
     lib.hymba_fuse_heads.restype = ctypes.c_int
     lib.hymba_debug_mask_ranges.argtypes = [pdesc, vp, vp]
@@ -201,6 +204,17 @@ def hymba_mixer_decode(desc: MixerDesc, params: MixerParams, x, z, dt, B, C, q, 
         _ptr(conv_state), _ptr(out), _ptr(y_attn_out), _ptr(y_ssm_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), stage_events, _stream(stream))
     _check("hymba_mixer_decode", st)
+
+
+def hymba_mixer_decode_noalloc(desc: MixerDesc, params: MixerParams, x, z, dt, B, C, q, k_new, v_new, k_cache,
+                               v_cache, cache_len, ssm_state, conv_state, out, y_attn_out=None, y_ssm_out=None,
+                               stream=None):
+    """hymba_mixer_decode with the library's own static scratch (no workspace)."""
+    st = load_library().hymba_mixer_decode_noalloc(
+        ctypes.byref(desc), ctypes.byref(params), _ptr(x), _ptr(z), _ptr(dt), _ptr(B), _ptr(C), _ptr(q),
+        _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(ssm_state),
+        _ptr(conv_state), _ptr(out), _ptr(y_attn_out), _ptr(y_ssm_out), _stream(stream))
+    _check("hymba_mixer_decode_noalloc", st)
 
 
 def hymba_fuse_heads(y_attn, y_ssm, beta_attn, beta_ssm, n_rows: int, width: int, eps: float, act,

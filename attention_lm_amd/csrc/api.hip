@@ -192,9 +192,14 @@ struct DecodeWs {
   size_t partial, y_ssm, y_attn, q_rot, k_rot, total;
   int n_split, keys_per_split;
 };
-DecodeWs decode_ws(const hymba_mixer_desc* d) {
+// Scratch of one decode call: split partials for `slots` splits per (sequence,
+// query head), the branch outputs the caller does not keep, and (fp32 path)
+// the rotated queries and new keys. slots < 0: the plan's largest split count
+// (room for any launch on any device).
+DecodeWs decode_ws(const hymba_mixer_desc* d, int slots = -1) {
   DecodeWs w;
   hymba::decode_split_plan(d->n_meta, d->window, d->cache_capacity, &w.n_split, &w.keys_per_split);
+  if (slots >= 0) w.n_split = slots;
   const size_t B = (size_t)d->batch;
   w.partial = 0;
   w.y_ssm = round256(B * d->n_q_heads * w.n_split * (d->head_dim_v + 2) * sizeof(float));
@@ -476,30 +481,46 @@ int hymba_mixer_prefill_continue(const hymba_mixer_desc* desc, const hymba_mixer
   return prefill_impl(desc, params, c, stream);
 }
 
-int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* params, const void* x,
-                       const void* z, const void* dt, const void* B, const void* C, const void* q,
-                       const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
-                       const int32_t* cache_len, float* ssm_state, void* conv_state, void* out, void* y_attn_out,
-                       void* y_ssm_out, void* workspace, size_t workspace_bytes, hipEvent_t* stage_events,
-                       hipStream_t stream) {
-  int st = check_desc(desc, true);
-  if (st != HYMBA_OK) return st;
-  st = check_params(params);
-  if (st != HYMBA_OK) return st;
-  const void* req[] = {x, z, dt, B, C, q, k_new, v_new, k_cache, v_cache, cache_len, ssm_state, conv_state, out};
+}  // extern "C"
+
+namespace {
+
+struct DecodeCall {
+  const void *x, *z, *dt, *B, *C, *q, *k_new, *v_new, *k_cache, *v_cache;
+  const int32_t* cache_len;
+  float* ssm_state;
+  void *conv_state, *out, *y_attn_out, *y_ssm_out;
+};
+
+int check_decode_io(const DecodeCall& c) {
+  const void* req[] = {c.x, c.z, c.dt, c.B, c.C, c.q, c.k_new, c.v_new, c.k_cache, c.v_cache, c.cache_len,
+                       c.ssm_state, c.conv_state, c.out};
   for (const void* p : req)
     if (!p) return HYMBA_EINVAL;
   for (const void* p : req)
     if (!aligned16(p)) return HYMBA_EALIGN;
-  if ((y_attn_out && !aligned16(y_attn_out)) || (y_ssm_out && !aligned16(y_ssm_out))) return HYMBA_EALIGN;
-  const DecodeWs ws = decode_ws(desc);
-  if (!workspace || workspace_bytes < ws.total) return HYMBA_EWORKSPACE;
-  if (((uintptr_t)workspace & 255u) != 0) return HYMBA_EALIGN;
+  if ((c.y_attn_out && !aligned16(c.y_attn_out)) || (c.y_ssm_out && !aligned16(c.y_ssm_out))) return HYMBA_EALIGN;
+  return HYMBA_OK;
+}
 
-  char* wsb = (char*)workspace;
+// splits (partials per query head) a decode launch on this device uses
+hipError_t decode_splits(const hymba_mixer_desc* d, int* n_split) {
+  hymba::AttnDecodeArgs aa = {};
+  aa.batch = d->batch; aa.cap = d->cache_capacity; aa.n_meta = d->n_meta; aa.window = d->window;
+  aa.n_q_heads = d->n_q_heads; aa.n_kv_heads = d->n_kv_heads; aa.head_dim_v = d->head_dim_v; aa.act = d->act;
+  hipError_t e = device_cus(&aa.n_cu);
+  if (e != hipSuccess) return e;
+  *n_split = hymba::decode_active_splits(aa);
+  return hipSuccess;
+}
+
+// The decode step on validated arguments, with its scratch at wsb laid out as
+// ws (room for at least n_split partial slots).
+int decode_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params, const DecodeCall& c, char* wsb,
+                const DecodeWs& ws, int n_split, hipEvent_t* stage_events, hipStream_t stream) {
   float* partial = (float*)(wsb + ws.partial);
-  void* y_ssm = y_ssm_out ? y_ssm_out : (void*)(wsb + ws.y_ssm);
-  void* y_attn = y_attn_out ? y_attn_out : (void*)(wsb + ws.y_attn);
+  void* y_ssm = c.y_ssm_out ? c.y_ssm_out : (void*)(wsb + ws.y_ssm);
+  void* y_attn = c.y_attn_out ? c.y_attn_out : (void*)(wsb + ws.y_attn);
 
   auto tm = [&](int i) -> hymba::Timing {
     hymba::Timing t;
@@ -512,31 +533,106 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
   // (one stream: the step's kernels are a few µs each, and a fork/join across
   // two streams measured ~10 µs slower per call than running them in order)
   hymba::SsmDecodeArgs sa;
-  sa.x = x; sa.z = z; sa.dt = dt; sa.B = B; sa.C = C;
+  sa.x = c.x; sa.z = c.z; sa.dt = c.dt; sa.B = c.B; sa.C = c.C;
   sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
-  sa.state = ssm_state; sa.conv_state = conv_state; sa.y = y_ssm;
+  sa.state = c.ssm_state; sa.conv_state = c.conv_state; sa.y = y_ssm;
   sa.batch = desc->batch; sa.d_inner = desc->d_inner; sa.act = desc->act;
   sa.head_width = desc->ssm_heads > 0 ? desc->d_inner / desc->ssm_heads : 0;
   HYMBA_TRY(hymba::launch_ssm_decode(sa, stream, tm(0)));
 
   hymba::AttnDecodeArgs aa;
-  aa.q = q; aa.k_new = k_new; aa.v_new = v_new; aa.k_cache = k_cache; aa.v_cache = v_cache;
-  aa.cache_len = cache_len; aa.partial = partial; aa.k_scale = params->k_scale;
-  aa.q_rot = (float*)(wsb + ws.q_rot); aa.k_rot = (float*)(wsb + ws.k_rot); aa.n_split = ws.n_split; aa.keys_per_split = ws.keys_per_split;
+  aa.q = c.q; aa.k_new = c.k_new; aa.v_new = c.v_new; aa.k_cache = c.k_cache; aa.v_cache = c.v_cache;
+  aa.cache_len = c.cache_len; aa.partial = partial; aa.k_scale = params->k_scale;
+  aa.q_rot = (float*)(wsb + ws.q_rot); aa.k_rot = (float*)(wsb + ws.k_rot);
+  aa.n_split = n_split; aa.keys_per_split = ws.keys_per_split;
   aa.batch = desc->batch; aa.cap = desc->cache_capacity; aa.n_meta = desc->n_meta; aa.window = desc->window;
   aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
   aa.rope_base = desc->rope_base; aa.act = desc->act; aa.ring = desc->cache_ring;
   HYMBA_TRY(device_cus(&aa.n_cu));
-  aa.n_split = hymba::decode_active_splits(aa);   // <= ws.n_split partial slots
   HYMBA_TRY(hymba::launch_attn_decode(aa, stream, tm(1)));
 
   hymba::DecodeCombineArgs ca;
   ca.partial = partial; ca.y_ssm = y_ssm; ca.beta_attn = params->beta_attn; ca.beta_ssm = params->beta_ssm;
-  ca.eps = desc->norm_eps; ca.y_attn = y_attn; ca.out = out;
-  ca.n_split = aa.n_split; ca.batch = desc->batch; ca.n_q_heads = desc->n_q_heads;
+  ca.eps = desc->norm_eps; ca.y_attn = y_attn; ca.out = c.out;
+  ca.n_split = n_split; ca.batch = desc->batch; ca.n_q_heads = desc->n_q_heads;
   ca.head_dim_v = desc->head_dim_v; ca.act = desc->act;
   HYMBA_TRY(hymba::launch_decode_combine(ca, stream, tm(2)));
   return HYMBA_OK;
+}
+
+// Library-owned scratch of the allocation-free decode entry point: one copy
+// per device, held until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in); it uses the
+// device address hipGetSymbolAddress gives for the current device.
+constexpr size_t kDecodeScratchBytes = (size_t)HYMBA_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up with that
+// device current the first time it is needed there.
+hipError_t scratch_on_device(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = (char*)p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* params, const void* x,
+                       const void* z, const void* dt, const void* B, const void* C, const void* q,
+                       const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
+                       const int32_t* cache_len, float* ssm_state, void* conv_state, void* out, void* y_attn_out,
+                       void* y_ssm_out, void* workspace, size_t workspace_bytes, hipEvent_t* stage_events,
+                       hipStream_t stream) {
+  int st = check_desc(desc, true);
+  if (st != HYMBA_OK) return st;
+  st = check_params(params);
+  if (st != HYMBA_OK) return st;
+  const DecodeCall c = {x, z, dt, B, C, q, k_new, v_new, k_cache, v_cache, cache_len, ssm_state, conv_state,
+                        out, y_attn_out, y_ssm_out};
+  st = check_decode_io(c);
+  if (st != HYMBA_OK) return st;
+  const DecodeWs ws = decode_ws(desc);
+  if (!workspace || workspace_bytes < ws.total) return HYMBA_EWORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HYMBA_EALIGN;
+  int n_split = 0;
+  HYMBA_TRY(decode_splits(desc, &n_split));   // <= ws.n_split partial slots
+  return decode_impl(desc, params, c, (char*)workspace, ws, n_split, stage_events, stream);
+}
+
+int hymba_mixer_decode_noalloc(const hymba_mixer_desc* desc, const hymba_mixer_params* params, const void* x,
+                               const void* z, const void* dt, const void* B, const void* C, const void* q,
+                               const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
+                               const int32_t* cache_len, float* ssm_state, void* conv_state, void* out,
+                               void* y_attn_out, void* y_ssm_out, hipStream_t stream) {
+  int st = check_desc(desc, true);
+  if (st != HYMBA_OK) return st;
+  st = check_params(params);
+  if (st != HYMBA_OK) return st;
+  const DecodeCall c = {x, z, dt, B, C, q, k_new, v_new, k_cache, v_cache, cache_len, ssm_state, conv_state,
+                        out, y_attn_out, y_ssm_out};
+  st = check_decode_io(c);
+  if (st != HYMBA_OK) return st;
+  int n_split = 0;
+  HYMBA_TRY(decode_splits(desc, &n_split));
+  const DecodeWs ws = decode_ws(desc, n_split);   // exactly the splits this launch uses
+  if (ws.total > kDecodeScratchBytes) return HYMBA_EWORKSPACE;
+  char* wsb = nullptr;
+  HYMBA_TRY(scratch_on_device(&wsb));
+  return decode_impl(desc, params, c, wsb, ws, n_split, nullptr, stream);
 }
 
 int hymba_fuse_heads(const void* y_attn, const void* y_ssm, const float* beta_attn, const float* beta_ssm,

@@ -52,6 +52,9 @@ extern "C" {
 #define HYMBA_ABI_VERSION 2
 #define HYMBA_PREFILL_STAGES 6
 #define HYMBA_DECODE_STAGES 3
+/* Bytes of the library-owned device scratch of hymba_mixer_decode_noalloc,
+ * one copy per device that the library runs on. */
+#define HYMBA_DECODE_SCRATCH_BYTES (16u << 20)
 
 typedef enum { HYMBA_F32 = 0, HYMBA_BF16 = 1 } hymba_dtype;
 
@@ -255,6 +258,29 @@ int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* p
                        void* out, void* y_attn_out, void* y_ssm_out,
                        void* workspace, size_t workspace_bytes,
                        hipEvent_t* stage_events, hipStream_t stream);
+
+/* hymba_mixer_decode without a workspace argument and without any device
+ * allocation, for callers that cannot allocate: code under HIP graph capture,
+ * serving loops that forbid hipMalloc, harnesses that manage all memory.
+ * Same arguments, results and in-place updates as hymba_mixer_decode (minus
+ * workspace and stage events); the kernels are the same. Its scratch (split
+ * partials [batch, n_q_heads, n_split, head_dim_v + 2] fp32 for the n_split
+ * splits the launch uses, and the branch outputs the caller does not ask for)
+ * lives in a static device array of HYMBA_DECODE_SCRATCH_BYTES bytes that the
+ * library holds on each device until the process ends. A geometry whose
+ * scratch does not fit returns HYMBA_EWORKSPACE before anything is enqueued
+ * (the decode workload of 64 sequences, 25 query heads of 128 values and a
+ * 1152-key window needs about 5.8 MB). No part of the scratch has to start
+ * at zero: every call writes all of it that it reads. All calls on one device
+ * share the array, so calls that overlap on one device (concurrent streams or
+ * threads) race and give undefined results; calls in one stream order are
+ * safe. The caller still provides every input and output.                */
+int hymba_mixer_decode_noalloc(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
+                               const void* x, const void* z, const void* dt, const void* B, const void* C,
+                               const void* q, const void* k_new, const void* v_new,
+                               const void* k_cache, const void* v_cache, const int32_t* cache_len,
+                               float* ssm_state, void* conv_state,
+                               void* out, void* y_attn_out, void* y_ssm_out, hipStream_t stream);
 
 /* The fusion on its own: for each of n_rows rows of `width` channels,
  *   out = (beta_attn * y_attn / sqrt(mean(y_attn^2) + eps)

@@ -166,6 +166,13 @@ def test_fuse_and_mask_validation(lib):
     d = c1_desc()
     assert lib.hymba_debug_mask_ranges(ctypes.byref(d), None, None) == -1
     assert lib.hymba_debug_mask_ranges(ctypes.byref(d), fake + 4, None) == -3
+    # the allocation-free decode validates its arguments before anything else
+    dd = c1_desc(n_tokens=1)
+    pp = _lib.MixerParams(fake, fake, fake, None, fake, fake)
+    na = lib.hymba_mixer_decode_noalloc
+    assert na(ctypes.byref(dd), ctypes.byref(pp), *([fake] * 13), None, None, None, None) == -1   # out missing
+    assert na(ctypes.byref(dd), ctypes.byref(pp), *([fake] * 13), fake + 4, fake, None, None, None) == -3
+    assert na(None, ctypes.byref(pp), *([fake] * 16), None) == -1
     # the prefill visibility export validates like a prefill call, then its own arguments
     assert lib.hymba_debug_prefill_visibility(ctypes.byref(d), 0, None, None) == -1
     assert lib.hymba_debug_prefill_visibility(ctypes.byref(d), 0, fake + 4, None) == -3
