@@ -60,11 +60,16 @@ class HymbaError(RuntimeError):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the HIP library (once). Raises if it has not been built."""
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built.
+
+    HYMBA_MIXER_LIB names another build of the same library to load instead
+    (the host-sanitizer build that the CPU tests drive)."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = os.environ.get("HYMBA_MIXER_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise ImportError(f"{path} not found: build it first (python -m attention_lm_amd.build)")
     lib = ctypes.CDLL(path)

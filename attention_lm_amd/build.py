@@ -72,6 +72,39 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def sanitizer_runtime_dir() -> str:
+    """Directory of the compiler's AddressSanitizer runtime (for LD_PRELOAD)."""
+    llvm = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "llvm")
+    base = os.path.join(llvm if os.path.isdir(llvm) else "/opt/rocm/llvm", "lib", "clang")
+    for ver in sorted(os.listdir(base), reverse=True):
+        d = os.path.join(base, ver, "lib", "linux")
+        if os.path.exists(os.path.join(d, "libclang_rt.asan-x86_64.so")):
+            return d
+    raise RuntimeError("AddressSanitizer runtime not found")
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """The same library with its host code built under AddressSanitizer and
+    UndefinedBehaviorSanitizer (device code unchanged): for running the
+    host-side argument checks under the sanitizers on a machine without a GPU.
+    Load it with the ASan runtime preloaded. Returns the library path."""
+    cc = hipcc()
+    os.makedirs(out_dir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1", "-g"] + san
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+        list(ex.map(_run, cmds))
+    lib = os.path.join(out_dir, "libhymba_mixer_hostsan.so")
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *san, "-Xarch_host", "-shared-libsan", "-o", lib, *objs])
+    return lib
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)

@@ -3,8 +3,7 @@
 // state update h = exp(dt A) h + dt B u, y = (C . h + D u) silu(z), and the
 // shifted conv history ("Jamba: Hybrid SSM-Transformer", "1. Layer
 // Interleaving Ratio"; "Lecture 04 - Beyond the Dense Transformer", section 2).
-// Shared by the stand-alone decode kernel and the decode attention kernel,
-// which does the step of its sequence's channels alongside the attention.
+// Used by the decode kernel of the Mamba branch (ssm_decode_kernel).
 #pragma once
 
 #include "common.hpp"

@@ -36,6 +36,16 @@
  *    accumulate in fp32; each output is rounded once to its storage type.
  *  - Return value: HYMBA_OK, or a negative hymba_status. HYMBA_EHIP means a
  *    HIP call failed; hymba_last_hip_error() gives its hipError_t (per thread).
+ *  - State kept by the library: the last HIP error (per thread); per calling
+ *    thread and device, a second stream (non-blocking, default priority) and
+ *    two events, created on the first prefill call, on which the Mamba branch
+ *    of a prefill runs beside the attention branch (joined on `stream` before
+ *    the fusion); the compute-unit count of each device, read once; and the
+ *    static scratch of hymba_mixer_decode_noalloc on each device. Nothing else
+ *    persists between calls.
+ *  - Beyond the minimal interface (tensors, sizes, stream), prefill and decode
+ *    take a caller workspace (the library never allocates) and an optional
+ *    array of events that time each stage.
  */
 #ifndef HYMBA_MIXER_H_
 #define HYMBA_MIXER_H_
@@ -56,7 +66,13 @@ extern "C" {
  * one copy per device that the library runs on. */
 #define HYMBA_DECODE_SCRATCH_BYTES (16u << 20)
 
+/* Activation dtype. C++ sees the same 32-bit enum with a fixed underlying
+ * type, so that checking a caller's out-of-range value is well defined. */
+#ifdef __cplusplus
+typedef enum : int32_t { HYMBA_F32 = 0, HYMBA_BF16 = 1 } hymba_dtype;
+#else
 typedef enum { HYMBA_F32 = 0, HYMBA_BF16 = 1 } hymba_dtype;
+#endif
 
 typedef enum {
   HYMBA_OK = 0,
