@@ -402,8 +402,8 @@ __device__ __forceinline__ void vm_wait_at_most(int n) {
 constexpr int kScanChan = 32;
 constexpr int kScanRows = 8;
 constexpr int kScanPairs = kStates / 2;
-constexpr int kScanStages = 4;
-constexpr int kScanRowsLoaded = 4;   // rows of phase B whose LDS values are in registers at once     // staging ring: three blocks in flight ahead of the one in use
+constexpr int kScanStages = 4;       // staging ring: three blocks in flight ahead of the one in use
+constexpr int kScanRowsLoaded = 4;   // rows of phase B whose LDS values are in registers at once
 static_assert(kScanChan * kScanRows == 256 && kScanChan * kScanPairs == 256, "one lane per item");
 
 template <typename T>
@@ -453,31 +453,41 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
   const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + seq * Dch, (uint32_t)L * row_b);
   const uint32_t col_b = (uint32_t)(c0 * sizeof(T));
 
-  // one array of a block: n 16-byte pieces, piece i at LDS dst + 16 i, loaded by
-  // one wave (lane i of each instruction writes dst + 16 (i0 + i))
-  auto load_array = [&](__amdgpu_buffer_rsrc_t rs, int n, char* dst, auto off) {
-    for (int i0 = 0; i0 < n; i0 += 64)
-      if (i0 + lane < n) buf_load16_lds(rs, off(i0 + lane), dst + 16 * i0);
-  };
+  // One array of a block: n 16-byte pieces, piece i at LDS dst + 16 i, loaded
+  // by one wave (lane i of each instruction writes dst + 16 (i0 + i)). A
+  // piece's byte offset is its block-independent part (row within the block,
+  // column), computed once per lane, plus the block's first row times the row
+  // stride, one scalar per block; uint32 arithmetic, so the rows before 0 wrap
+  // past the end of the descriptor and read zero.
+  constexpr int NXP = (R + kConv - 1) * CP, NDP = R * CP, NBP = R * SP;
+  constexpr int NXI = (NXP + 63) / 64;   // load instructions for x
+  static_assert((NDP + 63) / 64 == 1 && (NBP + 63) / 64 == 1, "dt, z, B, C pieces fit one instruction each");
+  uint32_t xo[NXI];
+#pragma unroll
+  for (int k = 0; k < NXI; ++k) {
+    const int it = 64 * k + lane;
+    xo[k] = (uint32_t)(it / CP) * row_b + col_b + (uint32_t)(16 * (it % CP));
+  }
+  const uint32_t dzo = (uint32_t)(lane / CP) * row_b + col_b + (uint32_t)(16 * (lane % CP));
+  const uint32_t bco = (uint32_t)(16 * lane);
   auto fetch = [&](int tb, Scan1Stage<T>& s) {
-    if (wave == 0)
-      load_array(xrs, (R + kConv - 1) * CP, (char*)&s.x[0][0], [&](int it) {
-        return (uint32_t)(tb - (kConv - 1) + it / CP) * row_b + col_b + (uint32_t)(16 * (it % CP));
-      });
-    if (wave == 1)
-      load_array(drs, R * CP, (char*)&s.dt[0][0], [&](int it) {
-        return (uint32_t)(tb + it / CP) * row_b + col_b + (uint32_t)(16 * (it % CP));
-      });
-    if (wave == 2)
-      load_array(zrs, R * CP, (char*)&s.z[0][0], [&](int it) {
-        return (uint32_t)(tb + it / CP) * row_b + col_b + (uint32_t)(16 * (it % CP));
-      });
-    if (wave == 3) {
-      auto off = [&](int it) { return (uint32_t)((tb * kStates) * (int)sizeof(T) + 16 * it); };
-      load_array(brs, R * SP, (char*)&s.b[0][0], off);
-      load_array(crs, R * SP, (char*)&s.c[0][0], off);
+    if (wave == 0) {
+      const uint32_t base = (uint32_t)(tb - (kConv - 1)) * row_b;
+#pragma unroll
+      for (int k = 0; k < NXI; ++k)
+        if (64 * k + lane < NXP) buf_load16_lds(xrs, xo[k] + base, (char*)&s.x[0][0] + 16 * 64 * k);
+    } else if (wave < 3) {
+      const uint32_t base = (uint32_t)tb * row_b;
+      if (lane < NDP) buf_load16_lds(wave == 1 ? drs : zrs, dzo + base, wave == 1 ? (char*)&s.dt[0][0] : (char*)&s.z[0][0]);
+    } else {
+      const uint32_t base = (uint32_t)(tb * kStates * (int)sizeof(T));
+      if (lane < NBP) {
+        buf_load16_lds(brs, bco + base, (char*)&s.b[0][0]);
+        buf_load16_lds(crs, bco + base, (char*)&s.c[0][0]);
+      }
     }
   };
+  const uint32_t yo = (uint32_t)sp * row_b + (uint32_t)(c * sizeof(T));   // phase C: this lane's row, channel
 
   float a0 = A[(int64_t)cc * kStates + 2 * sp] * kLog2e;
   float a1 = A[(int64_t)cc * kStates + 2 * sp + 1] * kLog2e;
@@ -500,9 +510,7 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
   // instructions per block) and one y store per finished block, at most
   // kScanStages - 1 of them in flight; vmcnt drains in issue order, so waiting
   // until that many remain means block ib's loads have landed.
-  const int n_ld = wave == 0 ? (R + kConv - 1) * CP / 64 + ((R + kConv - 1) * CP % 64 != 0)
-                   : wave < 3 ? (R * CP + 63) / 64
-                              : 2 * ((R * SP + 63) / 64);
+  const int n_ld = wave == 0 ? NXI : wave < 3 ? 1 : 2;   // load instructions of this wave per block
   const int nblk = (L + R - 1) / R;
 #pragma unroll
   for (int k = 0; k < kScanStages - 1; ++k) fetch(k * R, stage[k]);
@@ -559,8 +567,7 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
 #pragma unroll
       for (int p = 0; p < kScanPairs; ++p) acc += part[sp][p][cl];
       const float g = acc * silu(to_f32(s.z[sp][cl]));
-      const uint32_t off = cv ? (uint32_t)(ib * R + sp) * row_b + (uint32_t)(c * sizeof(T)) : kBufferNowhere;
-      buf_store(yrs, off, from_f32<T>(g));
+      buf_store(yrs, cv ? yo + (uint32_t)(ib * R) * row_b : kBufferNowhere, from_f32<T>(g));
     }
   }
   // the prefetches past the sequence land before the workgroup's LDS is released
