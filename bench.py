@@ -279,7 +279,7 @@ def traffic_for(kernel, workload):
 COUNTER_KERNELS = {
     "ssm_chunk_end": ("ssm_chunk_kernel<hymba::bf16, false>",),
     "ssm_chunk_carry": ("ssm_chunk_carry_kernel",),
-    "ssm_chunk_out": ("ssm_chunk_kernel<hymba::bf16, true>",),
+    "ssm_chunk_out": ("ssm_chunk_kernel<hymba::bf16, true>", "ssm_scan1_kernel<hymba::bf16>"),
     "rope_prefill": ("rope_prefill_kernel<hymba::bf16>",),
     "attn_prefill": ("attn_prefill_kernel<hymba::bf16",),
     "fuse": ("fuse_rows_kernel<hymba::bf16",),
@@ -326,6 +326,69 @@ def summarize_counters(fetch_csv, write_csv, calib_mib, command):
             "calibration": {"copy_MiB": calib_mib, "fetch_KiB_per_true_KiB": round(ffac, 4),
                             "write_KiB_per_true_KiB": round(wfac, 4)},
             "kernels": kernels}
+
+
+COMPUTE_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU_TRANS_F32",
+                    "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES",
+                    "GRBM_GUI_ACTIVE"]
+N_SIMD = 256 * 4
+
+
+def summarize_compute(csv_path, command):
+    """Per-kernel compute counters from one rocprofv3 --pmc pass over
+    COMPUTE_COUNTERS (values summed over the chip per dispatch): MFMA busy
+    fraction of the SIMDs' cycles, cycles in which MFMA and other VALU work
+    ran together, and instructions per launch (transcendental = v_exp_f32,
+    v_rcp_f32 and the like)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        name = r["Kernel_Name"]
+        key = None
+        for k, pats in COUNTER_KERNELS.items():
+            if any(p in name for p in pats):
+                key = k
+        if key is None:
+            continue
+        d = per.setdefault(key, {}).setdefault(r.get("Dispatch_Id", r.get("Correlation_Id")), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for key, disp in per.items():
+        rows = [v for v in disp.values() if all(c in v for c in COMPUTE_COUNTERS)]
+        if not rows:
+            continue
+        avg = {c: sum(v[c] for v in rows) / len(rows) for c in COMPUTE_COUNTERS}
+        act = avg["GRBM_GUI_ACTIVE"] * N_SIMD
+        out[key] = {
+            "dispatches": len(rows),
+            "gpu_active_cycles": round(avg["GRBM_GUI_ACTIVE"]),
+            "mfma_busy_frac": round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / act, 4) if act else None,
+            "mfma_valu_coexec_frac": round(avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / act, 4) if act else None,
+            "trans_f32_insts_per_launch": round(avg["SQ_INSTS_VALU_TRANS_F32"]),
+            "valu_insts_per_launch": round(avg["SQ_INSTS_VALU"]),
+            "mfma_insts_per_launch": round(avg["SQ_INSTS_MFMA"]),
+            "salu_insts_per_launch": round(avg["SQ_INSTS_SALU"]),
+            "wait_inst_any_frac_of_wave_cycles": round(avg["SQ_WAIT_INST_ANY"] / avg["SQ_WAVE_CYCLES"], 4)
+            if avg["SQ_WAVE_CYCLES"] else None,
+        }
+    return {"source_hash": source_hash(), "command": command, "counters": COMPUTE_COUNTERS, "kernels": out}
+
+
+def summarize_trace(stats_csv, title, command):
+    """Markdown table of a rocprofv3 --kernel-trace --stats summary."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# Kernel trace: {title}", "", "Command (repository root, one MI355X):", "", "```", command, "```", "",
+             f"Kernel sources: {source_hash()} (bench.py source_hash).", "",
+             "| kernel | calls | avg µs | min µs | max µs | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        name = r["Name"].split("(")[0]
+        if len(name) > 90:
+            name = name[:90]
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    return "\n".join(lines) + "\n"
 
 
 # ---------------------------------------------------------------------------
@@ -591,7 +654,18 @@ def main():
                     help="print per-kernel HBM bytes from two rocprofv3 --pmc counter CSVs (FETCH_SIZE, "
                          "WRITE_SIZE) of a run with --copy-calibration, and exit")
     ap.add_argument("--counter-command", default="", help="the command that produced the counter CSVs (recorded)")
+    ap.add_argument("--summarize-compute", metavar="CSV",
+                    help="print per-kernel compute counters (MFMA busy, transcendental and VALU instructions) from "
+                         "one rocprofv3 --pmc pass over the COMPUTE_COUNTERS list, and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "TITLE"),
+                    help="print a markdown table of a rocprofv3 --kernel-trace --stats summary, and exit")
     args = ap.parse_args()
+    if args.summarize_compute:
+        print(json.dumps(summarize_compute(args.summarize_compute, args.counter_command), indent=1))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.counter_command), end="")
+        return
     if args.summarize_counters:
         if not args.copy_calibration:
             ap.error("--summarize-counters needs the --copy-calibration size the counted run used")
