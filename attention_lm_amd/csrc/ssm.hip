@@ -435,11 +435,18 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cl = tid & (kScanChan - 1);         // channel within the block (all phases)
   const int sp = tid >> 5;                      // phase B: state pair; phases A, C: row of the block
-  const int c0 = blockIdx.x * kScanChan;
+  // Workgroups go to the chip's 8 XCDs in turn by launch index, and each XCD
+  // has its own L2. The two channel blocks that share a 128-byte line of x, dt
+  // and z get launch indices 8 apart, so they run on one XCD at about the same
+  // time and the line comes from HBM once.
+  const int nblk_c = (Dch + kScanChan - 1) / kScanChan;
+  int id = (int)blockIdx.x;
+  if (id < (int)gridDim.x / 16 * 16) id = id / 16 * 16 + (id % 8) * 2 + (id % 16) / 8;
+  const int c0 = (id % nblk_c) * kScanChan;
   const int c = c0 + cl;
   const bool cv = c < Dch;
   const int cc = cv ? c : Dch - 1;
-  const int64_t b = blockIdx.y;
+  const int64_t b = id / nblk_c;
   const int64_t seq = b * L;
   const uint32_t row_b = (uint32_t)(Dch * sizeof(T));
   // x over rows [0, L): a row index below 0 wraps past the end and reads zero
@@ -634,7 +641,7 @@ hipError_t chunk_out_t(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
 
 template <typename T>
 hipError_t scan1_t(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
-  const dim3 grid((unsigned)((a.d_inner + kScanChan - 1) / kScanChan), (unsigned)a.batch);
+  const dim3 grid((unsigned)((a.d_inner + kScanChan - 1) / kScanChan * a.batch));   // (channel block, sequence)
   HYMBA_LAUNCH(ssm_scan1_kernel<T>, grid, dim3(256), 0, stream, tm, (const T*)a.x, (const T*)a.z, (const T*)a.dt,
                (const T*)a.B, (const T*)a.C, a.A, a.D, a.conv_w, (const T*)a.conv_in, a.state_in, (T*)a.y,
                a.state_out, (T*)a.conv_state_out, a.L, a.d_inner);

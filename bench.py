@@ -293,7 +293,10 @@ def summarize_counters(fetch_csv, write_csv, calib_mib, command):
     """HBM bytes per launch of each kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each divided by what the
     same counter reads per KiB for the plain device copy of calib_mib MiB that
-    the same command ran (the largest copy dispatch)."""
+    the same command ran (the largest runtime copy dispatch). On gfx950 the
+    memory side serves reads as 128-byte requests, which FETCH_SIZE counts as
+    64 bytes: the copy reads 0.5 KiB per true KiB, and every kernel's reads are
+    scaled by that factor."""
     import csv
 
     def per_kernel(path, counter):
@@ -302,7 +305,7 @@ def summarize_counters(fetch_csv, write_csv, calib_mib, command):
             if r["Counter_Name"] != counter:
                 continue
             name, v = r["Kernel_Name"], float(r["Counter_Value"])
-            if "copyBuffer" in name or "direct_copy" in name:
+            if "__amd_rocclr_copyBuffer" in name:   # the runtime's device copy (hipMemcpy blit)
                 copies.append(v)
             for key, pats in COUNTER_KERNELS.items():
                 if any(p in name for p in pats):
@@ -382,7 +385,7 @@ def summarize_trace(stats_csv, title, command):
              f"Kernel sources: {source_hash()} (bench.py source_hash).", "",
              "| kernel | calls | avg µs | min µs | max µs | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
     for r in rows:
-        name = r["Name"].split("(")[0]
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
         if len(name) > 90:
             name = name[:90]
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -688,7 +691,9 @@ def main():
     legs = args.only or ALL_LEGS
     if args.copy_calibration:
         n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        # float32 elements: the copy moves 16-byte vectors per thread, the access
+        # width of this library's kernels
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
