@@ -544,15 +544,29 @@ struct PrefillIndex {
     const int nxb = (Lq + P - 1) / P;
     const int hb_n = Hkv * batch;
     const int n_items = nxb * hb_n;
-    int rank = wg;
-    if (n_items > n_cu && n_items <= 2 * n_cu) {
-      const int n_pair = n_items - n_cu, n_single = n_cu - n_pair;
-      if (wg < n_cu) rank = wg < n_pair ? n_single + wg : wg - n_pair;
-      else rank = n_items - 1 - (wg - n_cu);
+    int pb, hb;
+    const int n_xcd = n_cu / 32;   // 32 CUs per XCD
+    if (n_items > 2 * n_cu && n_xcd > 1 && hb_n % n_xcd == 0) {
+      // Many rounds of workgroups: launch index wg runs on XCD wg % n_xcd (each
+      // XCD has its own L2). XCD x takes the (sequence, kv head) streams
+      // x, x + n_xcd, .. one after another, each from its last position block
+      // down, so the workgroups it holds at once are neighbouring blocks of one
+      // or two streams and share their keys and values in its L2.
+      const int x = wg % n_xcd, k = wg / n_xcd;
+      hb = x + n_xcd * (k / nxb);
+      pb = nxb - 1 - k % nxb;
+    } else {
+      int rank = wg;
+      if (n_items > n_cu && n_items <= 2 * n_cu) {
+        const int n_pair = n_items - n_cu, n_single = n_cu - n_pair;
+        if (wg < n_cu) rank = wg < n_pair ? n_single + wg : wg - n_pair;
+        else rank = n_items - 1 - (wg - n_cu);
+      }
+      pb = nxb - 1 - rank / hb_n;
+      hb = rank % hb_n;
     }
-    const int pb = nxb - 1 - rank / hb_n;
-    g = (rank % hb_n) % Hkv;
-    b = (rank % hb_n) / Hkv;
+    g = hb % Hkv;
+    b = hb / Hkv;
     p0 = q_pos0 + pb * P;
     p1 = min(p0 + P, L);
     const int col = 32 * wave + (lane & 31);
