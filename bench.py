@@ -335,11 +335,13 @@ COMPUTE_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "S
                     "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES",
                     "GRBM_GUI_ACTIVE"]
 N_SIMD = 256 * 4
+N_XCD = 8
 
 
 def summarize_compute(csv_path, command):
     """Per-kernel compute counters from one rocprofv3 --pmc pass over
-    COMPUTE_COUNTERS (values summed over the chip per dispatch): MFMA busy
+    COMPUTE_COUNTERS (values summed over the chip per dispatch; the GPU-active
+    cycle count is summed over the 8 XCDs, so it is divided by 8): MFMA busy
     fraction of the SIMDs' cycles, cycles in which MFMA and other VALU work
     ran together, and instructions per launch (transcendental = v_exp_f32,
     v_rcp_f32 and the like)."""
@@ -361,10 +363,11 @@ def summarize_compute(csv_path, command):
         if not rows:
             continue
         avg = {c: sum(v[c] for v in rows) / len(rows) for c in COMPUTE_COUNTERS}
-        act = avg["GRBM_GUI_ACTIVE"] * N_SIMD
+        cycles = avg["GRBM_GUI_ACTIVE"] / N_XCD   # reported summed over the XCDs
+        act = cycles * N_SIMD
         out[key] = {
             "dispatches": len(rows),
-            "gpu_active_cycles": round(avg["GRBM_GUI_ACTIVE"]),
+            "gpu_active_cycles": round(cycles),
             "mfma_busy_frac": round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / act, 4) if act else None,
             "mfma_valu_coexec_frac": round(avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / act, 4) if act else None,
             "trans_f32_insts_per_launch": round(avg["SQ_INSTS_VALU_TRANS_F32"]),
