@@ -602,8 +602,12 @@ struct PrefillIndex {
   }
 };
 
-template <typename T, int DV>
-__global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
+// OCC: waves per SIMD the register allocation aims for. Three (bf16) when
+// there are many rounds of workgroups (the latency of one wave's tile chain is
+// hidden better), else two: the work order for one or two rounds places two
+// workgroups per CU.
+template <typename T, int DV, int OCC>
+__global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(OCC))) void attn_prefill_kernel(
     const T* __restrict__ q_rot, const T* __restrict__ k_rot, const T* __restrict__ v, T* __restrict__ y,
     int64_t k_rows, int64_t v_rows, int Lq, int q_pos0, int n_meta, int window, int Hq, int Hkv, int batch,
     int n_cu) {
@@ -679,14 +683,22 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
     stage.fetch(tile_j0(idx + 1), nxt);
     if (!(none_for(jt) && none_for(jt + 32))) {
       // K operands of both sub-tiles, then both score products
-      Frag kf[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) kf[c] = stage.kfrag(cur, c);
+      // (the K operands of one sub-tile at a time: fewer live registers)
       f32x16_t s0 = st.negm, s1 = st.negm;
+      {
+        Frag kf[4];
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) s0 = M::mma(kf[kc], qf[kc], s0);
+        for (int c = 0; c < 4; ++c) kf[c] = stage.kfrag(cur, c);
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) s1 = M::mma(kf[4 + kc], qf[kc], s1);
+        for (int kc = 0; kc < 4; ++kc) s0 = M::mma(kf[kc], qf[kc], s0);
+      }
+      {
+        Frag kf[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kf[c] = stage.kfrag(cur, 4 + c);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) s1 = M::mma(kf[kc], qf[kc], s1);
+      }
       // a sub-tile that some column sees only in part is masked (one that no
       // column of the wave sees ends up all -inf and adds nothing)
       if (!full_for(jt)) mask_scores(s0, lk, jt, hh, n_meta);
@@ -706,28 +718,21 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_prefill_kernel(
       if (__any(t > st.thr)) st.rescale(t, s0, &s1);
       // P of the first sub-tile and its V product, which runs while the second
       // sub-tile's P is formed
-      Frag va[NDB][2], pa, pb;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        va[d][0] = stage.vfrag(cur, d, 0);
-        va[d][1] = stage.vfrag(cur, d, 16);
-      }
+      // (the V operands of one dv block at a time)
+      Frag pa, pb;
       probs(s0, pa, pb);
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
-        st.acc[d] = M::mma(va[d][0], pa, st.acc[d]);
-        st.acc[d] = M::mma(va[d][1], pb, st.acc[d]);
-      }
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        va[d][0] = stage.vfrag(cur, d, 32);
-        va[d][1] = stage.vfrag(cur, d, 48);
+        const Frag v0 = stage.vfrag(cur, d, 0), v1 = stage.vfrag(cur, d, 16);
+        st.acc[d] = M::mma(v0, pa, st.acc[d]);
+        st.acc[d] = M::mma(v1, pb, st.acc[d]);
       }
       probs(s1, pa, pb);
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
-        st.acc[d] = M::mma(va[d][0], pa, st.acc[d]);
-        st.acc[d] = M::mma(va[d][1], pb, st.acc[d]);
+        const Frag v0 = stage.vfrag(cur, d, 32), v1 = stage.vfrag(cur, d, 48);
+        st.acc[d] = M::mma(v0, pa, st.acc[d]);
+        st.acc[d] = M::mma(v1, pb, st.acc[d]);
       }
     }
     stage.stash(nxt);
@@ -1479,10 +1484,24 @@ template <typename T, int DV>
 hipError_t attn_prefill_t(const AttnPrefillArgs& a, hipStream_t stream, Timing tm) {
   const int G = a.n_q_heads / a.n_kv_heads;
   const int P = kAttnCols / G;   // positions per workgroup
-  const int64_t n_items = (int64_t)((a.L + P - 1) / P) * a.n_kv_heads * a.batch;
-  HYMBA_LAUNCH((attn_prefill_kernel<T, DV>), dim3((unsigned)n_items), dim3(64 * kAttnWaves), 0, stream, tm,
-                     (const T*)a.q_rot, (const T*)a.k_rot, (const T*)a.v, (T*)a.y, a.k_rows, a.v_rows, a.L, a.q_pos0,
-                     a.n_meta, a.window, a.n_q_heads, a.n_kv_heads, a.batch, a.n_cu);
+  const int64_t hb_n = (int64_t)a.n_kv_heads * a.batch;
+  const int64_t n_items = (int64_t)((a.L + P - 1) / P) * hb_n;
+  const int n_xcd = a.n_cu / 32;
+  // the XCD-major order of PrefillIndex (many rounds of workgroups)
+  const bool many = n_items > 2 * (int64_t)a.n_cu && n_xcd > 1 && hb_n % n_xcd == 0;
+#define HYMBA_ATTN_PREFILL(OCC)                                                                                   \
+  HYMBA_LAUNCH((attn_prefill_kernel<T, DV, OCC>), dim3((unsigned)n_items), dim3(64 * kAttnWaves), 0, stream, tm, \
+               (const T*)a.q_rot, (const T*)a.k_rot, (const T*)a.v, (T*)a.y, a.k_rows, a.v_rows, a.L, a.q_pos0,   \
+               a.n_meta, a.window, a.n_q_heads, a.n_kv_heads, a.batch, a.n_cu)
+  if constexpr (sizeof(T) == 2) {
+    if (many)
+      HYMBA_ATTN_PREFILL(3);
+    else
+      HYMBA_ATTN_PREFILL(2);
+  } else {
+    HYMBA_ATTN_PREFILL(1);
+  }
+#undef HYMBA_ATTN_PREFILL
   return hipGetLastError();
 }
 
