@@ -286,6 +286,8 @@ COUNTER_KERNELS = {
     "ssm_decode": ("ssm_decode_kernel<hymba::bf16>",),
     "attn_decode": ("attn_decode_wave_kernel",),
     "decode_merge_fuse": ("decode_combine_kernel<hymba::bf16",),
+    "ssd_state": ("ssd_state_kernel",),
+    "ssd_out": ("ssd_out_kernel",),
 }
 
 
