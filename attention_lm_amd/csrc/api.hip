@@ -405,8 +405,10 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
   }
   if (fc) HYMBA_TRY(hipStreamWaitEvent(stream, fc->join, 0));
 
+  int n_cu = 0;
+  HYMBA_TRY(device_cus(&n_cu));
   HYMBA_TRY(hymba::launch_fuse(y_attn, y_ssm, params->beta_attn, params->beta_ssm, (int64_t)desc->batch * L,
-                               desc->d_inner, desc->norm_eps, desc->act, c.out, stream, tm(5)));
+                               desc->d_inner, desc->norm_eps, desc->act, c.out, stream, tm(5), n_cu));
   return HYMBA_OK;
 }
 
@@ -530,15 +532,22 @@ int decode_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params, 
     }
     return t;
   };
-  // (one stream: the step's kernels are a few µs each, and a fork/join across
-  // two streams measured ~10 µs slower per call than running them in order)
+  // One stream. In bf16 the Mamba step runs inside the attention launch, as
+  // workgroups of its own (its stage records its events back to back): the
+  // step's state traffic then overlaps the cache stream, where a launch of
+  // its own ran before the attention, and a fork/join across two streams
+  // measured ~10 µs slower per call than running the kernels in order.
   hymba::SsmDecodeArgs sa;
   sa.x = c.x; sa.z = c.z; sa.dt = c.dt; sa.B = c.B; sa.C = c.C;
   sa.A = params->A; sa.D = params->D; sa.conv_w = params->conv_w;
   sa.state = c.ssm_state; sa.conv_state = c.conv_state; sa.y = y_ssm;
   sa.batch = desc->batch; sa.d_inner = desc->d_inner; sa.act = desc->act;
   sa.head_width = desc->ssm_heads > 0 ? desc->d_inner / desc->ssm_heads : 0;
-  HYMBA_TRY(hymba::launch_ssm_decode(sa, stream, tm(0)));
+  const bool fused = desc->act == HYMBA_BF16;
+  if (fused)
+    HYMBA_TRY(hymba::no_kernel(stream, tm(0)));
+  else
+    HYMBA_TRY(hymba::launch_ssm_decode(sa, stream, tm(0)));
 
   hymba::AttnDecodeArgs aa;
   aa.q = c.q; aa.k_new = c.k_new; aa.v_new = c.v_new; aa.k_cache = c.k_cache; aa.v_cache = c.v_cache;
@@ -548,6 +557,7 @@ int decode_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params, 
   aa.batch = desc->batch; aa.cap = desc->cache_capacity; aa.n_meta = desc->n_meta; aa.window = desc->window;
   aa.n_q_heads = desc->n_q_heads; aa.n_kv_heads = desc->n_kv_heads; aa.head_dim_v = desc->head_dim_v;
   aa.rope_base = desc->rope_base; aa.act = desc->act; aa.ring = desc->cache_ring;
+  aa.ssm = fused ? &sa : nullptr;
   HYMBA_TRY(device_cus(&aa.n_cu));
   HYMBA_TRY(hymba::launch_attn_decode(aa, stream, tm(1)));
 
@@ -643,7 +653,10 @@ int hymba_fuse_heads(const void* y_attn, const void* y_ssm, const float* beta_at
   if (!y_attn || !y_ssm || !beta_attn || !beta_ssm || !out) return HYMBA_EINVAL;
   if (!aligned16(y_attn) || !aligned16(y_ssm) || !aligned16(beta_attn) || !aligned16(beta_ssm) || !aligned16(out))
     return HYMBA_EALIGN;
-  return hip_status(hymba::launch_fuse(y_attn, y_ssm, beta_attn, beta_ssm, n_rows, width, eps, act, out, stream));
+  int n_cu = 0;
+  HYMBA_TRY(device_cus(&n_cu));
+  return hip_status(hymba::launch_fuse(y_attn, y_ssm, beta_attn, beta_ssm, n_rows, width, eps, act, out, stream, {},
+                                       n_cu));
 }
 
 int hymba_debug_mask_ranges(const hymba_mixer_desc* desc, int32_t* ranges, hipStream_t stream) {

@@ -9,6 +9,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -1006,13 +1007,42 @@ constexpr int kMaxGroupFlash = 8;   // query heads per kv head (larger groups ar
 // (o, m, l) per split as the other decode kernels.
 constexpr int kWaveTile = 32;   // keys per tile
 
+// The decode step of the Mamba branch (ssm_step.hpp) as done by the extra
+// workgroups of the attention launch: wave r of R for sequence b takes the
+// channels r * 16 + i * R * 16 .. + 15 (one lane quad each), kSsmRoleItems
+// of them per lane quad with all their loads in flight together. The step
+// reads and rewrites the fp32 state while the attention workgroups stream
+// the cache, instead of in a launch of its own before them.
+constexpr int kSsmRoleItems = 4;
+constexpr int kDecodeSsmReserve = 2;   // wave slots per CU the split plan leaves to them
+__device__ __forceinline__ void decode_ssm_role(const ssm_step::Ptrs<bf16>& p, int r, int R, int64_t b) {
+  const int q = threadIdx.x & 3, quad = threadIdx.x >> 2;
+  const int stride = R * 16;
+  for (int c0 = r * 16; c0 < p.d_inner; c0 += kSsmRoleItems * stride) {   // wave-uniform
+    ssm_step::Item<bf16> it[kSsmRoleItems];
+#pragma unroll
+    for (int k = 0; k < kSsmRoleItems; ++k) {
+      const int c = c0 + k * stride + quad;
+      const bool ok = c < p.d_inner;   // the same for the whole quad
+      ssm_step::load(p, it[k], b, ok ? c : 0, q, ok);
+    }
+#pragma unroll
+    for (int k = 0; k < kSsmRoleItems; ++k) ssm_step::finish(p, it[k], q);
+  }
+}
+
 template <int DV, bool RING>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_decode_wave_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_new, const bf16* __restrict__ v_new,
     const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
     float* __restrict__ partial, const float* __restrict__ k_scale, int n_split, int cap, int n_meta, int window,
-    int Hq, int Hkv, double freq_step) {
+    int Hq, int Hkv, double freq_step, ssm_step::Ptrs<bf16> ssm) {
+  if ((int)blockIdx.x >= n_split) {   // a workgroup of the Mamba step (see decode_ssm_role)
+    decode_ssm_role(ssm, ((int)blockIdx.x - n_split) * (int)gridDim.y + (int)blockIdx.y,
+                    ((int)gridDim.x - n_split) * (int)gridDim.y, blockIdx.z);
+    return;
+  }
   typedef Mma<bf16> M;
   constexpr int KROWB = kHd * 2, VROWB = DV * 2;        // bytes per K / V row
   constexpr int VCH = VROWB / 16;                       // 16-byte chunks per V row
@@ -1511,18 +1541,33 @@ hipError_t attn_decode_t(const AttnDecodeArgs& a, hipStream_t stream, Timing tm)
   t_first.start = tm.start;
   t_last.stop = tm.stop;
   if constexpr (sizeof(T) == 2) {
-    // rotation inside the attention kernel: one launch for the stage
+    // rotation inside the attention kernel: one launch for the stage, with
+    // the Mamba step's workgroups (if any) after each (kv head, sequence)'s
+    // splits: as many per (kv head, sequence) as the wave slots the attention
+    // leaves free hold (at least one), so that the whole grid is resident
     const double freq_step = std::pow((double)a.rope_base, -2.0 / kHd);
+    int ssm_x = 0;
+    ssm_step::Ptrs<bf16> sp = {};
+    if (a.ssm) {
+      sp = ssm_step_ptrs<bf16>(*a.ssm);
+      const int64_t rows = (int64_t)a.batch * a.n_kv_heads;
+      const int64_t slots = decode_wave_slots_per_cu(DV) * (int64_t)a.n_cu;
+      ssm_x = (int)std::max<int64_t>(1, (slots - (int64_t)a.n_split * rows) / std::max<int64_t>(1, rows));
+      // (no more waves per sequence than 16-channel groups)
+      const int64_t groups = ((int64_t)a.ssm->d_inner + 15) / 16;
+      ssm_x = (int)std::min<int64_t>(ssm_x, std::max<int64_t>(1, (groups + a.n_kv_heads - 1) / a.n_kv_heads));
+    }
+    const dim3 grid((unsigned)(a.n_split + ssm_x), (unsigned)a.n_kv_heads, (unsigned)a.batch);
     if (a.ring)
-      HYMBA_LAUNCH((attn_decode_wave_kernel<DV, true>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(64), 0, stream,
-                   tm, (const bf16*)a.q, (const bf16*)a.k_new, (const bf16*)a.v_new, (const bf16*)a.k_cache,
-                   (const bf16*)a.v_cache, a.cache_len, a.partial, a.k_scale, a.n_split, a.cap, a.n_meta, a.window,
-                   a.n_q_heads, a.n_kv_heads, freq_step);
+      HYMBA_LAUNCH((attn_decode_wave_kernel<DV, true>), grid, dim3(64), 0, stream, tm, (const bf16*)a.q,
+                   (const bf16*)a.k_new, (const bf16*)a.v_new, (const bf16*)a.k_cache, (const bf16*)a.v_cache,
+                   a.cache_len, a.partial, a.k_scale, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads,
+                   a.n_kv_heads, freq_step, sp);
     else
-      HYMBA_LAUNCH((attn_decode_wave_kernel<DV, false>), dim3(a.n_split, a.n_kv_heads, a.batch), dim3(64), 0,
-                   stream, tm, (const bf16*)a.q, (const bf16*)a.k_new, (const bf16*)a.v_new, (const bf16*)a.k_cache,
-                   (const bf16*)a.v_cache, a.cache_len, a.partial, a.k_scale, a.n_split, a.cap, a.n_meta, a.window,
-                   a.n_q_heads, a.n_kv_heads, freq_step);
+      HYMBA_LAUNCH((attn_decode_wave_kernel<DV, false>), grid, dim3(64), 0, stream, tm, (const bf16*)a.q,
+                   (const bf16*)a.k_new, (const bf16*)a.v_new, (const bf16*)a.k_cache, (const bf16*)a.v_cache,
+                   a.cache_len, a.partial, a.k_scale, a.n_split, a.cap, a.n_meta, a.window, a.n_q_heads,
+                   a.n_kv_heads, freq_step, sp);
     return hipGetLastError();
   }
   const int64_t n = (int64_t)a.batch * (a.n_q_heads + a.n_kv_heads) * (kHd / 2);
@@ -1597,6 +1642,34 @@ static int64_t decode_max_visible(int n_meta, int window, int cap) {
   return max_vis;
 }
 
+// waves (one-wave workgroups) of the bf16 decode kernel that one CU holds,
+// as the runtime's occupancy query gives them for its registers and LDS;
+// asked once per value width (the same code object serves every device)
+template <int DV>
+int decode_wave_slots_t() {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int per_cu_blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_blocks, attn_decode_wave_kernel<DV, false>, 64, 0) !=
+          hipSuccess ||
+      per_cu_blocks < 1) {
+    (void)hipGetLastError();   // fall back to the LDS bound
+    const int stage = kWaveTile * DV * 2;
+    per_cu_blocks = std::max(1, (160 * 1024) / (2 * stage + 1536));
+  }
+  cached.store(per_cu_blocks, std::memory_order_relaxed);
+  return per_cu_blocks;
+}
+
+int decode_wave_slots_per_cu(int dv) {
+  switch (dv) {
+    case 32: return decode_wave_slots_t<32>();
+    case 64: return decode_wave_slots_t<64>();
+    default: return decode_wave_slots_t<128>();
+  }
+}
+
 void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_per_split) {
   // room for one partial per 32-key tile: the most splits any launch uses
   const int64_t max_vis = decode_max_visible(n_meta, window, cap);
@@ -1611,8 +1684,9 @@ int decode_active_splits(const AttnDecodeArgs& a) {
   // one wave per split, all resident at once: eight waves per CU (more were
   // measured no faster: the step is bound by the memory system), fewer where
   // the two V stages of a wave run short of LDS
-  const int64_t stage = (int64_t)kWaveTile * a.head_dim_v * 2;
-  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / (2 * stage + 1536)));
+  // (less the slots left to the Mamba step's workgroups of the same launch)
+  const int64_t per_cu =
+      std::max<int64_t>(1, std::min<int64_t>(8, decode_wave_slots_per_cu(a.head_dim_v)) - kDecodeSsmReserve);
   const int64_t tiles = (max_vis + kWaveTile - 1) / kWaveTile;
   const int64_t rows = (int64_t)a.batch * a.n_kv_heads;
   const int64_t want = std::max<int64_t>(1, (per_cu * a.n_cu) / std::max<int64_t>(1, rows));

@@ -31,7 +31,7 @@ inline hipError_t no_kernel(hipStream_t stream, Timing tm) {
 // fuse.hip ------------------------------------------------------------------
 hipError_t launch_fuse(const void* y_attn, const void* y_ssm, const float* beta_attn,
                        const float* beta_ssm, int64_t n_rows, int width, float eps,
-                       hymba_dtype act, void* out, hipStream_t stream, Timing tm = {});
+                       hymba_dtype act, void* out, hipStream_t stream, Timing tm = {}, int n_cu = 0);
 hipError_t launch_mask_ranges(int n_rows, int n_meta, int window, int32_t* ranges,
                               hipStream_t stream);
 
@@ -141,12 +141,17 @@ struct AttnDecodeArgs {
   int ring;                            // cache is the compact ring of n_meta + window rows
   float rope_base;
   hymba_dtype act;
+  // bf16: the Mamba branch's step of the same call, run by workgroups of its
+  // own inside the attention launch (null: none)
+  const SsmDecodeArgs* ssm = nullptr;
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream, Timing tm = {});
 // partial slots per (sequence, query head) the workspace holds: enough for any launch
 void decode_split_plan(int n_meta, int window, int cap, int* n_split, int* keys_per_split);
 // splits (partials per head) one launch uses, at most the plan's slot count
 int decode_active_splits(const AttnDecodeArgs& a);
+// waves of the bf16 decode attention kernel that one compute unit holds
+int decode_wave_slots_per_cu(int dv);
 
 // Whole K and V rows (all kv heads) of n positions per sequence, from one
 // buffer to another. The positions are [pa, pa + na) then [pb, pb + n - na).

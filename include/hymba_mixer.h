@@ -265,7 +265,10 @@ int hymba_mixer_prefill_continue(const hymba_mixer_desc* desc, const hymba_mixer
  *  stage_events NULL, or 2 * HYMBA_DECODE_STAGES caller-created events: start
  *             and end of each stage as for prefill (stages: SSM step, query/key
  *             rotation + attention partials, merge + fusion; the start event
- *             is taken by the stage's first kernel, the end by its last). */
+ *             is taken by the stage's first kernel, the end by its last). In
+ *             bf16 the SSM step runs inside the attention stage's launch, as
+ *             workgroups of its own, and its stage records both events back
+ *             to back. */
 int hymba_mixer_decode(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
                        const void* x, const void* z, const void* dt, const void* B, const void* C,
                        const void* q, const void* k_new, const void* v_new,
