@@ -55,10 +55,10 @@ __device__ __forceinline__ float wave_scan(float v, int lane) {
 // the chunk's B rows (and, for the output pass, C rows).
 template <typename T, int P>
 struct ChunkIn {
-  // (rows enough for the output pass to place its 64 x 68 M block here once
-  // the x rows are dead)
-  static constexpr int kXRows = (kQ + kTaps - 1) > (kQ * (kQ + kRowPad) + P - 1) / P
-                                    ? (kQ + kTaps - 1) : (kQ * (kQ + kRowPad) + P - 1) / P;
+  // (rows enough for the output pass to place its 64 x 68 M block, and the
+  // state pass its P x 68 transposed conv output, here once the x rows are dead)
+  static constexpr int kDead = (kQ > P ? kQ : P) * (kQ + kRowPad);
+  static constexpr int kXRows = (kQ + kTaps - 1) > (kDead + P - 1) / P ? (kQ + kTaps - 1) : (kDead + P - 1) / P;
   float xs[kXRows][P];
   float bs[kQ][kSt];
   float s2[kQ], dts[kQ];
@@ -174,18 +174,28 @@ __device__ __forceinline__ float conv_at(const ChunkIn<T, P>& ci, int j, int p) 
 }
 
 // Pass 1: agg[k][b][c][n] = sum_j exp(S_last - S_j) dt_j u_j[c] B_j[n] for the
-// head's channels c, and sdt[k][b][c] = the chunk's dt sum. Thread (c, 4
-// states) walks the chunk's rows with the conv window in registers.
+// head's channels c, and sdt[k][b][c] = the chunk's dt sum. The conv output of
+// each (row, channel), times its row weight, is formed once (into LDS, where
+// the staged x rows were, transposed to [channel][row]); the sum over rows is
+// a P x 16 product on the matrix cores, one 32-channel tile per wave. In bf16
+// the weighted conv outputs enter as a bf16 pair (the value rounded, then the
+// rounding error rounded), so the state keeps ~16 mantissa bits; B is exact
+// in bf16. fp32 uses fp32 products.
 template <typename T, int P>
 __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
     const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm, const float* __restrict__ A,
     const float* __restrict__ conv_w, const T* __restrict__ conv_in, float* __restrict__ agg,
     float* __restrict__ sdt, int L, int D, int H, int batch) {
+  typedef Mma<T> M;
+  constexpr int NU = kQ * P / kSsdThreads;   // conv outputs per thread
+  static_assert(kQ * P % kSsdThreads == 0 && P / 32 <= kSsdThreads / 64, "one 32-channel tile per wave");
   __shared__ ChunkIn<T, P> ci;
   __shared__ float wj[kQ];   // dt_j exp(S_last - S_j)
   const int k = blockIdx.x, h = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lq = lane & 31, hh = lane >> 5;
   const int t0 = k * kQ;
   {
     ChunkLoads<T, P> ld;
@@ -195,22 +205,57 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
   __syncthreads();
   if (tid < kQ) wj[tid] = ci.dts[tid] * __builtin_amdgcn_exp2f(ci.s2[kQ - 1] - ci.s2[tid]);
   __syncthreads();
+  float u[NU];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int e = tid + i * kSsdThreads, j = e / P, p = e % P;
+    u[i] = conv_at(ci, j, p) * wj[j];
+  }
+  __syncthreads();   // the staged x rows are dead: U^T takes their place
+  typedef float URow[kQ + kRowPad];
+  URow* const ut = reinterpret_cast<URow*>(&ci.xs[0][0]);
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int e = tid + i * kSsdThreads, j = e / P, p = e % P;
+    ut[p][j] = u[i];
+  }
+  __syncthreads();
   const int c0 = h * P;
   const int64_t row0 = ((int64_t)k * batch + b) * D + c0;   // (chunk, sequence, first channel of the head)
-  for (int o = tid; o < P * (kSt / 4); o += kSsdThreads) {
-    const int p = o / (kSt / 4), n0 = 4 * (o % (kSt / 4));
-    const float w0 = ci.cw[p][0], w1 = ci.cw[p][1], w2 = ci.cw[p][2], w3 = ci.cw[p][3];
-    float x0 = ci.xs[0][p], x1 = ci.xs[1][p], x2 = ci.xs[2][p];
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < kQ; ++j) {
-      const float x3 = ci.xs[j + 3][p];
-      const float u = fmaf(w0, x0, fmaf(w1, x1, fmaf(w2, x2, w3 * x3))) * wj[j];
-      const float4 bq = *reinterpret_cast<const float4*>(&ci.bs[j][n0]);
-      a0 = fmaf(u, bq.x, a0); a1 = fmaf(u, bq.y, a1); a2 = fmaf(u, bq.z, a2); a3 = fmaf(u, bq.w, a3);
-      x0 = x1; x1 = x2; x2 = x3;
+  if (wave < P / 32) {
+    // rows of the product: channels 32 wave + lq; columns: states lq (< 16)
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kQ / 16; ++ks) {
+      const int j0 = 16 * ks + 8 * hh;
+      float bv[8], av[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) bv[t] = lq < kSt ? ci.bs[j0 + t][lq] : 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) av[t] = ut[32 * wave + lq][j0 + t];
+      const typename M::Frag fb = M::from_f32(bv);
+      if constexpr (sizeof(T) == 2) {
+        float hi[8], lo[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          hi[t] = __uint_as_float((uint32_t)f32_to_bf16_bits(av[t]) << 16);
+          lo[t] = av[t] - hi[t];
+        }
+        acc = M::mma(M::from_f32(hi), fb, acc);
+        acc = M::mma(M::from_f32(lo), fb, acc);
+      } else {
+        acc = M::mma(M::from_f32(av), fb, acc);
+      }
     }
-    *reinterpret_cast<float4*>(agg + (row0 + p) * kSt + n0) = make_float4(a0, a1, a2, a3);
+    if (lq < kSt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = 32 * wave + 8 * (r >> 2) + 4 * hh + (r & 3);
+        agg[(row0 + p) * kSt + lq] = acc[r];
+      }
+    }
   }
   for (int p = tid; p < P; p += kSsdThreads) sdt[row0 + p] = ci.total;
 }
