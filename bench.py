@@ -282,7 +282,7 @@ COUNTER_KERNELS = {
     "ssm_chunk_out": ("ssm_chunk_kernel<hymba::bf16, true>", "ssm_scan1_kernel<hymba::bf16>"),
     "rope_prefill": ("rope_prefill_kernel<hymba::bf16>",),
     "attn_prefill": ("attn_prefill_kernel<hymba::bf16",),
-    "fuse": ("fuse_rows_kernel<hymba::bf16",),
+    "fuse": ("fuse_rows_kernel<hymba::bf16", "fuse_rows_stream_kernel<hymba::bf16"),
     "ssm_decode": ("ssm_decode_kernel<hymba::bf16>",),
     "ssm_attn_decode": ("attn_decode_wave_kernel",),
     "decode_merge_fuse": ("decode_combine_kernel<hymba::bf16",),
