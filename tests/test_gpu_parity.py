@@ -96,8 +96,11 @@ def test_prefill_visibility_bit_exact(shape):
 # fusion alone
 
 
+# (the last two take the streaming form on a 256-CU device: at least four rows
+# per wave of its resident grid, the row count ragged against that grid, and
+# rows that fill the last 16-byte pieces of a lane only in part)
 @pytest.mark.parametrize("act,rows,width", [("f32", 37, 128), ("bf16", 100, 3200), ("bf16", 5, 77), ("f32", 3, 13),
-                                            ("bf16", 0, 64)])
+                                            ("bf16", 0, 64), ("bf16", 8200, 3200), ("f32", 12300, 1000)])
 def test_fuse_heads(act, rows, width):
     g = np.random.default_rng(rows * 1000 + width)
     ya = g.standard_normal((rows, width)).astype(np.float32) * 3
