@@ -3,7 +3,8 @@
 // state update h = exp(dt A) h + dt B u, y = (C . h + D u) silu(z), and the
 // shifted conv history ("Jamba: Hybrid SSM-Transformer", "1. Layer
 // Interleaving Ratio"; "Lecture 04 - Beyond the Dense Transformer", section 2).
-// Used by the decode kernel of the Mamba branch (ssm_decode_kernel).
+// Used by the fp32 decode kernel of the Mamba branch (ssm_decode_kernel) and,
+// in bf16, by the Mamba-step workgroups inside the decode attention launch.
 #pragma once
 
 #include "common.hpp"

@@ -33,6 +33,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -249,11 +250,21 @@ def kernel_report(name, avg_ms, work, act):
     return r
 
 
+def _code_only(text):
+    """A kernel source without its comments, trailing blanks and empty lines
+    (the sources hold no string literal with a comment marker in it)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_hash():
+    """Hash of the kernel sources' code (comments excluded): the counter
+    summaries under profiles/ are valid while it is unchanged."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "attention_lm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "attention_lm_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
