@@ -419,6 +419,15 @@ def test_prefill_ssd_small_shapes(kw):
     run_prefill_parity(cfg)
 
 
+def test_prefill_ssd_many_items_per_workgroup():
+    """fp32, head width 32: 19 chunks x 32 heads x 3 sequences = 1824
+    (chunk, head, sequence) items, more than one round of workgroups of
+    either pass, with a ragged last chunk in every sequence."""
+    cfg = synth.config("tiny_f32").with_(batch=3, n_meta=8, n_tokens=1200, d_inner=1024, n_q_heads=8, n_kv_heads=2,
+                                          window=100, act="f32", seed=65, ssm_heads=32, name="ssd_many")
+    run_prefill_parity(cfg)
+
+
 def test_prefill_ssd_swa_layer_full():
     """The 1.5B-shaped window-1024 layer with its Mamba branch in the Mamba-2
     form: 50 heads of 64 channels."""
