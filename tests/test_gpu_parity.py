@@ -235,6 +235,17 @@ def test_prefill_batched_every_sequence():
     run_prefill_parity(cfg, rows=block_rows(cfg, head=20, tail=10))
 
 
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_prefill_xcd_order_g8(act):
+    """The attention's XCD-major work order (many rounds of workgroups) at
+    another group shape: 8 sequences, 16 query heads over 2 kv heads (16
+    positions per workgroup), head width 32; 69 position blocks x 16 streams.
+    Every row of every output against the oracle."""
+    cfg = synth.config("tiny_f32").with_(batch=8, n_meta=12, n_tokens=1088, d_inner=512, n_q_heads=16, n_kv_heads=2,
+                                          window=100, act=act, seed=71, name="split")
+    run_prefill_parity(cfg)
+
+
 def test_prefill_deterministic_and_branch_isolation():
     cfg = synth.config("tiny_f32").with_(**SMALL[0], name="det")
     inp = synth.make_prefill_inputs(cfg)
