@@ -17,6 +17,9 @@
 //   3. ssd_out_kernel: per (chunk, head, sequence), Y = [M | C exp(S)] x
 //      [U ; H^T] on the matrix cores, M[i][j] = (C_i . B_j) exp(S_i - S_j) dt_j
 //      below the diagonal (fp32 VALU into LDS), then D u and the silu(z) gate.
+//      In bf16 each fp32 operand enters as a bf16 value plus its bf16
+//      rounding error (three products): Y and D u can nearly cancel when dt
+//      is large, and one bf16 rounding of M and U would then show in y.
 // The conv (4 taps, causal, per channel) is recomputed in both passes from x
 // (and the carried history before row 0).
 #include <utility>
@@ -164,6 +167,35 @@ struct ChunkLoads {
     for (int e = tid; e < P * kTaps; e += kSsdThreads) ci.cw[e / kTaps][e % kTaps] = conv_w[(int64_t)c0 * kTaps + e];
   }
 };
+
+// An fp32 operand fragment (8 values) as two bf16 fragments: the values
+// rounded, then their rounding errors rounded. A product from the three
+// parts hi.hi + hi.lo + lo.hi keeps about 16 mantissa bits of each operand.
+__device__ __forceinline__ void split_bf16(const float* v, bf16x8_t& hi, bf16x8_t& lo) {
+  float h[8], l[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    h[t] = __uint_as_float((uint32_t)f32_to_bf16_bits(v[t]) << 16);
+    l[t] = v[t] - h[t];
+  }
+  hi = Mma<bf16>::from_f32(h);
+  lo = Mma<bf16>::from_f32(l);
+}
+// acc += A B^T for fp32 operand fragments a, b: in bf16, from their split
+// parts (three products); in fp32, one fp32 product.
+template <typename T>
+__device__ __forceinline__ f32x16_t mma_split(const float* a, const float* b, f32x16_t acc) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x8_t ah, al, bh, bl;
+    split_bf16(a, ah, al);
+    split_bf16(b, bh, bl);
+    acc = Mma<bf16>::mma(ah, bh, acc);
+    acc = Mma<bf16>::mma(ah, bl, acc);
+    return Mma<bf16>::mma(al, bh, acc);
+  } else {
+    return Mma<float>::mma(Mma<float>::from_f32(a), Mma<float>::from_f32(b), acc);
+  }
+}
 
 template <typename T, int P>
 __device__ __forceinline__ float conv_at(const ChunkIn<T, P>& ci, int j, int p) {
@@ -349,18 +381,15 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < kQ / 16; ++kb) {
-      if (kb <= (2 * ti + 1)) {   // key blocks past this tile's last row are all zero
-        const typename M::Frag fa = M::from_f32(&ms[ia][16 * kb + 8 * hh]);
-        const typename M::Frag fb = M::from_f32(&ut[pb][16 * kb + 8 * hh]);
-        acc = M::mma(fa, fb, acc);
-      }
+      if (kb <= (2 * ti + 1))   // key blocks past this tile's last row are all zero
+        acc = mma_split<T>(&ms[ia][16 * kb + 8 * hh], &ut[pb][16 * kb + 8 * hh], acc);
     }
     {   // the entering state: rows of C scaled by exp(S_i), against H^T
       const float es = __builtin_amdgcn_exp2f(ci.s2[ia]);
       float cv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) cv[e] = cs[ia][8 * hh + e] * es;
-      acc = M::mma(M::from_f32(cv), M::from_f32(&hs[pb][8 * hh]), acc);
+      acc = mma_split<T>(cv, &hs[pb][8 * hh], acc);
     }
     const float Dc = Dp[c0 + pb];
 #pragma unroll

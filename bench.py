@@ -55,7 +55,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["common.hpp", "launch.hpp", "ssm_step.hpp", "mma.hpp", "ssm.hip", "ssd.hip", "attn.hip", "fuse.hip",
                   "api.hip"]
 PREFILL_WORKLOADS = {"c3": "batched_prefill", "c2": "global_layer", "c1": "swa_layer"}
-ALL_LEGS = ["c3", "c2", "c1", "decode", "decode_affine", "ssd", "continue"]
+ALL_LEGS = ["c3", "c2", "c1", "decode", "decode_affine", "ssd", "ssd_batched", "continue"]
 
 
 def log(*a):
@@ -735,19 +735,20 @@ def main():
     if "decode_affine" in legs:
         subs["decode_affine"] = (synth.config("decode_affine"),
                                  bench_decode(synth.config("decode_affine"), args, ev, flush))
-    if "ssd" in legs:
-        base = synth.config("swa_layer")
-        scfg = base.with_(ssm_heads=50, name="swa_layer_ssd")
-        leg = prefill_leg(scfg, args, ev, flush)
-        sw = ssd_work(scfg)
-        names = {"ssm_chunk_end": "ssd_state", "ssm_chunk_carry": "ssd_carry", "ssm_chunk_out": "ssd_out"}
-        for k, n in names.items():
-            kr = leg["kernels"].pop(k)
-            leg["kernels"][n] = dict(kernel_report(n, kr["avg_us"] * 1e-3, sw[n], scfg.act),
-                                     median_us=kr.get("median_us"))
-        leg["workload"] = (f"{base.workload}, Mamba branch in the Mamba-2 form: 50 heads of 64 channels, one decay "
-                           f"rate and step size per head")
-        subs["ssd"] = (scfg, leg)
+    for leg_name, base_name in (("ssd", "swa_layer"), ("ssd_batched", "batched_prefill")):
+        if leg_name in legs:
+            base = synth.config(base_name)
+            scfg = base.with_(ssm_heads=50, name=f"{base_name}_ssd")
+            leg = prefill_leg(scfg, args, ev, flush)
+            sw = ssd_work(scfg)
+            names = {"ssm_chunk_end": "ssd_state", "ssm_chunk_carry": "ssd_carry", "ssm_chunk_out": "ssd_out"}
+            for k, n in names.items():
+                kr = leg["kernels"].pop(k)
+                leg["kernels"][n] = dict(kernel_report(n, kr["avg_us"] * 1e-3, sw[n], scfg.act),
+                                         median_us=kr.get("median_us"))
+            leg["workload"] = (f"{base.workload}, Mamba branch in the Mamba-2 form: 50 heads of 64 channels, one "
+                               f"decay rate and step size per head")
+            subs[leg_name] = (scfg, leg)
     if "continue" in legs:
         cfg = synth.config("swa_layer")
         log("[bench] prefill continuation")
@@ -801,7 +802,7 @@ def main():
         }
     else:
         res = {"metric": METRIC, "note": "headline leg (c3) not run"}
-    for name in ("c2", "c1", "decode", "decode_affine", "ssd", "continue"):
+    for name in ("c2", "c1", "decode", "decode_affine", "ssd", "ssd_batched", "continue"):
         if name in subs:
             res[{"c2": "global_layer", "c1": "swa_layer"}.get(name, name)] = subs[name][1]
     if "c3" in subs and not args.no_cpu:
