@@ -188,32 +188,6 @@ constexpr int BK = 64;                     // keys per LDS stage (two 32-key sub
 constexpr int kAttnWaves = 4;
 constexpr int kAttnCols = 32 * kAttnWaves;
 constexpr float kRescaleSlack = 8.0f;
-// wait for this wave's outstanding global loads, including those that write LDS
-// (gfx9 s_waitcnt: vmcnt 0; expcnt and lgkmcnt left at their maximum)
-__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// Workgroup barrier after LDS writes, without waiting for global loads in
-// flight (a __syncthreads() would wait for them, loads into LDS included):
-// lgkmcnt 0 (vmcnt and expcnt at their maximum), then s_barrier; the empty asm
-// statements keep the compiler from moving memory accesses across it.
-// Workgroup barrier for a tile pipeline: this wave first waits until at most
-// N of its global loads are outstanding (later tiles' loads may stay in
-// flight; a load into LDS has landed once it is no longer counted) and its LDS
-// operations are done; then as lds_barrier.
-template <int N>
-__device__ __forceinline__ void tile_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);   // vmcnt(N) lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // slot s of a 16-key chunk holds key kperm(s); an involution
 __device__ __forceinline__ int kperm(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
 

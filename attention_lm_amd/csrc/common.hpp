@@ -93,6 +93,34 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_
 // an offset that every descriptor above treats as out of range
 constexpr uint32_t kBufferNowhere = 0x80000000u;
 
+// Waits and barriers for kernels that keep global loads in flight across a
+// barrier (a __syncthreads() waits for every outstanding load, loads into LDS
+// included). gfx9 s_waitcnt fields: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8. The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+//
+// wait for all of this wave's outstanding global loads, including those that
+// write LDS (vmcnt 0; expcnt and lgkmcnt at their maximum)
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// workgroup barrier after LDS writes: lgkmcnt 0, vmcnt and expcnt untouched
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// workgroup barrier for a load pipeline: this wave first waits until at most
+// N of its global loads are outstanding (vmcnt drains in issue order, so the
+// earlier ones have landed, in LDS too) and its LDS operations are done
+template <int N>
+__device__ __forceinline__ void tile_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);   // vmcnt(N) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wave64 butterfly sum / max (deterministic order).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -292,7 +292,64 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
   for (int p = tid; p < P; p += kSsdThreads) sdt[row0 + p] = ci.total;
 }
 
+// n 16-byte pieces straight into LDS, piece q at dst + 16 q, read from byte
+// offset off(q) of descriptor r (an offset out of range reads zeros); the
+// workgroup's waves take 64 pieces per load instruction in turn.
+template <typename F>
+__device__ __forceinline__ void stage_pieces(__amdgpu_buffer_rsrc_t r, char* dst, int n, int wave, int lane, F off) {
+  for (int q0 = 64 * wave; q0 < n; q0 += kSsdThreads) {
+    const int q = q0 + lane;
+    if (q < n) buf_load16_lds(r, off(q), dst + 16 * q0);
+  }
+}
+
+// LDS of the output pass. The raw x rows and, once the conv has consumed
+// them, its output u share one area; u is stored transposed, [channel][row],
+// in bf16 as the value rounded and its rounding error rounded.
+template <typename T, int P>
+struct OutStage {
+  static constexpr int kUPitch = kQ + 4;                   // u row pitch (elements)
+  static constexpr int kParts = sizeof(T) == 2 ? 2 : 1;
+  static constexpr int kXBytes = (kQ + kTaps - 1) * P * (int)sizeof(T);
+  static constexpr int kUBytes = kParts * P * kUPitch * (int)sizeof(T);
+  __attribute__((aligned(16))) char area[kXBytes > kUBytes ? kXBytes : kUBytes];
+  __attribute__((aligned(16))) T bs[kQ][kSt];   // B rows of the chunk, as loaded
+  __attribute__((aligned(16))) T cs[kQ][kSt];   // C rows
+  __attribute__((aligned(16))) float hs[P][kSt];   // entering state
+  __attribute__((aligned(16))) float s2[kQ];    // A log2(e) (dt_0 + .. + dt_j)
+  __attribute__((aligned(16))) float dts[kQ];   // dt_j
+  __device__ __forceinline__ T (*xr())[P] { return reinterpret_cast<T (*)[P]>(area); }
+  __device__ __forceinline__ T (*u(int part))[kUPitch] {
+    return reinterpret_cast<T (*)[kUPitch]>(area + part * P * kUPitch * (int)sizeof(T));
+  }
+};
+
+// 8 operand values of row `row` of u at rows j0 .. j0 + 3 and j0 + 8 .. j0 + 11
+template <typename T, int P>
+__device__ __forceinline__ typename Mma<T>::Frag u_frag(OutStage<T, P>& st, int part, int row, int j0) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x2_t a = *reinterpret_cast<const u32x2_t*>(&st.u(part)[row][j0]);
+    const u32x2_t b = *reinterpret_cast<const u32x2_t*>(&st.u(part)[row][j0 + 8]);
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{a.x, a.y, b.x, b.y});
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(&st.u(part)[row][j0]);
+    const float4 b = *reinterpret_cast<const float4*>(&st.u(part)[row][j0 + 8]);
+    F32x8 f;
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+  }
+}
+
 // Pass 3: the chunk's outputs from its entering state carry[k] (see above).
+// The chunk's x rows (with three rows of history), B and C rows and entering
+// state load straight into LDS. Each thread forms the conv output of one
+// channel over a run of consecutive rows from registers. Each wave owns a
+// 32-row block of Y (rows i) and one or two 32-channel tiles: it forms the
+// decayed C B^T blocks that row block needs on the matrix cores with the
+// operands swapped, so that a lane holds row i of M and the result is already
+// the next product's A operand; the U operand takes the rows j in the same
+// order. The gate inputs z load while the products run.
 template <typename T, int P>
 __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(
     const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ dt, const T* __restrict__ Bm,
@@ -301,11 +358,13 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(
     T* __restrict__ y, float* __restrict__ state_out, T* __restrict__ conv_state_out, int L, int D, int H,
     int batch, int nchunk) {
   typedef Mma<T> M;
-  constexpr int NTP = P / 32;
-  __shared__ ChunkIn<T, P> ci;
-  __shared__ __attribute__((aligned(16))) float ut[P][kQ + kRowPad];   // u, [channel][row]
-  __shared__ __attribute__((aligned(16))) float cs[kQ][kSt];
-  __shared__ __attribute__((aligned(16))) float hs[P][kSt];            // entering state
+  typedef OutStage<T, P> S;
+  constexpr int E = Vec16<T>::n;                 // elements per 16-byte piece
+  constexpr int NTP = P / 32;                    // 32-channel tiles
+  constexpr int TPW = NTP > 1 ? NTP / 2 : 1;     // tiles per wave
+  constexpr int RB = kQ * P / kSsdThreads;       // conv rows per thread
+  static_assert(kQ == 64 && NTP >= 1 && NTP <= 4 && RB % 4 == 0, "two 32-row blocks; whole row runs per thread");
+  __shared__ S st;
   const int k = blockIdx.x, h = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -313,89 +372,184 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(
   const int lane = tid & 63, lq = lane & 31, hh = lane >> 5;
   const int t0 = k * kQ, nr = min(kQ, L - t0);
   const int c0 = h * P;
+
+  // --- staging: x, B, C and the entering state into LDS; dt and the taps into registers
   {
-    ChunkLoads<T, P> ld;
-    ld.issue(x, dt, Bm, Cm, b, h, t0, L, D, H, true);
-    const float4* hin = reinterpret_cast<const float4*>(carry + (((int64_t)k * batch + b) * D + c0) * kSt);
-    float4 hv[(P * kSt / 4 + kSsdThreads - 1) / kSsdThreads];
-#pragma unroll
-    for (int q = 0; q < (int)(sizeof(hv) / sizeof(hv[0])); ++q) {
-      const int it = tid + q * kSsdThreads;
-      if (it < P * kSt / 4) hv[q] = hin[it];
-    }
-    ld.commit(ci, cs, A, conv_w, conv_in, b, h, t0, D);
-#pragma unroll
-    for (int q = 0; q < (int)(sizeof(hv) / sizeof(hv[0])); ++q) {
-      const int it = tid + q * kSsdThreads;
-      if (it < P * kSt / 4) reinterpret_cast<float4*>(&hs[0][0])[it] = hv[q];
-    }
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + b * L * D, (uint32_t)((int64_t)L * D * sizeof(T)));
+    stage_pieces(xrs, st.area, (kQ + kTaps - 1) * (P / E), wave, lane, [&](int q) {
+      const int t = t0 - (kTaps - 1) + q / (P / E);
+      return t >= 0 ? (uint32_t)(((int64_t)t * D + c0 + (q % (P / E)) * E) * sizeof(T)) : kBufferNowhere;
+    });
+    const uint32_t rowb = kSt * sizeof(T);
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(Bm + b * L * kSt, (uint32_t)L * rowb);
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(Cm + b * L * kSt, (uint32_t)L * rowb);
+    auto bc_off = [&](int q) { return (uint32_t)t0 * rowb + 16u * q; };
+    stage_pieces(brs, reinterpret_cast<char*>(&st.bs[0][0]), kQ * kSt / E, wave, lane, bc_off);
+    stage_pieces(crs, reinterpret_cast<char*>(&st.cs[0][0]), kQ * kSt / E, wave, lane, bc_off);
+    const __amdgpu_buffer_rsrc_t hrs =
+        make_rsrc(carry + (((int64_t)k * batch + b) * D + c0) * kSt, (uint32_t)(P * kSt * sizeof(float)));
+    stage_pieces(hrs, reinterpret_cast<char*>(&st.hs[0][0]), P * kSt / 4, wave, lane,
+                 [](int q) { return 16u * q; });
   }
-  __syncthreads();
-  // u, transposed to [channel][row]
-  for (int e = tid; e < kQ * P; e += kSsdThreads) {
-    const int j = e / P, p = e % P;
-    ut[p][j] = conv_at(ci, j, p);
+  float dtv = 0.f;
+  if (wave == 0) {
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dt + b * L * H, (uint32_t)((int64_t)L * H * sizeof(T)));
+    const uint32_t off = (uint32_t)(((int64_t)(t0 + lane) * H + h) * sizeof(T));
+    if constexpr (sizeof(T) == 2)
+      dtv = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(drs, off, 0, 0) << 16);
+    else
+      dtv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(drs, off, 0, 0));
   }
-  __syncthreads();   // the staged x rows are dead: M takes their place
-  typedef float MRow[kQ + kRowPad];
-  static_assert(sizeof(ci.xs) >= sizeof(float) * kQ * (kQ + kRowPad), "M fits where x was staged");
-  MRow* const ms = reinterpret_cast<MRow*>(&ci.xs[0][0]);
-  // M = C B^T on the matrix cores (one 32 x 32 tile per wave), masked below
-  // the diagonal and decayed: M[i][j] = (C_i . B_j) exp(S_i - S_j) dt_j
-  {
-    const int ti = wave >> 1, tj = wave & 1;
-    f32x16_t g;
+  const int cp = tid % P, rb = tid / P;          // conv: channel, run of rows
+  float w[kTaps];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) g[r] = 0.f;
-    if (tj <= ti) g = M::mma(M::from_f32(&cs[32 * ti + lq][8 * hh]), M::from_f32(&ci.bs[32 * tj + lq][8 * hh]), g);
-    const int j = 32 * tj + lq;
-    const float s2j = ci.s2[j], dtj = ci.dts[j];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 32 * ti + 8 * (r >> 2) + 4 * hh + (r & 3);
-      ms[i][j] = j <= i ? g[r] * __builtin_amdgcn_exp2f(ci.s2[i] - s2j) * dtj : 0.f;
+  for (int j = 0; j < kTaps; ++j) w[j] = conv_w[(int64_t)(c0 + cp) * kTaps + j];
+  wait_loads();
+  if (wave == 0) {
+    const float cum = wave_scan(dtv, lane);
+    st.dts[lane] = dtv;
+    st.s2[lane] = A[h] * kLog2e * cum;
+  }
+  lds_barrier();   // every wave's loads have landed
+  if (t0 == 0 && conv_in) {   // rows -3 .. -1 (zeros so far): the carried history
+    if (tid < (kTaps - 1) * P) {
+      const int r = tid / P;
+      st.xr()[r][cp] = conv_in[(b * D + c0 + cp) * (kTaps - 1) + r];
     }
+    lds_barrier();
   }
-  // this lane's gate inputs, loaded while the block products run
+
+  // --- the wave's tiles and their gate inputs (in flight from here to the epilogue)
+  const bool active = NTP > 1 || wave < 2;
+  const int ti = NTP > 1 ? wave >> 1 : wave & 1;
+  const int tp0 = NTP > 1 ? (wave & 1) * TPW : 0;
+  const int ia = 32 * ti + lq;                   // this lane's row of M (A operand)
   const uint32_t rowb = (uint32_t)(D * sizeof(T));
   const __amdgpu_buffer_rsrc_t zrs = make_rsrc(z + (b * L + t0) * D, (uint32_t)nr * rowb);
-  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + (b * L + t0) * D, (uint32_t)nr * rowb);
-  __syncthreads();
-  // Y tiles of 32 rows x 32 channels, one per wave in turn
-  for (int tile = wave; tile < 2 * NTP; tile += kSsdThreads / 64) {
-    const int ti = tile / NTP, tp = tile % NTP;
-    const int ia = 32 * ti + lq, pb = 32 * tp + lq;   // this lane's A row and B column
-    const uint32_t col = (uint32_t)((c0 + pb) * sizeof(T));
-    float zv[16];
+  float zv[TPW][16];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const uint32_t col = (uint32_t)((c0 + 32 * (tp0 + tt) + lq) * sizeof(T));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 32 * ti + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const uint32_t off = (uint32_t)i * rowb + col;
+      const uint32_t off = active ? (uint32_t)i * rowb + col : kBufferNowhere;
       if constexpr (sizeof(T) == 2)
-        zv[r] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(zrs, off, 0, 0) << 16);
+        zv[tt][r] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(zrs, off, 0, 0) << 16);
       else
-        zv[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(zrs, off, 0, 0));
+        zv[tt][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(zrs, off, 0, 0));
     }
-    f32x16_t acc;
+  }
+
+  // --- conv: channel cp, rows rb RB .. rb RB + RB - 1, from registers
+  float uv[RB];
+  {
+    float xv[RB + kTaps - 1];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int m = 0; m < RB + kTaps - 1; ++m) xv[m] = to_f32(st.xr()[rb * RB + m][cp]);
 #pragma unroll
-    for (int kb = 0; kb < kQ / 16; ++kb) {
-      if (kb <= (2 * ti + 1))   // key blocks past this tile's last row are all zero
-        acc = mma_split<T>(&ms[ia][16 * kb + 8 * hh], &ut[pb][16 * kb + 8 * hh], acc);
+    for (int m = 0; m < RB; ++m) {
+      float v = w[0] * xv[m];
+#pragma unroll
+      for (int j = 1; j < kTaps; ++j) v = fmaf(w[j], xv[m + j], v);
+      uv[m] = v;
     }
-    {   // the entering state: rows of C scaled by exp(S_i), against H^T
-      const float es = __builtin_amdgcn_exp2f(ci.s2[ia]);
-      float cv[8];
+  }
+  lds_barrier();   // every x read is done: u takes the area
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cv[e] = cs[ia][8 * hh + e] * es;
-      acc = mma_split<T>(cv, &hs[pb][8 * hh], acc);
+  for (int m = 0; m < RB; m += 4) {
+    if constexpr (sizeof(T) == 2) {
+      float hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = __uint_as_float((uint32_t)f32_to_bf16_bits(uv[m + e]) << 16);
+        lo[e] = uv[m + e] - hi[e];
+      }
+      *reinterpret_cast<u32x2_t*>(&st.u(0)[cp][rb * RB + m]) = u32x2_t{pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+      *reinterpret_cast<u32x2_t*>(&st.u(1)[cp][rb * RB + m]) = u32x2_t{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])};
+    } else {
+      *reinterpret_cast<float4*>(&st.u(0)[cp][rb * RB + m]) = make_float4(uv[m], uv[m + 1], uv[m + 2], uv[m + 3]);
     }
-    const float Dc = Dp[c0 + pb];
+  }
+  lds_barrier();
+
+  if (active) {
+    f32x16_t acc[TPW];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 32 * ti + 8 * (r >> 2) + 4 * hh + (r & 3);
-      buf_store(yrs, (uint32_t)i * rowb + col, from_f32<T>(fmaf(Dc, ut[pb][i], acc[r]) * ssd_silu(zv[r])));
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tt][r] = 0.f;
+    const float s2i = st.s2[ia];
+    for (int tj = 0; tj <= ti; ++tj) {
+      // M^T block (rows j of block tj, columns i of block ti): B_j . C_i
+      f32x16_t g;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) g[r] = 0.f;
+      g = M::mma(M::frag_at(&st.bs[32 * tj + lq][8 * hh]), M::frag_at(&st.cs[ia][8 * hh]), g);
+      float mv[16];   // M[i][j] for this lane's i and j = 32 tj + 8 (r / 4) + 4 hh + r % 4
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j4 = 32 * tj + 8 * q + 4 * hh;
+        const float4 s2j = *reinterpret_cast<const float4*>(&st.s2[j4]);
+        const float4 dj = *reinterpret_cast<const float4*>(&st.dts[j4]);
+        const float sj[4] = {s2j.x, s2j.y, s2j.z, s2j.w}, djv[4] = {dj.x, dj.y, dj.z, dj.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          mv[4 * q + e] = (tj < ti || j4 + e <= ia) ? g[4 * q + e] * __builtin_amdgcn_exp2f(s2i - sj[e]) * djv[e] : 0.f;
+      }
+      // Y += M U over the block's rows j, 16 at a time
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int j0 = 32 * tj + 16 * q2 + 4 * hh;
+        if constexpr (sizeof(T) == 2) {
+          bf16x8_t ah, al;
+          split_bf16(&mv[8 * q2], ah, al);
+#pragma unroll
+          for (int tt = 0; tt < TPW; ++tt) {
+            const int pb = 32 * (tp0 + tt) + lq;
+            const bf16x8_t uh = u_frag(st, 0, pb, j0), ul = u_frag(st, 1, pb, j0);
+            acc[tt] = M::mma(ah, uh, acc[tt]);
+            acc[tt] = M::mma(ah, ul, acc[tt]);
+            acc[tt] = M::mma(al, uh, acc[tt]);
+          }
+        } else {
+          const typename M::Frag a = M::from_f32(&mv[8 * q2]);
+#pragma unroll
+          for (int tt = 0; tt < TPW; ++tt) acc[tt] = M::mma(a, u_frag(st, 0, 32 * (tp0 + tt) + lq, j0), acc[tt]);
+        }
+      }
+    }
+    // the entering state: rows of C scaled by exp(S_i), against H^T
+    const float es = __builtin_amdgcn_exp2f(s2i);
+    float cv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cv[e] = to_f32(st.cs[ia][8 * hh + e]) * es;
+    const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + (b * L + t0) * D, (uint32_t)nr * rowb);
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int pb = 32 * (tp0 + tt) + lq;
+      acc[tt] = mma_split<T>(cv, &st.hs[pb][8 * hh], acc[tt]);
+      const float Dc = Dp[c0 + pb];
+      const uint32_t col = (uint32_t)((c0 + pb) * sizeof(T));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i4 = 32 * ti + 8 * q + 4 * hh;
+        float u4[4];
+        if constexpr (sizeof(T) == 2) {
+          const u32x2_t a = *reinterpret_cast<const u32x2_t*>(&st.u(0)[pb][i4]);
+          const u32x2_t l = *reinterpret_cast<const u32x2_t*>(&st.u(1)[pb][i4]);
+          u4[0] = bf16_lo(a.x) + bf16_lo(l.x); u4[1] = bf16_hi(a.x) + bf16_hi(l.x);
+          u4[2] = bf16_lo(a.y) + bf16_lo(l.y); u4[3] = bf16_hi(a.y) + bf16_hi(l.y);
+        } else {
+          const float4 a = *reinterpret_cast<const float4*>(&st.u(0)[pb][i4]);
+          u4[0] = a.x; u4[1] = a.y; u4[2] = a.z; u4[3] = a.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q + e;
+          buf_store(yrs, (uint32_t)(i4 + e) * rowb + col, from_f32<T>(fmaf(Dc, u4[e], acc[tt][r]) * ssd_silu(zv[tt][r])));
+        }
+      }
     }
   }
   if (k == nchunk - 1) {

@@ -361,17 +361,6 @@ __global__ __launch_bounds__(64 * kCarrySegs) void ssm_chunk_carry_kernel(const 
   }
 }
 
-// Workgroup barrier for LDS data only: this wave's LDS operations are done
-// (lgkmcnt 0), then s_barrier; global loads in flight, including loads into
-// LDS, are not waited for (a __syncthreads() would wait for all of them). The
-// empty asm statements keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Wait until at most n of this wave's vector memory operations are
 // outstanding (0 <= n; counts of 63 and more wait for nothing). s_waitcnt
 // takes an immediate, so the count is dispatched to constant waits.
