@@ -36,7 +36,6 @@ constexpr int kQ = 64;         // rows per chunk
 constexpr int kSt = 16;        // states
 constexpr int kTaps = 4;       // conv taps
 constexpr int kSsdThreads = 256;
-constexpr int kRowPad = 4;     // LDS row padding (floats), keeps 16-byte alignment
 
 __device__ __forceinline__ float ssd_silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
@@ -51,122 +50,6 @@ __device__ __forceinline__ float wave_scan(float v, int lane) {
   }
   return v;
 }
-
-// What both passes stage for chunk k of head h of sequence b, in LDS: per
-// row, dt and S (log2 units: A log2(e) times the running dt sum); the conv
-// input rows t0 - 3 .. t0 + 63 of the head's channels (fp32); the conv taps;
-// the chunk's B rows (and, for the output pass, C rows).
-template <typename T, int P>
-struct ChunkIn {
-  // (rows enough for the output pass to place its 64 x 68 M block, and the
-  // state pass its P x 68 transposed conv output, here once the x rows are dead)
-  static constexpr int kDead = (kQ > P ? kQ : P) * (kQ + kRowPad);
-  static constexpr int kXRows = (kQ + kTaps - 1) > (kDead + P - 1) / P ? (kQ + kTaps - 1) : (kDead + P - 1) / P;
-  float xs[kXRows][P];
-  float bs[kQ][kSt];
-  float s2[kQ], dts[kQ];
-  float cw[P][kTaps];
-  float total;   // dt sum over the chunk
-};
-
-// Global loads of a chunk, issued together into registers (buffer loads: rows
-// at or past L read zeros), then written to LDS by commit().
-template <typename T, int P>
-struct ChunkLoads {
-  static constexpr int E = Vec16<T>::n;                          // elements per 16-byte load
-  static constexpr int XV = P / E;                                // 16-byte pieces per x row
-  static constexpr int NX = ((kQ + kTaps - 1) * XV + kSsdThreads - 1) / kSsdThreads;
-  static constexpr int BV = kSt / E;                              // pieces per B/C row
-  static constexpr int NB = (kQ * BV + kSsdThreads - 1) / kSsdThreads;
-  u32x4_t xv[NX], bv[NB], cv[NB];
-  float dt;
-
-  __device__ __forceinline__ void issue(const T* x, const T* dtp, const T* Bm, const T* Cm, int64_t b, int h,
-                                        int t0, int L, int D, int H, bool with_c) {
-    const int tid = threadIdx.x;
-    const int c0 = h * P;
-    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + b * L * D, (uint32_t)((int64_t)L * D * sizeof(T)));
-#pragma unroll
-    for (int q = 0; q < NX; ++q) {
-      const int it = tid + q * kSsdThreads, r = it / XV, v = it % XV, t = t0 - (kTaps - 1) + r;
-      const bool ok = it < (kQ + kTaps - 1) * XV && t >= 0;
-      xv[q] = buf_load16(xrs, ok ? (uint32_t)(((int64_t)t * D + c0 + v * E) * sizeof(T)) : kBufferNowhere);
-    }
-    const uint32_t rowb = kSt * sizeof(T);
-    const __amdgpu_buffer_rsrc_t brs = make_rsrc(Bm + b * L * kSt, (uint32_t)L * rowb);
-    const __amdgpu_buffer_rsrc_t crs = make_rsrc(Cm + b * L * kSt, (uint32_t)L * rowb);
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int it = tid + q * kSsdThreads, j = it / BV, v = it % BV;
-      const uint32_t off = it < kQ * BV ? (uint32_t)(t0 + j) * rowb + 16u * v : kBufferNowhere;
-      bv[q] = buf_load16(brs, off);
-      if (with_c) cv[q] = buf_load16(crs, off);
-    }
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dtp + b * L * H, (uint32_t)((int64_t)L * H * sizeof(T)));
-    dt = 0.f;
-    if (tid < 64) {
-      const uint32_t off = (uint32_t)(((int64_t)(t0 + tid) * H + h) * sizeof(T));
-      if constexpr (sizeof(T) == 2)
-        dt = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(drs, off, 0, 0) << 16);
-      else
-        dt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(drs, off, 0, 0));
-    }
-  }
-
-  __device__ __forceinline__ static void unpack(u32x4_t w, float* o) {
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { o[2 * e] = bf16_lo(w[e]); o[2 * e + 1] = bf16_hi(w[e]); }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(w[e]);
-    }
-  }
-
-  // LDS writes; rows before row 0 come from the carried history when given
-  __device__ __forceinline__ void commit(ChunkIn<T, P>& ci, float (*cs)[kSt], const float* A, const float* conv_w,
-                                         const T* conv_in, int64_t b, int h, int t0, int D) {
-    const int tid = threadIdx.x;
-    const int c0 = h * P;
-#pragma unroll
-    for (int q = 0; q < NX; ++q) {
-      const int it = tid + q * kSsdThreads, r = it / XV, v = it % XV, t = t0 - (kTaps - 1) + r;
-      if (it < (kQ + kTaps - 1) * XV) {
-        float f[E];
-        unpack(xv[q], f);
-        if (t < 0 && conv_in) {
-#pragma unroll
-          for (int e = 0; e < E; ++e)
-            f[e] = to_f32(conv_in[(b * D + c0 + v * E + e) * (kTaps - 1) + (kTaps - 1) + t]);
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) ci.xs[r][v * E + e] = f[e];
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int it = tid + q * kSsdThreads, j = it / BV, v = it % BV;
-      if (it < kQ * BV) {
-        float f[E];
-        unpack(bv[q], f);
-#pragma unroll
-        for (int e = 0; e < E; ++e) ci.bs[j][v * E + e] = f[e];
-        if (cs) {
-          unpack(cv[q], f);
-#pragma unroll
-          for (int e = 0; e < E; ++e) cs[j][v * E + e] = f[e];
-        }
-      }
-    }
-    if (tid < 64) {
-      const float cum = wave_scan(dt, tid);
-      ci.dts[tid] = dt;
-      ci.s2[tid] = A[h] * kLog2e * cum;
-      if (tid == 63) ci.total = cum;
-    }
-    for (int e = tid; e < P * kTaps; e += kSsdThreads) ci.cw[e / kTaps][e % kTaps] = conv_w[(int64_t)c0 * kTaps + e];
-  }
-};
 
 // An fp32 operand fragment (8 values) as two bf16 fragments: the values
 // rounded, then their rounding errors rounded. A product from the three
@@ -197,101 +80,6 @@ __device__ __forceinline__ f32x16_t mma_split(const float* a, const float* b, f3
   }
 }
 
-template <typename T, int P>
-__device__ __forceinline__ float conv_at(const ChunkIn<T, P>& ci, int j, int p) {
-  float u = 0.f;
-#pragma unroll
-  for (int k = 0; k < kTaps; ++k) u = fmaf(ci.cw[p][k], ci.xs[j + k][p], u);
-  return u;
-}
-
-// Pass 1: agg[k][b][c][n] = sum_j exp(S_last - S_j) dt_j u_j[c] B_j[n] for the
-// head's channels c, and sdt[k][b][c] = the chunk's dt sum. The conv output of
-// each (row, channel), times its row weight, is formed once (into LDS, where
-// the staged x rows were, transposed to [channel][row]); the sum over rows is
-// a P x 16 product on the matrix cores, one 32-channel tile per wave. In bf16
-// the weighted conv outputs enter as a bf16 pair (the value rounded, then the
-// rounding error rounded), so the state keeps ~16 mantissa bits; B is exact
-// in bf16. fp32 uses fp32 products.
-template <typename T, int P>
-__global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
-    const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm, const float* __restrict__ A,
-    const float* __restrict__ conv_w, const T* __restrict__ conv_in, float* __restrict__ agg,
-    float* __restrict__ sdt, int L, int D, int H, int batch) {
-  typedef Mma<T> M;
-  constexpr int NU = kQ * P / kSsdThreads;   // conv outputs per thread
-  static_assert(kQ * P % kSsdThreads == 0 && P / 32 <= kSsdThreads / 64, "one 32-channel tile per wave");
-  __shared__ ChunkIn<T, P> ci;
-  __shared__ float wj[kQ];   // dt_j exp(S_last - S_j)
-  const int k = blockIdx.x, h = blockIdx.y;
-  const int64_t b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, lq = lane & 31, hh = lane >> 5;
-  const int t0 = k * kQ;
-  {
-    ChunkLoads<T, P> ld;
-    ld.issue(x, dt, Bm, nullptr, b, h, t0, L, D, H, false);
-    ld.commit(ci, nullptr, A, conv_w, conv_in, b, h, t0, D);
-  }
-  __syncthreads();
-  if (tid < kQ) wj[tid] = ci.dts[tid] * __builtin_amdgcn_exp2f(ci.s2[kQ - 1] - ci.s2[tid]);
-  __syncthreads();
-  float u[NU];
-#pragma unroll
-  for (int i = 0; i < NU; ++i) {
-    const int e = tid + i * kSsdThreads, j = e / P, p = e % P;
-    u[i] = conv_at(ci, j, p) * wj[j];
-  }
-  __syncthreads();   // the staged x rows are dead: U^T takes their place
-  typedef float URow[kQ + kRowPad];
-  URow* const ut = reinterpret_cast<URow*>(&ci.xs[0][0]);
-#pragma unroll
-  for (int i = 0; i < NU; ++i) {
-    const int e = tid + i * kSsdThreads, j = e / P, p = e % P;
-    ut[p][j] = u[i];
-  }
-  __syncthreads();
-  const int c0 = h * P;
-  const int64_t row0 = ((int64_t)k * batch + b) * D + c0;   // (chunk, sequence, first channel of the head)
-  if (wave < P / 32) {
-    // rows of the product: channels 32 wave + lq; columns: states lq (< 16)
-    f32x16_t acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < kQ / 16; ++ks) {
-      const int j0 = 16 * ks + 8 * hh;
-      float bv[8], av[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) bv[t] = lq < kSt ? ci.bs[j0 + t][lq] : 0.f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) av[t] = ut[32 * wave + lq][j0 + t];
-      const typename M::Frag fb = M::from_f32(bv);
-      if constexpr (sizeof(T) == 2) {
-        float hi[8], lo[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          hi[t] = __uint_as_float((uint32_t)f32_to_bf16_bits(av[t]) << 16);
-          lo[t] = av[t] - hi[t];
-        }
-        acc = M::mma(M::from_f32(hi), fb, acc);
-        acc = M::mma(M::from_f32(lo), fb, acc);
-      } else {
-        acc = M::mma(M::from_f32(av), fb, acc);
-      }
-    }
-    if (lq < kSt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int p = 32 * wave + 8 * (r >> 2) + 4 * hh + (r & 3);
-        agg[(row0 + p) * kSt + lq] = acc[r];
-      }
-    }
-  }
-  for (int p = tid; p < P; p += kSsdThreads) sdt[row0 + p] = ci.total;
-}
-
 // n 16-byte pieces straight into LDS, piece q at dst + 16 q, read from byte
 // offset off(q) of descriptor r (an offset out of range reads zeros); the
 // workgroup's waves take 64 pieces per load instruction in turn.
@@ -300,6 +88,185 @@ __device__ __forceinline__ void stage_pieces(__amdgpu_buffer_rsrc_t r, char* dst
   for (int q0 = 64 * wave; q0 < n; q0 += kSsdThreads) {
     const int q = q0 + lane;
     if (q < n) buf_load16_lds(r, off(q), dst + 16 * q0);
+  }
+}
+
+// The chunk's x rows t0 - 3 .. t0 + 63 of channels c0 .. c0 + P - 1, raw and
+// row-major ([67][P]), into LDS at dst; rows before 0 and at or past L read
+// zeros (rows before 0 are replaced by the carried history later, if any).
+template <typename T, int P>
+__device__ __forceinline__ void stage_x(const T* x, char* dst, int64_t b, int t0, int L, int D, int c0, int wave,
+                                        int lane) {
+  constexpr int E = Vec16<T>::n;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + b * L * D, (uint32_t)((int64_t)L * D * sizeof(T)));
+  stage_pieces(xrs, dst, (kQ + kTaps - 1) * (P / E), wave, lane, [&](int q) {
+    const int t = t0 - (kTaps - 1) + q / (P / E);
+    return t >= 0 ? (uint32_t)(((int64_t)t * D + c0 + (q % (P / E)) * E) * sizeof(T)) : kBufferNowhere;
+  });
+}
+
+// Rows -3 .. -1 of chunk 0 from the carried history (raw x of those rows,
+// oldest first); called once every wave's loads into LDS have landed, and
+// followed by a barrier.
+template <typename T, int P>
+__device__ __forceinline__ void put_history(T (*xr)[P], const T* conv_in, int64_t b, int D, int c0, int tid) {
+  if (tid < (kTaps - 1) * P) {
+    const int r = tid / P, p = tid % P;
+    xr[r][p] = conv_in[(b * D + c0 + p) * (kTaps - 1) + r];
+  }
+}
+
+// dt of row t0 + lane for head h (zero at or past L)
+template <typename T>
+__device__ __forceinline__ float load_dt(const T* dt, int64_t b, int t0, int L, int H, int h, int lane) {
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(dt + b * L * H, (uint32_t)((int64_t)L * H * sizeof(T)));
+  const uint32_t off = (uint32_t)(((int64_t)(t0 + lane) * H + h) * sizeof(T));
+  if constexpr (sizeof(T) == 2)
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(drs, off, 0, 0) << 16);
+  else
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(drs, off, 0, 0));
+}
+
+// LDS of the state pass: the raw x rows (later the partial sums of the waves
+// that share a channel tile), B transposed to [state][row], the row weights.
+template <typename T, int P>
+struct StateStage {
+  static constexpr int kNT = P / 32;                 // 32-channel tiles
+  static constexpr int kNK = 4 / kNT;                // waves per tile, each a share of the rows
+  static constexpr int kBPitch = kQ + 8;             // B^T row pitch (elements)
+  static constexpr int kXBytes = (kQ + kTaps - 1) * P * (int)sizeof(T);
+  static constexpr int kRedBytes = (kNK - 1) * kNT * 64 * 8 * (int)sizeof(float);
+  __attribute__((aligned(16))) char area[kXBytes > kRedBytes ? kXBytes : kRedBytes];
+  __attribute__((aligned(16))) T bt[kSt][kBPitch];
+  __attribute__((aligned(16))) float wj[kQ];        // dt_j exp(S_last - S_j)
+  __device__ __forceinline__ T (*xr())[P] { return reinterpret_cast<T (*)[P]>(area); }
+  __device__ __forceinline__ float (*red())[64][8] { return reinterpret_cast<float (*)[64][8]>(area); }
+};
+
+// Pass 1: agg[k][b][c][n] = sum_j exp(S_last - S_j) dt_j u_j[c] B_j[n] for the
+// head's channels c, and sdt[k][b][c] = the chunk's dt sum. The sum over the
+// chunk's rows is a product on the matrix cores with the states as rows (16
+// of 32 used) and the channels as columns: a lane owns one channel and forms
+// that channel's conv outputs for its operand rows itself, from registers,
+// times the row weights; B^T is the other operand. In bf16 the weighted conv
+// outputs enter as a bf16 pair (the value rounded, then the rounding error
+// rounded), so the state keeps ~16 mantissa bits; B is exact in bf16. fp32
+// uses fp32 products. With fewer than four 32-channel tiles the waves of a
+// tile each take a share of the rows and their sums are added in LDS.
+template <typename T, int P>
+__global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
+    const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm, const float* __restrict__ A,
+    const float* __restrict__ conv_w, const T* __restrict__ conv_in, float* __restrict__ agg,
+    float* __restrict__ sdt, int L, int D, int H, int batch) {
+  typedef Mma<T> M;
+  typedef StateStage<T, P> S;
+  constexpr int E = Vec16<T>::n;
+  constexpr int NT = S::kNT, NK = S::kNK, KBW = 4 / NK;   // tiles, waves per tile, 16-row blocks per wave
+  static_assert(kQ == 64 && NT * NK == 4, "four waves over the channel tiles and row shares");
+  __shared__ S st;
+  const int k = blockIdx.x, h = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int t0 = k * kQ;
+  const int c0 = h * P;
+
+  stage_x<T, P>(x, st.area, b, t0, L, D, c0, wave, lane);
+  // B rows, 16 bytes per thread, written transposed
+  const uint32_t rowb = kSt * sizeof(T);
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(Bm + b * L * kSt, (uint32_t)L * rowb);
+  constexpr int NBP = kQ * kSt / E;
+  u32x4_t bv = {0u, 0u, 0u, 0u};
+  if (tid < NBP) bv = buf_load16(brs, (uint32_t)t0 * rowb + 16u * tid);
+  const float dtv = wave == 0 ? load_dt(dt, b, t0, L, H, h, lane) : 0.f;
+  const int tp = wave % NT, ks = wave / NT;   // channel tile, share of the rows
+  const int c = 32 * tp + lq;                 // this lane's channel (operand column)
+  float w[kTaps];
+#pragma unroll
+  for (int j = 0; j < kTaps; ++j) w[j] = conv_w[(int64_t)(c0 + c) * kTaps + j];
+  wait_loads();
+  if (tid < NBP) {
+    const int j = tid / (kSt / E), n0 = (tid % (kSt / E)) * E;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        st.bt[n0 + 2 * e][j] = bf16{(uint16_t)(bv[e] & 0xffffu)};
+        st.bt[n0 + 2 * e + 1][j] = bf16{(uint16_t)(bv[e] >> 16)};
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.bt[n0 + e][j] = __uint_as_float(bv[e]);
+    }
+  }
+  float total = 0.f;
+  if (wave == 0) {
+    const float cum = wave_scan(dtv, lane);
+    const float s2 = A[h] * kLog2e * cum;
+    st.wj[lane] = dtv * __builtin_amdgcn_exp2f(__shfl(s2, 63, 64) - s2);
+    total = __shfl(cum, 63, 64);
+  }
+  lds_barrier();   // every wave's loads have landed
+  if (t0 == 0 && conv_in) {
+    put_history<T, P>(st.xr(), conv_in, b, D, c0, tid);
+    lds_barrier();
+  }
+
+  // the product over this wave's 16-row blocks
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KBW; ++kk) {
+    const int j0 = 16 * (ks * KBW + kk) + 8 * hh;   // operand rows j0 .. j0 + 7
+    float xv[8 + kTaps - 1];
+#pragma unroll
+    for (int m = 0; m < 8 + kTaps - 1; ++m) xv[m] = to_f32(st.xr()[j0 + m][c]);
+    const float4 wa = *reinterpret_cast<const float4*>(&st.wj[j0]);
+    const float4 wb = *reinterpret_cast<const float4*>(&st.wj[j0 + 4]);
+    const float wr[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+    float uv[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      float v = w[0] * xv[m];
+#pragma unroll
+      for (int j = 1; j < kTaps; ++j) v = fmaf(w[j], xv[m + j], v);
+      uv[m] = v * wr[m];
+    }
+    typename M::Frag fb = M::frag_at(&st.bt[lq & (kSt - 1)][j0]);
+    if (lq >= kSt) fb = M::zero();
+    if constexpr (sizeof(T) == 2) {
+      bf16x8_t uh, ul;
+      split_bf16(uv, uh, ul);
+      acc = M::mma(fb, uh, acc);
+      acc = M::mma(fb, ul, acc);
+    } else {
+      acc = M::mma(fb, M::from_f32(uv), acc);
+    }
+  }
+  // acc[r] for r < 8: state 8 (r / 4) + 4 hh + r % 4 of channel c
+  const int64_t row0 = ((int64_t)k * batch + b) * D + c0;   // (chunk, sequence, first channel of the head)
+  if constexpr (NK > 1) {
+    lds_barrier();   // every x read is done: the partial sums take the area
+    if (ks > 0) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) st.red()[(ks - 1) * NT + tp][lane][r] = acc[r];
+    }
+    lds_barrier();
+    if (ks == 0) {
+#pragma unroll
+      for (int q = 1; q < NK; ++q)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[r] += st.red()[(q - 1) * NT + tp][lane][r];
+    }
+  }
+  if (ks == 0) {
+    float4* dst = reinterpret_cast<float4*>(agg + (row0 + c) * kSt + 4 * hh);
+    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    dst[2] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+  if (wave == 0) {
+    for (int p = lane; p < P; p += 64) sdt[row0 + p] = total;
   }
 }
 
@@ -375,11 +342,7 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(
 
   // --- staging: x, B, C and the entering state into LDS; dt and the taps into registers
   {
-    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + b * L * D, (uint32_t)((int64_t)L * D * sizeof(T)));
-    stage_pieces(xrs, st.area, (kQ + kTaps - 1) * (P / E), wave, lane, [&](int q) {
-      const int t = t0 - (kTaps - 1) + q / (P / E);
-      return t >= 0 ? (uint32_t)(((int64_t)t * D + c0 + (q % (P / E)) * E) * sizeof(T)) : kBufferNowhere;
-    });
+    stage_x<T, P>(x, st.area, b, t0, L, D, c0, wave, lane);
     const uint32_t rowb = kSt * sizeof(T);
     const __amdgpu_buffer_rsrc_t brs = make_rsrc(Bm + b * L * kSt, (uint32_t)L * rowb);
     const __amdgpu_buffer_rsrc_t crs = make_rsrc(Cm + b * L * kSt, (uint32_t)L * rowb);
@@ -391,15 +354,7 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(
     stage_pieces(hrs, reinterpret_cast<char*>(&st.hs[0][0]), P * kSt / 4, wave, lane,
                  [](int q) { return 16u * q; });
   }
-  float dtv = 0.f;
-  if (wave == 0) {
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dt + b * L * H, (uint32_t)((int64_t)L * H * sizeof(T)));
-    const uint32_t off = (uint32_t)(((int64_t)(t0 + lane) * H + h) * sizeof(T));
-    if constexpr (sizeof(T) == 2)
-      dtv = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(drs, off, 0, 0) << 16);
-    else
-      dtv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(drs, off, 0, 0));
-  }
+  const float dtv = wave == 0 ? load_dt(dt, b, t0, L, H, h, lane) : 0.f;
   const int cp = tid % P, rb = tid / P;          // conv: channel, run of rows
   float w[kTaps];
 #pragma unroll
@@ -411,11 +366,8 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(
     st.s2[lane] = A[h] * kLog2e * cum;
   }
   lds_barrier();   // every wave's loads have landed
-  if (t0 == 0 && conv_in) {   // rows -3 .. -1 (zeros so far): the carried history
-    if (tid < (kTaps - 1) * P) {
-      const int r = tid / P;
-      st.xr()[r][cp] = conv_in[(b * D + c0 + cp) * (kTaps - 1) + r];
-    }
+  if (t0 == 0 && conv_in) {
+    put_history<T, P>(st.xr(), conv_in, b, D, c0, tid);
     lds_barrier();
   }
 
