@@ -110,8 +110,8 @@ __device__ __forceinline__ void stage_x(const T* x, char* dst, int64_t b, int t0
 // followed by a barrier.
 template <typename T, int P>
 __device__ __forceinline__ void put_history(T (*xr)[P], const T* conv_in, int64_t b, int D, int c0, int tid) {
-  if (tid < (kTaps - 1) * P) {
-    const int r = tid / P, p = tid % P;
+  for (int e = tid; e < (kTaps - 1) * P; e += kSsdThreads) {
+    const int r = e / P, p = e % P;
     xr[r][p] = conv_in[(b * D + c0 + p) * (kTaps - 1) + r];
   }
 }

@@ -204,10 +204,23 @@ def test_ring_prefill_then_decode():
     check("out", host(run.layers[0]["out"]), ref["out"][:, 0], 5e-3)
 
 
+SSD_CHAINS = [
+    # bf16, head width 64
+    (dict(batch=2, n_meta=5, n_tokens=200, d_inner=256, n_q_heads=2, n_kv_heads=1, window=40, act="bf16", seed=65,
+          ssm_heads=4), [55, 57, 140]),
+    # fp32, head width 32 (four waves share each channel tile); a first call of the meta rows alone
+    (dict(batch=2, n_meta=5, n_tokens=150, d_inner=128, n_q_heads=2, n_kv_heads=1, window=20, act="f32", seed=66,
+          ssm_heads=4), [5, 70, 100]),
+    # bf16, head width 128 (two channel tiles per wave); a call of exactly one chunk
+    (dict(batch=1, n_meta=8, n_tokens=180, d_inner=256, n_q_heads=4, n_kv_heads=2, window=50, act="bf16", seed=67,
+          ssm_heads=2), [64, 65, 130]),
+]
+
+
 @pytest.mark.parametrize("ring", [False, True], ids=["rows", "ring"])
-def test_continuation_chain_ssd(ring):
+@pytest.mark.parametrize("kw,cuts", SSD_CHAINS, ids=[f"ssdchain{i}" for i in range(len(SSD_CHAINS))])
+def test_continuation_chain_ssd(kw, cuts, ring):
     """A chain of calls with the Mamba-2 form: the carried state enters the
     block form's chain, the conv history its first chunk."""
-    cfg = synth.config("tiny_f32").with_(batch=2, n_meta=5, n_tokens=200, d_inner=256, n_q_heads=2, n_kv_heads=1,
-                                         window=40, act="bf16", seed=65, ssm_heads=4, name="chain_ssd")
-    check_chain(cfg, [55, 57, 140], ring)
+    cfg = synth.config("tiny_f32").with_(**kw, name="chain_ssd")
+    check_chain(cfg, cuts, ring)

@@ -432,6 +432,9 @@ SSD_SMALL = [
     # bf16, head width 32, 8 heads
     dict(batch=1, n_meta=16, n_tokens=300, d_inner=256, n_q_heads=8, n_kv_heads=2, window=64, act="bf16", seed=64,
          ssm_heads=8),
+    # bf16, head width 128, three heads, a ragged last chunk
+    dict(batch=2, n_meta=2, n_tokens=190, d_inner=384, n_q_heads=3, n_kv_heads=1, window=50, act="bf16", seed=68,
+         ssm_heads=3),
 ]
 
 
