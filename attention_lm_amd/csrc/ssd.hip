@@ -11,19 +11,19 @@
 //
 // Prefill, sequences cut into chunks of 64 rows:
 //   1. ssd_state_kernel: per (chunk, head, sequence), the state a chunk
-//      leaves from a zero start (P x 16, fp32 VALU) and its dt sum;
+//      leaves from a zero start (P x 16, a product over the chunk's rows on
+//      the matrix cores) and its dt sum;
 //   2. the chunk carry chain of the selective scan (ssm.hip), with one decay
 //      rate per head, gives every chunk's entering state and the final state;
 //   3. ssd_out_kernel: per (chunk, head, sequence), Y = [M | C exp(S)] x
 //      [U ; H^T] on the matrix cores, M[i][j] = (C_i . B_j) exp(S_i - S_j) dt_j
-//      below the diagonal (fp32 VALU into LDS), then D u and the silu(z) gate.
-//      In bf16 each fp32 operand enters as a bf16 value plus its bf16
-//      rounding error (three products): Y and D u can nearly cancel when dt
-//      is large, and one bf16 rounding of M and U would then show in y.
+//      on and below the diagonal (C B^T on the matrix cores, the decay on the
+//      VALU, kept in registers), then D u and the silu(z) gate. In bf16 each
+//      fp32 operand enters as a bf16 value plus its bf16 rounding error
+//      (three products): Y and D u can nearly cancel when dt is large, and
+//      one bf16 rounding of M and U would then show in y.
 // The conv (4 taps, causal, per channel) is recomputed in both passes from x
 // (and the carried history before row 0).
-#include <utility>
-
 #include "common.hpp"
 #include "launch.hpp"
 #include "mma.hpp"
