@@ -384,10 +384,12 @@ def test_decode_full_config_key_affine():
     run_decode_parity(synth.config("decode_affine"))
 
 
-def test_decode_continues_prefill():
-    """decode(prefill of L-1 rows) on the GPU equals the oracle's prefill of L rows, last row."""
+@pytest.mark.parametrize("ssm_heads", [0, 5], ids=["mamba1", "mamba2"])
+def test_decode_continues_prefill(ssm_heads):
+    """decode(prefill of L-1 rows) on the GPU equals the oracle's prefill of L rows, last row
+    (the scan in either form: the Mamba-2 prefill's final state enters the Mamba-2 decode step)."""
     cfg = synth.config("tiny_f32").with_(batch=2, n_meta=6, n_tokens=90, d_inner=320, n_q_heads=5, n_kv_heads=1,
-                                         window=33, act="bf16", seed=31, name="cont")
+                                         window=33, act="bf16", seed=31, ssm_heads=ssm_heads, name="cont")
     full = synth.make_prefill_inputs(cfg)
     L = cfg.seq_rows
     short_cfg = cfg.with_(n_tokens=cfg.n_tokens - 1)
