@@ -109,17 +109,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// workgroup barrier for a load pipeline: this wave first waits until at most
-// N of its global loads are outstanding (vmcnt drains in issue order, so the
-// earlier ones have landed, in LDS too) and its LDS operations are done
-template <int N>
-__device__ __forceinline__ void tile_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);   // vmcnt(N) lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Wave64 butterfly sum / max (deterministic order).
 __device__ __forceinline__ float wave_sum(float v) {
