@@ -276,11 +276,14 @@ __global__ __launch_bounds__(kChanPerBlock) void ssm_chunk_kernel(
 // kCarrySegs segments, one per wave of a workgroup of 64 chains. Each wave
 // composes its segment from a zero start (end state and summed dt), the waves
 // swap those through LDS, and each wave walks its segment again from its true
-// start, storing every carry. That is four times the waves of one walk per
+// start, storing every carry. That is eight times the waves of one walk per
 // chain (the chain is latency-bound: few dependent steps, all memory); the
 // second walk reuses the loaded values when a segment fits in one batch.
-constexpr int kCarrySegs = 4;
-constexpr int kCarryBatch = 24;
+// Eight segments of up to 12 steps measured faster than four of 24 (SWA
+// layer 10.4 -> 9.6 us, batched Mamba-2 workload 104 -> 89 us) and than
+// sixteen of 6 (10.3 / 122 us).
+constexpr int kCarrySegs = 8;
+constexpr int kCarryBatch = 12;
 __global__ __launch_bounds__(64 * kCarrySegs) void ssm_chunk_carry_kernel(const float* __restrict__ A,
                                                                          const float* __restrict__ agg,
                                                                          const float* __restrict__ sdt,
