@@ -381,22 +381,29 @@ __device__ __forceinline__ void vm_wait_at_most(int n) {
 // ---------------------------------------------------------------------------
 // Single-pass scan, for batches whose (sequence, channel) count alone fills
 // the chip: one exp(dt A) per element instead of two, and no carry chain.
-// Workgroup = 32 channels of one sequence x 16 states, 256 lanes: lane l holds
-// channel c0 + l % 32 and the states 2 (l / 32), 2 (l / 32) + 1 in registers
-// for the whole sequence. Per block of kScanRows rows:
-//   A. one lane per (row, channel): the conv output u, dt and dt u as fp32 in
-//      LDS, and the block's B and C rows as fp32, grouped by state pair;
-//   B. every lane advances its two states over the block's rows and leaves its
-//      part of C . h for each row in LDS;
-//   C. one lane per (row, channel): y = the eight parts + D u, times silu(z).
+// Workgroup = 64 channels of one sequence x 16 states, 256 lanes: wave w holds
+// the states 4w .. 4w + 3 and lane l the channel c0 + l, in registers for the
+// whole sequence. Per block of kScanRows rows:
+//   A. two (row, channel) items per lane (rows w and w + 4, channel l): the
+//      conv output u, dt and dt u, and D u, as fp32 in LDS; the block's B and
+//      C rows as fp32, grouped by state quad;
+//   B. every lane advances its four states over the block's rows and leaves
+//      its part of C . h for each row in LDS;
+//   C. the same two items per lane: y = the four parts + D u, times silu(z).
 // Work that is per (row, channel) (conv, dt u, gate) is done once, not once
-// per state. The next block's raw inputs load straight into LDS meanwhile.
-constexpr int kScanChan = 32;
+// per state, and each exp(dt A) is formed once. The next blocks' raw inputs
+// load straight into LDS meanwhile. Four states per lane keep the register
+// footprint per SIMD small enough (about 3 waves of 72 VGPRs on the batched
+// workload) that workgroups of the attention branch fit beside the scan's on
+// every compute unit.
+constexpr int kScanChan = 64;
 constexpr int kScanRows = 8;
-constexpr int kScanPairs = kStates / 2;
-constexpr int kScanStages = 4;       // staging ring: three blocks in flight ahead of the one in use
-constexpr int kScanRowsLoaded = 4;   // rows of phase B whose LDS values are in registers at once
-static_assert(kScanChan * kScanRows == 256 && kScanChan * kScanPairs == 256, "one lane per item");
+constexpr int kScanQuads = kStates / 4;   // one wave per state quad
+constexpr int kScanStages = 3;            // staging ring: two blocks in flight ahead of the one in use
+constexpr int kScanRowsLoaded = 2;        // rows of phase B whose LDS values are in registers at once
+constexpr int kScanItems = kScanRows * kScanChan / 256;   // (row, channel) items per lane in phases A and C
+static_assert(kScanQuads * 64 == 256 && kScanChan == 64 && kScanItems * kScanQuads == kScanRows,
+              "wave = state quad = row offset, lane = channel");
 
 template <typename T>
 struct Scan1Stage {   // one block's inputs as loaded (16-byte pieces, row-major)
@@ -414,28 +421,23 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
     const float* __restrict__ conv_w, const T* __restrict__ conv_in, const float* __restrict__ state_in,
     T* __restrict__ y, float* __restrict__ state_out, T* __restrict__ conv_state_out, int L, int Dch) {
   constexpr int E = Vec16<T>::n;                // elements per 16-byte piece
-  constexpr int CP = kScanChan / E;             // pieces per 32-channel row
+  constexpr int CP = kScanChan / E;             // pieces per 64-channel row
   constexpr int SP = kStates / E;               // pieces per B or C row
   constexpr int R = kScanRows;
   __shared__ __attribute__((aligned(16))) Scan1Stage<T> stage[kScanStages];
-  __shared__ __attribute__((aligned(16))) float2 dd[R][kScanChan];      // (dt, dt u)
-  __shared__ float us[R][kScanChan];                                    // u, for the D u term
-  __shared__ __attribute__((aligned(16))) float4 bcs[R][kScanPairs];    // (B, B, C, C) of a state pair
-  __shared__ float part[R][kScanPairs][kScanChan];                      // each pair's share of C . h
+  __shared__ __attribute__((aligned(16))) float2 dd[R][kScanChan];             // (dt, dt u)
+  __shared__ float du[R][kScanChan];                                           // D u
+  __shared__ __attribute__((aligned(16))) float4 bcq[R][kScanQuads][2];        // B, then C, of a state quad
+  __shared__ float part[R][kScanQuads][kScanChan];                             // each quad's share of C . h
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cl = tid & (kScanChan - 1);         // channel within the block (all phases)
-  const int sp = tid >> 5;                      // phase B: state pair; phases A, C: row of the block
-  // Workgroups go to the chip's 8 XCDs in turn by launch index, and each XCD
-  // has its own L2. The two channel blocks that share a 128-byte line of x, dt
-  // and z get launch indices 8 apart, so they run on one XCD at about the same
-  // time and the line comes from HBM once.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // B: state quad; A, C: rows wave, wave + 4
+  // One 64-channel block of a bf16 row is one 128-byte line, so no two
+  // workgroups share a line of x, dt, z or y.
   const int nblk_c = (Dch + kScanChan - 1) / kScanChan;
-  int id = (int)blockIdx.x;
-  if (id < (int)gridDim.x / 16 * 16) id = id / 16 * 16 + (id % 8) * 2 + (id % 16) / 8;
+  const int id = (int)blockIdx.x;
   const int c0 = (id % nblk_c) * kScanChan;
-  const int c = c0 + cl;
+  const int c = c0 + lane;
   const bool cv = c < Dch;
   const int cc = cv ? c : Dch - 1;
   const int64_t b = id / nblk_c;
@@ -460,14 +462,19 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
   // past the end of the descriptor and read zero.
   constexpr int NXP = (R + kConv - 1) * CP, NDP = R * CP, NBP = R * SP;
   constexpr int NXI = (NXP + 63) / 64;   // load instructions for x
-  static_assert((NDP + 63) / 64 == 1 && (NBP + 63) / 64 == 1, "dt, z, B, C pieces fit one instruction each");
-  uint32_t xo[NXI];
+  constexpr int NDI = (NDP + 63) / 64;   // ... for dt, and for z
+  static_assert(NBP <= 64, "B and C pieces fit one instruction each");
+  uint32_t xo[NXI], dzo[NDI];
 #pragma unroll
   for (int k = 0; k < NXI; ++k) {
     const int it = 64 * k + lane;
     xo[k] = (uint32_t)(it / CP) * row_b + col_b + (uint32_t)(16 * (it % CP));
   }
-  const uint32_t dzo = (uint32_t)(lane / CP) * row_b + col_b + (uint32_t)(16 * (lane % CP));
+#pragma unroll
+  for (int k = 0; k < NDI; ++k) {
+    const int it = 64 * k + lane;
+    dzo[k] = (uint32_t)(it / CP) * row_b + col_b + (uint32_t)(16 * (it % CP));
+  }
   const uint32_t bco = (uint32_t)(16 * lane);
   auto fetch = [&](int tb, Scan1Stage<T>& s) {
     if (wave == 0) {
@@ -477,7 +484,11 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
         if (64 * k + lane < NXP) buf_load16_lds(xrs, xo[k] + base, (char*)&s.x[0][0] + 16 * 64 * k);
     } else if (wave < 3) {
       const uint32_t base = (uint32_t)tb * row_b;
-      if (lane < NDP) buf_load16_lds(wave == 1 ? drs : zrs, dzo + base, wave == 1 ? (char*)&s.dt[0][0] : (char*)&s.z[0][0]);
+#pragma unroll
+      for (int k = 0; k < NDI; ++k)
+        if (64 * k + lane < NDP)
+          buf_load16_lds(wave == 1 ? drs : zrs, dzo[k] + base,
+                         (wave == 1 ? (char*)&s.dt[0][0] : (char*)&s.z[0][0]) + 16 * 64 * k);
     } else {
       const uint32_t base = (uint32_t)(tb * kStates * (int)sizeof(T));
       if (lane < NBP) {
@@ -486,19 +497,21 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
       }
     }
   };
-  const uint32_t yo = (uint32_t)sp * row_b + (uint32_t)(c * sizeof(T));   // phase C: this lane's row, channel
+  const uint32_t yo = (uint32_t)(c * sizeof(T));   // phase C: this lane's channel
 
-  float a0 = A[(int64_t)cc * kStates + 2 * sp] * kLog2e;
-  float a1 = A[(int64_t)cc * kStates + 2 * sp + 1] * kLog2e;
+  const float4 a4 = *reinterpret_cast<const float4*>(A + (int64_t)cc * kStates + 4 * wave);
+  const float a0 = a4.x * kLog2e, a1 = a4.y * kLog2e, a2 = a4.z * kLog2e, a3 = a4.w * kLog2e;
   float w[kConv];
 #pragma unroll
   for (int j = 0; j < kConv; ++j) w[j] = conv_w[(int64_t)cc * kConv + j];
   const float Dc = Dp[cc];
-  float h0 = 0.f, h1 = 0.f;
+  float h0 = 0.f, h1 = 0.f, h2 = 0.f, h3 = 0.f;
   if (state_in) {
-    const float2 s2 = *reinterpret_cast<const float2*>(state_in + (b * Dch + cc) * kStates + 2 * sp);
-    h0 = s2.x;
-    h1 = s2.y;
+    const float4 s4 = *reinterpret_cast<const float4*>(state_in + (b * Dch + cc) * kStates + 4 * wave);
+    h0 = s4.x;
+    h1 = s4.y;
+    h2 = s4.z;
+    h3 = s4.w;
   }
 
   // Staging ring of kScanStages blocks: block ib + kScanStages - 1 is fetched
@@ -506,67 +519,73 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
   // that are never used, so every wave issues the same loads per block and a
   // wait can count them. Before block ib, this wave's memory operations issued
   // after block ib's loads are: the loads of the blocks fetched since (n_ld
-  // instructions per block) and one y store per finished block, at most
-  // kScanStages - 1 of them in flight; vmcnt drains in issue order, so waiting
-  // until that many remain means block ib's loads have landed.
-  const int n_ld = wave == 0 ? NXI : wave < 3 ? 1 : 2;   // load instructions of this wave per block
+  // instructions per block) and kScanItems y stores per finished block, for at
+  // most kScanStages - 1 blocks; vmcnt drains in issue order, so waiting until
+  // that many remain means block ib's loads have landed.
+  const int n_ld = wave == 0 ? NXI : wave < 3 ? NDI : 2;   // load instructions of this wave per block
   const int nblk = (L + R - 1) / R;
 #pragma unroll
   for (int k = 0; k < kScanStages - 1; ++k) fetch(k * R, stage[k]);
   for (int ib = 0; ib < nblk; ++ib) {
     Scan1Stage<T>& s = stage[ib % kScanStages];
-    vm_wait_at_most((kScanStages - 2) * n_ld + min(ib, kScanStages - 1));
+    vm_wait_at_most((kScanStages - 2) * n_ld + min(ib, kScanStages - 1) * kScanItems);
     lds_barrier();   // block ib has landed (every wave waited for its loads); block ib - 1 is done
     if (ib == 0 && conv_in) {   // rows -3 .. -1: the carried conv history (oldest first)
-      if (tid < (kConv - 1) * kScanChan) {
-        const int r = tid / kScanChan;
-        s.x[r][cl] = conv_in[(b * Dch + cc) * (kConv - 1) + r];
-      }
+      if (tid < (kConv - 1) * kScanChan) s.x[wave][lane] = conv_in[(b * Dch + cc) * (kConv - 1) + wave];
       lds_barrier();
     }
     fetch((ib + kScanStages - 1) * R, stage[(ib + kScanStages - 1) % kScanStages]);
-    // A: lane = (row sp, channel cl)
-    {
+    // A: lane = (rows wave + 4 k, channel lane)
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      const int r = wave + kScanQuads * k;
       float xv[kConv];
 #pragma unroll
-      for (int j = 0; j < kConv; ++j) xv[j] = to_f32(s.x[sp + j][cl]);
+      for (int j = 0; j < kConv; ++j) xv[j] = to_f32(s.x[r + j][lane]);
       const float u = fmaf(w[0], xv[0], fmaf(w[1], xv[1], fmaf(w[2], xv[2], w[3] * xv[3])));
-      const float d = to_f32(s.dt[sp][cl]);
-      dd[sp][cl] = make_float2(d, d * u);
-      us[sp][cl] = u;
-      if (tid < R * kScanPairs) {
-        const int t = tid / kScanPairs, p = tid % kScanPairs;
-        bcs[t][p] = make_float4(to_f32(s.b[t][2 * p]), to_f32(s.b[t][2 * p + 1]), to_f32(s.c[t][2 * p]),
-                                to_f32(s.c[t][2 * p + 1]));
-      }
+      const float d = to_f32(s.dt[r][lane]);
+      dd[r][lane] = make_float2(d, d * u);
+      du[r][lane] = Dc * u;
+    }
+    if (tid < R * kScanQuads) {
+      const int t = tid / kScanQuads, qd = tid % kScanQuads;
+      bcq[t][qd][0] = make_float4(to_f32(s.b[t][4 * qd]), to_f32(s.b[t][4 * qd + 1]), to_f32(s.b[t][4 * qd + 2]),
+                                  to_f32(s.b[t][4 * qd + 3]));
+      bcq[t][qd][1] = make_float4(to_f32(s.c[t][4 * qd]), to_f32(s.c[t][4 * qd + 1]), to_f32(s.c[t][4 * qd + 2]),
+                                  to_f32(s.c[t][4 * qd + 3]));
     }
     lds_barrier();
-    // B: lane = (state pair sp, channel cl); the values of kScanRowsLoaded rows
-    // are read from LDS together, so that the row loop waits once per group
+    // B: lane = (state quad wave, channel lane); the values of kScanRowsLoaded
+    // rows are read from LDS together, so that the row loop waits once per group
 #pragma unroll
     for (int t0 = 0; t0 < R; t0 += kScanRowsLoaded) {
       float2 q[kScanRowsLoaded];
-      float4 g[kScanRowsLoaded];
+      float4 gb[kScanRowsLoaded], gc[kScanRowsLoaded];
 #pragma unroll
       for (int t = 0; t < kScanRowsLoaded; ++t) {
-        q[t] = dd[t0 + t][cl];
-        g[t] = bcs[t0 + t][sp];
+        q[t] = dd[t0 + t][lane];
+        gb[t] = bcq[t0 + t][wave][0];
+        gc[t] = bcq[t0 + t][wave][1];
       }
 #pragma unroll
       for (int t = 0; t < kScanRowsLoaded; ++t) {
-        h0 = fmaf(fast_exp2(q[t].x * a0), h0, q[t].y * g[t].x);
-        h1 = fmaf(fast_exp2(q[t].x * a1), h1, q[t].y * g[t].y);
-        part[t0 + t][sp][cl] = fmaf(g[t].z, h0, g[t].w * h1);
+        h0 = fmaf(fast_exp2(q[t].x * a0), h0, q[t].y * gb[t].x);
+        h1 = fmaf(fast_exp2(q[t].x * a1), h1, q[t].y * gb[t].y);
+        h2 = fmaf(fast_exp2(q[t].x * a2), h2, q[t].y * gb[t].z);
+        h3 = fmaf(fast_exp2(q[t].x * a3), h3, q[t].y * gb[t].w);
+        part[t0 + t][wave][lane] = fmaf(gc[t].x, h0, fmaf(gc[t].y, h1, fmaf(gc[t].z, h2, gc[t].w * h3)));
       }
     }
     lds_barrier();
-    // C: lane = (row sp, channel cl)
-    {
-      float acc = Dc * us[sp][cl];
+    // C: lane = (rows wave + 4 k, channel lane)
 #pragma unroll
-      for (int p = 0; p < kScanPairs; ++p) acc += part[sp][p][cl];
-      const float g = acc * silu(to_f32(s.z[sp][cl]));
-      buf_store(yrs, cv ? yo + (uint32_t)(ib * R) * row_b : kBufferNowhere, from_f32<T>(g));
+    for (int k = 0; k < kScanItems; ++k) {
+      const int r = wave + kScanQuads * k;
+      float acc = du[r][lane];
+#pragma unroll
+      for (int p = 0; p < kScanQuads; ++p) acc += part[r][p][lane];
+      const float g = acc * silu(to_f32(s.z[r][lane]));
+      buf_store(yrs, cv ? yo + (uint32_t)(ib * R + r) * row_b : kBufferNowhere, from_f32<T>(g));
     }
   }
   // the prefetches past the sequence land before the workgroup's LDS is released
@@ -574,8 +593,8 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
 
   if (!cv) return;
   if (state_out)
-    *reinterpret_cast<float2*>(state_out + (b * Dch + c) * kStates + 2 * sp) = make_float2(h0, h1);
-  if (conv_state_out && sp == 0) {   // raw x of rows L-3, L-2, L-1 (before row 0: the carried history, or zero)
+    *reinterpret_cast<float4*>(state_out + (b * Dch + c) * kStates + 4 * wave) = make_float4(h0, h1, h2, h3);
+  if (conv_state_out && wave == 0) {   // raw x of rows L-3, L-2, L-1 (before row 0: the carried history, or zero)
     T* csp = conv_state_out + (b * Dch + c) * (kConv - 1);
 #pragma unroll
     for (int j = 0; j < kConv - 1; ++j) {
@@ -643,9 +662,9 @@ hipError_t scan1_t(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
 }  // namespace
 
 bool ssm_single_pass(int batch, int d_inner) {
-  // the single-pass form's workgroups (32 channels of one sequence) fill the
-  // chip on their own: at least four per compute unit of a 256-CU device
-  return (int64_t)batch * ((d_inner + kScanChan - 1) / kScanChan) >= 1024;
+  // the single-pass form's waves (64 channels x 4 states of one sequence
+  // each) fill the chip on their own: at least two per SIMD of a 256-CU device
+  return (int64_t)batch * ((d_inner + 31) / 32) >= 1024;
 }
 
 int ssm_prefill_chunk_rows(int batch, int L, int d_inner) {
