@@ -251,6 +251,32 @@ struct PrefillCall {
   hipEvent_t* stage_events;
 };
 
+// Where the Mamba branch forks off a concurrent prefill. The attention branch
+// starts with its RoPE pass on `stream`; the Mamba branch either forks at once
+// (the scan starts beside the RoPE pass) or right after the RoPE pass (the
+// attention workgroups then take the chip first and the scan's fill in beside
+// them). The longer branch should start first: forking late lets a long
+// attention branch start without a scan in its way, but delays the scan by
+// the RoPE pass. The branch lengths are estimated from their work at rates
+// measured on MI355X for these kernels: attention ~1.0e15 flop/s over the
+// visible (query, key) pairs, the single-pass scan ~3.2e12 and the chunked
+// scan ~2.0e12 (row, channel, state) elements per second. (Measured with the
+// 25q/5kv layers: global layer 0.515 -> 0.486 ms forking late, SWA layer
+// 0.116 -> 0.121 ms and the batched workload 1.90 -> 2.00 ms forking late.)
+// The Mamba-2 form always forks at once.
+bool fork_after_rope(const hymba_mixer_desc* d, int pos0, int n_rows) {
+  if (d->ssm_heads > 0) return false;
+  const double cap = d->window > 0 ? (double)d->n_meta + d->window : 1e300;
+  auto vis = [&](double n) {   // sum over rows i < n of min(i + 1, cap)
+    return n <= cap ? n * (n + 1) / 2 : cap * (cap + 1) / 2 + (n - cap) * cap;
+  };
+  const double pairs = (vis((double)pos0 + n_rows) - vis((double)pos0)) * d->batch;
+  const double attn_s = pairs * d->n_q_heads * (2.0 * d->head_dim + 2.0 * d->head_dim_v) / 1.0e15;
+  const double elems = (double)d->batch * n_rows * d->d_inner * d->d_state;
+  const double scan_s = elems / (hymba::ssm_single_pass(d->batch, d->d_inner) ? 3.2e12 : 2.0e12);
+  return attn_s > scan_s;
+}
+
 int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params, const PrefillCall& c,
                  hipStream_t stream) {
   const int M = desc->n_meta, W = desc->window;
@@ -280,11 +306,7 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
   ForkCtx* fc = nullptr;
   if (!c.stage_events) HYMBA_TRY(fork_ctx(&fc));
   hipStream_t ssm_stream = stream;
-  if (fc) {
-    HYMBA_TRY(hipEventRecord(fc->fork, stream));
-    HYMBA_TRY(hipStreamWaitEvent(fc->aux, fc->fork, 0));
-    ssm_stream = fc->aux;
-  }
+  if (fc) ssm_stream = fc->aux;
   // Mamba branch (conv + scan), on ssm_stream
   auto mamba_branch = [&]() -> hipError_t {
     hymba::SsmPrefillArgs sa;
@@ -314,6 +336,24 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
     return hipSuccess;
   };
 
+  // The fork point of the Mamba branch on the second stream: it waits for
+  // what was enqueued on `stream` before the fork.
+  auto fork_point = [&]() -> hipError_t {
+    TRY_E(hipEventRecord(fc->fork, stream));
+    return hipStreamWaitEvent(fc->aux, fc->fork, 0);
+  };
+  auto run_mamba = [&]() -> hipError_t {
+    TRY_E(mamba_branch());
+    return hipEventRecord(fc->join, fc->aux);
+  };
+  const bool late = fc && fork_after_rope(desc, c.pos0, L);
+  bool forked = false;
+  auto after_rope = [&]() -> hipError_t {
+    if (!late || forked) return hipSuccess;
+    forked = true;
+    TRY_E(fork_point());
+    return run_mamba();
+  };
   auto attention_branch = [&]() -> hipError_t {
     // Attention branch. Where the rotated keys and the values that attention
     // reads live (row j of k_src / v_src = position j - shift):
@@ -358,11 +398,13 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
         kc.n = kc.na + (L - kc.pb);
       }
       TRY_E(hymba::launch_rope_prefill(ra, stream, tm(3)));
+      TRY_E(after_rope());
     } else if (!ring) {
       ra.k_rot = c.k_cache; ra.k_rows = cap; ra.v_copy = c.v_cache; ra.v_rows = cap;
       ra.k_row0 = ra.v_row0 = c.pos0;
       aa.k_rot = c.k_cache; aa.k_rows = cap; aa.v = c.v_cache; aa.v_rows = cap; aa.q_pos0 = c.pos0;
       TRY_E(hymba::launch_rope_prefill(ra, stream, tm(3)));
+      TRY_E(after_rope());
     } else {
       // assembly row r: position r below n_meta, then a0 + (r - n_meta); the
       // attention runs on assembly rows as positions (the window rule depends on
@@ -381,6 +423,7 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
       ra.k_row0 = ra.v_row0 = M + nw;
       aa.k_rot = asm_k; aa.k_rows = R; aa.v = asm_v; aa.v_rows = R; aa.q_pos0 = M + nw;
       TRY_E(hymba::launch_rope_prefill(ra, stream, tm(3)));
+      TRY_E(after_rope());
       // the new rows that stay: the last `window` positions (after the gather above)
       kc.src.k = asm_k; kc.src.v = asm_v; kc.src.k_rows = kc.src.v_rows = R;
       kc.src.mode = hymba::KvSide::kLinear; kc.src.base = c.pos0 - (M + nw);
@@ -391,14 +434,14 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
     TRY_E(hymba::launch_attn_prefill(aa, stream, tm(4)));
     return hipSuccess;
   };
-  // Enqueued attention first when the branches run concurrently: its
-  // workgroups then take their slots before the scan's fill the chip, and
-  // scan waves still fit beside them (attention is register-limited to two
-  // waves per SIMD). With stage events, the order of the stage list.
+  // When the branches run concurrently the attention branch is enqueued
+  // first; a Mamba branch that forks at once follows it in host order (its
+  // scan starts beside the RoPE pass), one that forks late is enqueued right
+  // after the RoPE pass. With stage events, the order of the stage list.
   if (fc) {
+    if (!late) HYMBA_TRY(fork_point());
     HYMBA_TRY(attention_branch());
-    HYMBA_TRY(mamba_branch());
-    HYMBA_TRY(hipEventRecord(fc->join, fc->aux));
+    if (!late) HYMBA_TRY(run_mamba());
   } else {
     HYMBA_TRY(mamba_branch());
     HYMBA_TRY(attention_branch());
