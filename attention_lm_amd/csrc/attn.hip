@@ -83,8 +83,11 @@ __device__ __forceinline__ void rope_cs_step(int pos, int i, double r, float* c,
 // softmax exponent in base 2.
 
 // Two rows per workgroup: for the usual head counts a thread then has one
-// rotation item and at most one value-copy item, and both loads are issued
-// before either store (the kernel moves bytes; what limits it is latency).
+// rotation item and at most one value-copy item. A thread issues the loads of
+// its first items before the workgroup forms the rows' cos/sin (the angles do
+// not depend on them), so the loads' latency overlaps that arithmetic; beside
+// a scan that keeps the VALU busy, a pass that formed its angles first and
+// loaded afterwards spent most of its time waiting on one after the other.
 constexpr int kRopeRows = 2;
 constexpr int kRopeThreads = 256;
 
@@ -92,70 +95,89 @@ template <typename T>
 __global__ __launch_bounds__(kRopeThreads) void rope_prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ q_rot,
     T* __restrict__ k_rot, T* __restrict__ v_copy, int64_t k_rows, int64_t v_rows, int64_t k_row0, int64_t v_row0,
-    const float* __restrict__ k_scale, int L, int pos0, int Hq, int Hkv, int dv, float base, float q_scale) {
+    const float* __restrict__ k_scale, int L, int pos0, int Hq, int Hkv, int dv, double freq_step, float q_scale) {
   __shared__ float cs[kRopeRows][kHd / 2];
   __shared__ float sn[kRopeRows][kHd / 2];
   const int r0 = blockIdx.x * kRopeRows;
   const int64_t b = blockIdx.y;
   const int tid = threadIdx.x;
-  for (int t = tid; t < kRopeRows * (kHd / 2); t += blockDim.x) {
-    const int r = t / (kHd / 2), i = t % (kHd / 2);
-    rope_cs(pos0 + r0 + r, i, base, &cs[r][i], &sn[r][i]);
-  }
-  __syncthreads();
   const int nrows = min(kRopeRows, L - r0);
   const int H = Hq + Hkv;
   const int rot_items = nrows * H * 4;                      // (row, head, group of 8 pairs)
   const int per_row = Hkv * dv / 8;
   const int v_items = v_copy ? nrows * per_row : 0;         // (row, 8-element chunk)
-  for (int it = tid; it < max(rot_items, v_items); it += blockDim.x) {
-    // loads of both items first
-    const bool has_v = it < v_items;
-    float vf[8];
-    int64_t v_dst = 0;
-    if (has_v) {
+  const int n_items = max(rot_items, v_items);
+
+  // one (rotation, value-copy) item pair: loads, then rotation and stores
+  struct Item {
+    bool has_v, has_r;
+    int g8, rr;
+    float vf[8], lo[8], hi[8], slo[8], shi[8];   // slo, shi: per-dim output scale of the pair's halves
+    int64_t v_dst;
+    T* dst;
+  };
+  auto load = [&](int it, Item& m) {
+    m.has_v = it < v_items;
+    m.v_dst = 0;
+    if (m.has_v) {
       const int r = it / per_row, e = it % per_row;
-      load8(v + (b * L + r0 + r) * (int64_t)(Hkv * dv) + 8 * e, vf);
-      v_dst = (b * v_rows + v_row0 + r0 + r) * (int64_t)(Hkv * dv) + 8 * e;
+      load8(v + (b * L + r0 + r) * (int64_t)(Hkv * dv) + 8 * e, m.vf);
+      m.v_dst = (b * v_rows + v_row0 + r0 + r) * (int64_t)(Hkv * dv) + 8 * e;
     }
-    const bool has_r = it < rot_items;
-    const int g8 = it & 3, hr = it >> 2, hd = hr % H, rr = hr / H;
-    T* dst = nullptr;
-    float slo[8], shi[8], lo[8], hi[8];   // per-dim output scale of the pair's two halves
+    m.has_r = it < rot_items;
+    m.g8 = it & 3;
+    const int hr = it >> 2, hd = hr % H;
+    m.rr = hr / H;
+    m.dst = nullptr;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) slo[e] = shi[e] = 1.f;
-    if (has_r) {
-      const int row = r0 + rr;
+    for (int e = 0; e < 8; ++e) m.slo[e] = m.shi[e] = 1.f;
+    if (m.has_r) {
+      const int row = r0 + m.rr;
       const T* src;
       if (hd < Hq) {
         src = q + ((b * L + row) * Hq + hd) * kHd;
-        dst = q_rot + ((b * L + row) * Hq + hd) * kHd;
+        m.dst = q_rot + ((b * L + row) * Hq + hd) * kHd;
         if (k_scale) {   // shared-key affine: q (.) w of the head's kv group
           const float* w = k_scale + (hd / (Hq / Hkv)) * kHd;
-          load8(w + 8 * g8, slo);
-          load8(w + 32 + 8 * g8, shi);
+          load8(w + 8 * m.g8, m.slo);
+          load8(w + 32 + 8 * m.g8, m.shi);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { slo[e] *= q_scale; shi[e] *= q_scale; }
+        for (int e = 0; e < 8; ++e) { m.slo[e] *= q_scale; m.shi[e] *= q_scale; }
       } else {
         src = k + ((b * L + row) * Hkv + (hd - Hq)) * kHd;
-        dst = k_rot + ((b * k_rows + k_row0 + row) * Hkv + (hd - Hq)) * kHd;
+        m.dst = k_rot + ((b * k_rows + k_row0 + row) * Hkv + (hd - Hq)) * kHd;
       }
-      load8(src + 8 * g8, lo);
-      load8(src + 32 + 8 * g8, hi);
+      load8(src + 8 * m.g8, m.lo);
+      load8(src + 32 + 8 * m.g8, m.hi);
     }
-    if (has_r) {
+  };
+  auto finish = [&](Item& m) {
+    if (m.has_r) {
       float olo[8], ohi[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float c = cs[rr][8 * g8 + e], s = sn[rr][8 * g8 + e];
-        olo[e] = (lo[e] * c - hi[e] * s) * slo[e];
-        ohi[e] = (hi[e] * c + lo[e] * s) * shi[e];
+        const float c = cs[m.rr][8 * m.g8 + e], s = sn[m.rr][8 * m.g8 + e];
+        olo[e] = (m.lo[e] * c - m.hi[e] * s) * m.slo[e];
+        ohi[e] = (m.hi[e] * c + m.lo[e] * s) * m.shi[e];
       }
-      store8(dst + 8 * g8, olo);
-      store8(dst + 32 + 8 * g8, ohi);
+      store8(m.dst + 8 * m.g8, olo);
+      store8(m.dst + 32 + 8 * m.g8, ohi);
     }
-    if (has_v) store8(v_copy + v_dst, vf);
+    if (m.has_v) store8(v_copy + m.v_dst, m.vf);
+  };
+
+  Item m;
+  if (tid < n_items) load(tid, m);
+  for (int t = tid; t < kRopeRows * (kHd / 2); t += blockDim.x) {
+    const int r = t / (kHd / 2), i = t % (kHd / 2);
+    rope_cs_step(pos0 + r0 + r, i, freq_step, &cs[r][i], &sn[r][i]);
+  }
+  __syncthreads();
+  if (tid < n_items) finish(m);
+  for (int it = tid + (int)blockDim.x; it < n_items; it += blockDim.x) {   // heads past one round of threads
+    load(it, m);
+    finish(m);
   }
 }
 
@@ -1480,7 +1502,7 @@ hipError_t rope_t(const RopeArgs& a, hipStream_t stream, Timing tm) {
   HYMBA_LAUNCH(rope_prefill_kernel<T>, grid, dim3(kRopeThreads), 0, stream, tm, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (T*)a.q_rot, (T*)a.k_rot, (T*)a.v_copy, a.k_rows, a.v_rows, a.k_row0,
                      a.v_row0, a.k_scale, a.L, a.pos0, a.n_q_heads,
-                     a.n_kv_heads, a.head_dim_v, a.rope_base, kScaleLog2e);
+                     a.n_kv_heads, a.head_dim_v, std::pow((double)a.rope_base, -2.0 / kHd), kScaleLog2e);
   return hipGetLastError();
 }
 
