@@ -251,19 +251,22 @@ struct PrefillCall {
   hipEvent_t* stage_events;
 };
 
-// Where the Mamba branch forks off a concurrent prefill. The attention branch
-// starts with its RoPE pass on `stream`; the Mamba branch either forks at once
-// (the scan starts beside the RoPE pass) or right after the RoPE pass (the
+// How a concurrent prefill forks. The longer branch should start first. If
+// the attention branch is the longer one it runs on `stream` and the Mamba
+// branch forks onto the second stream right after the RoPE pass (the
 // attention workgroups then take the chip first and the scan's fill in beside
-// them). The longer branch should start first: forking late lets a long
-// attention branch start without a scan in its way, but delays the scan by
-// the RoPE pass. The branch lengths are estimated from their work at rates
+// them). Otherwise the Mamba branch runs on `stream`, its first kernel
+// starting at once, and the attention branch (RoPE pass, then attention)
+// forks onto the second stream, so that its workgroups arrive after the
+// scan's first pass has been dispatched. The branch lengths are estimated from their work at rates
 // measured on MI355X for these kernels: attention ~1.0e15 flop/s over the
 // visible (query, key) pairs, the single-pass scan ~3.2e12 and the chunked
 // scan ~2.0e12 (row, channel, state) elements per second. (Measured with the
 // 25q/5kv layers: global layer 0.515 -> 0.486 ms forking late, SWA layer
-// 0.116 -> 0.121 ms and the batched workload 1.90 -> 2.00 ms forking late.)
-// The Mamba-2 form always forks at once.
+// 0.116 -> 0.121 ms and the batched workload 1.90 -> 2.00 ms forking late;
+// with the Mamba branch on `stream` and the attention branch forked, SWA
+// layer 0.123 -> 0.110 ms against the attention branch on `stream`.) The
+// Mamba-2 form never forks late.
 bool fork_after_rope(const hymba_mixer_desc* d, int pos0, int n_rows) {
   if (d->ssm_heads > 0) return false;
   const double cap = d->window > 0 ? (double)d->n_meta + d->window : 1e300;
@@ -301,12 +304,15 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
     }
     return t;
   };
-  // The two branches are independent until the fusion: without stage events the
-  // Mamba branch runs on a second stream, concurrently with the attention branch.
+  // The two branches are independent until the fusion: without stage events
+  // they run concurrently, one of them on a second stream.
   ForkCtx* fc = nullptr;
   if (!c.stage_events) HYMBA_TRY(fork_ctx(&fc));
-  hipStream_t ssm_stream = stream;
-  if (fc) ssm_stream = fc->aux;
+  // The longer branch runs on `stream`, the other on the second stream (see
+  // fork_after_rope).
+  const bool late = fc && fork_after_rope(desc, c.pos0, L);
+  hipStream_t ssm_stream = stream, attn_stream = stream;
+  if (fc) (late ? ssm_stream : attn_stream) = fc->aux;
   // Mamba branch (conv + scan), on ssm_stream
   auto mamba_branch = [&]() -> hipError_t {
     hymba::SsmPrefillArgs sa;
@@ -336,23 +342,19 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
     return hipSuccess;
   };
 
-  // The fork point of the Mamba branch on the second stream: it waits for
-  // what was enqueued on `stream` before the fork.
+  // The fork point of the branch that runs on the second stream: it waits
+  // for what was enqueued on `stream` before the fork.
   auto fork_point = [&]() -> hipError_t {
     TRY_E(hipEventRecord(fc->fork, stream));
     return hipStreamWaitEvent(fc->aux, fc->fork, 0);
   };
-  auto run_mamba = [&]() -> hipError_t {
-    TRY_E(mamba_branch());
-    return hipEventRecord(fc->join, fc->aux);
-  };
-  const bool late = fc && fork_after_rope(desc, c.pos0, L);
   bool forked = false;
   auto after_rope = [&]() -> hipError_t {
     if (!late || forked) return hipSuccess;
     forked = true;
     TRY_E(fork_point());
-    return run_mamba();
+    TRY_E(mamba_branch());
+    return hipEventRecord(fc->join, fc->aux);
   };
   auto attention_branch = [&]() -> hipError_t {
     // Attention branch. Where the rotated keys and the values that attention
@@ -397,13 +399,13 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
         kc.na = std::min(M, L); kc.pa = 0; kc.pb = std::max(M, L - W);
         kc.n = kc.na + (L - kc.pb);
       }
-      TRY_E(hymba::launch_rope_prefill(ra, stream, tm(3)));
+      TRY_E(hymba::launch_rope_prefill(ra, attn_stream, tm(3)));
       TRY_E(after_rope());
     } else if (!ring) {
       ra.k_rot = c.k_cache; ra.k_rows = cap; ra.v_copy = c.v_cache; ra.v_rows = cap;
       ra.k_row0 = ra.v_row0 = c.pos0;
       aa.k_rot = c.k_cache; aa.k_rows = cap; aa.v = c.v_cache; aa.v_rows = cap; aa.q_pos0 = c.pos0;
-      TRY_E(hymba::launch_rope_prefill(ra, stream, tm(3)));
+      TRY_E(hymba::launch_rope_prefill(ra, attn_stream, tm(3)));
       TRY_E(after_rope());
     } else {
       // assembly row r: position r below n_meta, then a0 + (r - n_meta); the
@@ -418,11 +420,11 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
       g.dst.k = asm_k; g.dst.v = asm_v; g.dst.k_rows = g.dst.v_rows = R; g.dst.mode = hymba::KvSide::kIndex;
       g.dst.base = 0;
       g.na = M; g.pa = 0; g.pb = a0; g.n = M + nw;
-      TRY_E(hymba::launch_kv_copy(g, stream));
+      TRY_E(hymba::launch_kv_copy(g, attn_stream));
       ra.k_rot = asm_k; ra.k_rows = R; ra.v_copy = asm_v; ra.v_rows = R;
       ra.k_row0 = ra.v_row0 = M + nw;
       aa.k_rot = asm_k; aa.k_rows = R; aa.v = asm_v; aa.v_rows = R; aa.q_pos0 = M + nw;
-      TRY_E(hymba::launch_rope_prefill(ra, stream, tm(3)));
+      TRY_E(hymba::launch_rope_prefill(ra, attn_stream, tm(3)));
       TRY_E(after_rope());
       // the new rows that stay: the last `window` positions (after the gather above)
       kc.src.k = asm_k; kc.src.v = asm_v; kc.src.k_rows = kc.src.v_rows = R;
@@ -430,18 +432,22 @@ int prefill_impl(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
       kc.pb = std::max(c.pos0, c.pos0 + L - W); kc.na = 0; kc.pa = 0;
       kc.n = c.pos0 + L - kc.pb;
     }
-    TRY_E(hymba::launch_kv_copy(kc, stream));
-    TRY_E(hymba::launch_attn_prefill(aa, stream, tm(4)));
+    TRY_E(hymba::launch_kv_copy(kc, attn_stream));
+    TRY_E(hymba::launch_attn_prefill(aa, attn_stream, tm(4)));
     return hipSuccess;
   };
-  // When the branches run concurrently the attention branch is enqueued
-  // first; a Mamba branch that forks at once follows it in host order (its
-  // scan starts beside the RoPE pass), one that forks late is enqueued right
-  // after the RoPE pass. With stage events, the order of the stage list.
-  if (fc) {
-    if (!late) HYMBA_TRY(fork_point());
+  // Concurrent branches: with a late fork the attention branch runs on
+  // `stream` and forks the Mamba branch after its RoPE pass; otherwise the
+  // Mamba branch runs on `stream`, starting at once, and the attention branch
+  // forks onto the second stream. With stage events, the order of the stage
+  // list on `stream`.
+  if (fc && late) {
     HYMBA_TRY(attention_branch());
-    if (!late) HYMBA_TRY(run_mamba());
+  } else if (fc) {
+    HYMBA_TRY(fork_point());
+    HYMBA_TRY(mamba_branch());
+    HYMBA_TRY(attention_branch());
+    HYMBA_TRY(hipEventRecord(fc->join, fc->aux));
   } else {
     HYMBA_TRY(mamba_branch());
     HYMBA_TRY(attention_branch());

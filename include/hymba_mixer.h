@@ -38,9 +38,9 @@
  *    HIP call failed; hymba_last_hip_error() gives its hipError_t (per thread).
  *  - State kept by the library: the last HIP error (per thread); per calling
  *    thread and device, a second stream (non-blocking, default priority) and
- *    two events, created on the first prefill call, on which the Mamba branch
- *    of a prefill runs beside the attention branch (joined on `stream` before
- *    the fusion); the compute-unit count of each device, read once; and the
+ *    two events, created on the first prefill call, on which one branch of a
+ *    prefill runs beside the other (joined on `stream` before the fusion);
+ *    the compute-unit count of each device, read once; and the
  *    static scratch of hymba_mixer_decode_noalloc on each device. Nothing else
  *    persists between calls.
  *  - Beyond the minimal interface (tensors, sizes, stream), prefill and decode
@@ -196,10 +196,12 @@ int hymba_mixer_prefill_chunk_rows(const hymba_mixer_desc* desc);
  *                  carries, scan output, rotary, attention, fusion; one kernel
  *                  each; a stage with nothing to do records both back to back).
  *                  For per-kernel timing; the caller owns the events.
- * Without stage events the Mamba branch (conv + scan) runs on a second stream
- * of the calling thread, concurrently with the attention branch; both join on
- * `stream` before the fusion, so ordering on `stream` is as if serial. With
- * stage events every stage runs on `stream`, one after the other.            */
+ * Without stage events the two branches run concurrently: the one the
+ * library estimates to be longer on `stream`, the other on a second stream of
+ * the calling thread that waits for the work enqueued on `stream` before the
+ * call (the Mamba branch may instead wait for the RoPE pass too); both join
+ * on `stream` before the fusion, so ordering on `stream` is as if serial.
+ * With stage events every stage runs on `stream`, one after the other.       */
 int hymba_mixer_prefill(const hymba_mixer_desc* desc, const hymba_mixer_params* params,
                         const void* x, const void* z, const void* dt, const void* B, const void* C,
                         const void* q, const void* k, const void* v,
