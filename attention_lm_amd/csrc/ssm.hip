@@ -385,22 +385,22 @@ __device__ __forceinline__ void vm_wait_at_most(int n) {
 // the states 4w .. 4w + 3 and lane l the channel c0 + l, in registers for the
 // whole sequence. Per block of kScanRows rows:
 //   A. two (row, channel) items per lane (rows w and w + 4, channel l): the
-//      conv output u, dt and dt u, and D u, as fp32 in LDS; the block's B and
-//      C rows as fp32, grouped by state quad;
+//      conv output u, dt and dt u as fp32 in LDS (D u stays in the lane's
+//      registers); the block's B and C rows as fp32, grouped by state quad;
 //   B. every lane advances its four states over the block's rows and leaves
 //      its part of C . h for each row in LDS;
 //   C. the same two items per lane: y = the four parts + D u, times silu(z).
 // Work that is per (row, channel) (conv, dt u, gate) is done once, not once
 // per state, and each exp(dt A) is formed once. The next blocks' raw inputs
 // load straight into LDS meanwhile. Four states per lane keep the register
-// footprint per SIMD small enough (about 3 waves of 72 VGPRs on the batched
-// workload) that workgroups of the attention branch fit beside the scan's on
-// every compute unit.
+// footprint per SIMD small enough (3 to 4 waves of 56 VGPRs on the batched
+// workload) that a workgroup of the attention branch fits beside the scan's
+// on every compute unit.
 constexpr int kScanChan = 64;
 constexpr int kScanRows = 8;
 constexpr int kScanQuads = kStates / 4;   // one wave per state quad
 constexpr int kScanStages = 3;            // staging ring: two blocks in flight ahead of the one in use
-constexpr int kScanRowsLoaded = 2;        // rows of phase B whose LDS values are in registers at once
+constexpr int kScanRowsLoaded = 1;        // rows of phase B whose LDS values are in registers at once
 constexpr int kScanItems = kScanRows * kScanChan / 256;   // (row, channel) items per lane in phases A and C
 static_assert(kScanQuads * 64 == 256 && kScanChan == 64 && kScanItems * kScanQuads == kScanRows,
               "wave = state quad = row offset, lane = channel");
@@ -426,7 +426,6 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
   constexpr int R = kScanRows;
   __shared__ __attribute__((aligned(16))) Scan1Stage<T> stage[kScanStages];
   __shared__ __attribute__((aligned(16))) float2 dd[R][kScanChan];             // (dt, dt u)
-  __shared__ float du[R][kScanChan];                                           // D u
   __shared__ __attribute__((aligned(16))) float4 bcq[R][kScanQuads][2];        // B, then C, of a state quad
   __shared__ float part[R][kScanQuads][kScanChan];                             // each quad's share of C . h
 
@@ -536,6 +535,7 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
     }
     fetch((ib + kScanStages - 1) * R, stage[(ib + kScanStages - 1) % kScanStages]);
     // A: lane = (rows wave + 4 k, channel lane)
+    float du[kScanItems];   // D u of this lane's items, used again in phase C
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
       const int r = wave + kScanQuads * k;
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
       const float u = fmaf(w[0], xv[0], fmaf(w[1], xv[1], fmaf(w[2], xv[2], w[3] * xv[3])));
       const float d = to_f32(s.dt[r][lane]);
       dd[r][lane] = make_float2(d, d * u);
-      du[r][lane] = Dc * u;
+      du[k] = Dc * u;
     }
     if (tid < R * kScanQuads) {
       const int t = tid / kScanQuads, qd = tid % kScanQuads;
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(256) void ssm_scan1_kernel(
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
       const int r = wave + kScanQuads * k;
-      float acc = du[r][lane];
+      float acc = du[k];
 #pragma unroll
       for (int p = 0; p < kScanQuads; ++p) acc += part[r][p][lane];
       const float g = acc * silu(to_f32(s.z[r][lane]));
