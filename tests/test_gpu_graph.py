@@ -73,6 +73,20 @@ def test_prefill_graph(act):
     replay_and_check(capture(run), outs, ref)
 
 
+def test_prefill_graph_attention_branch_first():
+    """A geometry whose attention branch is the longer one: the Mamba branch
+    forks onto the second stream after the RoPE pass, inside the capture."""
+    from test_gpu_parity import LATE_FORK, attention_outweighs_scan
+    cfg = synth.config("tiny_f32").with_(**LATE_FORK, name="graph_late_fork")
+    assert attention_outweighs_scan(cfg)
+    run = Prefill(cfg, synth.make_prefill_inputs(cfg))
+    outs = dict(run.o, out=run.out)
+    run()
+    torch.cuda.synchronize()
+    ref = snap(outs)
+    replay_and_check(capture(run), outs, ref)
+
+
 def test_prefill_continue_graph():
     """A continuation on the compact cache: its carried conv history is staged
     by a device copy inside the call, and state, conv history and cache are

@@ -248,6 +248,31 @@ def test_prefill_ssd_batched_sequences():
     run_prefill_parity(cfg, rows=block_rows(cfg, head=20, tail=10))
 
 
+# A global layer whose attention branch outweighs its scan: the library runs
+# attention on the calling stream and forks the Mamba branch after the RoPE
+# pass (the estimate below is the library's rule: attention flops over the
+# visible pairs at 1e15 flop/s against scan elements at 2e12 per second).
+LATE_FORK = dict(batch=1, n_meta=16, n_tokens=3984, d_inner=512, n_q_heads=16, n_kv_heads=2, window=0, act="bf16",
+                 seed=75)
+
+
+def attention_outweighs_scan(cfg):
+    L = cfg.seq_rows
+    cap = cfg.n_meta + cfg.window if cfg.window > 0 else L
+    pairs = sum(min(i + 1, cap) for i in range(L)) * cfg.batch
+    attn_s = pairs * cfg.n_q_heads * (2 * cfg.head_dim + 2 * cfg.head_dim_v) / 1e15
+    scan_s = cfg.batch * L * cfg.d_inner * cfg.d_state / 2e12
+    return attn_s > scan_s
+
+
+def test_prefill_attention_branch_first():
+    """The concurrent prefill with the Mamba branch forked after the RoPE
+    pass: every row of every output against the oracle."""
+    cfg = synth.config("tiny_f32").with_(**LATE_FORK, name="late_fork")
+    assert attention_outweighs_scan(cfg)
+    run_prefill_parity(cfg)
+
+
 @pytest.mark.parametrize("act", ["bf16", "f32"])
 def test_prefill_xcd_order_g8(act):
     """The attention's XCD-major work order (many rounds of workgroups) at
