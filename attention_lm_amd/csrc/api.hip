@@ -15,7 +15,7 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 // Per calling thread and device: a second stream (default priority) and two
-// events, used to run the Mamba branch concurrently with the attention branch.
+// events, used to run one prefill branch concurrently with the other.
 // Per-thread so that calls from different host threads never share them.
 struct ForkCtx {
   hipStream_t aux = nullptr;

@@ -1,5 +1,5 @@
 """The C ABI's calls captured into HIP graphs (torch.cuda.graph on the calling
-stream; the prefill's Mamba branch forks onto the library's second stream and
+stream; one branch of the prefill forks onto the library's second stream and
 joins back inside the capture). Every replay must equal the eager call bit for
 bit, with the program's own eager work and synchronizations between replays:
 outputs cleared, and for the calls that update state in place (continuation,
