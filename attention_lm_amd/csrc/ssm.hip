@@ -663,8 +663,12 @@ hipError_t scan1_t(const SsmPrefillArgs& a, hipStream_t stream, Timing tm) {
 
 bool ssm_single_pass(int batch, int d_inner) {
   // the single-pass form's waves (64 channels x 4 states of one sequence
-  // each) fill the chip on their own: at least two per SIMD of a 256-CU device
-  return (int64_t)batch * ((d_inner + 31) / 32) >= 1024;
+  // each) fill the chip on their own: about one per SIMD of a 256-CU device
+  // or more. Measured on 4224-row sequences of 3200 channels (prefill step):
+  // the chunked form is faster at batch 2 and 4 (0.38 / 0.73 ms against
+  // 0.70 / 0.78), the single pass from batch 6 on (0.97 / 1.15 / 1.38 ms
+  // against 1.01 / 1.25 / 1.59 at batch 6 / 8 / 10)
+  return (int64_t)batch * ((d_inner + 31) / 32) >= 512;
 }
 
 int ssm_prefill_chunk_rows(int batch, int L, int d_inner) {

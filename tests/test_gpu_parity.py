@@ -173,6 +173,8 @@ SINGLE_PASS = [
     dict(batch=32, n_meta=5, n_tokens=60, d_inner=1024, n_q_heads=8, n_kv_heads=2, window=16, act="bf16", seed=71),
     dict(batch=40, n_meta=3, n_tokens=27, d_inner=1024, n_q_heads=16, n_kv_heads=4, window=0, act="f32", seed=72),
     dict(batch=12, n_meta=8, n_tokens=1, d_inner=3200, n_q_heads=25, n_kv_heads=5, window=4, act="bf16", seed=73),
+    # just over the batch threshold (6 x 100 channel pairs of 32: about one wave per SIMD)
+    dict(batch=6, n_meta=4, n_tokens=40, d_inner=3200, n_q_heads=25, n_kv_heads=5, window=16, act="bf16", seed=76),
     # 800 channels: the last 64-channel block of a row holds 32 channels
     dict(batch=42, n_meta=4, n_tokens=13, d_inner=800, n_q_heads=25, n_kv_heads=5, window=8, act="bf16", seed=74),
 ]
